@@ -1,0 +1,297 @@
+"""Pins for the fp64 oracle against facts fixed outside it.
+
+Each ``check_*`` helper raises AssertionError on a mismatch; the tests call them
+as they are, and tests/test_oracle_mutations.py calls them against oracles with
+planted mistakes to show that each mistake is caught.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import workloads as W
+from oracle import rtp_oracle as O
+from oracle import accept as A
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def _bits(x):
+    return W.f32_to_bf16_bits(np.asarray(x, np.float32))
+
+
+# ------------------------------------------------------------------ index (a1-a3)
+def check_index_worked():
+    g = _gold("index_worked.json")
+    Wq = np.zeros((16, 128), np.float32)
+    for i in range(16):
+        Wq[i, 8 * i] = 1.0
+    q = np.array([(k % 7) - 3 for k in range(128)], np.float32)
+    qi = O.index_query(_bits(Wq), _bits(q))
+    assert np.array_equal(qi, np.array(g["q_idx"], np.float64))
+    n = g["n_tokens"]
+    K = np.zeros((n, 16), np.float32)
+    K[np.arange(n), np.arange(n) % 16] = 1.0
+    s = O.index_scores(qi, _bits(K))
+    assert np.array_equal(s, np.array([g["q_idx"][t % 16] for t in range(n)], np.float64))
+
+
+def check_block_mass_worked():
+    g = _gold("block_mass_worked.json")
+    s = np.log(np.array(g["scores_ln_of"], np.float64))
+    m = O.block_masses(s, g["block"])
+    want = np.array(g["mass_numerators"], np.float64) / g["mass_denominator"]
+    assert m.shape == want.shape
+    assert np.allclose(m, want, rtol=0, atol=1e-15)
+    for c in g["selections"]:
+        sel = O.select_top_p(m, c["p"])
+        assert sel.blocks.tolist() == c["blocks"], (c, sel.blocks)
+        assert abs(sel.tau - c["tau_num"] / g["mass_denominator"]) < 1e-15
+
+
+def check_tie_break_worked():
+    g = _gold("tie_break_worked.json")
+    for case in g["cases"]:
+        s = np.log(np.array(case["scores_ln_of"], np.float64))
+        m = O.block_masses(s, case["block"])
+        want = np.array(case["mass_numerators"], np.float64) / case["mass_denominator"]
+        assert np.allclose(m, want, rtol=0, atol=1e-15)
+        for c in case["selections"]:
+            assert O.select_top_p(m, c["p"]).blocks.tolist() == c["blocks"], c
+
+
+def check_mass_vs_library():
+    g = np.random.default_rng(5)
+    for n, bk in ((1, 64), (63, 64), (64, 64), (1000, 64), (777, 128)):
+        s = g.standard_normal(n) * 4.0
+        m = O.block_masses(s, bk)
+        assert m.shape[0] == -(-n // bk)
+        assert abs(m.sum() - 1.0) < 1e-12
+        lse = scipy.special.logsumexp(s)
+        for j in range(m.shape[0]):
+            blk = s[j * bk:(j + 1) * bk]
+            assert abs(m[j] - math.exp(scipy.special.logsumexp(blk) - lse)) < 1e-12
+        ref = torch.softmax(torch.from_numpy(s), dim=0).numpy()
+        assert np.allclose(O.token_softmax(s), ref, rtol=0, atol=1e-15)
+
+
+# ------------------------------------------------------------- selection (a4-a5)
+def _greedy_python(m, p):
+    """Independent greedy: pure-Python sort and running sum."""
+    order = sorted(range(len(m)), key=lambda j: (-m[j], j))
+    if p >= 1.0:
+        return sorted(order)
+    tot = 0.0
+    out = []
+    for j in order:
+        out.append(j)
+        tot += m[j]
+        if tot >= p:
+            break
+    return sorted(out)
+
+
+def check_selection_bruteforce(trials=300, seed=7):
+    g = np.random.default_rng(seed)
+    for t in range(trials):
+        n = int(g.integers(1, 13))
+        if t % 3 == 0:
+            m = g.dirichlet(np.ones(n) * 0.3)
+        elif t % 3 == 1:
+            m = g.integers(1, 4, size=n).astype(np.float64)   # many exact ties
+            m /= m.sum()
+        else:
+            m = g.dirichlet(np.ones(n) * 3.0)
+        p = float(g.choice([0.3, 0.5, 0.8, 0.9, 0.95, 0.99, float(g.uniform(0.05, 0.999))]))
+        # keep p off exact subset sums (those crossings are pinned by the golden tie cases)
+        p += 3.3e-7
+        sel = O.select_top_p(m, p)
+        assert sel.blocks.tolist() == _greedy_python(m.tolist(), p)
+        # exhaustive: the oracle set has the fewest blocks among all subsets reaching p,
+        # and the largest mass among subsets of that size
+        best_k, best_mass = None, -1.0
+        for k in range(1, n + 1):
+            for sub in itertools.combinations(range(n), k):
+                ms = sum(m[list(sub)])
+                if ms >= p - 1e-12:
+                    best_mass = max(best_mass, ms)
+            if best_mass >= 0:
+                best_k = k
+                break
+        assert sel.k_star == best_k, (m, p, sel.k_star, best_k)
+        assert abs(m[sel.blocks].sum() - best_mass) < 1e-12
+        # coverage and minimality invariants
+        tot = m[sel.blocks].sum()
+        assert tot >= p - 1e-12
+        assert tot - m[sel.blocks].min() < p
+
+
+def check_p_one_selects_all():
+    g = np.random.default_rng(8)
+    m = g.dirichlet(np.ones(50))
+    m[3] = 0.0
+    assert O.select_top_p(m, 1.0).blocks.tolist() == list(range(50))
+
+
+def check_dominant_needle():
+    cfg = W.custom_config(B=1, Hkv=1, Hq=4, n_ret=2, ctx=(2048,), kind="depth_needles",
+                          top_p=(0.9, 0.95))
+    inp = W.make_inputs(cfg)
+    for r in range(2):
+        res = O.retrieval_head(inp, 0, r)
+        need = inp.needles[(0, r)]
+        # one dominant needle block per depth; three depths -> three equal blocks
+        assert res.selection.blocks.tolist() == sorted(need)
+    cfg1 = W.custom_config(B=2, Hkv=2, Hq=4, n_ret=2, ctx=(3000, 1500), kind="peaked_diffuse",
+                           top_p=(0.95, 0.95))
+    inp1 = W.make_inputs(cfg1)
+    for (b, r), pk in inp1.peaked.items():
+        if pk:
+            res = O.retrieval_head(inp1, b, r)
+            assert res.selection.blocks.tolist() == inp1.needles[(b, r)]
+            assert res.masses[inp1.needles[(b, r)][0]] > 0.95
+
+
+# ------------------------------------------------------------ attention (a6-a8)
+def _sdpa(q, K, V):
+    qt = torch.from_numpy(O.bf16_to_f64(q))[None, None, None, :]
+    kt = torch.from_numpy(O.bf16_to_f64(K))[None, None]
+    vt = torch.from_numpy(O.bf16_to_f64(V))[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)[0, 0, 0].numpy()
+
+
+def check_attention_vs_sdpa():
+    g = np.random.default_rng(9)
+    for n in (1, 5, 64, 300):
+        q = _bits(g.standard_normal(128))
+        K = _bits(g.standard_normal((n, 128)) * 1.5)
+        V = _bits(g.standard_normal((n, 128)))
+        o, lse = O.attend(q, K, V, np.arange(n))
+        assert np.allclose(o, _sdpa(q, K, V), rtol=0, atol=1e-12)
+        logits = O.bf16_to_f64(K) @ O.bf16_to_f64(q) / math.sqrt(128)
+        assert abs(lse - scipy.special.logsumexp(logits)) < 1e-11
+        sub = np.array(sorted(g.choice(n, size=max(1, n // 2), replace=False)))
+        o2, _ = O.attend(q, K, V, sub)
+        assert np.allclose(o2, _sdpa(q, K[sub], V[sub]), rtol=0, atol=1e-12)
+
+
+def check_attention_closed_forms():
+    g = np.random.default_rng(10)
+    V = _bits(g.standard_normal((6, 128)))
+    q = _bits(g.standard_normal(128))
+    K = _bits(g.standard_normal((6, 128)))
+    o, _ = O.attend(q, K, V, np.array([4]))
+    assert np.array_equal(o, O.bf16_to_f64(V[4]))            # single token -> its value
+    Ks = np.tile(K[2], (6, 1))
+    o, lse = O.attend(q, Ks, V, np.arange(6))
+    assert np.allclose(o, O.bf16_to_f64(V).mean(axis=0), rtol=0, atol=1e-15)   # equal keys -> mean
+    # a key 64 * 64 / sqrt(128) below the others carries no weight: uniform over the rest
+    q1 = np.zeros(128, np.float32); q1[0] = 64.0
+    K1 = np.zeros((3, 128), np.float32); K1[2, 0] = -64.0
+    o, lse = O.attend(_bits(q1), _bits(K1), V[:3], np.arange(3))
+    assert np.allclose(o, (O.bf16_to_f64(V[0]) + O.bf16_to_f64(V[1])) / 2, rtol=0, atol=1e-15)
+    assert abs(lse - math.log(2.0)) < 1e-15
+    o, lse = O.attend(q, K, V, np.array([], np.int64))
+    assert lse == float("-inf") and not o.any()
+
+
+def check_merge_is_union():
+    g = np.random.default_rng(11)
+    n = 500
+    q = _bits(g.standard_normal(128))
+    K = _bits(g.standard_normal((n, 128)))
+    V = _bits(g.standard_normal((n, 128)))
+    full, lse_full = O.attend(q, K, V, np.arange(n))
+    cuts = [0, 17, 17, 200, 333, n]            # includes an empty part
+    parts = [O.attend(q, K, V, np.arange(a, b)) for a, b in zip(cuts[:-1], cuts[1:])]
+    o, L = O.merge_partials(np.stack([p[0] for p in parts]), np.array([p[1] for p in parts]))
+    assert np.allclose(o, full, rtol=0, atol=1e-13)
+    assert abs(L - lse_full) < 1e-12
+
+
+def check_local_tokens_worked():
+    g = _gold("local_window_worked.json")
+    for c in g["cases"]:
+        t = O.local_tokens(c["N"], c["W"], c["S"])
+        if "tokens" in c:
+            assert t.tolist() == c["tokens"], c
+        else:
+            assert t.size == c["tokens_count"] and t[:5].tolist() == c["first"] and t[-1] == c["last"]
+    rng = np.random.default_rng(12)
+    for _ in range(200):       # brute-force predicate
+        n = int(rng.integers(1, 40)); w = int(rng.integers(0, 45)); s = int(rng.integers(0, 8))
+        want = [t for t in range(n) if t < s or t >= n - w]
+        assert O.local_tokens(n, w, s).tolist() == want
+
+
+def check_local_reduces_to_dense():
+    cfg = W.custom_config(B=1, Hkv=1, Hq=4, n_ret=1, ctx=(300,), window=296, sinks=4)
+    inp = W.make_inputs(cfg)
+    h = int(inp.loc_heads[0])
+    assert np.array_equal(O.local_head(inp, 0, h).out, O.dense_head(inp, 0, h).out)
+    cfg2 = W.custom_config(B=1, Hkv=1, Hq=4, n_ret=1, ctx=(300,), window=1, sinks=0)
+    inp2 = W.make_inputs(cfg2)
+    h = int(inp2.loc_heads[0])
+    assert np.array_equal(O.local_head(inp2, 0, h).out, O.bf16_to_f64(inp2.v_cache[0, 0, 299]))
+
+
+def check_p_one_is_dense():
+    cfg = W.custom_config(B=1, Hkv=2, Hq=4, n_ret=2, ctx=(1500,), top_p=(1.0, 1.0), kind="peaked_diffuse")
+    inp = W.make_inputs(cfg)
+    for r in range(2):
+        res = O.retrieval_head(inp, 0, r)
+        dn = O.dense_head(inp, 0, int(inp.ret_heads[r]))
+        assert np.array_equal(res.out, dn.out)
+        kv = int(inp.ret_heads[r]) // 2
+        assert np.allclose(dn.out, _sdpa(inp.q[0, inp.ret_heads[r]], inp.k_cache[0, kv, :1500],
+                                         inp.v_cache[0, kv, :1500]), rtol=0, atol=1e-12)
+
+
+def check_gqa_mapping():
+    # retrieval head uses its own index cache and its KV group's K/V
+    cfg = W.custom_config(B=1, Hkv=2, Hq=8, n_ret=2, ctx=(256,), ret_heads=(1, 6), top_p=(1.0, 1.0))
+    inp = W.make_inputs(cfg)
+    res = O.retrieval_head(inp, 0, 1)
+    assert np.allclose(res.out, _sdpa(inp.q[0, 6], inp.k_cache[0, 1, :256], inp.v_cache[0, 1, :256]),
+                       rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------ acceptance
+def check_acceptance_rule():
+    m = np.array([0.3, 0.3, 0.2, 0.1, 0.1])
+    sel = O.select_top_p(m, 0.75)              # 0.3, 0.3, 0.2 -> {0, 1, 2}
+    assert A.accept_selection(m, 0.75, [0, 1, 2], sel)[0]
+    assert not A.accept_selection(m, 0.75, [0, 1], sel)[0]          # R1/R3
+    assert not A.accept_selection(m, 0.75, [0, 1, 2, 3], sel)[0]    # R2/R4
+    # equal needles: dropping one violates R3 even though its mass equals tau
+    m2 = np.array([0.49, 0.49, 0.02])
+    assert A.accept_selection(m2, 0.9, [0, 1])[0]
+    assert not A.accept_selection(m2, 0.9, [0, 2])[0]
+    # ambiguous crossing within eps: one more block is acceptable
+    m3 = np.array([0.5, 0.4000000001, 0.0999999999])
+    assert A.accept_selection(m3, 0.9, [0, 1])[0]
+    assert A.accept_selection(m3, 0.9, [0, 1, 2])[0]
+    assert A.accept_selection(m, 1.0, [0, 1, 2, 3, 4])[0]
+    assert not A.accept_selection(m, 1.0, [0, 1, 2, 3])[0]
+
+
+CHECKS = [check_index_worked, check_block_mass_worked, check_tie_break_worked, check_mass_vs_library,
+          check_selection_bruteforce, check_p_one_selects_all, check_dominant_needle,
+          check_attention_vs_sdpa, check_attention_closed_forms, check_merge_is_union,
+          check_local_tokens_worked, check_local_reduces_to_dense, check_p_one_is_dense,
+          check_gqa_mapping, check_acceptance_rule]
+
+
+@pytest.mark.parametrize("check", CHECKS, ids=[c.__name__ for c in CHECKS])
+def test_pin(check):
+    check()
