@@ -1,0 +1,182 @@
+/*
+ * rtp.h - C ABI of the MI355X (gfx950) decode-time sparse attention library
+ * (librtp.so): RTPurbo's retrieval-head indexer with exact block top-p, block-sparse
+ * split attention with a cross-split log-sum-exp reduce, and the local heads'
+ * sliding-window + sink attention.
+ *
+ * Sources (page title, section):
+ *   Review        - the Korean paper review of RTPurbo (dongryeollee1.github.io),
+ *                   "Method": "Adaptive sparse attention" (index score equation
+ *                   s_h(m,n) = (W^Q_h q^pre)^T (W^K_h k^pre), S_h(m) = Top-P(s_h, p);
+ *                   window + sink for local heads) and "Hardware-aware top-p decoding
+ *                   kernel" (block-wise top-p, 256-bin histogram, last CTA finds the
+ *                   threshold and writes the block mask, score and select fused).
+ *   Strikes-Back  - "Full Attention Strikes Back: Transferring Full Attention into
+ *                   Sparse within Hundred Training Steps" (aitrends.kr): method item 2
+ *                   (O_h(m), a softmax of q.k/sqrt(d_h) over S_h(m)) and the
+ *                   architecture paragraph (Kernel 1 at D16: per-block scoring and
+ *                   histogram threshold; Kernel 2 at D128: block-sparse attention and a
+ *                   cross-split reduce; atomic counters).
+ *
+ * Conventions shared by every call:
+ *   - Fixed sizes: head_dim 128 (RTP_HEAD_DIM), index dim 16 (RTP_INDEX_DIM),
+ *     KV block 64 or 128 tokens, query heads per KV head (Hq / Hkv) in {1, 2, 4, 8}.
+ *   - Every tensor argument is a DEVICE pointer owned by the caller, contiguous,
+ *     row-major, with the layout given at each argument.  bf16 tensors are passed as
+ *     const void* (raw bf16 bits).  The library allocates nothing and keeps no global
+ *     mutable state; it is reentrant for disjoint workspaces.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Each call
+ *     checks its scalar arguments on the host (no device access, no synchronization),
+ *     then enqueues its kernels on `stream` and returns.  Buffers must stay alive until
+ *     the stream has passed the call.
+ *   - Device-resident values (seq_lens, head lists, top_p) are preconditions and are
+ *     not checked: 1 <= seq_lens[b] <= max_ctx, head ids in [0, Hq) and ascending, the
+ *     retrieval and local lists disjoint, 0 < top_p.  Violations are undefined
+ *     behaviour (a device fault surfaces at the caller's next synchronization).
+ *   - Workspaces must be zero-filled once before their first use; the kernels return
+ *     every counter in them to zero, so a workspace can be reused by later calls on
+ *     the same stream.  Calls that share a workspace must not overlap.
+ *   - Return codes: RTP_OK; RTP_EINVAL for a null pointer, a non-positive size, an
+ *     inconsistent shape or a workspace that is too small; RTP_EUNSUPPORTED for a block
+ *     size or head grouping outside the fixed set; RTP_ELAUNCH when HIP reports a
+ *     launch error.  On any error nothing is enqueued, except for RTP_ELAUNCH.
+ *   - n_ret == 0 (resp. n_loc == 0, n_heads == 0) is a no-op returning RTP_OK.
+ */
+#ifndef RTP_H_
+#define RTP_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RTP_HEAD_DIM 128
+#define RTP_INDEX_DIM 16
+
+typedef enum {
+  RTP_OK = 0,
+  RTP_EINVAL = 1,
+  RTP_EUNSUPPORTED = 2,
+  RTP_ELAUNCH = 3
+} rtp_status;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* rtp_status_string(int status);
+
+/* Library version string, e.g. "rtp 1.0 gfx950". */
+const char* rtp_version(void);
+
+/* Bytes of workspace rtp_index_topp needs for these sizes (0 if a size is invalid). */
+size_t rtp_index_topp_workspace_size(int B, int n_ret, int max_ctx, int block);
+
+/*
+ * Kernel 1: low-rank index scoring + exact block top-p selection
+ * (Review, Adaptive sparse attention equation and Hardware-aware top-p decoding
+ * kernel; Strikes-Back architecture paragraph, Kernel 1 at D16).
+ *
+ * For each sequence b and retrieval head r (query head hq = ret_heads[r]):
+ *   q_idx   = W^Q_r q_pre[b, hq]                          (fp64 on the device)
+ *   s_n     = q_idx . k_idx[b, r, n]        for n < N = seq_lens[b]
+ *   m_j     = sum_{n in block j} softmax_n(s)             (block j = tokens [j*block, (j+1)*block) ∩ [0, N))
+ *   S       = the shortest prefix of the blocks ordered by m_j descending (ties by
+ *             ascending j) whose cumulative mass reaches top_p[b, r]; every block
+ *             when top_p >= 1 or no prefix reaches it.
+ * The threshold is found exactly by a mass-weighted radix select over 256-bin LDS
+ * histograms run by the last workgroup of each (b, r) to finish scoring (found with
+ * an atomic counter), so scoring and selection are one launch.  Block masses carry
+ * a relative error below 1e-6 against exact arithmetic.
+ *
+ *   q_pre     bf16 [B, Hq, 128]        pre-RoPE queries (rows ret_heads[] are read)
+ *   w_q       bf16 [n_ret, 16, 128]    W^Q of each retrieval head
+ *   k_idx     bf16 [B, n_ret, max_ctx, 16]  index keys W^K_r k_pre (rows >= N never read)
+ *   seq_lens  int32 [B]                 N_b, 1 <= N_b <= max_ctx
+ *   ret_heads int32 [n_ret]             query-head id of each retrieval head, ascending
+ *   top_p     fp32 [B, n_ret]           0 < p; p >= 1 selects every block
+ *   sel_idx   out int32 [B, n_ret, ceil(max_ctx / block)]  selected block ids,
+ *             ascending, in the first sel_cnt[b, r] entries (the rest untouched)
+ *   sel_cnt   out int32 [B, n_ret]      number of selected blocks (>= 1)
+ *   workspace device scratch of >= rtp_index_topp_workspace_size(B, n_ret, max_ctx, block)
+ *             bytes, zero-filled before first use
+ */
+rtp_status rtp_index_topp(const void* q_pre, const void* w_q, const void* k_idx,
+                          const int* seq_lens, const int* ret_heads, const float* top_p,
+                          int B, int Hq, int n_ret, int max_ctx, int block,
+                          int* sel_idx, int* sel_cnt,
+                          void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Kernel 2: block-sparse exact attention over the selected blocks, split along the
+ * context (Strikes-Back method item 2, O_h(m) with the value vector; architecture
+ * paragraph, Kernel 2 at D128).
+ *
+ * For each sequence b, retrieval head r (query head hq, KV head g = hq / (Hq/Hkv))
+ * and context split c (blocks [c*split_tokens/block, (c+1)*split_tokens/block)):
+ *   T_c = tokens n < N of the blocks in sel_idx[b, r, :sel_cnt[b, r]] that fall in c
+ *   o_part[b, r, c]   = sum_{n in T_c} softmax_n(q[b,hq] . K[b,g,n] / sqrt(128)) V[b,g,n]
+ *   lse_part[b, r, c] = log sum_{n in T_c} exp(q[b,hq] . K[b,g,n] / sqrt(128))
+ * with o = 0 and lse = -inf for an empty T_c.  One workgroup serves every retrieval
+ * head of a KV group, so a block selected by several heads of the group is read once.
+ *
+ *   q          bf16 [B, Hq, 128]        queries (post-RoPE)
+ *   k_cache    bf16 [B, Hkv, max_ctx, 128]
+ *   v_cache    bf16 [B, Hkv, max_ctx, 128]
+ *   seq_lens, ret_heads as in rtp_index_topp
+ *   sel_idx, sel_cnt    as written by rtp_index_topp for the same B, n_ret, max_ctx, block
+ *   split_tokens  multiple of block; split_tokens / block <= 2048
+ *   o_part     out fp32 [B, n_ret, n_split, 128], n_split = ceil(max_ctx / split_tokens)
+ *   lse_part   out fp32 [B, n_ret, n_split]
+ */
+rtp_status rtp_sparse_attn_split(const void* q, const void* k_cache, const void* v_cache,
+                                 const int* seq_lens, const int* ret_heads,
+                                 const int* sel_idx, const int* sel_cnt,
+                                 int B, int Hq, int Hkv, int n_ret, int max_ctx, int block,
+                                 int split_tokens, float* o_part, float* lse_part, void* stream);
+
+/*
+ * Cross-split log-sum-exp reduce (Strikes-Back architecture paragraph):
+ *   L = log sum_c exp(lse_part[b, i, c]);  out[b, heads[i]] = sum_c exp(lse_c - L) o_part[b, i, c]
+ * Splits with lse = -inf carry weight 0; a row whose splits are all empty is written 0.
+ *
+ *   o_part    fp32 [B, n_heads, n_split, 128]
+ *   lse_part  fp32 [B, n_heads, n_split]
+ *   heads     int32 [n_heads]   query-head id of partial row i
+ *   out       out fp32 [B, Hq, 128]; only rows heads[] are written
+ */
+rtp_status rtp_split_reduce(const float* o_part, const float* lse_part, const int* heads,
+                            int B, int Hq, int n_heads, int n_split, float* out, void* stream);
+
+/* Bytes of workspace rtp_local_window_attn needs (0 if a size is invalid). */
+size_t rtp_local_window_workspace_size(int B, int Hq, int Hkv, int n_loc, int max_ctx,
+                                       int window, int sinks);
+
+/*
+ * Local heads: exact attention over attention sinks + a sliding window
+ * (Review, Adaptive sparse attention: local heads keep a window and sinks; Review,
+ * Experiments: sink 4, window 8192).
+ *
+ * For each sequence b and local head hq = loc_heads[i] (KV head g = hq / (Hq/Hkv)):
+ *   T = [0, min(sinks, N)) union [max(0, N - window), N)   (no token counted twice)
+ *   out[b, hq] = sum_{n in T} softmax_n(q[b,hq] . K[b,g,n] / sqrt(128)) V[b,g,n]
+ * The window is split across workgroups (one per KV group and split, serving every
+ * local head of the group); the last workgroup of each (b, g) merges the splits.
+ *
+ *   q, k_cache, v_cache, seq_lens as in rtp_sparse_attn_split
+ *   loc_heads int32 [n_loc]  query-head ids of the local heads, ascending
+ *   window >= 0, sinks >= 0, window + sinks >= 1
+ *   out       out fp32 [B, Hq, 128]; only rows loc_heads[] are written
+ *   workspace >= rtp_local_window_workspace_size(B, Hq, Hkv, n_loc, max_ctx, window, sinks)
+ *             bytes,
+ *             zero-filled before first use
+ */
+rtp_status rtp_local_window_attn(const void* q, const void* k_cache, const void* v_cache,
+                                 const int* seq_lens, const int* loc_heads,
+                                 int B, int Hq, int Hkv, int n_loc, int max_ctx,
+                                 int window, int sinks, float* out,
+                                 void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RTP_H_ */

@@ -1,0 +1,135 @@
+"""Thin ctypes binding of librtp.so (see include/rtp.h).
+
+Argument marshalling only: every function passes raw device pointers, sizes and
+the current HIP stream to the C ABI of the same name and raises on a non-zero
+status.  PyTorch provides device memory and streams; all computation runs in the
+HIP kernels of librtp.so.  A missing library raises at first use.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librtp.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "rtp.h")
+
+RTP_OK, RTP_EINVAL, RTP_EUNSUPPORTED, RTP_ELAUNCH = 0, 1, 2, 3
+
+_lib = None
+
+
+class RTPError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+
+
+_vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+_SIGS = {
+    "rtp_status_string": ([_i], ctypes.c_char_p),
+    "rtp_version": ([], ctypes.c_char_p),
+    "rtp_index_topp_workspace_size": ([_i, _i, _i, _i], _sz),
+    "rtp_index_topp": ([_vp] * 6 + [_i] * 5 + [_vp, _vp, _vp, _sz, _vp], _i),
+    "rtp_sparse_attn_split": ([_vp] * 7 + [_i] * 7 + [_vp, _vp, _vp], _i),
+    "rtp_split_reduce": ([_vp] * 3 + [_i] * 4 + [_vp, _vp], _i),
+    "rtp_local_window_workspace_size": ([_i] * 7, _sz),
+    "rtp_local_window_attn": ([_vp] * 5 + [_i] * 7 + [_vp, _vp, _sz, _vp], _i),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load librtp.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m long_context_sparse_amd.build` (or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def declared_functions() -> list:
+    """Names of the functions include/rtp.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rtp_[a-z0-9_]+)\s*\(", text)))
+
+
+def status_string(status: int) -> str:
+    return lib().rtp_status_string(int(status)).decode()
+
+
+def version() -> str:
+    return lib().rtp_version().decode()
+
+
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("librtp arguments must be contiguous device tensors")
+    return t.data_ptr()
+
+
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _s(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(fn: str, st: int) -> None:
+    if st != RTP_OK:
+        raise RTPError(fn, st)
+
+
+def rtp_index_topp_workspace_size(B: int, n_ret: int, max_ctx: int, block: int) -> int:
+    return int(lib().rtp_index_topp_workspace_size(B, n_ret, max_ctx, block))
+
+
+def rtp_local_window_workspace_size(B: int, Hq: int, Hkv: int, n_loc: int, max_ctx: int,
+                                    window: int, sinks: int) -> int:
+    return int(lib().rtp_local_window_workspace_size(B, Hq, Hkv, n_loc, max_ctx, window, sinks))
+
+
+def rtp_index_topp(q_pre, w_q, k_idx, seq_lens, ret_heads, top_p, B, Hq, n_ret, max_ctx, block,
+                   sel_idx, sel_cnt, workspace, stream=None) -> None:
+    st = lib().rtp_index_topp(_p(q_pre), _p(w_q), _p(k_idx), _p(seq_lens), _p(ret_heads), _p(top_p),
+                              B, Hq, n_ret, max_ctx, block, _p(sel_idx), _p(sel_cnt), _p(workspace),
+                              _nbytes(workspace), _s(stream))
+    _check("rtp_index_topp", st)
+
+
+def rtp_sparse_attn_split(q, k_cache, v_cache, seq_lens, ret_heads, sel_idx, sel_cnt, B, Hq, Hkv,
+                          n_ret, max_ctx, block, split_tokens, o_part, lse_part, stream=None) -> None:
+    st = lib().rtp_sparse_attn_split(_p(q), _p(k_cache), _p(v_cache), _p(seq_lens), _p(ret_heads),
+                                     _p(sel_idx), _p(sel_cnt), B, Hq, Hkv, n_ret, max_ctx, block,
+                                     split_tokens, _p(o_part), _p(lse_part), _s(stream))
+    _check("rtp_sparse_attn_split", st)
+
+
+def rtp_split_reduce(o_part, lse_part, heads, B, Hq, n_heads, n_split, out, stream=None) -> None:
+    st = lib().rtp_split_reduce(_p(o_part), _p(lse_part), _p(heads), B, Hq, n_heads, n_split, _p(out),
+                                _s(stream))
+    _check("rtp_split_reduce", st)
+
+
+def rtp_local_window_attn(q, k_cache, v_cache, seq_lens, loc_heads, B, Hq, Hkv, n_loc, max_ctx,
+                          window, sinks, out, workspace, stream=None) -> None:
+    st = lib().rtp_local_window_attn(_p(q), _p(k_cache), _p(v_cache), _p(seq_lens), _p(loc_heads), B, Hq,
+                                     Hkv, n_loc, max_ctx, window, sinks, _p(out), _p(workspace),
+                                     _nbytes(workspace), _s(stream))
+    _check("rtp_local_window_attn", st)

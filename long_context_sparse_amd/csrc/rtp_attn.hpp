@@ -1,0 +1,208 @@
+// Decode attention core shared by the block-sparse split kernel and the local
+// window kernel: one wave64 streams 16-token sub-tiles of one KV head's K and V
+// (bf16, head_dim 128) and keeps an online softmax for up to G query heads of the
+// KV group, so every K/V byte is read once for all heads that need it.
+//
+// Lane layout of a 16-token sub-tile (4 KB of K, 4 KB of V): one 16-byte load per
+// lane covers 4 consecutive rows (1 KB contiguous); lane l holds dims
+// 8*(l & 15) .. +8 of rows 4*i + (l >> 4), i = 0..3.  A query-key dot product is a
+// packed bf16 dot (v_dot2) per dword, then a 16-lane transpose-reduce leaves lane l
+// with the full logit of row 4*((l >> 2) & 3) + (l >> 4) (4 replicas).  Softmax
+// statistics are kept in the base-2 domain.
+#pragma once
+
+#include "rtp_common.hpp"
+
+namespace rtp {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+template <int G>
+struct AttnState {
+  float m[G];       // running max (log2 domain), wave-uniform
+  float l[G];       // per-lane partial denominators (one replica of each row counted)
+  float acc[G][8];  // per-lane partial numerators for this lane's 8 dims
+};
+
+template <int G>
+__device__ __forceinline__ void attn_init(AttnState<G>& s) {
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    s.m[h] = -INFINITY;
+    s.l[h] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s.acc[h][k] = 0.f;
+  }
+}
+
+struct SubTile {
+  uint4 k[4], v[4];
+};
+
+// Loads rows [row0, row0 + 16) of kg/vg (row stride 128); rows at or beyond row_end
+// are never read and come back as zeros.
+__device__ __forceinline__ void load_subtile(SubTile& t, const uint16_t* __restrict__ kg,
+                                             const uint16_t* __restrict__ vg, int row0, int row_end,
+                                             int lane) {
+  const int R = lane >> 4, c16 = lane & 15;
+  const bool full = row0 + 16 <= row_end;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = row0 + 4 * i + R;
+    const bool ok = full || row < row_end;
+    const size_t off = (size_t)row * kHeadDim + c16 * 8;
+    t.k[i] = ok ? ld16(kg + off) : make_uint4(0, 0, 0, 0);
+    t.v[i] = ok ? ld16(vg + off) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+// Online-softmax update with one loaded sub-tile.  Rows at or beyond row_end are
+// masked; hmask picks the heads (bit h) that attend to these rows and must be 0 unless
+// row0 < row_end.  qk[h] holds head h's 8 query dims of this lane.
+template <int G>
+__device__ __forceinline__ void attn_subtile(AttnState<G>& s, const SubTile& t, int row0,
+                                             int row_end, uint32_t hmask, const uint4 (&qk)[G],
+                                             float scale_log2, int lane) {
+  const int R = lane >> 4;
+  const int isel = (lane >> 2) & 3;
+  const bool myvalid = row0 + 4 * isel + R < row_end;
+  const bool b3 = (lane >> 3) & 1, b2 = (lane >> 2) & 1;
+  const bool counted = (lane & 3) == 0;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    if (!((hmask >> h) & 1u)) continue;
+    float part[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float a = dot2(t.k[i].x, qk[h].x, 0.f);
+      a = dot2(t.k[i].y, qk[h].y, a);
+      a = dot2(t.k[i].z, qk[h].z, a);
+      part[i] = dot2(t.k[i].w, qk[h].w, a);
+    }
+    // transpose-reduce over the 16 lanes that share R
+    const float x0 = b3 ? part[0] : part[2];
+    const float x1 = b3 ? part[1] : part[3];
+    const float y0 = __shfl_xor(x0, 8);
+    const float y1 = __shfl_xor(x1, 8);
+    const float k0 = (b3 ? part[2] : part[0]) + y0;
+    const float k1 = (b3 ? part[3] : part[1]) + y1;
+    const float xs = b2 ? k0 : k1;
+    float v = (b2 ? k1 : k0) + __shfl_xor(xs, 4);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 1);
+    const float lg = myvalid ? v * scale_log2 : -INFINITY;
+    const float mnew = fmaxf(s.m[h], wave_maxf(lg));
+    const float alpha = fast_exp2(s.m[h] - mnew);
+    const float p = fast_exp2(lg - mnew);
+    s.l[h] = s.l[h] * alpha + (counted ? p : 0.f);
+    s.m[h] = mnew;
+    float pi[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pi[i] = __shfl(p, (lane & 0x30) | (i << 2));
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s.acc[h][k] *= alpha;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s.acc[h][0] = fmaf(pi[i], bf_lo(t.v[i].x), s.acc[h][0]);
+      s.acc[h][1] = fmaf(pi[i], bf_hi(t.v[i].x), s.acc[h][1]);
+      s.acc[h][2] = fmaf(pi[i], bf_lo(t.v[i].y), s.acc[h][2]);
+      s.acc[h][3] = fmaf(pi[i], bf_hi(t.v[i].y), s.acc[h][3]);
+      s.acc[h][4] = fmaf(pi[i], bf_lo(t.v[i].z), s.acc[h][4]);
+      s.acc[h][5] = fmaf(pi[i], bf_hi(t.v[i].z), s.acc[h][5]);
+      s.acc[h][6] = fmaf(pi[i], bf_lo(t.v[i].w), s.acc[h][6]);
+      s.acc[h][7] = fmaf(pi[i], bf_hi(t.v[i].w), s.acc[h][7]);
+    }
+  }
+}
+
+// Streams this wave's items i = wave, wave + WAVES, ... through attn_subtile with the
+// next item's loads in flight while the current one is computed.  item(i, row0, hmask)
+// gives the first row and the head mask of item i (hmask 0 skips it).
+template <int G, int WAVES, class ItemFn>
+__device__ __forceinline__ void attn_stream(AttnState<G>& s, const uint16_t* __restrict__ kg,
+                                            const uint16_t* __restrict__ vg, int nitems, int row_end,
+                                            ItemFn item, const uint4 (&qk)[G], float scale_log2,
+                                            int wave, int lane) {
+  int i = wave;
+  if (i >= nitems) return;
+  SubTile cur;
+  int row0;
+  uint32_t hm;
+  item(i, row0, hm);
+  load_subtile(cur, kg, vg, row0, hm ? row_end : row0, lane);
+  while (true) {
+    const int i2 = i + WAVES;
+    const bool more = i2 < nitems;
+    SubTile nxt;
+    int row2 = 0;
+    uint32_t hm2 = 0;
+    if (more) {
+      item(i2, row2, hm2);
+      load_subtile(nxt, kg, vg, row2, hm2 ? row_end : row2, lane);
+    }
+    attn_subtile<G>(s, cur, row0, row_end, hm, qk, scale_log2, lane);
+    if (!more) break;
+    cur = nxt;
+    row0 = row2;
+    hm = hm2;
+    i = i2;
+  }
+}
+
+// Combine the per-lane state of every wave of the workgroup through LDS and leave,
+// for head h and dim d, the normalised output and the natural-log LSE.
+// sm/sl: [waves][G]; sacc: [waves][G][128].
+template <int G, int WAVES>
+__device__ __forceinline__ void attn_publish_wave(const AttnState<G>& s, float* sm, float* sl,
+                                                  float* sacc, int wave, int lane) {
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float lt = wave_sumf(s.l[h]);
+    float a[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      float v = s.acc[h][k];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      a[k] = v;
+    }
+    if (lane < 16) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sacc[(wave * G + h) * kHeadDim + lane * 8 + k] = a[k];
+    }
+    if (lane == 0) {
+      sm[wave * G + h] = s.m[h];
+      sl[wave * G + h] = lt;
+    }
+  }
+}
+
+// After a barrier: merged (o[d], lse) of head h from the WAVES published states.
+template <int G, int WAVES>
+__device__ __forceinline__ void attn_merge(const float* sm, const float* sl, const float* sacc,
+                                           int h, int d, float& o, float& lse) {
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < WAVES; ++w) M = fmaxf(M, sm[w * G + h]);
+  if (M == -INFINITY) {
+    o = 0.f;
+    lse = -INFINITY;
+    return;
+  }
+  float L = 0.f, A = 0.f;
+#pragma unroll
+  for (int w = 0; w < WAVES; ++w) {
+    const float f = fast_exp2(sm[w * G + h] - M);
+    L = fmaf(sl[w * G + h], f, L);
+    A = fmaf(sacc[(w * G + h) * kHeadDim + d], f, A);
+  }
+  o = A / L;
+  lse = (M + __log2f(L)) * kLn2f;
+}
+
+}  // namespace rtp

@@ -1,0 +1,397 @@
+// Kernel 2 of the decode path and the local heads' kernel.
+//
+// Kernel 2: exact softmax(q K^T / sqrt(128)) V over only the blocks the index kernel
+// selected, split along the context ("Full Attention Strikes Back", method item 2 and
+// architecture paragraph: Kernel 2 at D128 with a cross-split reduce).  Workgroup =
+// (split, KV group, sequence); it builds the union of its retrieval heads' selected
+// blocks inside the split (binary search into each ascending list, LDS head-mask per
+// block, ordered compaction), so a block picked by several heads of the group is read
+// from HBM once, then streams the union's 16-token sub-tiles through the shared
+// attention core and writes per-head (o, lse) partials.
+//
+// Local heads: the same core over attention sinks + the sliding window (RTPurbo
+// review, Adaptive sparse attention: local heads keep only window + sinks).
+// Workgroup = (split, KV group, sequence); split 0 holds the sinks, splits 1.. hold
+// consecutive window chunks.  Each workgroup writes per-head partials to the
+// workspace; the last one of each (sequence, KV group), found with an atomic counter,
+// merges them with the log-sum-exp rule and writes the output rows.
+
+#include "rtp_attn.hpp"
+
+namespace rtp {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kMaxSplitBlocks = 2048;
+
+__device__ __forceinline__ int lower_bound_dev(const int* __restrict__ a, int n, int key) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] < key) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// contiguous range [beg, end) of an ascending head list that falls in KV group g
+__device__ __forceinline__ void group_range(const int* __restrict__ heads, int n, int g, int G,
+                                            int& beg, int& end) {
+  beg = lower_bound_dev(heads, n, g * G);
+  end = lower_bound_dev(heads, n, (g + 1) * G);
+}
+
+template <int BK, int G>
+__global__ __launch_bounds__(kThreads) void sparse_attn_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const int* __restrict__ seq_lens, const int* __restrict__ ret_heads,
+    const int* __restrict__ sel_idx, const int* __restrict__ sel_cnt, int Hq, int Hkv, int n_ret,
+    int max_ctx, int nblk_max, int split_blocks, int n_split, float* __restrict__ o_part,
+    float* __restrict__ lse_part) {
+  constexpr int ST = BK / 16;  // sub-tiles per block
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int rbeg, rend;
+  group_range(ret_heads, n_ret, g, G, rbeg, rend);
+  const int nh = rend - rbeg;
+  if (nh == 0) return;
+  const int N = seq_lens[b];
+  const int nblk = (N + BK - 1) / BK;
+  const int jlo = c * split_blocks, jhi = min(jlo + split_blocks, nblk);
+
+  __shared__ uint32_t s_hm[kMaxSplitBlocks / 4];
+  __shared__ uint32_t s_list[kMaxSplitBlocks];
+  __shared__ int s_wcnt[kWaves];
+  __shared__ float s_m[kWaves * G], s_l[kWaves * G];
+  __shared__ float s_acc[kWaves * G * kHeadDim];
+
+  int nL = 0;
+  if (jlo < jhi) {
+    const int nb = jhi - jlo;
+    for (int i = tid; i < (nb + 3) / 4; i += kThreads) s_hm[i] = 0;
+    __syncthreads();
+    for (int h = 0; h < nh; ++h) {
+      const size_t hr = (size_t)b * n_ret + rbeg + h;
+      const int cnt = sel_cnt[hr];
+      const int* sl = sel_idx + hr * nblk_max;
+      const int a = lower_bound_dev(sl, cnt, jlo);
+      const int e = lower_bound_dev(sl, cnt, jhi);
+      for (int i = a + tid; i < e; i += kThreads) {
+        const int off = sl[i] - jlo;
+        atomicOr(&s_hm[off >> 2], (1u << h) << ((off & 3) * 8));
+      }
+    }
+    __syncthreads();
+    // ordered compaction of the blocks some head selected: entry = (offset << 8) | mask
+    const int seg = ((nb + kWaves - 1) / kWaves + 63) / 64 * 64;
+    const int sb = wave * seg, se = min(nb, sb + seg);
+    int cnt = 0;
+    for (int base = sb; base < se; base += 64) {
+      const int off = base + lane;
+      const uint32_t mk = off < se ? (s_hm[off >> 2] >> ((off & 3) * 8)) & 0xffu : 0u;
+      cnt += __popcll(__ballot(mk != 0));
+    }
+    if (lane == 0) s_wcnt[wave] = cnt;
+    __syncthreads();
+    int pos = 0;
+    for (int w = 0; w < wave; ++w) pos += s_wcnt[w];
+    for (int base = sb; base < se; base += 64) {
+      const int off = base + lane;
+      const uint32_t mk = off < se ? (s_hm[off >> 2] >> ((off & 3) * 8)) & 0xffu : 0u;
+      const uint64_t bal = __ballot(mk != 0);
+      if (mk) s_list[pos + __popcll(bal & lanemask_lt())] = ((uint32_t)off << 8) | mk;
+      pos += __popcll(bal);
+    }
+    __syncthreads();
+    for (int w = 0; w < kWaves; ++w) nL += s_wcnt[w];
+  }
+
+  AttnState<G> st;
+  attn_init(st);
+  uint4 qk[G];
+  const int c16 = lane & 15;
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    qk[h] = h < nh ? ld16(q + ((size_t)b * Hq + ret_heads[rbeg + h]) * kHeadDim + c16 * 8)
+                   : make_uint4(0, 0, 0, 0);
+  const size_t kvoff = ((size_t)b * Hkv + g) * (size_t)max_ctx * kHeadDim;
+  const float scale = (float)(kLog2e / 11.313708498984761);  // log2(e) / sqrt(128)
+  auto item = [&](int i, int& row0, uint32_t& hm) {
+    const uint32_t ent = s_list[i / ST];
+    row0 = (jlo + (int)(ent >> 8)) * BK + 16 * (i % ST);
+    hm = row0 < N ? (ent & 0xffu) : 0u;
+  };
+  attn_stream<G, kWaves>(st, kc + kvoff, vc + kvoff, nL * ST, N, item, qk, scale, wave, lane);
+  attn_publish_wave<G, kWaves>(st, s_m, s_l, s_acc, wave, lane);
+  __syncthreads();
+  for (int idx = tid; idx < nh * kHeadDim; idx += kThreads) {
+    const int h = idx >> 7, d = idx & (kHeadDim - 1);
+    float o, lse;
+    attn_merge<G, kWaves>(s_m, s_l, s_acc, h, d, o, lse);
+    const size_t hr = (size_t)b * n_ret + rbeg + h;
+    o_part[(hr * n_split + c) * kHeadDim + d] = o;
+    if (d == 0) lse_part[hr * n_split + c] = lse;
+  }
+}
+
+template <int G>
+__global__ __launch_bounds__(kThreads) void local_window_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const int* __restrict__ seq_lens, const int* __restrict__ loc_heads, int Hq, int Hkv, int n_loc,
+    int max_ctx, int window, int sinks, int split_tokens, int n_split, float* __restrict__ out,
+    int* __restrict__ counters, float* __restrict__ ws_lse, float* __restrict__ ws_o) {
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int ibeg, iend;
+  group_range(loc_heads, n_loc, g, G, ibeg, iend);
+  const int nh = iend - ibeg;
+  if (nh == 0) return;
+  const int N = seq_lens[b];
+  const int s_end = min(sinks, N);
+  const int w0 = max(s_end, N - window);
+  int t0, t1;
+  if (c == 0) {
+    t0 = 0;
+    t1 = s_end;
+  } else {
+    t0 = w0 + (c - 1) * split_tokens;
+    t1 = min(N, t0 + split_tokens);
+  }
+  const int nitems = t1 > t0 ? (t1 - t0 + 15) / 16 : 0;
+
+  __shared__ float s_m[kWaves * G], s_l[kWaves * G];
+  __shared__ float s_acc[kWaves * G * kHeadDim];
+  __shared__ int s_flag;
+
+  AttnState<G> st;
+  attn_init(st);
+  uint4 qk[G];
+  const int c16 = lane & 15;
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    qk[h] = h < nh ? ld16(q + ((size_t)b * Hq + loc_heads[ibeg + h]) * kHeadDim + c16 * 8)
+                   : make_uint4(0, 0, 0, 0);
+  const size_t kvoff = ((size_t)b * Hkv + g) * (size_t)max_ctx * kHeadDim;
+  const float scale = (float)(kLog2e / 11.313708498984761);
+  const uint32_t allh = (1u << nh) - 1u;
+  auto item = [&](int i, int& row0, uint32_t& hm) {
+    row0 = t0 + 16 * i;
+    hm = allh;
+  };
+  attn_stream<G, kWaves>(st, kc + kvoff, vc + kvoff, nitems, t1, item, qk, scale, wave, lane);
+  attn_publish_wave<G, kWaves>(st, s_m, s_l, s_acc, wave, lane);
+  __syncthreads();
+  for (int idx = tid; idx < nh * kHeadDim; idx += kThreads) {
+    const int h = idx >> 7, d = idx & (kHeadDim - 1);
+    float o, lse;
+    attn_merge<G, kWaves>(s_m, s_l, s_acc, h, d, o, lse);
+    const size_t hr = (size_t)b * n_loc + ibeg + h;
+    ws_o[(hr * n_split + c) * kHeadDim + d] = o;
+    if (d == 0) ws_lse[hr * n_split + c] = lse;
+  }
+  __syncthreads();
+  const size_t grp = (size_t)b * Hkv + g;
+  if (tid == 0) {
+    __threadfence();  // release the partials device-wide
+    const int prev = atomicAdd(&counters[grp], 1);
+    s_flag = prev == n_split - 1;
+    if (s_flag) __threadfence();  // acquire every split's partials
+  }
+  __syncthreads();
+  if (!s_flag) return;
+  for (int idx = tid; idx < nh * kHeadDim; idx += kThreads) {
+    const int h = idx >> 7, d = idx & (kHeadDim - 1);
+    const size_t hr = (size_t)b * n_loc + ibeg + h;
+    const float* lp = ws_lse + hr * n_split;
+    const float* op = ws_o + hr * n_split * kHeadDim + d;
+    float M = -INFINITY;
+    for (int s = 0; s < n_split; ++s) M = fmaxf(M, lp[s]);
+    float L = 0.f, A = 0.f;
+    if (M != -INFINITY) {
+      for (int s = 0; s < n_split; ++s) {
+        const float w = __expf(lp[s] - M);
+        L += w;
+        A = fmaf(w, op[(size_t)s * kHeadDim], A);
+      }
+    }
+    out[((size_t)b * Hq + loc_heads[ibeg + h]) * kHeadDim + d] = L > 0.f ? A / L : 0.f;
+  }
+  if (tid == 0) counters[grp] = 0;  // ready for the next call
+}
+
+__global__ __launch_bounds__(kHeadDim) void split_reduce_kernel(
+    const float* __restrict__ o_part, const float* __restrict__ lse_part,
+    const int* __restrict__ heads, int Hq, int n_heads, int n_split, float* __restrict__ out) {
+  const int i = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const size_t hr = (size_t)b * n_heads + i;
+  const float* lp = lse_part + hr * n_split;
+  const float* op = o_part + hr * n_split * kHeadDim + d;
+  float M = -INFINITY;
+  for (int s = 0; s < n_split; ++s) M = fmaxf(M, lp[s]);
+  float L = 0.f, A = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < n_split; ++s) {
+      const float w = __expf(lp[s] - M);
+      L += w;
+      A = fmaf(w, op[(size_t)s * kHeadDim], A);
+    }
+  }
+  out[((size_t)b * Hq + heads[i]) * kHeadDim + d] = L > 0.f ? A / L : 0.f;
+}
+
+struct LocalLayout {
+  int split_tokens, n_split;
+  size_t off_counters, off_lse, off_o, total;
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Window split: >= ~1024 workgroups over the batch, 64..4096 tokens a split.
+LocalLayout local_layout(int B, int Hkv, int n_loc, int window) {
+  LocalLayout L{};
+  const long long groups = (long long)B * Hkv;
+  int st = 4096;
+  while (st > 64 && groups * ceil_div(max(window, 1), st) < 1024) st >>= 1;
+  L.split_tokens = st;
+  L.n_split = 1 + ceil_div(window, st);
+  L.off_counters = 0;
+  L.off_lse = align256((size_t)groups * sizeof(int));
+  L.off_o = L.off_lse + align256((size_t)B * n_loc * L.n_split * sizeof(float));
+  L.total = L.off_o + align256((size_t)B * n_loc * L.n_split * kHeadDim * sizeof(float));
+  return L;
+}
+
+inline bool group_ok(int Hq, int Hkv) {
+  if (Hkv <= 0 || Hq % Hkv) return false;
+  const int G = Hq / Hkv;
+  return G == 1 || G == 2 || G == 4 || G == 8;
+}
+
+template <int BK>
+void launch_sparse(int G, dim3 grid, hipStream_t s, const uint16_t* q, const uint16_t* k,
+                   const uint16_t* v, const int* sl, const int* rh, const int* si, const int* sc,
+                   int Hq, int Hkv, int n_ret, int max_ctx, int nblk_max, int sb, int n_split,
+                   float* op, float* lp) {
+#define RTP_SPARSE(GG)                                                                        \
+  hipLaunchKernelGGL((sparse_attn_kernel<BK, GG>), grid, dim3(kThreads), 0, s, q, k, v, sl, rh, \
+                     si, sc, Hq, Hkv, n_ret, max_ctx, nblk_max, sb, n_split, op, lp)
+  switch (G) {
+    case 1: RTP_SPARSE(1); break;
+    case 2: RTP_SPARSE(2); break;
+    case 4: RTP_SPARSE(4); break;
+    default: RTP_SPARSE(8); break;
+  }
+#undef RTP_SPARSE
+}
+
+}  // namespace
+}  // namespace rtp
+
+using namespace rtp;
+
+extern "C" rtp_status rtp_sparse_attn_split(const void* q, const void* k_cache, const void* v_cache,
+                                            const int* seq_lens, const int* ret_heads,
+                                            const int* sel_idx, const int* sel_cnt, int B, int Hq,
+                                            int Hkv, int n_ret, int max_ctx, int block,
+                                            int split_tokens, float* o_part, float* lse_part,
+                                            void* stream) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || n_ret < 0 || n_ret > Hq || max_ctx <= 0) return RTP_EINVAL;
+  if (Hq % Hkv) return RTP_EINVAL;
+  if (!group_ok(Hq, Hkv)) return RTP_EUNSUPPORTED;
+  if (block != 64 && block != 128) return RTP_EUNSUPPORTED;
+  if (split_tokens <= 0 || split_tokens % block) return RTP_EINVAL;
+  if (split_tokens / block > kMaxSplitBlocks) return RTP_EUNSUPPORTED;
+  if (n_ret == 0) return RTP_OK;
+  if (!q || !k_cache || !v_cache || !seq_lens || !ret_heads || !sel_idx || !sel_cnt || !o_part ||
+      !lse_part)
+    return RTP_EINVAL;
+  if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache) & 15) return RTP_EINVAL;
+  const int nblk_max = ceil_div(max_ctx, block);
+  const int sb = split_tokens / block;
+  const int n_split = ceil_div(max_ctx, split_tokens);
+  if (n_split > 65535) return RTP_EUNSUPPORTED;
+  dim3 grid(n_split, Hkv, B);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint16_t* kk = static_cast<const uint16_t*>(k_cache);
+  const uint16_t* vv = static_cast<const uint16_t*>(v_cache);
+  const int G = Hq / Hkv;
+  if (block == 64)
+    launch_sparse<64>(G, grid, s, qq, kk, vv, seq_lens, ret_heads, sel_idx, sel_cnt, Hq, Hkv, n_ret,
+                      max_ctx, nblk_max, sb, n_split, o_part, lse_part);
+  else
+    launch_sparse<128>(G, grid, s, qq, kk, vv, seq_lens, ret_heads, sel_idx, sel_cnt, Hq, Hkv,
+                       n_ret, max_ctx, nblk_max, sb, n_split, o_part, lse_part);
+  return hipGetLastError() == hipSuccess ? RTP_OK : RTP_ELAUNCH;
+}
+
+extern "C" rtp_status rtp_split_reduce(const float* o_part, const float* lse_part, const int* heads,
+                                       int B, int Hq, int n_heads, int n_split, float* out,
+                                       void* stream) {
+  if (B <= 0 || Hq <= 0 || n_heads < 0 || n_heads > Hq || n_split <= 0) return RTP_EINVAL;
+  if (n_heads == 0) return RTP_OK;
+  if (!o_part || !lse_part || !heads || !out) return RTP_EINVAL;
+  if (B > 65535) return RTP_EUNSUPPORTED;
+  hipLaunchKernelGGL(split_reduce_kernel, dim3(n_heads, B), dim3(kHeadDim), 0,
+                     static_cast<hipStream_t>(stream), o_part, lse_part, heads, Hq, n_heads, n_split,
+                     out);
+  return hipGetLastError() == hipSuccess ? RTP_OK : RTP_ELAUNCH;
+}
+
+extern "C" size_t rtp_local_window_workspace_size(int B, int Hq, int Hkv, int n_loc, int max_ctx,
+                                                  int window, int sinks) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || n_loc <= 0 || n_loc > Hq || max_ctx <= 0 || window < 0 ||
+      sinks < 0 || window + sinks < 1 || Hq % Hkv)
+    return 0;
+  return local_layout(B, Hkv, n_loc, window < max_ctx ? window : max_ctx).total;
+}
+
+extern "C" rtp_status rtp_local_window_attn(const void* q, const void* k_cache, const void* v_cache,
+                                            const int* seq_lens, const int* loc_heads, int B, int Hq,
+                                            int Hkv, int n_loc, int max_ctx, int window, int sinks,
+                                            float* out, void* workspace, size_t ws_bytes,
+                                            void* stream) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || n_loc < 0 || n_loc > Hq || max_ctx <= 0) return RTP_EINVAL;
+  if (Hq % Hkv || window < 0 || sinks < 0 || window + sinks < 1) return RTP_EINVAL;
+  if (!group_ok(Hq, Hkv)) return RTP_EUNSUPPORTED;
+  if (n_loc == 0) return RTP_OK;
+  if (!q || !k_cache || !v_cache || !seq_lens || !loc_heads || !out || !workspace) return RTP_EINVAL;
+  if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache) & 15) return RTP_EINVAL;
+  if ((uintptr_t)workspace & 255) return RTP_EINVAL;
+  const LocalLayout L = local_layout(B, Hkv, n_loc, window < max_ctx ? window : max_ctx);
+  if (ws_bytes < L.total) return RTP_EINVAL;
+  if (L.n_split > 65535) return RTP_EUNSUPPORTED;
+  char* ws = static_cast<char*>(workspace);
+  int* counters = reinterpret_cast<int*>(ws + L.off_counters);
+  float* ws_lse = reinterpret_cast<float*>(ws + L.off_lse);
+  float* ws_o = reinterpret_cast<float*>(ws + L.off_o);
+  dim3 grid(L.n_split, Hkv, B);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint16_t* kk = static_cast<const uint16_t*>(k_cache);
+  const uint16_t* vv = static_cast<const uint16_t*>(v_cache);
+#define RTP_LOCAL(GG)                                                                         \
+  hipLaunchKernelGGL(local_window_kernel<GG>, grid, dim3(kThreads), 0, s, qq, kk, vv, seq_lens, \
+                     loc_heads, Hq, Hkv, n_loc, max_ctx, window, sinks, L.split_tokens,          \
+                     L.n_split, out, counters, ws_lse, ws_o)
+  switch (Hq / Hkv) {
+    case 1: RTP_LOCAL(1); break;
+    case 2: RTP_LOCAL(2); break;
+    case 4: RTP_LOCAL(4); break;
+    default: RTP_LOCAL(8); break;
+  }
+#undef RTP_LOCAL
+  return hipGetLastError() == hipSuccess ? RTP_OK : RTP_ELAUNCH;
+}
+
+extern "C" const char* rtp_status_string(int status) {
+  switch (status) {
+    case RTP_OK: return "RTP_OK";
+    case RTP_EINVAL: return "RTP_EINVAL: invalid argument";
+    case RTP_EUNSUPPORTED: return "RTP_EUNSUPPORTED: size outside the supported set";
+    case RTP_ELAUNCH: return "RTP_ELAUNCH: kernel launch failed";
+    default: return "RTP_UNKNOWN";
+  }
+}
+
+extern "C" const char* rtp_version(void) { return "rtp 1.0 gfx950"; }

@@ -1,0 +1,94 @@
+"""Host side of the C ABI: the library loads, exports every declared symbol, and
+rejects bad arguments with the documented status before touching a device."""
+import ctypes
+
+import pytest
+
+from long_context_sparse_amd import abi
+
+FAKE = 4096  # a non-null, 256-aligned stand-in pointer; never dereferenced on these paths
+
+
+def test_exports_every_declared_symbol():
+    L = abi.lib()
+    names = abi.declared_functions()
+    assert {"rtp_index_topp", "rtp_sparse_attn_split", "rtp_split_reduce", "rtp_local_window_attn"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version():
+    assert abi.status_string(0) == "RTP_OK"
+    assert "EINVAL" in abi.status_string(1)
+    assert "EUNSUPPORTED" in abi.status_string(2)
+    assert "ELAUNCH" in abi.status_string(3)
+    assert "gfx950" in abi.version()
+
+
+def test_workspace_sizes():
+    s = abi.rtp_index_topp_workspace_size(4, 8, 131072, 64)
+    assert s >= 4 * 8 * 2048 * 8          # one fp64 per block at least
+    assert abi.rtp_index_topp_workspace_size(4, 8, 131072, 32) == 0
+    assert abi.rtp_index_topp_workspace_size(0, 8, 131072, 64) == 0
+    assert abi.rtp_local_window_workspace_size(4, 32, 8, 24, 131072, 8192, 4) > 0
+    assert abi.rtp_local_window_workspace_size(4, 32, 8, 24, 131072, 0, 0) == 0
+
+
+def _topp(**kw):
+    a = dict(q_pre=FAKE, w_q=FAKE, k_idx=FAKE, seq_lens=FAKE, ret_heads=FAKE, top_p=FAKE, B=1, Hq=4,
+             n_ret=2, max_ctx=1024, block=64, sel_idx=FAKE, sel_cnt=FAKE, ws=FAKE, ws_bytes=0, stream=None)
+    a.update(kw)
+    if a["ws_bytes"] == 0 and "ws_bytes" not in kw:
+        a["ws_bytes"] = abi.rtp_index_topp_workspace_size(a["B"], a["n_ret"], a["max_ctx"], a["block"]) - 1
+    return abi.lib().rtp_index_topp(a["q_pre"], a["w_q"], a["k_idx"], a["seq_lens"], a["ret_heads"], a["top_p"],
+                                    a["B"], a["Hq"], a["n_ret"], a["max_ctx"], a["block"], a["sel_idx"],
+                                    a["sel_cnt"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_index_topp_rejects():
+    assert _topp() == abi.RTP_EINVAL                    # workspace one byte short
+    assert _topp(block=32) == abi.RTP_EUNSUPPORTED
+    assert _topp(block=256) == abi.RTP_EUNSUPPORTED
+    assert _topp(B=0) == abi.RTP_EINVAL
+    assert _topp(n_ret=5) == abi.RTP_EINVAL             # more retrieval heads than heads
+    assert _topp(max_ctx=0) == abi.RTP_EINVAL
+    assert _topp(q_pre=None, ws_bytes=1 << 30) == abi.RTP_EINVAL
+    assert _topp(k_idx=FAKE + 2, ws_bytes=1 << 30) == abi.RTP_EINVAL   # misaligned
+    assert _topp(ws=FAKE + 16, ws_bytes=1 << 30) == abi.RTP_EINVAL    # workspace not 256-aligned
+    assert _topp(n_ret=0) == abi.RTP_OK                 # no-op
+
+
+def _sparse(**kw):
+    a = dict(B=1, Hq=8, Hkv=2, n_ret=2, max_ctx=4096, block=64, split=1024)
+    a.update(kw)
+    ptr = kw.get("ptr", FAKE)
+    return abi.lib().rtp_sparse_attn_split(ptr, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["B"], a["Hq"], a["Hkv"],
+                                           a["n_ret"], a["max_ctx"], a["block"], a["split"], FAKE, FAKE, None)
+
+
+def test_sparse_attn_rejects():
+    assert _sparse(split=100) == abi.RTP_EINVAL           # not a multiple of the block
+    assert _sparse(split=0) == abi.RTP_EINVAL
+    assert _sparse(block=96) == abi.RTP_EUNSUPPORTED
+    assert _sparse(Hq=8, Hkv=3) == abi.RTP_EINVAL         # heads not divisible
+    assert _sparse(Hq=48, Hkv=2) == abi.RTP_EUNSUPPORTED  # 24 query heads per KV head
+    assert _sparse(split=64 * 4096) == abi.RTP_EUNSUPPORTED
+    assert _sparse(ptr=None) == abi.RTP_EINVAL
+    assert _sparse(n_ret=0) == abi.RTP_OK
+
+
+def test_reduce_and_local_reject():
+    L = abi.lib()
+    assert L.rtp_split_reduce(FAKE, FAKE, FAKE, 1, 4, 5, 2, FAKE, None) == abi.RTP_EINVAL
+    assert L.rtp_split_reduce(FAKE, FAKE, FAKE, 1, 4, 2, 0, FAKE, None) == abi.RTP_EINVAL
+    assert L.rtp_split_reduce(None, FAKE, FAKE, 1, 4, 2, 2, FAKE, None) == abi.RTP_EINVAL
+    assert L.rtp_split_reduce(FAKE, FAKE, FAKE, 1, 4, 0, 2, FAKE, None) == abi.RTP_OK
+    ws = abi.rtp_local_window_workspace_size(1, 8, 2, 6, 4096, 1024, 4)
+    assert L.rtp_local_window_attn(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 6, 4096, 1024, 4, FAKE, FAKE,
+                                   ws - 1, None) == abi.RTP_EINVAL
+    assert L.rtp_local_window_attn(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 6, 4096, 0, 0, FAKE, FAKE,
+                                   1 << 30, None) == abi.RTP_EINVAL
+    assert L.rtp_local_window_attn(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 6, 4096, -1, 4, FAKE, FAKE,
+                                   1 << 30, None) == abi.RTP_EINVAL
+    assert L.rtp_local_window_attn(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 0, 4096, 16, 4, FAKE, FAKE,
+                                   0, None) == abi.RTP_OK

@@ -330,3 +330,22 @@ def custom_config(name: str = "custom", **kw) -> DecodeConfig:
     base["ctx"] = tuple(int(v) for v in base["ctx"])
     base["top_p"] = tuple(float(v) for v in base["top_p"])
     return DecodeConfig(name=name, **base)
+
+
+def to_device(inp: DecodeInputs, device="cuda") -> Dict[str, "object"]:
+    """Upload the inputs as torch tensors (bf16 tensors keep their bit patterns)."""
+    import torch
+
+    def bf(a: np.ndarray):
+        return torch.from_numpy(np.ascontiguousarray(a)).view(torch.bfloat16).to(device)
+
+    def i32(a: np.ndarray):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+
+    q = bf(inp.q)
+    return {
+        "q": q, "q_pre": q, "w_q": bf(inp.w_q), "k_idx": bf(inp.k_idx),
+        "k_cache": bf(inp.k_cache), "v_cache": bf(inp.v_cache),
+        "seq_lens": i32(inp.seq_lens), "ret_heads": i32(inp.ret_heads), "loc_heads": i32(inp.loc_heads),
+        "top_p": torch.from_numpy(np.ascontiguousarray(inp.top_p, dtype=np.float32)).to(device),
+    }
