@@ -1,0 +1,329 @@
+"""Decode-step benchmark of the sparse attention path on one MI355X.
+
+One step = the whole hot path for one decode token of every sequence and query
+head of a workload: rtp_index_topp -> rtp_sparse_attn_split -> rtp_split_reduce for
+the retrieval heads, rtp_local_window_attn (second stream) for the local heads.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ctx128k] [--also ctx1m]
+
+Prints ONE JSON line.  `value` is the effective HBM bandwidth of the step,
+algorithmic bytes / step latency, with every input resident in HBM before the
+timed region.  Algorithmic bytes are what the method must move (index keys of
+every cached token of every retrieval head, K/V rows of the union of selected
+tokens and window/sink tokens per KV head, queries, projections, outputs),
+counted from the block sets the device selected; scratch traffic (block LSEs,
+split partials) is excluded.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+from typing import Dict, List, Optional
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sparse-decode step latency (µs) + effective HBM GB/s at 128K and 1M ctx"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, vendor figure
+KERNEL_NAMES = {
+    "index_topp": "index_topp_kernel",
+    "sparse_attn": "sparse_attn_kernel",
+    "split_reduce": "split_reduce_kernel",
+    "local_window": "local_window_kernel",
+}
+
+
+def log(*a) -> None:
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ algorithmic bytes
+def block_token_mask(blocks: np.ndarray, block: int, n: int) -> np.ndarray:
+    m = np.zeros(n, dtype=bool)
+    for j in blocks.tolist():
+        m[j * block:min(n, (j + 1) * block)] = True
+    return m
+
+
+def local_token_mask(n: int, window: int, sinks: int) -> np.ndarray:
+    m = np.zeros(n, dtype=bool)
+    m[:min(sinks, n)] = True
+    m[max(0, n - window):n] = True
+    return m
+
+
+def algorithmic_bytes(cfg, inp, sel_idx: np.ndarray, sel_cnt: np.ndarray) -> Dict[str, float]:
+    """Bytes each call (and the whole step) must move for the given block selection.
+
+    index_topp:   W^Q (4 KiB a retrieval head) + 32 B per cached token per retrieval
+                  head (16 bf16 index dims) + the q_pre row + the selected-block list.
+    sparse_attn:  512 B (K and V rows, 128 bf16 each) per (KV head, token) in the union
+                  of the group's retrieval heads' selected blocks + the q rows.
+    split_reduce: the fp32 output rows of the retrieval heads.
+    local_window: 512 B per (KV head, token) in sinks + window for groups holding local
+                  heads + q rows + fp32 output rows.
+    step:         the sum, with K/V counted once per (KV head, token) over the union of
+                  both token sets.
+    """
+    G = cfg.Hq // cfg.Hkv
+    ret = [int(h) for h in inp.ret_heads]
+    loc = [int(h) for h in inp.loc_heads]
+    out = dict(index_topp=0.0, sparse_attn=0.0, split_reduce=0.0, local_window=0.0, step=0.0)
+    out["index_topp"] += len(ret) * 16 * 128 * 2
+    kv_step = 0
+    for b in range(cfg.B):
+        n = int(inp.seq_lens[b])
+        for r in range(len(ret)):
+            cnt = int(sel_cnt[b, r])
+            out["index_topp"] += 32.0 * n + 256 + 4 * cnt + 4
+            out["sparse_attn"] += 256
+            out["split_reduce"] += 512
+        for h in loc:
+            out["local_window"] += 256 + 512
+        for g in range(cfg.Hkv):
+            rs = [r for r, h in enumerate(ret) if h // G == g]
+            has_loc = any(h // G == g for h in loc)
+            sel = np.zeros(n, dtype=bool)
+            for r in rs:
+                sel |= block_token_mask(sel_idx[b, r, :int(sel_cnt[b, r])], cfg.block, n)
+            win = local_token_mask(n, cfg.window, cfg.sinks) if has_loc else np.zeros(n, dtype=bool)
+            out["sparse_attn"] += 512.0 * int(sel.sum())
+            out["local_window"] += 512.0 * int(win.sum())
+            kv_step += int((sel | win).sum())
+    kv_sep = (out["sparse_attn"] + out["local_window"]) - 256 * cfg.B * len(ret) - 768 * cfg.B * len(loc)
+    out["step"] = (out["index_topp"] + out["sparse_attn"] + out["split_reduce"] + out["local_window"]
+                   - kv_sep + 512.0 * kv_step)
+    out["kv_tokens_selected"] = float(sum(int(sel_cnt[b, r]) for b in range(cfg.B) for r in range(len(ret))))
+    return out
+
+
+# ------------------------------------------------------------------ traffic records
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "long_context_sparse_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode())
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str, kernel: str) -> Optional[float]:
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None
+    when there is none or it was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{KERNEL_NAMES.get(kernel, kernel)}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ":" in line:
+                k, v = line[2:].split(":", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_sources_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------------ GPU measurement
+def measure(name: str, steps: int, warmup: int, cold_iters: int, calib_copy: bool) -> Dict:
+    import torch
+
+    import workloads as W
+    from long_context_sparse_amd import DecodeStep, StepShape
+
+    cfg = W.get_config(name)
+    t0 = time.time()
+    inp = W.make_inputs(cfg)
+    log(f"[bench] {name}: inputs built in {time.time() - t0:.1f}s")
+    dev = torch.device("cuda:0")
+    t = W.to_device(inp, dev)
+    shape = StepShape(B=cfg.B, Hq=cfg.Hq, Hkv=cfg.Hkv, n_ret=cfg.n_ret, n_loc=cfg.n_loc, max_ctx=cfg.max_ctx,
+                      block=cfg.block, split_tokens=cfg.split_tokens, window=cfg.window, sinks=cfg.sinks)
+    step = DecodeStep(shape, device=dev)
+    step(t)
+    torch.cuda.synchronize()
+    sel_idx = step.sel_idx.cpu().numpy()
+    sel_cnt = step.sel_cnt.cpu().numpy()
+    alg = algorithmic_bytes(cfg, inp, sel_idx, sel_cnt)
+
+    # timed region: `steps` back-to-back decode steps, inputs resident in HBM
+    main = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        step(t)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    ev0.record(main)
+    for _ in range(steps):
+        step(t)
+    ev1.record(main)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_per_step = ev0.elapsed_time(ev1) / steps
+    log(f"[bench] {name}: {steps} steps, {ms_per_step * 1e3:.1f} us/step (wall {wall * 1e3 / steps:.1f} us/step)")
+
+    # per-call durations: the four calls one after another on the main stream, with
+    # events around each call on that stream
+    calls = [("index_topp", step.index_topp), ("sparse_attn", step.sparse_attn),
+             ("split_reduce", step.reduce), ("local_window", step.local)]
+    calls = [(k, f) for k, f in calls if (cfg.n_ret if k != "local_window" else cfg.n_loc)]
+    per = {k: [] for k, _ in calls}
+    iters = max(steps, 20)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(iters)]
+    for it in range(iters):
+        evs[it][0].record(main)
+        for i, (k, f) in enumerate(calls):
+            f(t, main)
+            evs[it][i + 1].record(main)
+    torch.cuda.synchronize()
+    for it in range(iters):
+        for i, (k, _) in enumerate(calls):
+            per[k].append(evs[it][i].elapsed_time(evs[it][i + 1]) * 1e3)
+    kern_us = {k: float(np.mean(v)) for k, v in per.items()}
+
+    # cold caches: a 1 GiB write evicts L2 and the 256 MB last-level cache before each step
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cold = []
+    for _ in range(cold_iters):
+        flush.fill_(1.0)
+        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(main)
+        step(t)
+        b_.record(main)
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b_) * 1e3)
+    del flush
+
+    if calib_copy:
+        # plain device copy of known size, for scaling HBM counters (1 GiB read + 1 GiB written)
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    lat_us = ms_per_step * 1e3
+    dom = max(kern_us, key=kern_us.get)
+    res = dict(
+        workload=name, cfg=cfg, inp=inp, alg=alg, latency_us=lat_us, wall_us=wall * 1e6 / steps,
+        kern_us=kern_us, dominant=dom, cold_us=float(np.median(cold)) if cold else None,
+        gbs=alg["step"] / (lat_us * 1e-6) / 1e9,
+        sel_frac=float(np.mean([sel_cnt[b, r] / -(-int(inp.seq_lens[b]) // cfg.block)
+                                for b in range(cfg.B) for r in range(cfg.n_ret)])) if cfg.n_ret else 0.0,
+    )
+    del step, t
+    torch.cuda.empty_cache()
+    return res
+
+
+def config_of(cfg) -> Dict:
+    ctx = sorted(set(cfg.ctx))
+    return {"workload": cfg.name, "batch": cfg.B, "ctx": ctx[0] if len(ctx) == 1 else [min(ctx), max(ctx)],
+            "kv_heads": cfg.Hkv, "q_heads": cfg.Hq, "retrieval_heads": cfg.n_ret, "head_dim": 128,
+            "index_dim": 16, "block": cfg.block, "top_p": sorted(set(cfg.top_p)), "window": cfg.window,
+            "sinks": cfg.sinks, "split_tokens": cfg.split_tokens}
+
+
+def roofline_of(r: Dict) -> Dict:
+    k = r["dominant"]
+    us = r["kern_us"][k]
+    ach = r["alg"][k] / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "kernel": KERNEL_NAMES[k], "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+            "traffic": read_traffic(r["workload"], k),
+            "alg_bytes_per_launch": int(r["alg"][k]), "avg_launch_us": round(us, 2)}
+
+
+# ------------------------------------------------------------------ CPU baseline
+def cpu_baseline(r: Dict, reps: int) -> Dict:
+    """The fp64 oracle (unchanged) over the same workload on the host, one BLAS thread."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import rtp_oracle as O
+
+    inp, cfg = r["inp"], r["cfg"]
+    times = []
+    with threadpool_limits(limits=1):
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            O.decode_step(inp)
+            times.append(time.perf_counter() - t0)
+    sec = statistics.median(times)
+    return {"value": round(r["alg"]["step"] / sec / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"whole {cfg.name} step ({cfg.B} seqs x {cfg.Hq} heads), median of {reps} runs, "
+                      f"{sec:.2f} s each; GB/s = the step's algorithmic bytes / oracle time",
+            "seconds_per_step": round(sec, 3)}
+
+
+def main(argv: Optional[List[str]] = None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="ctx128k")
+    ap.add_argument("--also", default="ctx1m", help="comma-separated extra workloads ('' for none)")
+    ap.add_argument("--cold-iters", type=int, default=20)
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true", help="also run a 1 GiB device copy (counter scaling)")
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}); the path shards by sequence, "
+              "KV head or context across GPUs, which this build does not run.", file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+
+    head = measure(a.workload, a.steps, a.warmup, a.cold_iters, a.calib_copy)
+    extras = {}
+    for name in [x for x in a.also.split(",") if x and x != a.workload]:
+        extras[name] = measure(name, a.steps, a.warmup, a.cold_iters, False)
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        cpu = cpu_baseline(head, a.cpu_reps)
+
+    def summary(r):
+        return {"latency_us": round(r["latency_us"], 2), "effective_gbs": round(r["gbs"], 1),
+                "frac_of_peak": round(r["gbs"] / PEAK_HBM_GBS, 4), "alg_bytes": int(r["alg"]["step"]),
+                "cold_latency_us": None if r["cold_us"] is None else round(r["cold_us"], 2),
+                "cold_effective_gbs": None if not r["cold_us"] else round(r["alg"]["step"] / r["cold_us"] / 1e3, 1),
+                "kernel_us": {KERNEL_NAMES[k]: round(v, 2) for k, v in r["kern_us"].items()},
+                "mean_selected_block_fraction": round(r["sel_frac"], 4),
+                "roofline": roofline_of(r), "config": config_of(r["cfg"])}
+
+    line = {
+        "metric": METRIC, "value": round(head["gbs"], 1), "unit": "GB/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(head["latency_us"] / 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": config_of(head["cfg"]),
+        "latency_us": round(head["latency_us"], 2),
+        "frac_of_peak": round(head["gbs"] / PEAK_HBM_GBS, 4),
+        "roofline": roofline_of(head),
+        "cpu_baseline": cpu,
+        "detail": summary(head),
+        "also": {k: summary(v) for k, v in extras.items()},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

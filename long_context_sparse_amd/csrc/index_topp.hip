@@ -445,7 +445,7 @@ __global__ __launch_bounds__(kThreads) void index_topp_kernel(
     int total = 0;
     for (int w = 0; w < kWaves; ++w) total += s_wcnt[w];
     sel_cnt[head] = total;
-    counters[head] = 0;  // ready for the next call
+    atomicExch(&counters[head], 0);  // ready for the next call
   }
 }
 

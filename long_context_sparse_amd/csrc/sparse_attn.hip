@@ -216,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void local_window_kernel(
     }
     out[((size_t)b * Hq + loc_heads[ibeg + h]) * kHeadDim + d] = L > 0.f ? A / L : 0.f;
   }
-  if (tid == 0) counters[grp] = 0;  // ready for the next call
+  if (tid == 0) atomicExch(&counters[grp], 0);  // ready for the next call
 }
 
 __global__ __launch_bounds__(kHeadDim) void split_reduce_kernel(
