@@ -5,10 +5,10 @@
 // top-p of the score distribution, found by a histogram threshold that the last
 // workgroup computes, fused with scoring in one launch (review, Hardware-aware
 // top-p decoding kernel; "Full Attention Strikes Back" architecture paragraph:
-// Kernel 1 at D16, 256-bin histogram, atomic counters).
+// Kernel 1 at D16, histogram threshold, atomic counters).
 //
 // gfx950 design
-//   grid (chunk, retrieval head, sequence), 256 threads = 4 wave64.
+//   grid (chunk, retrieval head, sequence), 512 threads = 8 wave64.
 //   Scoring: each wave streams whole KV blocks of the 32 B/token index-key cache with
 //   16-byte loads; one load instruction covers 1 KB (32 tokens, two lanes per token).
 //   q_idx and the scores are fp64 so that block masses carry < 1e-6 relative error;
@@ -17,46 +17,51 @@
 //   and e_j = exp(lse_j - M_c) go to the workspace.
 //   Selection: the last workgroup per (b, r) (device-scope release/acquire around an
 //   atomic arrival counter, needed across the 8 XCDs' separate L2s) forms
-//   m_j = e_j exp(M_c - M) / Z, takes the order-preserving bits of m_j as the radix
-//   key (ties broken by block id, which extends the key), and runs 256-bin LDS
-//   histograms of (count, fixed-point mass) from the most significant digit down.
-//   Each pass keeps the bin where the cumulative mass crosses p; once the crossing
-//   bin holds <= 64 blocks one wave ranks them exactly.  Masses are summed as
-//   fixed-point integers (2^-62 units), so every cumulative sum is exact and the
-//   result is deterministic.  The selected ids are written in ascending order by a
-//   ballot-based ordered compaction, and the arrival counter is reset to zero.
+//   m_j = e_j exp(M_c - M) / Z for every block into LDS and finds the greedy
+//   threshold exactly: a key = (fp32 mass bits, inverted block id) orders blocks by
+//   mass with ties by ascending id; masses are summed as fixed-point integers (2^-62
+//   units) so every cumulative sum is exact and order-independent.  While more than
+//   512 candidates remain, 63 evenly spaced candidates are sorted into splitters, a
+//   64-bin LDS histogram of (count, mass) over the splitter intervals locates the
+//   interval where the cumulative mass crosses p, and that interval becomes the new
+//   candidate set; the last <= 512 candidates are ranked exactly and scanned.  The
+//   selected ids are written in ascending order by a ballot-based ordered compaction,
+//   and the arrival counter is reset to zero.
 
 #include "rtp_common.hpp"
 
 namespace rtp {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxChunkBlocks = 128;
 constexpr int kMaxChunks = 1024;
-constexpr int kMaxBlocks = 1 << 17;     // nblk limit (also bounds the tie-break key)
-constexpr int kResolve = 64;
+constexpr int kMaxRows = kThreads / kWaves;   // rows of kThreads blocks in the selection
+constexpr int kMaxBlocks = kMaxRows * kThreads;
+constexpr int kSplitters = 63;                // splitters per refinement level (64 buckets)
+constexpr int kFinal = kThreads;              // candidates ranked directly (one per thread)
 
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct K1Layout {
-  int nblk_max, chunk_blocks, chunk_shift, n_chunk;
+  int nblk_max, chunk_blocks, chunk_shift, n_chunk, rows;
   size_t off_counters, off_stats, off_e, total;
 };
 
-// Chunk size: aim for >= 2048 workgroups over the whole batch, 8..128 blocks a chunk,
+// Chunk size: aim for >= 1024 workgroups over the whole batch, 8..128 blocks a chunk,
 // at most kMaxChunks chunks per head.
 K1Layout k1_layout(int B, int n_ret, int max_ctx, int block) {
   K1Layout L{};
   L.nblk_max = ceil_div(max_ctx, block);
   long long total_blocks = (long long)B * n_ret * L.nblk_max;
   int cb = kMaxChunkBlocks;
-  while (cb > 8 && total_blocks / cb < 2048) cb >>= 1;
+  while (cb > 8 && total_blocks / cb < 1024) cb >>= 1;
   while (ceil_div(L.nblk_max, cb) > kMaxChunks && cb < kMaxChunkBlocks) cb <<= 1;
   L.chunk_blocks = cb;
   L.chunk_shift = __builtin_ctz(cb);
   L.n_chunk = ceil_div(L.nblk_max, cb);
+  L.rows = ceil_div(L.nblk_max, kThreads);
   const size_t heads = (size_t)B * n_ret;
   L.off_counters = 0;
   L.off_stats = align_up(heads * sizeof(int), 256);
@@ -65,33 +70,266 @@ K1Layout k1_layout(int B, int n_ret, int max_ctx, int block) {
   return L;
 }
 
-// Radix digits of the composite key (hi = bits of the clamped fp64 mass, whose top
-// three bits are always 001; lo = 0xFFFFFF - block id).
-__constant__ int kShift[11] = {53, 45, 37, 29, 21, 13, 5, 0, 16, 8, 0};
-__constant__ int kWidth[11] = {8, 8, 8, 8, 8, 8, 8, 5, 8, 8, 8};
+// ------------------------------------------------------------------ selection tail
+// Composite selection key of block j with fp32 mass m >= 0: the mass bits (order-
+// preserving for non-negative floats) above the inverted block id, so that keys are
+// distinct and descending key order is descending mass with ties by ascending id.
+// Key 0 marks "no block".
+__device__ __forceinline__ uint64_t key_of(float m, int j) {
+  return ((uint64_t)__float_as_uint(m) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+}
+// Mass in fixed point, 2^-62 units: integer sums are exact and order-independent.
+__device__ __forceinline__ uint64_t fixed_mass(float m) { return (uint64_t)((double)m * 0x1p62); }
 
-struct Elem {
-  uint64_t hi;
-  uint32_t lo;
-  uint64_t fm;
+struct TailSmem {
+  uint64_t samp[kSplitters];      // sampled candidate keys
+  uint64_t split[kSplitters];     // the same, sorted descending
+  uint32_t bcnt[kSplitters + 1];  // per bucket: candidate count
+  uint64_t bmass[kSplitters + 1]; // per bucket: fixed-point mass
+  int rowtab[kMaxRows * kWaves];  // per (row, wave) counts, then exclusive prefixes
+  uint64_t u64[kWaves];
+  int i32[kWaves];
+  double f64[kWaves];
+  uint64_t lo, hi, cab, thr;
+  int cnt;
 };
 
-__device__ __forceinline__ Elem make_elem(double e, double f, int j) {
-  const double m = e * f;
-  Elem x;
-  x.hi = (uint64_t)__double_as_longlong(fmax(m, 0x1p-511));
-  x.lo = 0xFFFFFFu - (uint32_t)j;
-  x.fm = (uint64_t)(m * 0x1p62);
-  return x;
-}
-
-__device__ __forceinline__ bool geq(uint64_t hi, uint32_t lo, uint64_t thi, uint32_t tlo) {
-  return hi > thi || (hi == thi && lo >= tlo);
-}
-
-__device__ __forceinline__ uint64_t shfl_up_u64(uint64_t v, int d) {
-  uint32_t a = __shfl_up((uint32_t)v, d), b = __shfl_up((uint32_t)(v >> 32), d);
+// A wave-uniform 64-bit value moved to scalar registers.
+__device__ __forceinline__ uint64_t uni64(uint64_t v) {
+  const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t b = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
   return ((uint64_t)b << 32) | a;
+}
+
+// Buffers used by one phase at a time.
+union PhaseSmem {
+  double lse[kMaxChunkBlocks];    // scoring: block lse of this chunk
+  double f[kMaxChunks];           // selection: per-chunk factors exp(M_c - M)
+  struct {
+    uint64_t ckey[kFinal], cfm[kFinal], skey[kFinal], sfm[kFinal];
+  } fin;                          // selection: final candidates
+};
+
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Sum over the workgroup; every thread gets the total.
+__device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, uint64_t* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_sum_u64(v);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  uint64_t t = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) t += red[w];
+  __syncthreads();
+  return t;
+}
+
+// Exclusive prefix sum over the workgroup in thread order; `total` gets the sum.
+template <class T>
+__device__ __forceinline__ T block_excl_scan(T v, T* red, T& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  T incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const T y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) red[wave] = incl;
+  __syncthreads();
+  T base = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    base += w < wave ? red[w] : T(0);
+    total += red[w];
+  }
+  __syncthreads();
+  return base + incl - v;
+}
+
+// Block j = row * kThreads + thread.  For a predicate on (row), fills rowtab with the
+// exclusive prefix, in ascending block order, of the number of blocks satisfying it
+// per (row, wave); returns the total.  A caller then gets the ordinal of a satisfying
+// block as rowtab[row * kWaves + wave] + (satisfying lanes below it in its wave).
+template <class Pred>
+__device__ __forceinline__ int rows_prefix(int rows, Pred pred, TailSmem& sm) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll 1
+  for (int i = 0; i < rows; ++i) {
+    const uint64_t bal = __ballot(pred(i));
+    if (lane == 0) sm.rowtab[i * kWaves + wave] = __popcll(bal);
+  }
+  __syncthreads();
+  const int v = tid < rows * kWaves ? sm.rowtab[tid] : 0;
+  int total;
+  const int excl = block_excl_scan(v, sm.i32, total);
+  if (tid < rows * kWaves) sm.rowtab[tid] = excl;
+  __syncthreads();
+  return total;
+}
+
+// Exact greedy top-p threshold over the masses in LDS (mass < 0: no block).  Returns
+// the key of the last admitted block: the selected set is every block whose key is
+// >= it.  Precondition: the total fixed-point mass reaches P.
+//
+// Candidates are the keys in [lo, hi) with fixed mass `cab` strictly above them, and
+// cab < P <= cab + mass(candidates) holds throughout.  While more than kFinal remain,
+// kSplitters candidates evenly spaced in block order are sorted and split the
+// candidates into 64 buckets; the bucket where the cumulative mass crosses P becomes
+// the new candidate range.  Buckets 0..62 each hold their splitter, so every level
+// removes at least 62 candidates.  The last <= kFinal candidates are ranked exactly
+// (one per thread) and scanned in descending order.
+__device__ __noinline__ uint64_t final_resolve(const float* __restrict__ sm_m, int rows, uint64_t P,
+                                                TailSmem& sm, PhaseSmem& ph);
+
+__device__ uint64_t select_threshold(const float* __restrict__ sm_m, int rows, int nblk, uint64_t P,
+                                     TailSmem& sm, PhaseSmem& ph) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint64_t lo = 1, hi = ~0ull, cab = 0;
+  int cnt = nblk;
+  auto key = [&](int i) {
+    const float m = sm_m[i * kThreads + tid];
+    return m >= 0.f ? key_of(m, i * kThreads + tid) : 0ull;
+  };
+  while (cnt > kFinal) {
+    auto cand = [&](int i) {
+      const uint64_t k = key(i);
+      return k >= lo && k < hi;
+    };
+    rows_prefix(rows, cand, sm);
+    const int stride = cnt / kSplitters;  // >= 8 since cnt > kFinal
+#pragma unroll 1
+  for (int i = 0; i < rows; ++i) {
+      const uint64_t k = key(i);
+      const bool c = k >= lo && k < hi;
+      const uint64_t bal = __ballot(c);
+      const int ord = sm.rowtab[i * kWaves + wave] + __popcll(bal & lanemask_lt());
+      if (c && ord % stride == 0 && ord / stride < kSplitters) sm.samp[ord / stride] = k;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      if (lane < kSplitters) {  // rank sort of the (distinct) splitters, descending
+        const uint64_t my = sm.samp[lane];
+        int rank = 0;
+#pragma unroll 1
+        for (int i = 0; i < kSplitters; ++i) rank += sm.samp[i] > my ? 1 : 0;
+        sm.split[rank] = my;
+      }
+      sm.bcnt[lane] = 0;
+      sm.bmass[lane] = 0;
+      if (lane == 0) sm.cnt = 0;
+    }
+    __syncthreads();
+    // bucket of a candidate = number of splitters strictly above its key
+#pragma unroll 1
+  for (int i = 0; i < rows; ++i) {
+      const uint64_t k = key(i);
+      if (k >= lo && k < hi) {
+        int a = 0, n = kSplitters;  // first index with split[a] <= k
+        while (n > 0) {
+          const int h = n >> 1;
+          if (sm.split[a + h] > k) {
+            a += h + 1;
+            n -= h + 1;
+          } else {
+            n = h;
+          }
+        }
+        atomicAdd(&sm.bcnt[a], 1u);
+        atomicAdd((unsigned long long*)&sm.bmass[a],
+                  (unsigned long long)fixed_mass(sm_m[i * kThreads + tid]));
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // bucket b = lane, in descending key order: the one where cab + cumulative mass crosses P
+      const uint64_t bm = sm.bmass[lane];
+      uint64_t incl = bm;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint64_t y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+      }
+      if (cab + incl >= P && cab + incl - bm < P) {
+        sm.cab = cab + incl - bm;
+        sm.cnt = (int)sm.bcnt[lane];
+        sm.hi = lane > 0 ? sm.split[lane - 1] : hi;
+        sm.lo = lane < kSplitters ? sm.split[lane] : lo;
+      }
+    }
+    __syncthreads();
+    const int nc = __builtin_amdgcn_readfirstlane(sm.cnt);
+    if (nc <= 0 || nc >= cnt) {  // cannot happen while the invariant holds; stop safely
+      cnt = -1;
+      break;
+    }
+    lo = uni64(sm.lo);
+    hi = uni64(sm.hi);
+    cab = uni64(sm.cab);
+    cnt = __builtin_amdgcn_readfirstlane(nc);
+    __syncthreads();
+  }
+  if (cnt < 0) return 0;  // select every block rather than loop
+  if (tid == 0) {
+    sm.lo = lo;
+    sm.hi = hi;
+    sm.cab = cab;
+  }
+  __syncthreads();
+  return final_resolve(sm_m, rows, P, sm, ph);
+}
+
+// The last <= kFinal candidates [sm.lo, sm.hi), fixed mass sm.cab above them: gather them
+// in block order, rank them exactly, scan in descending order.  A separate function so
+// its registers are not live together with the refinement loop's.
+
+__device__ __noinline__ uint64_t final_resolve(const float* __restrict__ sm_m, int rows, uint64_t P,
+                                                TailSmem& sm, PhaseSmem& ph) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t lo = uni64(sm.lo), hi = uni64(sm.hi), cab = uni64(sm.cab);
+  auto key = [&](int i) {
+    const float m = sm_m[i * kThreads + tid];
+    return m >= 0.f ? key_of(m, i * kThreads + tid) : 0ull;
+  };
+  auto cand = [&](int i) {
+    const uint64_t k = key(i);
+    return k >= lo && k < hi;
+  };
+  const int total = rows_prefix(rows, cand, sm);
+#pragma unroll 1
+  for (int i = 0; i < rows; ++i) {
+    const uint64_t k = key(i);
+    const bool c = k >= lo && k < hi;
+    const uint64_t bal = __ballot(c);
+    const int ord = sm.rowtab[i * kWaves + wave] + __popcll(bal & lanemask_lt());
+    if (c && ord < kFinal) {
+      ph.fin.ckey[ord] = k;
+      ph.fin.cfm[ord] = fixed_mass(sm_m[i * kThreads + tid]);
+    }
+  }
+  if (tid == 0) sm.thr = 0;
+  __syncthreads();
+  const int nf = total < kFinal ? total : kFinal;
+  if (tid < nf) {
+    const uint64_t my = ph.fin.ckey[tid];
+    int rank = 0;
+#pragma unroll 1
+    for (int i = 0; i < nf; ++i) rank += ph.fin.ckey[i] > my ? 1 : 0;
+    ph.fin.skey[rank] = my;
+    ph.fin.sfm[rank] = ph.fin.cfm[tid];
+  }
+  __syncthreads();
+  const uint64_t f = tid < nf ? ph.fin.sfm[tid] : 0ull;
+  uint64_t tot64;
+  const uint64_t excl = block_excl_scan(f, sm.u64, tot64);
+  if (tid < nf && cab + excl < P && cab + excl + f >= P) sm.thr = ph.fin.skey[tid];
+  __syncthreads();
+  return uni64(sm.thr);
 }
 
 template <int BK>
@@ -113,25 +351,13 @@ __global__ __launch_bounds__(kThreads) void index_topp_kernel(
   const size_t head = (size_t)b * n_ret + r;
 
   __shared__ double s_qidx[kIndexDim];
-  __shared__ double s_lse[kMaxChunkBlocks];
-  __shared__ double s_f[kMaxChunks];
-  __shared__ uint32_t s_hcnt[256];
-  __shared__ uint64_t s_hmass[256];
-  __shared__ uint64_t s_chi[kResolve];
-  __shared__ uint32_t s_clo[kResolve];
-  __shared__ uint64_t s_cfm[kResolve];
-  __shared__ uint64_t s_shi[kResolve];
-  __shared__ uint32_t s_slo[kResolve];
-  __shared__ uint64_t s_sfm[kResolve];
-  __shared__ double s_red[kWaves];
-  __shared__ int s_wcnt[kWaves];
+  __shared__ PhaseSmem ph;
+  __shared__ TailSmem sm;
   __shared__ int s_flag;
-  __shared__ int s_bin, s_bcnt, s_ncand;
-  __shared__ uint64_t s_cab, s_thi;
-  __shared__ uint32_t s_tlo;
+  extern __shared__ float s_mass[];   // selection: one fp32 mass per block (rows * kThreads)
 
   // ---- q_idx = W^Q_r q_pre[b, hq] in fp64 (16 outputs x 16 partial dot products)
-  {
+  if (tid < 256) {
     const int hq = ret_heads[r];
     const int i = tid >> 4, part = tid & 15;
     const uint4 wv = ld16(w_q + ((size_t)r * kIndexDim + i) * kHeadDim + part * 8);
@@ -200,7 +426,7 @@ __global__ __launch_bounds__(kThreads) void index_topp_kernel(
         sum += half ? 0.0 : e;
       }
       sum = wave_sum(sum);
-      if (lane == 0) s_lse[j - j0] = m + log(sum);
+      if (lane == 0) ph.lse[j - j0] = m + log(sum);
     }
   }
   __syncthreads();
@@ -208,8 +434,8 @@ __global__ __launch_bounds__(kThreads) void index_topp_kernel(
   // ---- chunk epilogue: M_c, Z_c, e_j = exp(lse_j - M_c)
   if (wave == 0) {
     const int nb = j1 - j0;
-    const double l0 = lane < nb ? s_lse[lane] : -INFINITY;
-    const double l1 = lane + 64 < nb ? s_lse[lane + 64] : -INFINITY;
+    const double l0 = lane < nb ? ph.lse[lane] : -INFINITY;
+    const double l1 = lane + 64 < nb ? ph.lse[lane + 64] : -INFINITY;
     const double Mc = wave_max(fmax(l0, l1));
     const double e0 = lane < nb ? exp(l0 - Mc) : 0.0;
     const double e1 = lane + 64 < nb ? exp(l1 - Mc) : 0.0;
@@ -231,219 +457,68 @@ __global__ __launch_bounds__(kThreads) void index_topp_kernel(
   __syncthreads();
   if (!s_flag) return;
 
-  // ---- M, Z and the per-chunk factors f_c = exp(M_c - M) / Z
+  // ---- M, Z and the per-chunk factors exp(M_c - M)
   const double2* st = stats + head * n_chunk_max;
   double mloc = -INFINITY;
   for (int i = tid; i < nch; i += kThreads) mloc = fmax(mloc, st[i].x);
   mloc = wave_max(mloc);
-  if (lane == 0) s_red[wave] = mloc;
+  if (lane == 0) sm.f64[wave] = mloc;
   __syncthreads();
-  double M = s_red[0];
+  double M = sm.f64[0];
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) M = fmax(M, s_red[w]);
+  for (int w = 1; w < kWaves; ++w) M = fmax(M, sm.f64[w]);
   __syncthreads();
   double zloc = 0.0;
   for (int i = tid; i < nch; i += kThreads) {
     const double2 v = st[i];
     const double f = exp(v.x - M);
-    s_f[i] = f;
+    ph.f[i] = f;
     zloc += v.y * f;
   }
   zloc = wave_sum(zloc);
-  if (lane == 0) s_red[wave] = zloc;
+  if (lane == 0) sm.f64[wave] = zloc;
   __syncthreads();
-  double Z = s_red[0];
+  double Z = sm.f64[0];
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) Z += s_red[w];
+  for (int w = 1; w < kWaves; ++w) Z += sm.f64[w];
   const double invZ = 1.0 / Z;
-  for (int i = tid; i < nch; i += kThreads) s_f[i] *= invZ;
-  __syncthreads();
 
+  // ---- every block's mass into LDS (block j = row * kThreads + thread), -1 past nblk
+  const int rows = (nblk + kThreads - 1) / kThreads;
   const double* eb = blk_e + head * nblk_max;
-  auto elem = [&](int j) { return make_elem(eb[j], s_f[j >> chunk_shift], j); };
+  uint64_t fsum = 0;
+#pragma unroll 1
+  for (int i = 0; i < rows; ++i) {
+    const int j = i * kThreads + tid;
+    const float m = j < nblk ? (float)(eb[j] * (ph.f[j >> chunk_shift] * invZ)) : -1.0f;
+    s_mass[j] = m;
+    fsum += m > 0.f ? fixed_mass(m) : 0ull;
+  }
+  __syncthreads();  // ph.f is dead from here on
 
-  // threshold T: block j is selected iff (hi_j, lo_j) >= (thi, tlo)
-  uint64_t thi = 0;
-  uint32_t tlo = 0;
+  // threshold key: block j is selected iff key_of(m_j, j) >= thr
+  uint64_t thr = 0;
   const float p = top_p[head];
   if (p < 1.0f && nblk > 1) {
     const uint64_t P = (uint64_t)ceil(ldexp((double)p, 62));
-    uint64_t pfx_hi = 1, cab = 0;  // prefix so far; fixed mass strictly above the candidates
-    uint32_t pfx_lo = 0;
-    bool done = false;
-    for (int k = 0; k < 11 && !done; ++k) {
-      const int sh = kShift[k], wd = kWidth[k], nbins = 1 << wd;
-      for (int i = tid; i < 256; i += kThreads) {
-        s_hcnt[i] = 0;
-        s_hmass[i] = 0;
-      }
-      __syncthreads();
-      for (int j = tid; j < nblk; j += kThreads) {
-        const Elem x = elem(j);
-        bool cand;
-        uint32_t d;
-        if (k < 8) {
-          cand = (x.hi >> (sh + wd)) == pfx_hi;
-          d = (uint32_t)(x.hi >> sh) & (nbins - 1);
-        } else {
-          cand = x.hi == pfx_hi && (x.lo >> (sh + wd)) == pfx_lo;
-          d = (x.lo >> sh) & (nbins - 1);
-        }
-        if (cand) {
-          atomicAdd(&s_hcnt[d], 1u);
-          atomicAdd((unsigned long long*)&s_hmass[d], (unsigned long long)x.fm);
-        }
-      }
-      __syncthreads();
-      if (wave == 0) {
-        // bins in descending order: lane L owns bins nbins-1-4L .. nbins-4-4L
-        uint64_t bm[4];
-        uint32_t bc[4];
-        uint64_t tot = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int bin = nbins - 1 - 4 * lane - q;
-          bm[q] = bin >= 0 ? s_hmass[bin] : 0;
-          bc[q] = bin >= 0 ? s_hcnt[bin] : 0;
-          tot += bm[q];
-        }
-        uint64_t incl = tot;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint64_t y = shfl_up_u64(incl, o);
-          if (lane >= o) incl += y;
-        }
-        uint64_t run = cab + (incl - tot);
-        int hit = -1;
-        uint64_t hit_above = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (hit < 0 && run + bm[q] >= P && bm[q] > 0) {
-            hit = q;
-            hit_above = run;
-          }
-          run += bm[q];
-        }
-        const uint64_t any = __ballot(hit >= 0);
-        const int first = any ? __builtin_ctzll(any) : -1;
-        if (lane == 0 && first < 0) s_bin = -1;
-        if (lane == first) {
-          s_bin = nbins - 1 - 4 * lane - hit;
-          s_bcnt = (int)bc[hit];
-          s_cab = hit_above;
-        }
-      }
-      __syncthreads();
-      const int bin = s_bin;
-      if (bin < 0) {  // no prefix reaches p (only possible on the first pass): select all
-        thi = 0;
-        tlo = 0;
-        done = true;
-        break;
-      }
-      cab = s_cab;
-      const int bcnt = s_bcnt;
-      if (k < 8) {
-        pfx_hi = (pfx_hi << wd) | (uint64_t)bin;
-      } else {
-        pfx_lo = (pfx_lo << wd) | (uint32_t)bin;
-      }
-      if (bcnt == 1 || k == 10) {
-        if (k < 8) {
-          thi = pfx_hi << sh;
-          tlo = 0;
-        } else {
-          thi = pfx_hi;
-          tlo = pfx_lo << sh;
-        }
-        done = true;
-      } else if (bcnt <= kResolve) {
-        // gather the candidates and rank them exactly in one wave
-        if (tid == 0) s_ncand = 0;
-        __syncthreads();
-        for (int j = tid; j < nblk; j += kThreads) {
-          const Elem x = elem(j);
-          const bool cand = k < 8 ? (x.hi >> sh) == pfx_hi : (x.hi == pfx_hi && (x.lo >> sh) == pfx_lo);
-          if (cand) {
-            const int slot = atomicAdd(&s_ncand, 1);
-            s_chi[slot] = x.hi;
-            s_clo[slot] = x.lo;
-            s_cfm[slot] = x.fm;
-          }
-        }
-        __syncthreads();
-        const int nc = s_ncand;
-        if (wave == 0 && lane < nc) {
-          const uint64_t mh = s_chi[lane];
-          const uint32_t ml = s_clo[lane];
-          int rank = 0;
-          for (int i = 0; i < nc; ++i) {
-            const uint64_t oh = s_chi[i];
-            const uint32_t ol = s_clo[i];
-            rank += (oh > mh || (oh == mh && ol > ml)) ? 1 : 0;
-          }
-          s_shi[rank] = mh;   // ranks are a permutation of 0..nc-1
-          s_slo[rank] = ml;
-          s_sfm[rank] = s_cfm[lane];
-        }
-        __syncthreads();
-        if (wave == 0) {
-          const uint64_t f = lane < nc ? s_sfm[lane] : 0;
-          uint64_t incl = f;
-#pragma unroll
-          for (int o = 1; o < 64; o <<= 1) {
-            const uint64_t y = shfl_up_u64(incl, o);
-            if (lane >= o) incl += y;
-          }
-          const bool cross = lane < nc && cab + incl >= P;
-          const uint64_t any = __ballot(cross);
-          const int first = any ? __builtin_ctzll(any) : nc - 1;
-          if (lane == first) {
-            s_thi = s_shi[lane];
-            s_tlo = s_slo[lane];
-          }
-        }
-        __syncthreads();
-        thi = s_thi;
-        tlo = s_tlo;
-        done = true;
-      }
-      __syncthreads();
-    }
+    if (block_sum_u64(fsum, sm.u64) >= P) thr = select_threshold(s_mass, rows, nblk, P, sm, ph);
   }
 
-  // ---- ordered compaction of the selected ids (ascending), one contiguous segment a wave
+  // ---- ordered compaction of the selected ids (ascending)
+  auto sel = [&](int i) {
+    const int j = i * kThreads + tid;
+    const float m = s_mass[j];
+    return m >= 0.f && key_of(m, j) >= thr;
+  };
+  const int total = rows_prefix(rows, sel, sm);
   int* out = sel_idx + head * nblk_max;
-  const int seg = ((nblk + kWaves - 1) / kWaves + 63) / 64 * 64;
-  const int sb = wave * seg, se = min(nblk, sb + seg);
-  int cnt = 0;
-  for (int base = sb; base < se; base += 64) {
-    const int j = base + lane;
-    bool sel = false;
-    if (j < se) {
-      const Elem x = elem(j);
-      sel = geq(x.hi, x.lo, thi, tlo);
-    }
-    cnt += __popcll(__ballot(sel));
-  }
-  if (lane == 0) s_wcnt[wave] = cnt;
-  __syncthreads();
-  int off = 0;
-  for (int w = 0; w < wave; ++w) off += s_wcnt[w];
-  for (int base = sb; base < se; base += 64) {
-    const int j = base + lane;
-    bool sel = false;
-    if (j < se) {
-      const Elem x = elem(j);
-      sel = geq(x.hi, x.lo, thi, tlo);
-    }
-    const uint64_t mask = __ballot(sel);
-    if (sel) out[off + __popcll(mask & lanemask_lt())] = j;
-    off += __popcll(mask);
+#pragma unroll 1
+  for (int i = 0; i < rows; ++i) {
+    const bool sl = sel(i);
+    const uint64_t bal = __ballot(sl);
+    if (sl) out[sm.rowtab[i * kWaves + wave] + __popcll(bal & lanemask_lt())] = i * kThreads + tid;
   }
   if (tid == 0) {
-    int total = 0;
-    for (int w = 0; w < kWaves; ++w) total += s_wcnt[w];
     sel_cnt[head] = total;
     atomicExch(&counters[head], 0);  // ready for the next call
   }
@@ -467,6 +542,7 @@ extern "C" rtp_status rtp_index_topp(const void* q_pre, const void* w_q, const v
   if (B <= 0 || Hq <= 0 || n_ret < 0 || n_ret > Hq || max_ctx <= 0) return RTP_EINVAL;
   if (block != 64 && block != 128) return RTP_EUNSUPPORTED;
   if (ceil_div(max_ctx, block) > kMaxBlocks) return RTP_EUNSUPPORTED;
+  if (B > 65535 || n_ret > 65535) return RTP_EUNSUPPORTED;
   if (n_ret == 0) return RTP_OK;
   if (!q_pre || !w_q || !k_idx || !seq_lens || !ret_heads || !top_p || !sel_idx || !sel_cnt ||
       !workspace)
@@ -480,17 +556,18 @@ extern "C" rtp_status rtp_index_topp(const void* q_pre, const void* w_q, const v
   double2* stats = reinterpret_cast<double2*>(ws + L.off_stats);
   double* blk_e = reinterpret_cast<double*>(ws + L.off_e);
   dim3 grid(L.n_chunk, n_ret, B);
+  const size_t dyn = (size_t)L.rows * kThreads * sizeof(float);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint16_t* qp = static_cast<const uint16_t*>(q_pre);
   const uint16_t* wq = static_cast<const uint16_t*>(w_q);
   const uint16_t* ki = static_cast<const uint16_t*>(k_idx);
   if (block == 64)
-    hipLaunchKernelGGL(index_topp_kernel<64>, grid, dim3(kThreads), 0, s, qp, wq, ki, seq_lens,
-                       ret_heads, top_p, Hq, n_ret, max_ctx, L.nblk_max, L.chunk_blocks, L.chunk_shift, L.n_chunk,
-                       sel_idx, sel_cnt, counters, stats, blk_e);
+    hipLaunchKernelGGL(index_topp_kernel<64>, grid, dim3(kThreads), dyn, s, qp, wq, ki, seq_lens,
+                       ret_heads, top_p, Hq, n_ret, max_ctx, L.nblk_max, L.chunk_blocks, L.chunk_shift,
+                       L.n_chunk, sel_idx, sel_cnt, counters, stats, blk_e);
   else
-    hipLaunchKernelGGL(index_topp_kernel<128>, grid, dim3(kThreads), 0, s, qp, wq, ki, seq_lens,
-                       ret_heads, top_p, Hq, n_ret, max_ctx, L.nblk_max, L.chunk_blocks, L.chunk_shift, L.n_chunk,
-                       sel_idx, sel_cnt, counters, stats, blk_e);
+    hipLaunchKernelGGL(index_topp_kernel<128>, grid, dim3(kThreads), dyn, s, qp, wq, ki, seq_lens,
+                       ret_heads, top_p, Hq, n_ret, max_ctx, L.nblk_max, L.chunk_blocks, L.chunk_shift,
+                       L.n_chunk, sel_idx, sel_cnt, counters, stats, blk_e);
   return hipGetLastError() == hipSuccess ? RTP_OK : RTP_ELAUNCH;
 }
