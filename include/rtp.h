@@ -159,7 +159,8 @@ size_t rtp_local_window_workspace_size(int B, int Hq, int Hkv, int n_loc, int ma
  *   T = [0, min(sinks, N)) union [max(0, N - window), N)   (no token counted twice)
  *   out[b, hq] = sum_{n in T} softmax_n(q[b,hq] . K[b,g,n] / sqrt(128)) V[b,g,n]
  * The window is split across workgroups (one per KV group and split, serving every
- * local head of the group); the last workgroup of each (b, g) merges the splits.
+ * local head of the group) that write partials to the workspace; a second kernel on
+ * the same stream merges them with the log-sum-exp rule.
  *
  *   q, k_cache, v_cache, seq_lens as in rtp_sparse_attn_split
  *   loc_heads int32 [n_loc]  query-head ids of the local heads, ascending

@@ -13,20 +13,29 @@
 //   16-byte loads; one load instruction covers 1 KB (32 tokens, two lanes per token).
 //   q_idx and the scores are fp64 so that block masses carry < 1e-6 relative error;
 //   exponentials are fp32 hardware exp2 on arguments already reduced in fp64, summed
-//   in fp64.  Per block: lse_j = max + log(sum exp(s - max)).  Per chunk: M_c, Z_c
-//   and e_j = exp(lse_j - M_c) go to the workspace.
-//   Selection: the last workgroup per (b, r) (device-scope release/acquire around an
-//   atomic arrival counter, needed across the 8 XCDs' separate L2s) forms
-//   m_j = e_j exp(M_c - M) / Z for every block into LDS and finds the greedy
-//   threshold exactly: a key = (fp32 mass bits, inverted block id) orders blocks by
-//   mass with ties by ascending id; masses are summed as fixed-point integers (2^-62
-//   units) so every cumulative sum is exact and order-independent.  While more than
-//   512 candidates remain, 63 evenly spaced candidates are sorted into splitters, a
-//   64-bin LDS histogram of (count, mass) over the splitter intervals locates the
-//   interval where the cumulative mass crosses p, and that interval becomes the new
-//   candidate set; the last <= 512 candidates are ranked exactly and scanned.  The
-//   selected ids are written in ascending order by a ballot-based ordered compaction,
-//   and the arrival counter is reset to zero.
+//   in fp64; wave reductions run on DPP lane moves.  Per block: max_j and
+//   sum_j = sum exp(s - max_j); per chunk M_c = max_j max_j, and the chunk publishes
+//   e_j = sum_j exp(max_j - M_c) (fp32) and M_c (tagged fp64) to the workspace.
+//   Publication without fences: every published 64-bit word carries the call's tag
+//   (1..4095, advanced by every call) in its low 12 bits (the low mantissa bits of an
+//   fp64, or beside an fp32), words are written and read with relaxed device-scope
+//   atomics, and the reader waits for the current tag.
+//   Every workgroup then bumps an arrival counter; the last one of each (b, r) does
+//   the selection.  So no device-scope fence (an L2 write-back on every workgroup of
+//   every XCD) is needed, and a word from the previous call is never taken as current.
+//   Selection (last workgroup): M = max_c M_c and every block's mass
+//   m_j = e_j exp(M_c - M) / Z in fp32,
+//   ROWS per thread in registers, then the greedy threshold exactly: a key = (fp32
+//   mass bits, inverted block id) orders blocks by mass with ties by ascending id;
+//   masses are summed as fixed-point integers (2^-62 units) so every cumulative sum
+//   is exact and order-independent.  While more than 64 candidates of unequal mass
+//   remain, a 256-bin LDS histogram of (count, mass) over (bits - lo) >> shift (bins
+//   about log-uniform in mass) finds the bin where the cumulative mass crosses p, whose
+//   bit range becomes the new candidate range (>= 128x narrower); the last <= 64
+//   candidates are ranked exactly by one wave, and a run of equal masses is resolved by
+//   count in ascending block order.  The selected ids are written in ascending order by
+//   a ballot-based ordered compaction; the arrival counter is reset and the tag
+//   advanced.
 
 #include "rtp_common.hpp"
 
@@ -37,20 +46,23 @@ constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxChunkBlocks = 128;
 constexpr int kMaxChunks = 1024;
-constexpr int kMaxRows = kThreads / kWaves;   // rows of kThreads blocks in the selection
+constexpr int kMaxRows = 32;                  // blocks per thread in the selection
 constexpr int kMaxBlocks = kMaxRows * kThreads;
-constexpr int kSplitters = 63;                // splitters per refinement level (64 buckets)
-constexpr int kFinal = kThreads;              // candidates ranked directly (one per thread)
+constexpr int kBins = 256;                    // histogram bins per refinement level
+constexpr int kFinal = kWave;                 // candidates ranked directly (one per lane)
+constexpr int kSpinBudget = 1 << 12;          // re-reads a thread may spend waiting for a tag
+constexpr uint64_t kTagBits = 0xFFFull;
 
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct K1Layout {
-  int nblk_max, chunk_blocks, chunk_shift, n_chunk, rows;
-  size_t off_counters, off_stats, off_e, total;
+  int nblk_max, chunk_blocks, n_chunk, rows;
+  size_t off_counters, off_tag, off_cmax, off_e, total;
 };
 
 // Chunk size: aim for >= 1024 workgroups over the whole batch, 8..128 blocks a chunk,
-// at most kMaxChunks chunks per head.
+// at most kMaxChunks chunks per head.  rows = blocks per thread in the selection
+// (a power of two).
 K1Layout k1_layout(int B, int n_ret, int max_ctx, int block) {
   K1Layout L{};
   L.nblk_max = ceil_div(max_ctx, block);
@@ -59,40 +71,50 @@ K1Layout k1_layout(int B, int n_ret, int max_ctx, int block) {
   while (cb > 8 && total_blocks / cb < 1024) cb >>= 1;
   while (ceil_div(L.nblk_max, cb) > kMaxChunks && cb < kMaxChunkBlocks) cb <<= 1;
   L.chunk_blocks = cb;
-  L.chunk_shift = __builtin_ctz(cb);
   L.n_chunk = ceil_div(L.nblk_max, cb);
-  L.rows = ceil_div(L.nblk_max, kThreads);
+  L.rows = 1;
+  while (L.rows * kThreads < L.nblk_max) L.rows <<= 1;
   const size_t heads = (size_t)B * n_ret;
   L.off_counters = 0;
-  L.off_stats = align_up(heads * sizeof(int), 256);
-  L.off_e = L.off_stats + align_up(heads * L.n_chunk * 2 * sizeof(double), 256);
-  L.total = L.off_e + align_up(heads * (size_t)L.nblk_max * sizeof(double), 256);
+  L.off_tag = align_up(heads * sizeof(int), 256);
+  L.off_cmax = L.off_tag + align_up(heads * sizeof(uint32_t), 256);
+  L.off_e = L.off_cmax + align_up(heads * L.n_chunk * sizeof(uint64_t), 256);
+  L.total = L.off_e + align_up(heads * (size_t)L.nblk_max * sizeof(uint64_t), 256);
   return L;
 }
 
-// ------------------------------------------------------------------ selection tail
+// ------------------------------------------------------------------ published words
+// fp64 values passed from the scoring workgroups to the selecting one: the low 12
+// mantissa bits hold the call's tag (relative precision 2^-40 remains).
+__device__ __forceinline__ uint64_t tagged(double x, uint32_t tag) {
+  return ((uint64_t)__double_as_longlong(x) & ~kTagBits) | tag;
+}
+__device__ __forceinline__ double untag(uint64_t w) { return __longlong_as_double((long long)(w & ~kTagBits)); }
+__device__ __forceinline__ uint64_t ld_dev(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Re-read a published word until it carries `tag` (bounded by the thread's budget).
+__device__ __forceinline__ uint64_t settle(const uint64_t* p, uint64_t w, uint32_t tag, int& budget) {
+  while ((uint32_t)(w & kTagBits) != tag && budget > 0) {
+    --budget;
+    __builtin_amdgcn_s_sleep(1);
+    w = ld_dev(p);
+  }
+  return w;
+}
+
+// ------------------------------------------------------------------ selection helpers
 // Composite selection key of block j with fp32 mass m >= 0: the mass bits (order-
 // preserving for non-negative floats) above the inverted block id, so that keys are
 // distinct and descending key order is descending mass with ties by ascending id.
-// Key 0 marks "no block".
 __device__ __forceinline__ uint64_t key_of(float m, int j) {
   return ((uint64_t)__float_as_uint(m) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
 }
 // Mass in fixed point, 2^-62 units: integer sums are exact and order-independent.
 __device__ __forceinline__ uint64_t fixed_mass(float m) { return (uint64_t)((double)m * 0x1p62); }
-
-struct TailSmem {
-  uint64_t samp[kSplitters];      // sampled candidate keys
-  uint64_t split[kSplitters];     // the same, sorted descending
-  uint32_t bcnt[kSplitters + 1];  // per bucket: candidate count
-  uint64_t bmass[kSplitters + 1]; // per bucket: fixed-point mass
-  int rowtab[kMaxRows * kWaves];  // per (row, wave) counts, then exclusive prefixes
-  uint64_t u64[kWaves];
-  int i32[kWaves];
-  double f64[kWaves];
-  uint64_t lo, hi, cab, thr;
-  int cnt;
-};
 
 // A wave-uniform 64-bit value moved to scalar registers.
 __device__ __forceinline__ uint64_t uni64(uint64_t v) {
@@ -101,33 +123,50 @@ __device__ __forceinline__ uint64_t uni64(uint64_t v) {
   return ((uint64_t)b << 32) | a;
 }
 
-// Buffers used by one phase at a time.
-union PhaseSmem {
-  double lse[kMaxChunkBlocks];    // scoring: block lse of this chunk
-  double f[kMaxChunks];           // selection: per-chunk factors exp(M_c - M)
-  struct {
-    uint64_t ckey[kFinal], cfm[kFinal], skey[kFinal], sfm[kFinal];
-  } fin;                          // selection: final candidates
+struct TailSmem {
+  uint64_t bmass[kBins];          // per bin: fixed-point mass
+  uint32_t bcnt[kBins];           // per bin: candidate count
+  int rowtab[kMaxRows * kWaves];  // per (row, wave) counts, then exclusive prefixes
+  uint64_t u64[kWaves];
+  double f64[kWaves];
+  int i32[kWaves];
+  uint32_t u32a[kWaves], u32b[kWaves];
+  uint64_t ckey[kFinal], cfm[kFinal], skey[kFinal], sfm[kFinal];  // final candidates
+  uint64_t cab, thr;
+  int cnt, bin;
 };
 
-__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+template <class T, class Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  for (int o = 32; o > 0; o >>= 1) v = op(v, __shfl_xor(v, o));
   return v;
 }
 
-// Sum over the workgroup; every thread gets the total.
-__device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, uint64_t* red) {
+// Reduction over the workgroup; every thread gets the result.
+template <class T, class Op>
+__device__ __forceinline__ T block_reduce(T v, T* red, Op op) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  v = wave_sum_u64(v);
+  v = wave_reduce(v, op);
   if (lane == 0) red[wave] = v;
   __syncthreads();
-  uint64_t t = 0;
+  T t = red[0];
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) t += red[w];
+  for (int w = 1; w < kWaves; ++w) t = op(t, red[w]);
   __syncthreads();
   return t;
 }
+
+struct SumOp {
+  template <class T>
+  __device__ T operator()(T a, T b) const { return a + b; }
+};
+struct MinOp {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; }
+};
+struct MaxOp {
+  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; }
+};
 
 // Exclusive prefix sum over the workgroup in thread order; `total` gets the sum.
 template <class T>
@@ -152,194 +191,166 @@ __device__ __forceinline__ T block_excl_scan(T v, T* red, T& total) {
   return base + incl - v;
 }
 
-// Block j = row * kThreads + thread.  For a predicate on (row), fills rowtab with the
-// exclusive prefix, in ascending block order, of the number of blocks satisfying it
-// per (row, wave); returns the total.  A caller then gets the ordinal of a satisfying
-// block as rowtab[row * kWaves + wave] + (satisfying lanes below it in its wave).
-template <class Pred>
-__device__ __forceinline__ int rows_prefix(int rows, Pred pred, TailSmem& sm) {
+// Block j = row * kThreads + thread; flags[row] says whether this thread's block of the
+// row satisfies some predicate.  Fills rowtab with the exclusive prefix, in ascending
+// block order, of the satisfying blocks per (row, wave) and returns their total; the
+// ordinal of a satisfying block is then rowtab[row * kWaves + wave] + (satisfying
+// lanes below it in its wave).
+template <int ROWS>
+__device__ __forceinline__ int rows_prefix(const bool (&flags)[ROWS], TailSmem& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-#pragma unroll 1
-  for (int i = 0; i < rows; ++i) {
-    const uint64_t bal = __ballot(pred(i));
+#pragma unroll
+  for (int i = 0; i < ROWS; ++i) {
+    const uint64_t bal = __ballot(flags[i]);
     if (lane == 0) sm.rowtab[i * kWaves + wave] = __popcll(bal);
   }
   __syncthreads();
-  const int v = tid < rows * kWaves ? sm.rowtab[tid] : 0;
+  const int v = tid < ROWS * kWaves ? sm.rowtab[tid] : 0;
   int total;
   const int excl = block_excl_scan(v, sm.i32, total);
-  if (tid < rows * kWaves) sm.rowtab[tid] = excl;
+  if (tid < ROWS * kWaves) sm.rowtab[tid] = excl;
   __syncthreads();
   return total;
 }
 
-// Exact greedy top-p threshold over the masses in LDS (mass < 0: no block).  Returns
-// the key of the last admitted block: the selected set is every block whose key is
-// >= it.  Precondition: the total fixed-point mass reaches P.
-//
-// Candidates are the keys in [lo, hi) with fixed mass `cab` strictly above them, and
-// cab < P <= cab + mass(candidates) holds throughout.  While more than kFinal remain,
-// kSplitters candidates evenly spaced in block order are sorted and split the
-// candidates into 64 buckets; the bucket where the cumulative mass crosses P becomes
-// the new candidate range.  Buckets 0..62 each hold their splitter, so every level
-// removes at least 62 candidates.  The last <= kFinal candidates are ranked exactly
-// (one per thread) and scanned in descending order.
-__device__ __noinline__ uint64_t final_resolve(const float* __restrict__ sm_m, int rows, uint64_t P,
-                                                TailSmem& sm, PhaseSmem& ph);
-
-__device__ uint64_t select_threshold(const float* __restrict__ sm_m, int rows, int nblk, uint64_t P,
-                                     TailSmem& sm, PhaseSmem& ph) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint64_t lo = 1, hi = ~0ull, cab = 0;
-  int cnt = nblk;
-  auto key = [&](int i) {
-    const float m = sm_m[i * kThreads + tid];
-    return m >= 0.f ? key_of(m, i * kThreads + tid) : 0ull;
-  };
-  while (cnt > kFinal) {
-    auto cand = [&](int i) {
-      const uint64_t k = key(i);
-      return k >= lo && k < hi;
-    };
-    rows_prefix(rows, cand, sm);
-    const int stride = cnt / kSplitters;  // >= 8 since cnt > kFinal
-#pragma unroll 1
-  for (int i = 0; i < rows; ++i) {
-      const uint64_t k = key(i);
-      const bool c = k >= lo && k < hi;
-      const uint64_t bal = __ballot(c);
-      const int ord = sm.rowtab[i * kWaves + wave] + __popcll(bal & lanemask_lt());
-      if (c && ord % stride == 0 && ord / stride < kSplitters) sm.samp[ord / stride] = k;
-    }
-    __syncthreads();
-    if (wave == 0) {
-      if (lane < kSplitters) {  // rank sort of the (distinct) splitters, descending
-        const uint64_t my = sm.samp[lane];
-        int rank = 0;
-#pragma unroll 1
-        for (int i = 0; i < kSplitters; ++i) rank += sm.samp[i] > my ? 1 : 0;
-        sm.split[rank] = my;
-      }
-      sm.bcnt[lane] = 0;
-      sm.bmass[lane] = 0;
-      if (lane == 0) sm.cnt = 0;
-    }
-    __syncthreads();
-    // bucket of a candidate = number of splitters strictly above its key
-#pragma unroll 1
-  for (int i = 0; i < rows; ++i) {
-      const uint64_t k = key(i);
-      if (k >= lo && k < hi) {
-        int a = 0, n = kSplitters;  // first index with split[a] <= k
-        while (n > 0) {
-          const int h = n >> 1;
-          if (sm.split[a + h] > k) {
-            a += h + 1;
-            n -= h + 1;
-          } else {
-            n = h;
-          }
-        }
-        atomicAdd(&sm.bcnt[a], 1u);
-        atomicAdd((unsigned long long*)&sm.bmass[a],
-                  (unsigned long long)fixed_mass(sm_m[i * kThreads + tid]));
-      }
-    }
-    __syncthreads();
-    if (wave == 0) {
-      // bucket b = lane, in descending key order: the one where cab + cumulative mass crosses P
-      const uint64_t bm = sm.bmass[lane];
-      uint64_t incl = bm;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint64_t y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
-      }
-      if (cab + incl >= P && cab + incl - bm < P) {
-        sm.cab = cab + incl - bm;
-        sm.cnt = (int)sm.bcnt[lane];
-        sm.hi = lane > 0 ? sm.split[lane - 1] : hi;
-        sm.lo = lane < kSplitters ? sm.split[lane] : lo;
-      }
-    }
-    __syncthreads();
-    const int nc = __builtin_amdgcn_readfirstlane(sm.cnt);
-    if (nc <= 0 || nc >= cnt) {  // cannot happen while the invariant holds; stop safely
-      cnt = -1;
-      break;
-    }
-    lo = uni64(sm.lo);
-    hi = uni64(sm.hi);
-    cab = uni64(sm.cab);
-    cnt = __builtin_amdgcn_readfirstlane(nc);
-    __syncthreads();
-  }
-  if (cnt < 0) return 0;  // select every block rather than loop
-  if (tid == 0) {
-    sm.lo = lo;
-    sm.hi = hi;
-    sm.cab = cab;
-  }
-  __syncthreads();
-  return final_resolve(sm_m, rows, P, sm, ph);
+template <int ROWS>
+__device__ __forceinline__ int ordinal(const bool (&flags)[ROWS], int i, const TailSmem& sm) {
+  const int wave = threadIdx.x >> 6;
+  return sm.rowtab[i * kWaves + wave] + __popcll(__ballot(flags[i]) & lanemask_lt());
 }
 
-// The last <= kFinal candidates [sm.lo, sm.hi), fixed mass sm.cab above them: gather them
-// in block order, rank them exactly, scan in descending order.  A separate function so
-// its registers are not live together with the refinement loop's.
-
-__device__ __noinline__ uint64_t final_resolve(const float* __restrict__ sm_m, int rows, uint64_t P,
-                                                TailSmem& sm, PhaseSmem& ph) {
+// Exact greedy top-p threshold over the masses m[] (block i * kThreads + thread; < 0
+// for none).  Returns the key of the last admitted block: the selected set is every
+// block whose key is >= it.  Preconditions: the total fixed-point mass reaches P;
+// [lo, hi] spans the mass bits of all blocks.
+//
+// Candidates are the blocks whose mass bits lie in [lo, hi], with fixed mass `cab`
+// strictly above them, and cab < P <= cab + mass(candidates) holds throughout.  A
+// level puts every candidate into one of kBins bins by (bits - lo) >> shift, a
+// monotone map, so bins are contiguous ranges of mass (about log-uniform, since fp32
+// bits grow with log2 of the value); the bin where cab + cumulative mass from the top
+// crosses P holds the threshold, and its candidates' bit range becomes the new range,
+// at least kBins/2 times narrower.  It ends when <= kFinal candidates remain (ranked
+// exactly), or when all candidates have equal mass: the threshold is then the k-th of
+// them in ascending block order, k = ceil((P - cab) / mass).
+template <int ROWS>
+__device__ uint64_t select_threshold(const float (&m)[ROWS], int nblk, uint64_t P, uint32_t lo,
+                                     uint32_t hi, TailSmem& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint64_t lo = uni64(sm.lo), hi = uni64(sm.hi), cab = uni64(sm.cab);
-  auto key = [&](int i) {
-    const float m = sm_m[i * kThreads + tid];
-    return m >= 0.f ? key_of(m, i * kThreads + tid) : 0ull;
-  };
+  uint64_t cab = 0;
+  int cnt = nblk;
   auto cand = [&](int i) {
-    const uint64_t k = key(i);
-    return k >= lo && k < hi;
+    const uint32_t bits = __float_as_uint(m[i]);
+    return m[i] >= 0.f && bits >= lo && bits <= hi;
   };
-  const int total = rows_prefix(rows, cand, sm);
-#pragma unroll 1
-  for (int i = 0; i < rows; ++i) {
-    const uint64_t k = key(i);
-    const bool c = k >= lo && k < hi;
-    const uint64_t bal = __ballot(c);
-    const int ord = sm.rowtab[i * kWaves + wave] + __popcll(bal & lanemask_lt());
-    if (c && ord < kFinal) {
-      ph.fin.ckey[ord] = k;
-      ph.fin.cfm[ord] = fixed_mass(sm_m[i * kThreads + tid]);
+  while (cnt > kFinal && lo < hi) {
+    const uint32_t span = hi - lo;
+    const int shift = max(0, 32 - (int)__clz(span) - 8);  // (span >> shift) < kBins
+    if (tid < kBins) {
+      sm.bmass[tid] = 0;
+      sm.bcnt[tid] = 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) {
+      if (cand(i)) {
+        const int bin = (int)((__float_as_uint(m[i]) - lo) >> shift);
+        atomicAdd((unsigned long long*)&sm.bmass[bin], (unsigned long long)fixed_mass(m[i]));
+        atomicAdd(&sm.bcnt[bin], 1u);
+      }
+    }
+    __syncthreads();
+    // thread t holds bin kBins-1-t, so thread order is descending mass
+    const uint64_t bm = tid < kBins ? sm.bmass[kBins - 1 - tid] : 0ull;
+    uint64_t tot;
+    const uint64_t above = block_excl_scan(bm, sm.u64, tot);
+    if (tid < kBins && bm > 0 && cab + above < P && cab + above + bm >= P) {
+      sm.cab = cab + above;
+      sm.cnt = (int)sm.bcnt[kBins - 1 - tid];
+      sm.bin = kBins - 1 - tid;
+    }
+    __syncthreads();
+    cab = uni64(sm.cab);
+    cnt = __builtin_amdgcn_readfirstlane(sm.cnt);
+    const uint32_t bin = __builtin_amdgcn_readfirstlane(sm.bin);
+    // the crossing bin's bit range
+    uint32_t bmin = 0xFFFFFFFFu, bmax = 0;
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) {
+      const uint32_t bits = __float_as_uint(m[i]);
+      if (cand(i) && ((bits - lo) >> shift) == bin) {
+        bmin = min(bmin, bits);
+        bmax = max(bmax, bits);
+      }
+    }
+    bmin = block_reduce(bmin, sm.u32a, MinOp());
+    bmax = block_reduce(bmax, sm.u32b, MaxOp());
+    lo = __builtin_amdgcn_readfirstlane(bmin);
+    hi = __builtin_amdgcn_readfirstlane(bmax);
+  }
+  bool fl[ROWS];
+#pragma unroll
+  for (int i = 0; i < ROWS; ++i) fl[i] = cand(i);
+  if (tid == 0) sm.thr = 0;
+  const int total = rows_prefix(fl, sm);
+  if (cnt > kFinal) {
+    // every candidate has mass bits lo: admit them in ascending block order
+    const uint64_t f = fixed_mass(__uint_as_float(lo));
+    if (f == 0) return 0;  // cannot happen while the invariant holds
+    const uint64_t k = (P - cab + f - 1) / f;  // >= 1, <= cnt
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) {
+      const int ord = ordinal(fl, i, sm);
+      if (fl[i] && (uint64_t)ord + 1 == k) sm.thr = key_of(m[i], i * kThreads + tid);
+    }
+    __syncthreads();
+    return uni64(sm.thr);
+  }
+  // the last <= kFinal candidates: gather in block order, rank in one wave, scan
+#pragma unroll
+  for (int i = 0; i < ROWS; ++i) {
+    const int ord = ordinal(fl, i, sm);
+    if (fl[i] && ord < kFinal) {
+      sm.ckey[ord] = key_of(m[i], i * kThreads + tid);
+      sm.cfm[ord] = fixed_mass(m[i]);
     }
   }
-  if (tid == 0) sm.thr = 0;
   __syncthreads();
   const int nf = total < kFinal ? total : kFinal;
-  if (tid < nf) {
-    const uint64_t my = ph.fin.ckey[tid];
+  if (wave == 0) {
+    uint64_t my = 0, myf = 0;
     int rank = 0;
-#pragma unroll 1
-    for (int i = 0; i < nf; ++i) rank += ph.fin.ckey[i] > my ? 1 : 0;
-    ph.fin.skey[rank] = my;
-    ph.fin.sfm[rank] = ph.fin.cfm[tid];
+    if (lane < nf) {
+      my = sm.ckey[lane];
+      myf = sm.cfm[lane];
+#pragma unroll 8
+      for (int i = 0; i < nf; ++i) rank += sm.ckey[i] > my ? 1 : 0;
+      sm.skey[rank] = my;
+      sm.sfm[rank] = myf;
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t f = lane < nf ? sm.sfm[lane] : 0ull;
+    uint64_t incl = f;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint64_t y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane < nf && cab + incl - f < P && cab + incl >= P) sm.thr = sm.skey[lane];
   }
-  __syncthreads();
-  const uint64_t f = tid < nf ? ph.fin.sfm[tid] : 0ull;
-  uint64_t tot64;
-  const uint64_t excl = block_excl_scan(f, sm.u64, tot64);
-  if (tid < nf && cab + excl < P && cab + excl + f >= P) sm.thr = ph.fin.skey[tid];
   __syncthreads();
   return uni64(sm.thr);
 }
 
-template <int BK>
+template <int BK, int ROWS>
 __global__ __launch_bounds__(kThreads) void index_topp_kernel(
     const uint16_t* __restrict__ q_pre, const uint16_t* __restrict__ w_q,
     const uint16_t* __restrict__ k_idx, const int* __restrict__ seq_lens,
     const int* __restrict__ ret_heads, const float* __restrict__ top_p, int Hq, int n_ret,
-    int max_ctx, int nblk_max, int chunk_blocks, int chunk_shift, int n_chunk_max, int* __restrict__ sel_idx,
-    int* __restrict__ sel_cnt, int* __restrict__ counters, double2* __restrict__ stats,
-    double* __restrict__ blk_e) {
+    int max_ctx, int nblk_max, int chunk_blocks, int n_chunk_max, int* __restrict__ sel_idx,
+    int* __restrict__ sel_cnt, int* __restrict__ counters, uint32_t* __restrict__ tags,
+    uint64_t* __restrict__ cmax, uint64_t* __restrict__ blk_e) {
   constexpr int NL = BK / 32;              // 1 KB loads per lane per block
   constexpr int U = BK == 64 ? 2 : 1;      // blocks in flight per wave
   const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
@@ -351,12 +362,40 @@ __global__ __launch_bounds__(kThreads) void index_topp_kernel(
   const size_t head = (size_t)b * n_ret + r;
 
   __shared__ double s_qidx[kIndexDim];
-  __shared__ PhaseSmem ph;
+  __shared__ double s_mx[kMaxChunkBlocks], s_sum[kMaxChunkBlocks];  // scoring: per-block max, sum
+  __shared__ double s_f[kMaxChunks];  // selection: per-chunk factor exp(M_c - M)
   __shared__ TailSmem sm;
   __shared__ int s_flag;
-  extern __shared__ float s_mass[];   // selection: one fp32 mass per block (rows * kThreads)
+  __shared__ uint32_t s_tag;
 
-  // ---- q_idx = W^Q_r q_pre[b, hq] in fp64 (16 outputs x 16 partial dot products)
+  // ---- scoring: max and sum of every block of this chunk into LDS.  Wave w takes blocks
+  // j0 + w + kWaves * (U * k + u); the next U blocks' loads are in flight while the
+  // current U blocks are reduced.
+  const int half = lane & 1;
+  const uint16_t* kb = k_idx + head * (size_t)max_ctx * kIndexDim + half * 8;
+  const int j0 = c * chunk_blocks;
+  const int j1 = min(j0 + chunk_blocks, nblk);
+  auto load = [&](uint4 (&v)[U][NL], int jj) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = jj + u * kWaves;
+#pragma unroll
+      for (int t = 0; t < NL; ++t) {
+        const int tok = j * BK + 32 * t + (lane >> 1);
+        v[u][t] = (j < j1 && tok < N) ? ld16(kb + (size_t)tok * kIndexDim) : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  // the first blocks' loads go out before q_idx is formed
+  int jj = j0 + wave;
+  uint4 cur[U][NL];
+  if (jj < j1) load(cur, jj);
+
+  // ---- this call's tag; q_idx = W^Q_r q_pre[b, hq] in fp64 (16 outputs x 16 partial dots)
+  if (tid == 0) {
+    const uint32_t t = __hip_atomic_load(&tags[head], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_tag = t == 0 ? 1u : t;
+  }
   if (tid < 256) {
     const int hq = ret_heads[r];
     const int i = tid >> 4, part = tid & 15;
@@ -375,152 +414,169 @@ __global__ __launch_bounds__(kThreads) void index_topp_kernel(
     if (part == 0) s_qidx[i] = a;
   }
   __syncthreads();
-  const int half = lane & 1;
+  const uint32_t tag = s_tag;
   double qh[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) qh[k] = s_qidx[half * 8 + k];
 
-  // ---- scoring: lse of every block of this chunk
-  const uint16_t* kb = k_idx + head * (size_t)max_ctx * kIndexDim + half * 8;
-  const int j0 = c * chunk_blocks;
-  const int j1 = min(j0 + chunk_blocks, nblk);
-  for (int jj = j0 + wave; jj < j1; jj += kWaves * U) {
-    uint4 v[U][NL];
+  if (jj < j1) {
+    while (true) {
+      const int jn = jj + kWaves * U;
+      uint4 nxt[U][NL];
+      if (jn < j1) load(nxt, jn);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = jj + u * kWaves;
+      for (int u = 0; u < U; ++u) {
+        const int j = jj + u * kWaves;
+        if (j >= j1) break;
+        // scores in fp64, two 4-term chains per lane, then the pair sum (both lanes of
+        // the pair then hold the token's score)
+        double sc[NL];
+        float mxf = -INFINITY;
 #pragma unroll
-      for (int t = 0; t < NL; ++t) {
-        const int tok = j * BK + 32 * t + (lane >> 1);
-        v[u][t] = (j < j1 && tok < N) ? ld16(kb + (size_t)tok * kIndexDim) : make_uint4(0, 0, 0, 0);
+        for (int t = 0; t < NL; ++t) {
+          const uint4 x = cur[u][t];
+          double a0 = qh[0] * (double)bf_lo(x.x);
+          double a1 = qh[1] * (double)bf_hi(x.x);
+          a0 = fma(qh[2], (double)bf_lo(x.y), a0);
+          a1 = fma(qh[3], (double)bf_hi(x.y), a1);
+          a0 = fma(qh[4], (double)bf_lo(x.z), a0);
+          a1 = fma(qh[5], (double)bf_hi(x.z), a1);
+          a0 = fma(qh[6], (double)bf_lo(x.w), a0);
+          a1 = fma(qh[7], (double)bf_hi(x.w), a1);
+          double a = a0 + a1;
+          a += dpp_f64<kDppXor1>(a);  // commutative: both lanes of the pair get the same value
+          const int tok = j * BK + 32 * t + (lane >> 1);
+          sc[t] = tok < N ? a : -INFINITY;
+          mxf = fmaxf(mxf, (float)sc[t]);
+        }
+        // reference for the block's exponentials: the max of the fp32-rounded scores
+        // (pairs already agree, so the butterfly starts at distance 2)
+        mxf = fmaxf(mxf, dpp_f32<kDppXor2>(mxf));
+        mxf = fmaxf(mxf, dpp_f32<kDppHalfMirror>(mxf));
+        mxf = fmaxf(mxf, dpp_f32<kDppMirror>(mxf));
+        mxf = fmaxf(fmaxf(readlane_f32(mxf, 0), readlane_f32(mxf, 16)),
+                    fmaxf(readlane_f32(mxf, 32), readlane_f32(mxf, 48)));
+        const double mx = (double)mxf;
+        // each lane of a pair exponentiates its own half of the pair's tokens
+        double sum = 0.0;
+#pragma unroll
+        for (int tt = 0; tt < NL / 2; ++tt) {
+          const double st = half ? sc[2 * tt + 1] : sc[2 * tt];
+          sum += (double)fast_exp2((float)((st - mx) * kLog2e));
+        }
+        sum = wave_sum(sum);
+        if (lane == 0) {
+          s_mx[j - j0] = mx;
+          s_sum[j - j0] = sum;
+        }
       }
-    }
+      if (jn >= j1) break;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = jj + u * kWaves;
-      if (j >= j1) break;
-      double s[NL];
-      double m = -INFINITY;
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int t = 0; t < NL; ++t) {
-        const uint4 x = v[u][t];
-        double a = qh[0] * (double)bf_lo(x.x);
-        a = fma(qh[1], (double)bf_hi(x.x), a);
-        a = fma(qh[2], (double)bf_lo(x.y), a);
-        a = fma(qh[3], (double)bf_hi(x.y), a);
-        a = fma(qh[4], (double)bf_lo(x.z), a);
-        a = fma(qh[5], (double)bf_hi(x.z), a);
-        a = fma(qh[6], (double)bf_lo(x.w), a);
-        a = fma(qh[7], (double)bf_hi(x.w), a);
-        a += __shfl_xor(a, 1);  // commutative: both lanes of the pair hold the same score
-        const int tok = j * BK + 32 * t + (lane >> 1);
-        s[t] = tok < N ? a : -INFINITY;
-        m = fmax(m, s[t]);
-      }
-      m = wave_max(m);
-      double sum = 0.0;
-#pragma unroll
-      for (int t = 0; t < NL; ++t) {
-        const float x = (float)((s[t] - m) * kLog2e);
-        const double e = (double)fast_exp2(x);
-        sum += half ? 0.0 : e;
-      }
-      sum = wave_sum(sum);
-      if (lane == 0) ph.lse[j - j0] = m + log(sum);
+        for (int t = 0; t < NL; ++t) cur[u][t] = nxt[u][t];
+      jj = jn;
     }
   }
   __syncthreads();
 
-  // ---- chunk epilogue: M_c, Z_c, e_j = exp(lse_j - M_c)
+  // ---- publish e_j = sum_j exp(max_j - M_c) (fp32) and the chunk maximum M_c; the
+  // last workgroup of (b, r) to arrive selects
+  uint64_t* e_io = blk_e + head * nblk_max;
   if (wave == 0) {
     const int nb = j1 - j0;
-    const double l0 = lane < nb ? ph.lse[lane] : -INFINITY;
-    const double l1 = lane + 64 < nb ? ph.lse[lane + 64] : -INFINITY;
-    const double Mc = wave_max(fmax(l0, l1));
-    const double e0 = lane < nb ? exp(l0 - Mc) : 0.0;
-    const double e1 = lane + 64 < nb ? exp(l1 - Mc) : 0.0;
-    double* eb = blk_e + head * nblk_max + j0;
-    if (lane < nb) eb[lane] = e0;
-    if (lane + 64 < nb) eb[lane + 64] = e1;
-    const double Zc = wave_sum(e0 + e1);
-    if (lane == 0) stats[head * n_chunk_max + c] = make_double2(Mc, Zc);
-  }
-  __syncthreads();
-
-  // ---- arrival: the last workgroup of (b, r) selects
-  if (tid == 0) {
-    __threadfence();  // release this workgroup's e_j and chunk stats device-wide
-    const int prev = atomicAdd(&counters[head], 1);
-    s_flag = prev == nch - 1;
-    if (s_flag) __threadfence();  // acquire every other workgroup's results
+    const double x0 = lane < nb ? s_mx[lane] : -INFINITY;
+    const double x1 = lane + 64 < nb ? s_mx[lane + 64] : -INFINITY;
+    const double mc = wave_max(fmax(x0, x1));
+    if (lane < nb) {
+      const float e = (float)(s_sum[lane] * (double)fast_exp2((float)((x0 - mc) * kLog2e)));
+      st_dev(e_io + j0 + lane, ((uint64_t)__float_as_uint(e) << 32) | tag);
+    }
+    if (lane + 64 < nb) {
+      const float e = (float)(s_sum[lane + 64] * (double)fast_exp2((float)((x1 - mc) * kLog2e)));
+      st_dev(e_io + j0 + lane + 64, ((uint64_t)__float_as_uint(e) << 32) | tag);
+    }
+    if (lane == 0) {
+      st_dev(cmax + head * n_chunk_max + c, tagged(mc, tag));
+      s_flag = atomicAdd(&counters[head], 1) == nch - 1;
+    }
   }
   __syncthreads();
   if (!s_flag) return;
 
-  // ---- M, Z and the per-chunk factors exp(M_c - M)
-  const double2* st = stats + head * n_chunk_max;
+  // ---- M = max_c M_c, f_c = exp(M_c - M), m_j = e_j f_c / Z with Z = sum_j e_j f_c
+  int budget = kSpinBudget;
+  const uint64_t* cm = cmax + head * n_chunk_max;
   double mloc = -INFINITY;
-  for (int i = tid; i < nch; i += kThreads) mloc = fmax(mloc, st[i].x);
-  mloc = wave_max(mloc);
-  if (lane == 0) sm.f64[wave] = mloc;
-  __syncthreads();
-  double M = sm.f64[0];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) M = fmax(M, sm.f64[w]);
-  __syncthreads();
-  double zloc = 0.0;
   for (int i = tid; i < nch; i += kThreads) {
-    const double2 v = st[i];
-    const double f = exp(v.x - M);
-    ph.f[i] = f;
-    zloc += v.y * f;
+    const double mc = untag(settle(cm + i, ld_dev(cm + i), tag, budget));
+    s_f[i] = mc;
+    mloc = fmax(mloc, mc);
   }
-  zloc = wave_sum(zloc);
-  if (lane == 0) sm.f64[wave] = zloc;
+  const double M = block_reduce(mloc, sm.f64, [](double a, double b) { return fmax(a, b); });
+  for (int i = tid; i < nch; i += kThreads) s_f[i] = exp(s_f[i] - M);
   __syncthreads();
-  double Z = sm.f64[0];
+  const int cshift = __ffs(chunk_blocks) - 1;
+  uint64_t w[ROWS];
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) Z += sm.f64[w];
-  const double invZ = 1.0 / Z;
-
-  // ---- every block's mass into LDS (block j = row * kThreads + thread), -1 past nblk
-  const int rows = (nblk + kThreads - 1) / kThreads;
-  const double* eb = blk_e + head * nblk_max;
-  uint64_t fsum = 0;
-#pragma unroll 1
-  for (int i = 0; i < rows; ++i) {
+  for (int i = 0; i < ROWS; ++i) {
     const int j = i * kThreads + tid;
-    const float m = j < nblk ? (float)(eb[j] * (ph.f[j >> chunk_shift] * invZ)) : -1.0f;
-    s_mass[j] = m;
-    fsum += m > 0.f ? fixed_mass(m) : 0ull;
+    w[i] = j < nblk ? ld_dev(e_io + j) : 0ull;
   }
-  __syncthreads();  // ph.f is dead from here on
+  float m[ROWS];
+  double zloc = 0.0;
+#pragma unroll
+  for (int i = 0; i < ROWS; ++i) {
+    const int j = i * kThreads + tid;
+    m[i] = -1.0f;  // no block
+    if (j < nblk) {
+      const uint64_t x = settle(e_io + j, w[i], tag, budget);
+      const double e = (double)__uint_as_float((uint32_t)(x >> 32)) * s_f[j >> cshift];
+      m[i] = (float)e;
+      zloc += e;
+    }
+  }
+  const double invZ = 1.0 / block_reduce(zloc, sm.f64, SumOp());
+  uint64_t fsum = 0;
+  uint32_t bmin = 0xFFFFFFFFu, bmax = 0;
+#pragma unroll
+  for (int i = 0; i < ROWS; ++i) {
+    if (m[i] >= 0.f) {
+      m[i] = (float)((double)m[i] * invZ);
+      fsum += fixed_mass(m[i]);
+      bmin = min(bmin, __float_as_uint(m[i]));
+      bmax = max(bmax, __float_as_uint(m[i]));
+    }
+  }
 
   // threshold key: block j is selected iff key_of(m_j, j) >= thr
   uint64_t thr = 0;
   const float p = top_p[head];
   if (p < 1.0f && nblk > 1) {
     const uint64_t P = (uint64_t)ceil(ldexp((double)p, 62));
-    if (block_sum_u64(fsum, sm.u64) >= P) thr = select_threshold(s_mass, rows, nblk, P, sm, ph);
+    fsum = block_reduce(fsum, sm.u64, SumOp());
+    bmin = block_reduce(bmin, sm.u32a, MinOp());
+    bmax = block_reduce(bmax, sm.u32b, MaxOp());
+    if (fsum >= P)
+      thr = select_threshold<ROWS>(m, nblk, P, __builtin_amdgcn_readfirstlane(bmin),
+                                   __builtin_amdgcn_readfirstlane(bmax), sm);
   }
 
   // ---- ordered compaction of the selected ids (ascending)
-  auto sel = [&](int i) {
-    const int j = i * kThreads + tid;
-    const float m = s_mass[j];
-    return m >= 0.f && key_of(m, j) >= thr;
-  };
-  const int total = rows_prefix(rows, sel, sm);
+  bool sel[ROWS];
+#pragma unroll
+  for (int i = 0; i < ROWS; ++i) sel[i] = m[i] >= 0.f && key_of(m[i], i * kThreads + tid) >= thr;
+  const int total = rows_prefix(sel, sm);
   int* out = sel_idx + head * nblk_max;
-#pragma unroll 1
-  for (int i = 0; i < rows; ++i) {
-    const bool sl = sel(i);
-    const uint64_t bal = __ballot(sl);
-    if (sl) out[sm.rowtab[i * kWaves + wave] + __popcll(bal & lanemask_lt())] = i * kThreads + tid;
+#pragma unroll
+  for (int i = 0; i < ROWS; ++i) {
+    const int ord = ordinal(sel, i, sm);
+    if (sel[i]) out[ord] = i * kThreads + tid;
   }
   if (tid == 0) {
     sel_cnt[head] = total;
     atomicExch(&counters[head], 0);  // ready for the next call
+    __hip_atomic_store(&tags[head], tag % 4095u + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -553,21 +609,33 @@ extern "C" rtp_status rtp_index_topp(const void* q_pre, const void* w_q, const v
   if (ws_bytes < L.total) return RTP_EINVAL;
   char* ws = static_cast<char*>(workspace);
   int* counters = reinterpret_cast<int*>(ws + L.off_counters);
-  double2* stats = reinterpret_cast<double2*>(ws + L.off_stats);
-  double* blk_e = reinterpret_cast<double*>(ws + L.off_e);
+  uint32_t* tags = reinterpret_cast<uint32_t*>(ws + L.off_tag);
+  uint64_t* cmax = reinterpret_cast<uint64_t*>(ws + L.off_cmax);
+  uint64_t* blk_e = reinterpret_cast<uint64_t*>(ws + L.off_e);
   dim3 grid(L.n_chunk, n_ret, B);
-  const size_t dyn = (size_t)L.rows * kThreads * sizeof(float);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint16_t* qp = static_cast<const uint16_t*>(q_pre);
   const uint16_t* wq = static_cast<const uint16_t*>(w_q);
   const uint16_t* ki = static_cast<const uint16_t*>(k_idx);
-  if (block == 64)
-    hipLaunchKernelGGL(index_topp_kernel<64>, grid, dim3(kThreads), dyn, s, qp, wq, ki, seq_lens,
-                       ret_heads, top_p, Hq, n_ret, max_ctx, L.nblk_max, L.chunk_blocks, L.chunk_shift,
-                       L.n_chunk, sel_idx, sel_cnt, counters, stats, blk_e);
-  else
-    hipLaunchKernelGGL(index_topp_kernel<128>, grid, dim3(kThreads), dyn, s, qp, wq, ki, seq_lens,
-                       ret_heads, top_p, Hq, n_ret, max_ctx, L.nblk_max, L.chunk_blocks, L.chunk_shift,
-                       L.n_chunk, sel_idx, sel_cnt, counters, stats, blk_e);
+#define RTP_K1(BKV, RV)                                                                         \
+  hipLaunchKernelGGL((index_topp_kernel<BKV, RV>), grid, dim3(kThreads), 0, s, qp, wq, ki,        \
+                     seq_lens, ret_heads, top_p, Hq, n_ret, max_ctx, L.nblk_max, L.chunk_blocks, \
+                     L.n_chunk, sel_idx, sel_cnt, counters, tags, cmax, blk_e)
+#define RTP_K1_ROWS(BKV)                 \
+  switch (L.rows) {                      \
+    case 1: RTP_K1(BKV, 1); break;       \
+    case 2: RTP_K1(BKV, 2); break;       \
+    case 4: RTP_K1(BKV, 4); break;       \
+    case 8: RTP_K1(BKV, 8); break;       \
+    case 16: RTP_K1(BKV, 16); break;     \
+    default: RTP_K1(BKV, 32); break;     \
+  }
+  if (block == 64) {
+    RTP_K1_ROWS(64)
+  } else {
+    RTP_K1_ROWS(128)
+  }
+#undef RTP_K1_ROWS
+#undef RTP_K1
   return hipGetLastError() == hipSuccess ? RTP_OK : RTP_ELAUNCH;
 }

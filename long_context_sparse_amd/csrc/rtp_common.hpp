@@ -19,25 +19,65 @@ constexpr float kLn2f = 0.69314718055994530941723212145818f;
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Cross-lane moves on the VALU (DPP, gfx9 controls), no LDS traffic.  Every lane's
+// source is inside its row, so no lane reads out of range.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within each 8 lanes
+constexpr int kDppMirror = 0x140;     // lane i <- lane 15-i within each 16 lanes
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)b, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+__device__ __forceinline__ float readlane_f32(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)b, l);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+// Wave-wide reductions: a butterfly within each row of 16 lanes (after it every lane of
+// a row holds the same row result), then the four rows combined in a fixed order, so
+// the result is identical in every lane and independent of the lane order.
+template <class T, class Op>
+__device__ __forceinline__ T wave_reduce_dpp(T v, Op op) {
+  if constexpr (sizeof(T) == 8) {
+    v = op(v, dpp_f64<kDppXor1>(v));
+    v = op(v, dpp_f64<kDppXor2>(v));
+    v = op(v, dpp_f64<kDppHalfMirror>(v));
+    v = op(v, dpp_f64<kDppMirror>(v));
+    return op(op(readlane_f64(v, 0), readlane_f64(v, 16)), op(readlane_f64(v, 32), readlane_f64(v, 48)));
+  } else {
+    v = op(v, dpp_f32<kDppXor1>(v));
+    v = op(v, dpp_f32<kDppXor2>(v));
+    v = op(v, dpp_f32<kDppHalfMirror>(v));
+    v = op(v, dpp_f32<kDppMirror>(v));
+    return op(op(readlane_f32(v, 0), readlane_f32(v, 16)), op(readlane_f32(v, 32), readlane_f32(v, 48)));
+  }
+}
+
 __device__ __forceinline__ double wave_max(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o));
-  return v;
+  return wave_reduce_dpp(v, [](double a, double b) { return fmax(a, b); });
 }
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  return wave_reduce_dpp(v, [](double a, double b) { return a + b; });
 }
 __device__ __forceinline__ float wave_maxf(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  return wave_reduce_dpp(v, [](float a, float b) { return fmaxf(a, b); });
 }
 __device__ __forceinline__ float wave_sumf(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  return wave_reduce_dpp(v, [](float a, float b) { return a + b; });
 }
 
 // 2^x on the hardware transcendental unit (no range reduction needed for decode logits).

@@ -12,9 +12,9 @@
 // Local heads: the same core over attention sinks + the sliding window (RTPurbo
 // review, Adaptive sparse attention: local heads keep only window + sinks).
 // Workgroup = (split, KV group, sequence); split 0 holds the sinks, splits 1.. hold
-// consecutive window chunks.  Each workgroup writes per-head partials to the
-// workspace; the last one of each (sequence, KV group), found with an atomic counter,
-// merges them with the log-sum-exp rule and writes the output rows.
+// consecutive window chunks.  Each workgroup writes per-head (o, lse) partials to the
+// workspace, and a merge kernel (one workgroup per output row, the same kernel as the
+// cross-split reduce) combines them with the log-sum-exp rule.
 
 #include "rtp_attn.hpp"
 
@@ -138,8 +138,8 @@ template <int G>
 __global__ __launch_bounds__(kThreads) void local_window_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int* __restrict__ seq_lens, const int* __restrict__ loc_heads, int Hq, int Hkv, int n_loc,
-    int max_ctx, int window, int sinks, int split_tokens, int n_split, float* __restrict__ out,
-    int* __restrict__ counters, float* __restrict__ ws_lse, float* __restrict__ ws_o) {
+    int max_ctx, int window, int sinks, int split_tokens, int n_split, float* __restrict__ ws_o,
+    float* __restrict__ ws_lse) {
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int ibeg, iend;
@@ -161,7 +161,6 @@ __global__ __launch_bounds__(kThreads) void local_window_kernel(
 
   __shared__ float s_m[kWaves * G], s_l[kWaves * G];
   __shared__ float s_acc[kWaves * G * kHeadDim];
-  __shared__ int s_flag;
 
   AttnState<G> st;
   attn_init(st);
@@ -189,51 +188,55 @@ __global__ __launch_bounds__(kThreads) void local_window_kernel(
     ws_o[(hr * n_split + c) * kHeadDim + d] = o;
     if (d == 0) ws_lse[hr * n_split + c] = lse;
   }
-  __syncthreads();
-  const size_t grp = (size_t)b * Hkv + g;
-  if (tid == 0) {
-    __threadfence();  // release the partials device-wide
-    const int prev = atomicAdd(&counters[grp], 1);
-    s_flag = prev == n_split - 1;
-    if (s_flag) __threadfence();  // acquire every split's partials
-  }
-  __syncthreads();
-  if (!s_flag) return;
-  for (int idx = tid; idx < nh * kHeadDim; idx += kThreads) {
-    const int h = idx >> 7, d = idx & (kHeadDim - 1);
-    const size_t hr = (size_t)b * n_loc + ibeg + h;
-    const float* lp = ws_lse + hr * n_split;
-    const float* op = ws_o + hr * n_split * kHeadDim + d;
-    float M = -INFINITY;
-    for (int s = 0; s < n_split; ++s) M = fmaxf(M, lp[s]);
-    float L = 0.f, A = 0.f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < n_split; ++s) {
-        const float w = __expf(lp[s] - M);
-        L += w;
-        A = fmaf(w, op[(size_t)s * kHeadDim], A);
-      }
-    }
-    out[((size_t)b * Hq + loc_heads[ibeg + h]) * kHeadDim + d] = L > 0.f ? A / L : 0.f;
-  }
-  if (tid == 0) atomicExch(&counters[grp], 0);  // ready for the next call
 }
 
-__global__ __launch_bounds__(kHeadDim) void split_reduce_kernel(
-    const float* __restrict__ o_part, const float* __restrict__ lse_part,
-    const int* __restrict__ heads, int Hq, int n_heads, int n_split, float* __restrict__ out) {
+// Log-sum-exp merge of n_split partials for one output row per workgroup (128 threads,
+// thread = output dim): L = log sum_c exp(lse_c); out = sum_c exp(lse_c - L) o_c.
+// The split weights go through LDS in chunks of kMergeChunk; the partial rows are read
+// eight splits at a time so their loads overlap.  Rows whose partials are all empty
+// (lse = -inf) are written 0.
+constexpr int kMergeChunk = 512;
+
+__global__ __launch_bounds__(kHeadDim) void merge_kernel(
+    const float* __restrict__ o_part, const float* __restrict__ lse_part, const int* __restrict__ heads,
+    int Hq, int n_heads, int n_split, float* __restrict__ out) {
   const int i = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const int lane = d & 63, wave = d >> 6;
   const size_t hr = (size_t)b * n_heads + i;
   const float* lp = lse_part + hr * n_split;
   const float* op = o_part + hr * n_split * kHeadDim + d;
-  float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, lp[s]);
+  __shared__ float s_w[kMergeChunk];
+  __shared__ float s_red[2];
+  float mloc = -INFINITY;
+  for (int c = d; c < n_split; c += kHeadDim) mloc = fmaxf(mloc, lp[c]);
+  mloc = wave_maxf(mloc);
+  if (lane == 0) s_red[wave] = mloc;
+  __syncthreads();
+  const float M = fmaxf(s_red[0], s_red[1]);
   float L = 0.f, A = 0.f;
   if (M != -INFINITY) {
-    for (int s = 0; s < n_split; ++s) {
-      const float w = __expf(lp[s] - M);
-      L += w;
-      A = fmaf(w, op[(size_t)s * kHeadDim], A);
+    for (int c0 = 0; c0 < n_split; c0 += kMergeChunk) {
+      const int nc = min(kMergeChunk, n_split - c0);
+      __syncthreads();
+      for (int c = d; c < nc; c += kHeadDim) s_w[c] = __expf(lp[c0 + c] - M);
+      __syncthreads();
+      int c = 0;
+      for (; c + 8 <= nc; c += 8) {
+        float ov[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) ov[u] = op[(size_t)(c0 + c + u) * kHeadDim];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float w = s_w[c + u];
+          L += w;
+          A = fmaf(w, ov[u], A);
+        }
+      }
+      for (; c < nc; ++c) {
+        const float w = s_w[c];
+        L += w;
+        A = fmaf(w, op[(size_t)(c0 + c) * kHeadDim], A);
+      }
     }
   }
   out[((size_t)b * Hq + heads[i]) * kHeadDim + d] = L > 0.f ? A / L : 0.f;
@@ -241,7 +244,7 @@ __global__ __launch_bounds__(kHeadDim) void split_reduce_kernel(
 
 struct LocalLayout {
   int split_tokens, n_split;
-  size_t off_counters, off_lse, off_o, total;
+  size_t off_lse, off_o, total;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -254,9 +257,8 @@ LocalLayout local_layout(int B, int Hkv, int n_loc, int window) {
   while (st > 64 && groups * ceil_div(max(window, 1), st) < 1024) st >>= 1;
   L.split_tokens = st;
   L.n_split = 1 + ceil_div(window, st);
-  L.off_counters = 0;
-  L.off_lse = align256((size_t)groups * sizeof(int));
-  L.off_o = L.off_lse + align256((size_t)B * n_loc * L.n_split * sizeof(float));
+  L.off_lse = 0;
+  L.off_o = align256((size_t)B * n_loc * L.n_split * sizeof(float));
   L.total = L.off_o + align256((size_t)B * n_loc * L.n_split * kHeadDim * sizeof(float));
   return L;
 }
@@ -332,7 +334,7 @@ extern "C" rtp_status rtp_split_reduce(const float* o_part, const float* lse_par
   if (n_heads == 0) return RTP_OK;
   if (!o_part || !lse_part || !heads || !out) return RTP_EINVAL;
   if (B > 65535) return RTP_EUNSUPPORTED;
-  hipLaunchKernelGGL(split_reduce_kernel, dim3(n_heads, B), dim3(kHeadDim), 0,
+  hipLaunchKernelGGL(merge_kernel, dim3(n_heads, B), dim3(kHeadDim), 0,
                      static_cast<hipStream_t>(stream), o_part, lse_part, heads, Hq, n_heads, n_split,
                      out);
   return hipGetLastError() == hipSuccess ? RTP_OK : RTP_ELAUNCH;
@@ -362,7 +364,6 @@ extern "C" rtp_status rtp_local_window_attn(const void* q, const void* k_cache, 
   if (ws_bytes < L.total) return RTP_EINVAL;
   if (L.n_split > 65535) return RTP_EUNSUPPORTED;
   char* ws = static_cast<char*>(workspace);
-  int* counters = reinterpret_cast<int*>(ws + L.off_counters);
   float* ws_lse = reinterpret_cast<float*>(ws + L.off_lse);
   float* ws_o = reinterpret_cast<float*>(ws + L.off_o);
   dim3 grid(L.n_split, Hkv, B);
@@ -373,13 +374,15 @@ extern "C" rtp_status rtp_local_window_attn(const void* q, const void* k_cache, 
 #define RTP_LOCAL(GG)                                                                         \
   hipLaunchKernelGGL(local_window_kernel<GG>, grid, dim3(kThreads), 0, s, qq, kk, vv, seq_lens, \
                      loc_heads, Hq, Hkv, n_loc, max_ctx, window, sinks, L.split_tokens,          \
-                     L.n_split, out, counters, ws_lse, ws_o)
+                     L.n_split, ws_o, ws_lse)
   switch (Hq / Hkv) {
     case 1: RTP_LOCAL(1); break;
     case 2: RTP_LOCAL(2); break;
     case 4: RTP_LOCAL(4); break;
     default: RTP_LOCAL(8); break;
   }
+  hipLaunchKernelGGL(merge_kernel, dim3(n_loc, B), dim3(kHeadDim), 0, s, ws_o, ws_lse, loc_heads, Hq,
+                     n_loc, L.n_split, out);
 #undef RTP_LOCAL
   return hipGetLastError() == hipSuccess ? RTP_OK : RTP_ELAUNCH;
 }

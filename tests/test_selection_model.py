@@ -3,8 +3,9 @@ oracle with the acceptance rule on large, tied and near-tied mass vectors.
 
 The model restates the algorithm the index kernel runs in its last workgroup
 (fp32 block masses, composite keys (mass bits, inverted block id), fixed-point
-masses in 2^-62 units, splitter refinement while more than 512 candidates remain,
-exact ranking of the rest).  It exercises the algorithm's logic at sizes and
+masses in 2^-62 units, refinement by 256-bin histograms over the mass bits while
+more than 64 candidates of unequal mass remain, exact ranking of the rest, and the
+equal-mass case resolved by count in ascending block order).  It exercises the algorithm's logic at sizes and
 distributions the device sees (up to 16384 blocks) without a GPU; the device code
 itself is covered by the GPU parity tests.
 """
@@ -14,15 +15,9 @@ import pytest
 from oracle import accept as A
 from oracle import rtp_oracle as O
 
-SPLITTERS = 63
-FINAL = 512
+BINS = 256
+FINAL = 64
 MASK64 = (1 << 64) - 1
-
-
-def _keys(mf):
-    bits = mf.astype(np.float32).view(np.uint32).astype(np.uint64)
-    j = np.arange(mf.shape[0], dtype=np.uint64)
-    return (bits << np.uint64(32)) | (np.uint64(0xFFFFFFFF) - j)
 
 
 def _fixed(mf):
@@ -30,51 +25,63 @@ def _fixed(mf):
 
 
 def model_select(m64, p):
-    """Blocks the device algorithm selects for fp64 masses m64 and threshold p (fp32)."""
+    """Blocks the device algorithm selects for fp64 masses m64 and threshold p (fp32).
+
+    Returns (blocks, levels)."""
     mf = np.asarray(m64, dtype=np.float32)
     n = mf.shape[0]
     p = float(np.float32(p))
     if p >= 1.0 or n == 1:
         return np.arange(n), 0
-    keys = [int(k) for k in _keys(mf)]
+    bits = [int(b) for b in mf.view(np.uint32)]
+    keys = [(bits[j] << 32) | (0xFFFFFFFF - j) for j in range(n)]
     fm = _fixed(mf)
     P = int(np.ceil(np.ldexp(p, 62)))
     if sum(fm) < P:
         return np.arange(n), 0
-    lo, hi, cab, cnt = 1, MASK64, 0, n
+    lo, hi, cab, cnt = min(bits), max(bits), 0, n
     levels = 0
-    while cnt > FINAL:
-        cands = [j for j in range(n) if lo <= keys[j] < hi]
-        assert len(cands) == cnt
-        stride = cnt // SPLITTERS
-        samp = [keys[cands[o]] for o in range(0, SPLITTERS * stride, stride)]
-        split = sorted(samp, reverse=True)
-        bc = [0] * (SPLITTERS + 1)
-        bm = [0] * (SPLITTERS + 1)
-        for j in cands:
-            a = sum(1 for s in split if s > keys[j])
-            bc[a] += 1
-            bm[a] += fm[j]
-        run = cab
-        for b in range(SPLITTERS + 1):
-            if run + bm[b] >= P and run < P:
-                new = (bc[b], split[b - 1] if b > 0 else hi, split[b] if b < SPLITTERS else lo, run)
+    while cnt > FINAL and lo < hi:
+        span = hi - lo
+        shift = max(0, span.bit_length() - 8)
+        bm = [0] * BINS
+        bc = [0] * BINS
+        bmin = [None] * BINS
+        bmax = [None] * BINS
+        for j in range(n):
+            if lo <= bits[j] <= hi:
+                b = (bits[j] - lo) >> shift
+                assert 0 <= b < BINS
+                bm[b] += fm[j]
+                bc[b] += 1
+                bmin[b] = bits[j] if bmin[b] is None else min(bmin[b], bits[j])
+                bmax[b] = bits[j] if bmax[b] is None else max(bmax[b], bits[j])
+        above = cab
+        for b in range(BINS - 1, -1, -1):
+            if bm[b] > 0 and above < P <= above + bm[b]:
+                new = (above, bc[b], bmin[b], bmax[b])
                 break
-            run += bm[b]
-        nc, hi, lo, cab = new
-        assert 0 < nc < cnt
-        cnt = nc
+            above += bm[b]
+        cab, nc, nlo, nhi = new
+        assert nhi - nlo < max(1, span) or span == 0
+        cnt, lo, hi = nc, nlo, nhi
         levels += 1
-    cands = sorted((keys[j] for j in range(n) if lo <= keys[j] < hi), reverse=True)
-    run = cab
-    thr = None
-    for k in cands:
-        f = fm[MASK64 & (0xFFFFFFFF - (k & 0xFFFFFFFF))]
-        if run < P <= run + f:
-            thr = k
-            break
-        run += f
-    assert thr is not None
+    cands = [j for j in range(n) if lo <= bits[j] <= hi]
+    assert len(cands) == cnt
+    if cnt > FINAL:
+        # all candidates have equal mass: the k-th in ascending block order
+        f = fm[cands[0]]
+        k = -(-(P - cab) // f)
+        thr = keys[cands[k - 1]]
+    else:
+        run = cab
+        thr = None
+        for j in sorted(cands, key=lambda j: keys[j], reverse=True):
+            if run < P <= run + fm[j]:
+                thr = keys[j]
+                break
+            run += fm[j]
+        assert thr is not None
     return np.array([j for j in range(n) if keys[j] >= thr]), levels
 
 
@@ -110,8 +117,7 @@ def test_model_matches_oracle(kind, n, p):
     sel = O.select_top_p(m, float(np.float32(p)))
     ok, why = A.accept_selection(m, float(np.float32(p)), G, sel)
     assert ok, why
-    if kind in ("diffuse", "peaked") and n > FINAL:
-        assert levels <= 3
+    assert levels <= 5
 
 
 def test_model_ties_follow_block_order():
