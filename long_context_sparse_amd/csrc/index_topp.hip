@@ -60,7 +60,7 @@ struct K1Layout {
   size_t off_counters, off_tag, off_cmax, off_e, total;
 };
 
-// Chunk size: aim for >= 1024 workgroups over the whole batch, 8..128 blocks a chunk,
+// Chunk size: aim for >= 512 workgroups over the whole batch, 8..128 blocks a chunk,
 // at most kMaxChunks chunks per head.  rows = blocks per thread in the selection
 // (a power of two).
 K1Layout k1_layout(int B, int n_ret, int max_ctx, int block) {
@@ -68,7 +68,7 @@ K1Layout k1_layout(int B, int n_ret, int max_ctx, int block) {
   L.nblk_max = ceil_div(max_ctx, block);
   long long total_blocks = (long long)B * n_ret * L.nblk_max;
   int cb = kMaxChunkBlocks;
-  while (cb > 8 && total_blocks / cb < 1024) cb >>= 1;
+  while (cb > 8 && total_blocks / cb < 512) cb >>= 1;
   while (ceil_div(L.nblk_max, cb) > kMaxChunks && cb < kMaxChunkBlocks) cb <<= 1;
   L.chunk_blocks = cb;
   L.n_chunk = ceil_div(L.nblk_max, cb);

@@ -25,20 +25,40 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxSplitBlocks = 2048;
 
-__device__ __forceinline__ int lower_bound_dev(const int* __restrict__ a, int n, int key) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (a[mid] < key) lo = mid + 1; else hi = mid;
-  }
-  return lo;
-}
-
-// contiguous range [beg, end) of an ascending head list that falls in KV group g
+// Contiguous range [beg, end) of an ascending head list that falls in KV group g,
+// found by one wave with 64 parallel loads per round (every lane gets the result).
 __device__ __forceinline__ void group_range(const int* __restrict__ heads, int n, int g, int G,
                                             int& beg, int& end) {
-  beg = lower_bound_dev(heads, n, g * G);
-  end = lower_bound_dev(heads, n, (g + 1) * G);
+  const int lane = threadIdx.x & 63;
+  beg = 0;
+  end = 0;
+  for (int i0 = 0; i0 < n; i0 += 64) {
+    const int i = i0 + lane;
+    const int h = i < n ? heads[i] : 0x7fffffff;
+    beg += __popcll(__ballot(h < g * G));
+    end += __popcll(__ballot(h < (g + 1) * G));
+  }
+}
+
+// First index of the ascending list a[0, n) whose value is >= key (n if none), found by
+// one wave: each round probes 64 evenly spaced entries of the remaining range, so a
+// list of 16K entries takes three rounds of parallel loads.
+__device__ __forceinline__ int lower_bound_wave(const int* __restrict__ a, int n, int key) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, hi = n;  // the answer lies in [lo, hi]
+  while (lo < hi) {
+    const int step = (hi - lo + 63) / 64;
+    const int idx = lo + lane * step;
+    const int k = __popcll(__ballot(idx < hi && a[idx] < key));  // probes below key: a prefix
+    if (k == 0) break;
+    if (step == 1) {
+      lo += k;
+      break;
+    }
+    hi = min(hi, lo + k * step);
+    lo += (k - 1) * step + 1;
+  }
+  return lo;
 }
 
 template <int BK, int G>
@@ -65,18 +85,21 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(
   __shared__ float s_m[kWaves * G], s_l[kWaves * G];
   __shared__ float s_acc[kWaves * G * kHeadDim];
 
+  __shared__ int s_rng[2 * G];
   int nL = 0;
   if (jlo < jhi) {
     const int nb = jhi - jlo;
     for (int i = tid; i < (nb + 3) / 4; i += kThreads) s_hm[i] = 0;
+    // each head's entries in [jlo, jhi): one wave per (head, bound)
+    for (int pr = wave; pr < 2 * nh; pr += kWaves) {
+      const size_t hr = (size_t)b * n_ret + rbeg + (pr >> 1);
+      const int v = lower_bound_wave(sel_idx + hr * nblk_max, sel_cnt[hr], (pr & 1) ? jhi : jlo);
+      if (lane == 0) s_rng[pr] = v;
+    }
     __syncthreads();
     for (int h = 0; h < nh; ++h) {
-      const size_t hr = (size_t)b * n_ret + rbeg + h;
-      const int cnt = sel_cnt[hr];
-      const int* sl = sel_idx + hr * nblk_max;
-      const int a = lower_bound_dev(sl, cnt, jlo);
-      const int e = lower_bound_dev(sl, cnt, jhi);
-      for (int i = a + tid; i < e; i += kThreads) {
+      const int* sl = sel_idx + ((size_t)b * n_ret + rbeg + h) * nblk_max;
+      for (int i = s_rng[2 * h] + tid; i < s_rng[2 * h + 1]; i += kThreads) {
         const int off = sl[i] - jlo;
         atomicOr(&s_hm[off >> 2], (1u << h) << ((off & 3) * 8));
       }

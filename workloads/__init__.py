@@ -138,13 +138,13 @@ def _named() -> Dict[str, DecodeConfig]:
     # window unspecified for 128K and 1M: the pages' main configuration (8192 + 4 sinks)
     c["ctx128k"] = DecodeConfig(
         name="ctx128k", seed=3, B=4, Hkv=8, Hq=32, n_ret=8, ctx=(131072,) * 4, block=64,
-        top_p=(0.95,) * 8, window=8192, sinks=4, split_tokens=4096, kind="peaked_diffuse")
+        top_p=(0.95,) * 8, window=8192, sinks=4, split_tokens=1024, kind="peaked_diffuse")
     c["ctx1m"] = DecodeConfig(
         name="ctx1m", seed=4, B=1, Hkv=8, Hq=32, n_ret=4, ctx=(1 << 20,), block=128,
         top_p=(0.95,) * 4, window=8192, sinks=4, split_tokens=65536, kind="depth_needles")
     c["mixed"] = DecodeConfig(
         name="mixed", seed=5, B=16, Hkv=8, Hq=32, n_ret=6, ctx=_mixed_ctx(5), block=64,
-        top_p=_mixed_p(5, 6), window=2048, sinks=4, split_tokens=4096, kind="peaked_diffuse")
+        top_p=_mixed_p(5, 6), window=2048, sinks=4, split_tokens=1024, kind="peaked_diffuse")
     return c
 
 
