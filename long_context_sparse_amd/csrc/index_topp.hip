@@ -23,9 +23,9 @@
 //   Every workgroup then bumps an arrival counter; the last one of each (b, r) does
 //   the selection.  So no device-scope fence (an L2 write-back on every workgroup of
 //   every XCD) is needed, and a word from the previous call is never taken as current.
-//   Selection (last workgroup): M = max_c M_c and every block's mass
-//   m_j = e_j exp(M_c - M) / Z in fp32,
-//   ROWS per thread in registers, then the greedy threshold exactly: a key = (fp32
+//   Selection (last workgroup): M = max_c M_c, Z = sum_c Z_c exp(M_c - M) and every
+//   block's mass m_j = e_j exp(M_c - M) / Z in fp32 into LDS, then the greedy
+//   threshold exactly: a key = (fp32
 //   mass bits, inverted block id) orders blocks by mass with ties by ascending id;
 //   masses are summed as fixed-point integers (2^-62 units) so every cumulative sum
 //   is exact and order-independent.  While more than 64 candidates of unequal mass
@@ -45,13 +45,14 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxChunkBlocks = 128;
-constexpr int kMaxChunks = 1024;
+constexpr int kMaxChunks = 1024;  // two per thread in the selection
 constexpr int kMaxRows = 32;                  // blocks per thread in the selection
 constexpr int kMaxBlocks = kMaxRows * kThreads;
 constexpr int kBins = 256;                    // histogram bins per refinement level
 constexpr int kFinal = kWave;                 // candidates ranked directly (one per lane)
 constexpr int kSpinBudget = 1 << 12;          // re-reads a thread may spend waiting for a tag
 constexpr uint64_t kTagBits = 0xFFFull;
+static_assert(kMaxChunks == 2 * kThreads, "the selection reads two chunk records per thread");
 
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -61,8 +62,7 @@ struct K1Layout {
 };
 
 // Chunk size: aim for >= 512 workgroups over the whole batch, 8..128 blocks a chunk,
-// at most kMaxChunks chunks per head.  rows = blocks per thread in the selection
-// (a power of two).
+// at most kMaxChunks chunks per head.  rows = blocks per thread in the selection.
 K1Layout k1_layout(int B, int n_ret, int max_ctx, int block) {
   K1Layout L{};
   L.nblk_max = ceil_div(max_ctx, block);
@@ -72,13 +72,12 @@ K1Layout k1_layout(int B, int n_ret, int max_ctx, int block) {
   while (ceil_div(L.nblk_max, cb) > kMaxChunks && cb < kMaxChunkBlocks) cb <<= 1;
   L.chunk_blocks = cb;
   L.n_chunk = ceil_div(L.nblk_max, cb);
-  L.rows = 1;
-  while (L.rows * kThreads < L.nblk_max) L.rows <<= 1;
+  L.rows = ceil_div(L.nblk_max, kThreads);
   const size_t heads = (size_t)B * n_ret;
   L.off_counters = 0;
   L.off_tag = align_up(heads * sizeof(int), 256);
   L.off_cmax = L.off_tag + align_up(heads * sizeof(uint32_t), 256);
-  L.off_e = L.off_cmax + align_up(heads * L.n_chunk * sizeof(uint64_t), 256);
+  L.off_e = L.off_cmax + align_up(heads * L.n_chunk * 2 * sizeof(uint64_t), 256);
   L.total = L.off_e + align_up(heads * (size_t)L.nblk_max * sizeof(uint64_t), 256);
   return L;
 }
@@ -128,12 +127,12 @@ struct TailSmem {
   uint32_t bcnt[kBins];           // per bin: candidate count
   int rowtab[kMaxRows * kWaves];  // per (row, wave) counts, then exclusive prefixes
   uint64_t u64[kWaves];
-  double f64[kWaves];
-  int i32[kWaves];
+  double f64[kWaves], f64b[kWaves];
   uint32_t u32a[kWaves], u32b[kWaves];
-  uint64_t ckey[kFinal], cfm[kFinal], skey[kFinal], sfm[kFinal];  // final candidates
+  uint64_t ckey[kFinal], cfm[kFinal];  // final candidates (any order)
   uint64_t cab, thr;
-  int cnt, bin;
+  uint32_t lo, hi;
+  int cnt, nfin, total;
 };
 
 template <class T, class Op>
@@ -191,159 +190,190 @@ __device__ __forceinline__ T block_excl_scan(T v, T* red, T& total) {
   return base + incl - v;
 }
 
-// Block j = row * kThreads + thread; flags[row] says whether this thread's block of the
-// row satisfies some predicate.  Fills rowtab with the exclusive prefix, in ascending
+// Selection rows: block j = row * kThreads + thread, row < rows, masses in LDS (< 0 for
+// no block).  Every pass reads a thread's masses kRowBatch rows at a time so the LDS
+// latencies overlap.
+constexpr int kRowBatch = 8;
+
+template <class F>
+__device__ __forceinline__ void for_rows(const float* __restrict__ sm_m, int rows, F f) {
+  const int tid = threadIdx.x;
+  for (int i0 = 0; i0 < rows; i0 += kRowBatch) {
+    float mm[kRowBatch];
+#pragma unroll
+    for (int u = 0; u < kRowBatch; ++u) mm[u] = i0 + u < rows ? sm_m[(i0 + u) * kThreads + tid] : -1.0f;
+#pragma unroll
+    for (int u = 0; u < kRowBatch; ++u)
+      if (i0 + u < rows) f(i0 + u, mm[u]);
+  }
+}
+
+// For a predicate on (row, mass), fills rowtab with the exclusive prefix, in ascending
 // block order, of the satisfying blocks per (row, wave) and returns their total; the
 // ordinal of a satisfying block is then rowtab[row * kWaves + wave] + (satisfying
-// lanes below it in its wave).
-template <int ROWS>
-__device__ __forceinline__ int rows_prefix(const bool (&flags)[ROWS], TailSmem& sm) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-#pragma unroll
-  for (int i = 0; i < ROWS; ++i) {
-    const uint64_t bal = __ballot(flags[i]);
+// lanes below it in its wave).  One wave scans the table.
+template <class Pred>
+__device__ __forceinline__ int rows_prefix(const float* __restrict__ sm_m, int rows, Pred pred,
+                                           TailSmem& sm) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for_rows(sm_m, rows, [&](int i, float m) {
+    const uint64_t bal = __ballot(pred(i, m));
     if (lane == 0) sm.rowtab[i * kWaves + wave] = __popcll(bal);
+  });
+  __syncthreads();
+  if (wave == 0) {
+    constexpr int R = (kMaxRows * kWaves + 63) / 64;  // table entries a lane
+    const int n = rows * kWaves;
+    int v[R], tot = 0;
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const int idx = lane * R + k;
+      v[k] = idx < n ? sm.rowtab[idx] : 0;
+      tot += v[k];
+    }
+    int incl = tot;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    int run = incl - tot;
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const int idx = lane * R + k;
+      if (idx < n) sm.rowtab[idx] = run;
+      run += v[k];
+    }
+    if (lane == 63) sm.total = incl;
   }
   __syncthreads();
-  const int v = tid < ROWS * kWaves ? sm.rowtab[tid] : 0;
-  int total;
-  const int excl = block_excl_scan(v, sm.i32, total);
-  if (tid < ROWS * kWaves) sm.rowtab[tid] = excl;
-  __syncthreads();
-  return total;
+  return sm.total;
 }
 
-template <int ROWS>
-__device__ __forceinline__ int ordinal(const bool (&flags)[ROWS], int i, const TailSmem& sm) {
+__device__ __forceinline__ int ordinal(bool flag, int i, const TailSmem& sm) {
   const int wave = threadIdx.x >> 6;
-  return sm.rowtab[i * kWaves + wave] + __popcll(__ballot(flags[i]) & lanemask_lt());
+  return sm.rowtab[i * kWaves + wave] + __popcll(__ballot(flag) & lanemask_lt());
 }
 
-// Exact greedy top-p threshold over the masses m[] (block i * kThreads + thread; < 0
-// for none).  Returns the key of the last admitted block: the selected set is every
-// block whose key is >= it.  Preconditions: the total fixed-point mass reaches P;
-// [lo, hi] spans the mass bits of all blocks.
+__device__ __forceinline__ uint64_t key_at(int i, float m) {
+  return key_of(m, i * kThreads + (int)threadIdx.x);
+}
+
+// Exact greedy top-p threshold over the masses in LDS.  Returns the key of the last
+// admitted block: the selected set is every block whose key is >= it.  Preconditions:
+// the total fixed-point mass reaches P; [lo, hi] spans the mass bits of all blocks;
+// the bins and the final-candidate count are zero.
 //
 // Candidates are the blocks whose mass bits lie in [lo, hi], with fixed mass `cab`
 // strictly above them, and cab < P <= cab + mass(candidates) holds throughout.  A
 // level puts every candidate into one of kBins bins by (bits - lo) >> shift, a
 // monotone map, so bins are contiguous ranges of mass (about log-uniform, since fp32
-// bits grow with log2 of the value); the bin where cab + cumulative mass from the top
-// crosses P holds the threshold, and its candidates' bit range becomes the new range,
-// at least kBins/2 times narrower.  It ends when <= kFinal candidates remain (ranked
-// exactly), or when all candidates have equal mass: the threshold is then the k-th of
-// them in ascending block order, k = ceil((P - cab) / mass).
-template <int ROWS>
-__device__ uint64_t select_threshold(const float (&m)[ROWS], int nblk, uint64_t P, uint32_t lo,
-                                     uint32_t hi, TailSmem& sm) {
+// bits grow with log2 of the value); one wave scans the bins from the top, finds the
+// bin where cab + cumulative mass crosses P, takes its bit range as the new candidate
+// range (at least kBins/2 times narrower) and clears the bins.  It ends when <= kFinal
+// candidates remain (ranked exactly by one wave), or when the range is a single mass
+// value: the threshold is then the k-th candidate in ascending block order,
+// k = ceil((P - cab) / mass).
+__device__ uint64_t select_threshold(const float* __restrict__ sm_m, int rows, int nblk, uint64_t P,
+                                     uint32_t lo, uint32_t hi, TailSmem& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint64_t cab = 0;
   int cnt = nblk;
-  auto cand = [&](int i) {
-    const uint32_t bits = __float_as_uint(m[i]);
-    return m[i] >= 0.f && bits >= lo && bits <= hi;
+  auto cand = [&](float m) {
+    const uint32_t bits = __float_as_uint(m);
+    return m >= 0.f && bits >= lo && bits <= hi;
   };
   while (cnt > kFinal && lo < hi) {
     const uint32_t span = hi - lo;
     const int shift = max(0, 32 - (int)__clz(span) - 8);  // (span >> shift) < kBins
-    if (tid < kBins) {
-      sm.bmass[tid] = 0;
-      sm.bcnt[tid] = 0;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < ROWS; ++i) {
-      if (cand(i)) {
-        const int bin = (int)((__float_as_uint(m[i]) - lo) >> shift);
-        atomicAdd((unsigned long long*)&sm.bmass[bin], (unsigned long long)fixed_mass(m[i]));
+    for_rows(sm_m, rows, [&](int i, float m) {
+      if (cand(m)) {
+        const int bin = (int)((__float_as_uint(m) - lo) >> shift);
+        atomicAdd((unsigned long long*)&sm.bmass[bin], (unsigned long long)fixed_mass(m));
         atomicAdd(&sm.bcnt[bin], 1u);
       }
-    }
+    });
     __syncthreads();
-    // thread t holds bin kBins-1-t, so thread order is descending mass
-    const uint64_t bm = tid < kBins ? sm.bmass[kBins - 1 - tid] : 0ull;
-    uint64_t tot;
-    const uint64_t above = block_excl_scan(bm, sm.u64, tot);
-    if (tid < kBins && bm > 0 && cab + above < P && cab + above + bm >= P) {
-      sm.cab = cab + above;
-      sm.cnt = (int)sm.bcnt[kBins - 1 - tid];
-      sm.bin = kBins - 1 - tid;
+    if (wave == 0) {
+      // lane l holds bins kBins-1-4l .. kBins-4-4l (descending mass)
+      uint64_t bm[4], run;
+      uint32_t bc[4];
+      uint64_t tot = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int bin = kBins - 1 - 4 * lane - k;
+        bm[k] = sm.bmass[bin];
+        bc[k] = sm.bcnt[bin];
+        tot += bm[k];
+        sm.bmass[bin] = 0;  // cleared for the next level
+        sm.bcnt[bin] = 0;
+      }
+      uint64_t incl = tot;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint64_t y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+      }
+      run = cab + incl - tot;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (bm[k] > 0 && run < P && run + bm[k] >= P) {
+          const uint32_t bin = kBins - 1 - 4 * lane - k;
+          const uint32_t blo = lo + (bin << shift);
+          sm.cab = run;
+          sm.cnt = (int)bc[k];
+          sm.lo = blo;
+          sm.hi = min(hi, blo + ((1u << shift) - 1u));
+        }
+        run += bm[k];
+      }
     }
     __syncthreads();
     cab = uni64(sm.cab);
     cnt = __builtin_amdgcn_readfirstlane(sm.cnt);
-    const uint32_t bin = __builtin_amdgcn_readfirstlane(sm.bin);
-    // the crossing bin's bit range
-    uint32_t bmin = 0xFFFFFFFFu, bmax = 0;
-#pragma unroll
-    for (int i = 0; i < ROWS; ++i) {
-      const uint32_t bits = __float_as_uint(m[i]);
-      if (cand(i) && ((bits - lo) >> shift) == bin) {
-        bmin = min(bmin, bits);
-        bmax = max(bmax, bits);
-      }
-    }
-    bmin = block_reduce(bmin, sm.u32a, MinOp());
-    bmax = block_reduce(bmax, sm.u32b, MaxOp());
-    lo = __builtin_amdgcn_readfirstlane(bmin);
-    hi = __builtin_amdgcn_readfirstlane(bmax);
+    lo = __builtin_amdgcn_readfirstlane(sm.lo);
+    hi = __builtin_amdgcn_readfirstlane(sm.hi);
   }
-  bool fl[ROWS];
-#pragma unroll
-  for (int i = 0; i < ROWS; ++i) fl[i] = cand(i);
   if (tid == 0) sm.thr = 0;
-  const int total = rows_prefix(fl, sm);
   if (cnt > kFinal) {
     // every candidate has mass bits lo: admit them in ascending block order
+    auto tie = [&](int i, float m) { return m >= 0.f && __float_as_uint(m) == lo; };
+    rows_prefix(sm_m, rows, tie, sm);
     const uint64_t f = fixed_mass(__uint_as_float(lo));
     if (f == 0) return 0;  // cannot happen while the invariant holds
     const uint64_t k = (P - cab + f - 1) / f;  // >= 1, <= cnt
-#pragma unroll
-    for (int i = 0; i < ROWS; ++i) {
-      const int ord = ordinal(fl, i, sm);
-      if (fl[i] && (uint64_t)ord + 1 == k) sm.thr = key_of(m[i], i * kThreads + tid);
-    }
+    for_rows(sm_m, rows, [&](int i, float m) {
+      const bool c = tie(i, m);
+      const int ord = ordinal(c, i, sm);
+      if (c && (uint64_t)ord + 1 == k) sm.thr = key_at(i, m);
+    });
     __syncthreads();
     return uni64(sm.thr);
   }
-  // the last <= kFinal candidates: gather in block order, rank in one wave, scan
-#pragma unroll
-  for (int i = 0; i < ROWS; ++i) {
-    const int ord = ordinal(fl, i, sm);
-    if (fl[i] && ord < kFinal) {
-      sm.ckey[ord] = key_of(m[i], i * kThreads + tid);
-      sm.cfm[ord] = fixed_mass(m[i]);
+  // the last <= kFinal candidates: gathered in any order, ranked by key in one wave
+  // (keys are distinct, so the order is unique), then scanned from the top
+  for_rows(sm_m, rows, [&](int i, float m) {
+    if (cand(m)) {
+      const int slot = atomicAdd(&sm.nfin, 1);
+      sm.ckey[slot] = key_at(i, m);
+      sm.cfm[slot] = fixed_mass(m);
     }
-  }
+  });
   __syncthreads();
-  const int nf = total < kFinal ? total : kFinal;
   if (wave == 0) {
-    uint64_t my = 0, myf = 0;
-    int rank = 0;
-    if (lane < nf) {
-      my = sm.ckey[lane];
-      myf = sm.cfm[lane];
-#pragma unroll 8
-      for (int i = 0; i < nf; ++i) rank += sm.ckey[i] > my ? 1 : 0;
-      sm.skey[rank] = my;
-      sm.sfm[rank] = myf;
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's LDS writes are done
-    __builtin_amdgcn_wave_barrier();
-    const uint64_t f = lane < nf ? sm.sfm[lane] : 0ull;
-    uint64_t incl = f;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint64_t y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
-    if (lane < nf && cab + incl - f < P && cab + incl >= P) sm.thr = sm.skey[lane];
+    const int nf = sm.nfin;
+    const uint64_t my = lane < nf ? sm.ckey[lane] : 0ull;
+    const uint64_t f = lane < nf ? sm.cfm[lane] : 0ull;
+    uint64_t above = 0;  // mass of the candidates with a larger key
+    for (int i = 0; i < nf; ++i) above += sm.ckey[i] > my ? sm.cfm[i] : 0ull;
+    if (lane < nf && cab + above < P && cab + above + f >= P) sm.thr = my;
+    if (lane == 0) sm.nfin = 0;
   }
   __syncthreads();
   return uni64(sm.thr);
 }
 
-template <int BK, int ROWS>
+template <int BK>
 __global__ __launch_bounds__(kThreads) void index_topp_kernel(
     const uint16_t* __restrict__ q_pre, const uint16_t* __restrict__ w_q,
     const uint16_t* __restrict__ k_idx, const int* __restrict__ seq_lens,
@@ -363,10 +393,11 @@ __global__ __launch_bounds__(kThreads) void index_topp_kernel(
 
   __shared__ double s_qidx[kIndexDim];
   __shared__ double s_mx[kMaxChunkBlocks], s_sum[kMaxChunkBlocks];  // scoring: per-block max, sum
-  __shared__ double s_f[kMaxChunks];  // selection: per-chunk factor exp(M_c - M)
+  __shared__ double s_f[kMaxChunks];  // selection: per-chunk factor exp(M_c - M) / Z
   __shared__ TailSmem sm;
   __shared__ int s_flag;
   __shared__ uint32_t s_tag;
+  extern __shared__ float s_mass[];  // selection: one fp32 mass per block (rows * kThreads)
 
   // ---- scoring: max and sum of every block of this chunk into LDS.  Wave w takes blocks
   // j0 + w + kWaves * (U * k + u); the next U blocks' loads are in flight while the
@@ -461,7 +492,8 @@ __global__ __launch_bounds__(kThreads) void index_topp_kernel(
         double sum = 0.0;
 #pragma unroll
         for (int tt = 0; tt < NL / 2; ++tt) {
-          const double st = half ? sc[2 * tt + 1] : sc[2 * tt];
+          const long long b0 = __double_as_longlong(sc[2 * tt]), b1 = __double_as_longlong(sc[2 * tt + 1]);
+          const double st = __longlong_as_double(half ? b1 : b0);
           sum += (double)fast_exp2((float)((st - mx) * kLog2e));
         }
         sum = wave_sum(sum);
@@ -480,73 +512,116 @@ __global__ __launch_bounds__(kThreads) void index_topp_kernel(
   }
   __syncthreads();
 
-  // ---- publish e_j = sum_j exp(max_j - M_c) (fp32) and the chunk maximum M_c; the
-  // last workgroup of (b, r) to arrive selects
+  // ---- publish e_j = sum_j exp(max_j - M_c) (fp32) and the chunk's (M_c, Z_c = sum_j e_j);
+  // the last workgroup of (b, r) to arrive selects
   uint64_t* e_io = blk_e + head * nblk_max;
   if (wave == 0) {
     const int nb = j1 - j0;
     const double x0 = lane < nb ? s_mx[lane] : -INFINITY;
     const double x1 = lane + 64 < nb ? s_mx[lane + 64] : -INFINITY;
     const double mc = wave_max(fmax(x0, x1));
+    float e0 = 0.f, e1 = 0.f;
     if (lane < nb) {
-      const float e = (float)(s_sum[lane] * (double)fast_exp2((float)((x0 - mc) * kLog2e)));
-      st_dev(e_io + j0 + lane, ((uint64_t)__float_as_uint(e) << 32) | tag);
+      e0 = (float)(s_sum[lane] * (double)fast_exp2((float)((x0 - mc) * kLog2e)));
+      st_dev(e_io + j0 + lane, ((uint64_t)__float_as_uint(e0) << 32) | tag);
     }
     if (lane + 64 < nb) {
-      const float e = (float)(s_sum[lane + 64] * (double)fast_exp2((float)((x1 - mc) * kLog2e)));
-      st_dev(e_io + j0 + lane + 64, ((uint64_t)__float_as_uint(e) << 32) | tag);
+      e1 = (float)(s_sum[lane + 64] * (double)fast_exp2((float)((x1 - mc) * kLog2e)));
+      st_dev(e_io + j0 + lane + 64, ((uint64_t)__float_as_uint(e1) << 32) | tag);
     }
+    const double zc = wave_sum((double)e0 + (double)e1);
     if (lane == 0) {
-      st_dev(cmax + head * n_chunk_max + c, tagged(mc, tag));
+      uint64_t* cs = cmax + (head * n_chunk_max + c) * 2;
+      st_dev(cs, tagged(mc, tag));
+      st_dev(cs + 1, tagged(zc, tag));
       s_flag = atomicAdd(&counters[head], 1) == nch - 1;
     }
   }
   __syncthreads();
   if (!s_flag) return;
 
-  // ---- M = max_c M_c, f_c = exp(M_c - M), m_j = e_j f_c / Z with Z = sum_j e_j f_c
+  // ---- M = max_c M_c, Z = sum_c Z_c exp(M_c - M); then m_j = e_j exp(M_c - M) / Z for
+  // every block, into LDS
   int budget = kSpinBudget;
-  const uint64_t* cm = cmax + head * n_chunk_max;
-  double mloc = -INFINITY;
-  for (int i = tid; i < nch; i += kThreads) {
-    const double mc = untag(settle(cm + i, ld_dev(cm + i), tag, budget));
-    s_f[i] = mc;
-    mloc = fmax(mloc, mc);
+  const uint64_t* cs = cmax + head * n_chunk_max * 2;
+  if (tid < kBins) {
+    sm.bmass[tid] = 0;
+    sm.bcnt[tid] = 0;
   }
-  const double M = block_reduce(mloc, sm.f64, [](double a, double b) { return fmax(a, b); });
-  for (int i = tid; i < nch; i += kThreads) s_f[i] = exp(s_f[i] - M);
+  if (tid == 0) sm.nfin = 0;
+  double cm[2], cz[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {  // nch <= kMaxChunks = 2 * kThreads
+    const int i = tid + k * kThreads;
+    cm[k] = -INFINITY;
+    cz[k] = 0.0;
+    if (i < nch) {
+      const uint64_t a = ld_dev(cs + 2 * i), z = ld_dev(cs + 2 * i + 1);
+      cm[k] = untag(settle(cs + 2 * i, a, tag, budget));
+      cz[k] = untag(settle(cs + 2 * i + 1, z, tag, budget));
+    }
+  }
+  const double M = block_reduce(fmax(cm[0], cm[1]), sm.f64, [](double a, double b) { return fmax(a, b); });
+  double f[2], zloc = 0.0;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    f[k] = cm[k] == -INFINITY ? 0.0 : exp(cm[k] - M);
+    zloc += cz[k] * f[k];
+  }
+  const double invZ = 1.0 / block_reduce(zloc, sm.f64b, SumOp());
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = tid + k * kThreads;
+    if (i < nch) s_f[i] = f[k] * invZ;
+  }
   __syncthreads();
   const int cshift = __ffs(chunk_blocks) - 1;
-  uint64_t w[ROWS];
-#pragma unroll
-  for (int i = 0; i < ROWS; ++i) {
-    const int j = i * kThreads + tid;
-    w[i] = j < nblk ? ld_dev(e_io + j) : 0ull;
-  }
-  float m[ROWS];
-  double zloc = 0.0;
-#pragma unroll
-  for (int i = 0; i < ROWS; ++i) {
-    const int j = i * kThreads + tid;
-    m[i] = -1.0f;  // no block
-    if (j < nblk) {
-      const uint64_t x = settle(e_io + j, w[i], tag, budget);
-      const double e = (double)__uint_as_float((uint32_t)(x >> 32)) * s_f[j >> cshift];
-      m[i] = (float)e;
-      zloc += e;
-    }
-  }
-  const double invZ = 1.0 / block_reduce(zloc, sm.f64, SumOp());
+  const int rows = (nblk + kThreads - 1) / kThreads;
   uint64_t fsum = 0;
   uint32_t bmin = 0xFFFFFFFFu, bmax = 0;
+  constexpr int LB = 8;  // global reads in flight per thread
+  for (int i0 = 0; i0 < rows; i0 += LB) {
+    uint64_t w[LB];
 #pragma unroll
-  for (int i = 0; i < ROWS; ++i) {
-    if (m[i] >= 0.f) {
-      m[i] = (float)((double)m[i] * invZ);
-      fsum += fixed_mass(m[i]);
-      bmin = min(bmin, __float_as_uint(m[i]));
-      bmax = max(bmax, __float_as_uint(m[i]));
+    for (int u = 0; u < LB; ++u) {
+      const int j = (i0 + u) * kThreads + tid;
+      w[u] = (i0 + u < rows && j < nblk) ? ld_dev(e_io + j) : 0ull;
     }
+#pragma unroll
+    for (int u = 0; u < LB; ++u) {
+      const int j = (i0 + u) * kThreads + tid;
+      if (i0 + u < rows) {
+        float m = -1.0f;  // no block
+        if (j < nblk) {
+          const uint64_t x = settle(e_io + j, w[u], tag, budget);
+          m = (float)((double)__uint_as_float((uint32_t)(x >> 32)) * s_f[j >> cshift]);
+          fsum += fixed_mass(m);
+          bmin = min(bmin, __float_as_uint(m));
+          bmax = max(bmax, __float_as_uint(m));
+        }
+        s_mass[j] = m;
+      }
+    }
+  }
+  // one reduction for (sum, min, max)
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    fsum += __shfl_xor(fsum, o);
+    bmin = min(bmin, (uint32_t)__shfl_xor((int)bmin, o));
+    bmax = max(bmax, (uint32_t)__shfl_xor((int)bmax, o));
+  }
+  if (lane == 0) {
+    sm.u64[wave] = fsum;
+    sm.u32a[wave] = bmin;
+    sm.u32b[wave] = bmax;
+  }
+  __syncthreads();
+  fsum = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < kWaves; ++w2) {
+    fsum += sm.u64[w2];
+    bmin = min(bmin, sm.u32a[w2]);
+    bmax = max(bmax, sm.u32b[w2]);
   }
 
   // threshold key: block j is selected iff key_of(m_j, j) >= thr
@@ -554,25 +629,20 @@ __global__ __launch_bounds__(kThreads) void index_topp_kernel(
   const float p = top_p[head];
   if (p < 1.0f && nblk > 1) {
     const uint64_t P = (uint64_t)ceil(ldexp((double)p, 62));
-    fsum = block_reduce(fsum, sm.u64, SumOp());
-    bmin = block_reduce(bmin, sm.u32a, MinOp());
-    bmax = block_reduce(bmax, sm.u32b, MaxOp());
     if (fsum >= P)
-      thr = select_threshold<ROWS>(m, nblk, P, __builtin_amdgcn_readfirstlane(bmin),
-                                   __builtin_amdgcn_readfirstlane(bmax), sm);
+      thr = select_threshold(s_mass, rows, nblk, P, __builtin_amdgcn_readfirstlane(bmin),
+                             __builtin_amdgcn_readfirstlane(bmax), sm);
   }
 
   // ---- ordered compaction of the selected ids (ascending)
-  bool sel[ROWS];
-#pragma unroll
-  for (int i = 0; i < ROWS; ++i) sel[i] = m[i] >= 0.f && key_of(m[i], i * kThreads + tid) >= thr;
-  const int total = rows_prefix(sel, sm);
+  auto sel = [&](int i, float m) { return m >= 0.f && key_at(i, m) >= thr; };
+  const int total = rows_prefix(s_mass, rows, sel, sm);
   int* out = sel_idx + head * nblk_max;
-#pragma unroll
-  for (int i = 0; i < ROWS; ++i) {
-    const int ord = ordinal(sel, i, sm);
-    if (sel[i]) out[ord] = i * kThreads + tid;
-  }
+  for_rows(s_mass, rows, [&](int i, float m) {
+    const bool sl = sel(i, m);
+    const int ord = ordinal(sl, i, sm);
+    if (sl) out[ord] = i * kThreads + tid;
+  });
   if (tid == 0) {
     sel_cnt[head] = total;
     atomicExch(&counters[head], 0);  // ready for the next call
@@ -617,25 +687,14 @@ extern "C" rtp_status rtp_index_topp(const void* q_pre, const void* w_q, const v
   const uint16_t* qp = static_cast<const uint16_t*>(q_pre);
   const uint16_t* wq = static_cast<const uint16_t*>(w_q);
   const uint16_t* ki = static_cast<const uint16_t*>(k_idx);
-#define RTP_K1(BKV, RV)                                                                         \
-  hipLaunchKernelGGL((index_topp_kernel<BKV, RV>), grid, dim3(kThreads), 0, s, qp, wq, ki,        \
-                     seq_lens, ret_heads, top_p, Hq, n_ret, max_ctx, L.nblk_max, L.chunk_blocks, \
-                     L.n_chunk, sel_idx, sel_cnt, counters, tags, cmax, blk_e)
-#define RTP_K1_ROWS(BKV)                 \
-  switch (L.rows) {                      \
-    case 1: RTP_K1(BKV, 1); break;       \
-    case 2: RTP_K1(BKV, 2); break;       \
-    case 4: RTP_K1(BKV, 4); break;       \
-    case 8: RTP_K1(BKV, 8); break;       \
-    case 16: RTP_K1(BKV, 16); break;     \
-    default: RTP_K1(BKV, 32); break;     \
-  }
-  if (block == 64) {
-    RTP_K1_ROWS(64)
-  } else {
-    RTP_K1_ROWS(128)
-  }
-#undef RTP_K1_ROWS
-#undef RTP_K1
+  const size_t dyn = (size_t)L.rows * kThreads * sizeof(float);
+  if (block == 64)
+    hipLaunchKernelGGL(index_topp_kernel<64>, grid, dim3(kThreads), dyn, s, qp, wq, ki, seq_lens,
+                       ret_heads, top_p, Hq, n_ret, max_ctx, L.nblk_max, L.chunk_blocks, L.n_chunk,
+                       sel_idx, sel_cnt, counters, tags, cmax, blk_e);
+  else
+    hipLaunchKernelGGL(index_topp_kernel<128>, grid, dim3(kThreads), dyn, s, qp, wq, ki, seq_lens,
+                       ret_heads, top_p, Hq, n_ret, max_ctx, L.nblk_max, L.chunk_blocks, L.n_chunk,
+                       sel_idx, sel_cnt, counters, tags, cmax, blk_e);
   return hipGetLastError() == hipSuccess ? RTP_OK : RTP_ELAUNCH;
 }

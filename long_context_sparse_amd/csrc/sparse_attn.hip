@@ -213,56 +213,74 @@ __global__ __launch_bounds__(kThreads) void local_window_kernel(
   }
 }
 
-// Log-sum-exp merge of n_split partials for one output row per workgroup (128 threads,
-// thread = output dim): L = log sum_c exp(lse_c); out = sum_c exp(lse_c - L) o_c.
-// The split weights go through LDS in chunks of kMergeChunk; the partial rows are read
-// eight splits at a time so their loads overlap.  Rows whose partials are all empty
-// (lse = -inf) are written 0.
-constexpr int kMergeChunk = 512;
+// Log-sum-exp merge of n_split partials for one output row per workgroup:
+// L = log sum_c exp(lse_c); out = sum_c exp(lse_c - L) o_c.  512 threads = 4 groups of
+// 128 (one thread per output dim); group k takes splits k, k + 4, ..., reading eight
+// of its partial rows at a time so the loads overlap; the four group sums are added in
+// a fixed order.  Split weights go through LDS in chunks of kMergeChunk.  A row whose
+// partials are all empty (lse = -inf) is written 0.
+constexpr int kMergeThreads = 512;
+constexpr int kMergeGroups = kMergeThreads / kHeadDim;
+constexpr int kMergeChunk = 1024;
 
-__global__ __launch_bounds__(kHeadDim) void merge_kernel(
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     const float* __restrict__ o_part, const float* __restrict__ lse_part, const int* __restrict__ heads,
     int Hq, int n_heads, int n_split, float* __restrict__ out) {
-  const int i = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-  const int lane = d & 63, wave = d >> 6;
+  const int i = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int d = tid & (kHeadDim - 1), grp = tid / kHeadDim;
+  const int lane = tid & 63, wave = tid >> 6;
   const size_t hr = (size_t)b * n_heads + i;
   const float* lp = lse_part + hr * n_split;
   const float* op = o_part + hr * n_split * kHeadDim + d;
   __shared__ float s_w[kMergeChunk];
-  __shared__ float s_red[2];
+  __shared__ float s_red[kMergeThreads / 64];
+  __shared__ float s_L[kMergeGroups], s_A[kMergeGroups][kHeadDim];
   float mloc = -INFINITY;
-  for (int c = d; c < n_split; c += kHeadDim) mloc = fmaxf(mloc, lp[c]);
+  for (int c = tid; c < n_split; c += kMergeThreads) mloc = fmaxf(mloc, lp[c]);
   mloc = wave_maxf(mloc);
   if (lane == 0) s_red[wave] = mloc;
   __syncthreads();
-  const float M = fmaxf(s_red[0], s_red[1]);
+  float M = s_red[0];
+#pragma unroll
+  for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, s_red[w]);
   float L = 0.f, A = 0.f;
   if (M != -INFINITY) {
     for (int c0 = 0; c0 < n_split; c0 += kMergeChunk) {
       const int nc = min(kMergeChunk, n_split - c0);
       __syncthreads();
-      for (int c = d; c < nc; c += kHeadDim) s_w[c] = __expf(lp[c0 + c] - M);
+      for (int c = tid; c < nc; c += kMergeThreads) s_w[c] = __expf(lp[c0 + c] - M);
       __syncthreads();
-      int c = 0;
-      for (; c + 8 <= nc; c += 8) {
+      int c = grp;
+      for (; c + 7 * kMergeGroups < nc; c += 8 * kMergeGroups) {
         float ov[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) ov[u] = op[(size_t)(c0 + c + u) * kHeadDim];
+        for (int u = 0; u < 8; ++u) ov[u] = op[(size_t)(c0 + c + u * kMergeGroups) * kHeadDim];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const float w = s_w[c + u];
+          const float w = s_w[c + u * kMergeGroups];
           L += w;
           A = fmaf(w, ov[u], A);
         }
       }
-      for (; c < nc; ++c) {
+      for (; c < nc; c += kMergeGroups) {
         const float w = s_w[c];
         L += w;
         A = fmaf(w, op[(size_t)(c0 + c) * kHeadDim], A);
       }
     }
   }
-  out[((size_t)b * Hq + heads[i]) * kHeadDim + d] = L > 0.f ? A / L : 0.f;
+  if (d == 0) s_L[grp] = L;
+  s_A[grp][d] = A;
+  __syncthreads();
+  if (grp == 0) {
+    float Lt = s_L[0], At = s_A[0][d];
+#pragma unroll
+    for (int k = 1; k < kMergeGroups; ++k) {
+      Lt += s_L[k];
+      At += s_A[k][d];
+    }
+    out[((size_t)b * Hq + heads[i]) * kHeadDim + d] = Lt > 0.f ? At / Lt : 0.f;
+  }
 }
 
 struct LocalLayout {
@@ -357,7 +375,7 @@ extern "C" rtp_status rtp_split_reduce(const float* o_part, const float* lse_par
   if (n_heads == 0) return RTP_OK;
   if (!o_part || !lse_part || !heads || !out) return RTP_EINVAL;
   if (B > 65535) return RTP_EUNSUPPORTED;
-  hipLaunchKernelGGL(merge_kernel, dim3(n_heads, B), dim3(kHeadDim), 0,
+  hipLaunchKernelGGL(merge_kernel, dim3(n_heads, B), dim3(kMergeThreads), 0,
                      static_cast<hipStream_t>(stream), o_part, lse_part, heads, Hq, n_heads, n_split,
                      out);
   return hipGetLastError() == hipSuccess ? RTP_OK : RTP_ELAUNCH;
@@ -404,7 +422,7 @@ extern "C" rtp_status rtp_local_window_attn(const void* q, const void* k_cache, 
     case 4: RTP_LOCAL(4); break;
     default: RTP_LOCAL(8); break;
   }
-  hipLaunchKernelGGL(merge_kernel, dim3(n_loc, B), dim3(kHeadDim), 0, s, ws_o, ws_lse, loc_heads, Hq,
+  hipLaunchKernelGGL(merge_kernel, dim3(n_loc, B), dim3(kMergeThreads), 0, s, ws_o, ws_lse, loc_heads, Hq,
                      n_loc, L.n_split, out);
 #undef RTP_LOCAL
   return hipGetLastError() == hipSuccess ? RTP_OK : RTP_ELAUNCH;
