@@ -549,6 +549,14 @@ __global__ __launch_bounds__(kThreads) void index_topp_kernel(
     sm.bcnt[tid] = 0;
   }
   if (tid == 0) sm.nfin = 0;
+  const int rows = (nblk + kThreads - 1) / kThreads;
+  constexpr int LB = 16;  // global reads in flight per thread
+  uint64_t w[LB];         // the first LB rows' words go out before the reductions below
+#pragma unroll
+  for (int u = 0; u < LB; ++u) {
+    const int j = u * kThreads + tid;
+    w[u] = (u < rows && j < nblk) ? ld_dev(e_io + j) : 0ull;
+  }
   double cm[2], cz[2];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {  // nch <= kMaxChunks = 2 * kThreads
@@ -576,16 +584,15 @@ __global__ __launch_bounds__(kThreads) void index_topp_kernel(
   }
   __syncthreads();
   const int cshift = __ffs(chunk_blocks) - 1;
-  const int rows = (nblk + kThreads - 1) / kThreads;
   uint64_t fsum = 0;
   uint32_t bmin = 0xFFFFFFFFu, bmax = 0;
-  constexpr int LB = 8;  // global reads in flight per thread
   for (int i0 = 0; i0 < rows; i0 += LB) {
-    uint64_t w[LB];
+    if (i0 > 0) {
 #pragma unroll
-    for (int u = 0; u < LB; ++u) {
-      const int j = (i0 + u) * kThreads + tid;
-      w[u] = (i0 + u < rows && j < nblk) ? ld_dev(e_io + j) : 0ull;
+      for (int u = 0; u < LB; ++u) {
+        const int j = (i0 + u) * kThreads + tid;
+        w[u] = (i0 + u < rows && j < nblk) ? ld_dev(e_io + j) : 0ull;
+      }
     }
 #pragma unroll
     for (int u = 0; u < LB; ++u) {
@@ -645,7 +652,7 @@ __global__ __launch_bounds__(kThreads) void index_topp_kernel(
   });
   if (tid == 0) {
     sel_cnt[head] = total;
-    atomicExch(&counters[head], 0);  // ready for the next call
+    __hip_atomic_store(&counters[head], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
     __hip_atomic_store(&tags[head], tag % 4095u + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }

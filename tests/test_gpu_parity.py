@@ -59,6 +59,15 @@ EDGE = [
          split_tokens=256, kind="needles3x", needles=(8, 8), top_p=(0.49, 0.3)),
     dict(name="many_splits", B=1, Hkv=2, Hq=8, n_ret=2, ctx=(20000,), block=64, window=5000, sinks=4,
          split_tokens=64, kind="peaked_diffuse"),
+    # thousands of exactly equal block masses: resolved by count in ascending block order
+    dict(name="flat_ties", B=2, Hkv=1, Hq=4, n_ret=3, ctx=(200000, 130000), block=64, window=64, sinks=4,
+         split_tokens=4096, kind="flat", top_p=(0.3, 0.5, 0.77)),
+    # near ties spread over a tiny mass range: several refinement levels
+    dict(name="near_flat", B=2, Hkv=2, Hq=8, n_ret=4, ctx=(300000, 77777), block=64, window=64, sinks=4,
+         split_tokens=4096, kind="near_flat", top_p=(0.5, 0.9, 0.95, 0.99)),
+    # the largest context a sequence may have at block 128 and one at block 64
+    dict(name="max_blocks_128", B=1, Hkv=1, Hq=4, n_ret=2, ctx=(2097152,), block=128, window=256, sinks=4,
+         split_tokens=65536, kind="peaked_diffuse"),
 ]
 
 
@@ -77,6 +86,12 @@ def test_edge_workloads(spec):
             for r in range(cfg.n_ret):
                 nblk = -(-int(inp.seq_lens[b]) // cfg.block)
                 assert run.gpu_blocks(b, r).tolist() == list(range(nblk))
+    if name == "flat_ties":
+        # equal masses are admitted in ascending block order: the selection is a prefix
+        for b in range(cfg.B):
+            for r in range(cfg.n_ret):
+                G = run.gpu_blocks(b, r)
+                assert G.tolist() == list(range(len(G)))
     if name == "needle_ties":
         # 8 needles of bit-identical mass; ties are admitted in ascending block id
         for r, p in enumerate(cfg.top_p):

@@ -77,6 +77,8 @@ class DecodeConfig:
                            0.25 with 10% of blocks boosted by +2
       * ``depth_needles``  needles at context depths 0.1 / 0.5 / 0.9, margin +6
       * ``random``         no planting
+      * ``flat``           every index key equal (all full blocks tie exactly)
+      * ``near_flat``      index scores spread by about 1e-3 (near ties)
     """
 
     name: str
@@ -298,6 +300,12 @@ def make_inputs(cfg: DecodeConfig, seed: Optional[int] = None, pad_value: int = 
             kb = f64_to_bf16_bits(flat)
         elif cfg.kind == "random":
             kb = f64_to_bf16_bits(raw)
+        elif cfg.kind == "flat":
+            # every index key equal: every full block has the same mass (exact ties)
+            kb = np.tile(f64_to_bf16_bits(0.5 * qn), (n, 1))
+        elif cfg.kind == "near_flat":
+            # scores spread by about 1e-3: many blocks within a tiny mass range
+            kb = f64_to_bf16_bits(1e-3 * raw + 0.5 * qn)
         else:
             raise ValueError(f"unknown workload kind {cfg.kind!r}")
         k_idx[b, r, :n] = kb
