@@ -8,7 +8,8 @@
 // 8*(l & 15) .. +8 of rows 4*i + (l >> 4), i = 0..3.  A query-key dot product is a
 // packed bf16 dot (v_dot2) per dword, then a 16-lane transpose-reduce leaves lane l
 // with the full logit of row 4*((l >> 2) & 3) + (l >> 4) (4 replicas).  Softmax
-// statistics are kept in the base-2 domain.
+// statistics are kept in the base-2 domain.  Every cross-lane step is a DPP lane move
+// inside a 16-lane row, so the inner loop issues no LDS traffic.
 #pragma once
 
 #include "rtp_common.hpp"
@@ -84,26 +85,31 @@ __device__ __forceinline__ void attn_subtile(AttnState<G>& s, const SubTile& t, 
       a = dot2(t.k[i].z, qk[h].z, a);
       part[i] = dot2(t.k[i].w, qk[h].w, a);
     }
-    // transpose-reduce over the 16 lanes that share R
+    // transpose-reduce over the 16 lanes that share R (one DPP row), on DPP lane moves:
+    // the row mirror (partner l ^ 15) exchanges parts by bit 3, the half-row mirror
+    // (partner l ^ 7) by bit 2, then xor 2 and xor 1 finish the row sum
     const float x0 = b3 ? part[0] : part[2];
     const float x1 = b3 ? part[1] : part[3];
-    const float y0 = __shfl_xor(x0, 8);
-    const float y1 = __shfl_xor(x1, 8);
+    const float y0 = dpp_f32<kDppMirror>(x0);
+    const float y1 = dpp_f32<kDppMirror>(x1);
     const float k0 = (b3 ? part[2] : part[0]) + y0;
     const float k1 = (b3 ? part[3] : part[1]) + y1;
     const float xs = b2 ? k0 : k1;
-    float v = (b2 ? k1 : k0) + __shfl_xor(xs, 4);
-    v += __shfl_xor(v, 2);
-    v += __shfl_xor(v, 1);
+    float v = (b2 ? k1 : k0) + dpp_f32<kDppHalfMirror>(xs);
+    v += dpp_f32<kDppXor2>(v);
+    v += dpp_f32<kDppXor1>(v);
     const float lg = myvalid ? v * scale_log2 : -INFINITY;
     const float mnew = fmaxf(s.m[h], wave_maxf(lg));
     const float alpha = fast_exp2(s.m[h] - mnew);
     const float p = fast_exp2(lg - mnew);
     s.l[h] = s.l[h] * alpha + (counted ? p : 0.f);
     s.m[h] = mnew;
+    // p of row 4 * i + R sits in lane 4 * i of this lane's DPP row
     float pi[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pi[i] = __shfl(p, (lane & 0x30) | (i << 2));
+    pi[0] = dpp_f32<kDppRowBcast0>(p);
+    pi[1] = dpp_f32<kDppRowBcast0 + 4>(p);
+    pi[2] = dpp_f32<kDppRowBcast0 + 8>(p);
+    pi[3] = dpp_f32<kDppRowBcast0 + 12>(p);
 #pragma unroll
     for (int k = 0; k < 8; ++k) s.acc[h][k] *= alpha;
 #pragma unroll

@@ -25,6 +25,7 @@ constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within each 8 lanes
 constexpr int kDppMirror = 0x140;     // lane i <- lane 15-i within each 16 lanes
+constexpr int kDppRowBcast0 = 0x150;  // + n: every lane <- lane n of its 16-lane row
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {

@@ -71,6 +71,8 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(
   constexpr int ST = BK / 16;  // sub-tiles per block
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the first 64 selected counts go out with the head list (one memory round trip)
+  const int cnt_l = lane < n_ret ? sel_cnt[(size_t)b * n_ret + lane] : 0;
   int rbeg, rend;
   group_range(ret_heads, n_ret, g, G, rbeg, rend);
   const int nh = rend - rbeg;
@@ -85,23 +87,29 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(
   __shared__ float s_m[kWaves * G], s_l[kWaves * G];
   __shared__ float s_acc[kWaves * G * kHeadDim];
 
-  __shared__ int s_rng[2 * G];
   int nL = 0;
   if (jlo < jhi) {
     const int nb = jhi - jlo;
     for (int i = tid; i < (nb + 3) / 4; i += kThreads) s_hm[i] = 0;
-    // each head's entries in [jlo, jhi): one wave per (head, bound)
-    for (int pr = wave; pr < 2 * nh; pr += kWaves) {
-      const size_t hr = (size_t)b * n_ret + rbeg + (pr >> 1);
-      const int v = lower_bound_wave(sel_idx + hr * nblk_max, sel_cnt[hr], (pr & 1) ? jhi : jlo);
-      if (lane == 0) s_rng[pr] = v;
-    }
     __syncthreads();
-    for (int h = 0; h < nh; ++h) {
-      const int* sl = sel_idx + ((size_t)b * n_ret + rbeg + h) * nblk_max;
-      for (int i = s_rng[2 * h] + tid; i < s_rng[2 * h + 1]; i += kThreads) {
-        const int off = sl[i] - jlo;
-        atomicOr(&s_hm[off >> 2], (1u << h) << ((off & 3) * 8));
+    // mark each head's selected blocks in [jlo, jhi): one wave per head.  A list of at
+    // most 64 entries is read in one round; a longer one is searched for its range.
+    for (int h = wave; h < nh; h += kWaves) {
+      const int hh = rbeg + h;
+      const size_t hr = (size_t)b * n_ret + hh;
+      const int cnt = hh < 64 ? __shfl(cnt_l, hh) : sel_cnt[hr];
+      const int* sl = sel_idx + hr * nblk_max;
+      const uint32_t bit = 1u << h;
+      if (cnt <= 64) {
+        const int v = lane < cnt ? sl[lane] : -1;
+        if (v >= jlo && v < jhi) atomicOr(&s_hm[(v - jlo) >> 2], bit << (((v - jlo) & 3) * 8));
+      } else {
+        const int a = lower_bound_wave(sl, cnt, jlo);
+        const int e = lower_bound_wave(sl, cnt, jhi);
+        for (int i = a + lane; i < e; i += 64) {
+          const int off = sl[i] - jlo;
+          atomicOr(&s_hm[off >> 2], bit << ((off & 3) * 8));
+        }
       }
     }
     __syncthreads();
@@ -214,14 +222,15 @@ __global__ __launch_bounds__(kThreads) void local_window_kernel(
 }
 
 // Log-sum-exp merge of n_split partials for one output row per workgroup:
-// L = log sum_c exp(lse_c); out = sum_c exp(lse_c - L) o_c.  512 threads = 4 groups of
-// 128 (one thread per output dim); group k takes splits k, k + 4, ..., reading eight
-// of its partial rows at a time so the loads overlap; the four group sums are added in
-// a fixed order.  Split weights go through LDS in chunks of kMergeChunk.  A row whose
-// partials are all empty (lse = -inf) is written 0.
-constexpr int kMergeThreads = 512;
+// L = log sum_c exp(lse_c); out = sum_c exp(lse_c - L) o_c.  1024 threads = 8 groups of
+// 128 (one thread per output dim); group k takes splits k, k + 8, ...  Each thread
+// issues the loads of its partial values and their LSEs before the row maximum is
+// reduced, kMergeBatch splits at a time, so one memory round trip serves up to 128
+// splits; the eight group sums are added in a fixed order.  A row whose partials are
+// all empty (lse = -inf) is written 0.
+constexpr int kMergeThreads = 1024;
 constexpr int kMergeGroups = kMergeThreads / kHeadDim;
-constexpr int kMergeChunk = 1024;
+constexpr int kMergeBatch = 16;
 
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     const float* __restrict__ o_part, const float* __restrict__ lse_part, const int* __restrict__ heads,
@@ -232,9 +241,16 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
   const size_t hr = (size_t)b * n_heads + i;
   const float* lp = lse_part + hr * n_split;
   const float* op = o_part + hr * n_split * kHeadDim + d;
-  __shared__ float s_w[kMergeChunk];
   __shared__ float s_red[kMergeThreads / 64];
   __shared__ float s_L[kMergeGroups], s_A[kMergeGroups][kHeadDim];
+  // this thread's first batch of partials, in flight while the maximum is reduced
+  float ov[kMergeBatch], lv[kMergeBatch];
+#pragma unroll
+  for (int u = 0; u < kMergeBatch; ++u) {
+    const int c = grp + u * kMergeGroups;
+    ov[u] = c < n_split ? op[(size_t)c * kHeadDim] : 0.f;
+    lv[u] = c < n_split ? lp[c] : -INFINITY;
+  }
   float mloc = -INFINITY;
   for (int c = tid; c < n_split; c += kMergeThreads) mloc = fmaxf(mloc, lp[c]);
   mloc = wave_maxf(mloc);
@@ -245,27 +261,20 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
   for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, s_red[w]);
   float L = 0.f, A = 0.f;
   if (M != -INFINITY) {
-    for (int c0 = 0; c0 < n_split; c0 += kMergeChunk) {
-      const int nc = min(kMergeChunk, n_split - c0);
-      __syncthreads();
-      for (int c = tid; c < nc; c += kMergeThreads) s_w[c] = __expf(lp[c0 + c] - M);
-      __syncthreads();
-      int c = grp;
-      for (; c + 7 * kMergeGroups < nc; c += 8 * kMergeGroups) {
-        float ov[8];
+    for (int c0 = 0; c0 < n_split; c0 += kMergeBatch * kMergeGroups) {
+      if (c0 > 0) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) ov[u] = op[(size_t)(c0 + c + u * kMergeGroups) * kHeadDim];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const float w = s_w[c + u * kMergeGroups];
-          L += w;
-          A = fmaf(w, ov[u], A);
+        for (int u = 0; u < kMergeBatch; ++u) {
+          const int c = c0 + grp + u * kMergeGroups;
+          ov[u] = c < n_split ? op[(size_t)c * kHeadDim] : 0.f;
+          lv[u] = c < n_split ? lp[c] : -INFINITY;
         }
       }
-      for (; c < nc; c += kMergeGroups) {
-        const float w = s_w[c];
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const float w = __expf(lv[u] - M);  // 0 for empty or absent splits
         L += w;
-        A = fmaf(w, op[(size_t)(c0 + c) * kHeadDim], A);
+        A = fmaf(w, ov[u], A);
       }
     }
   }
