@@ -73,12 +73,65 @@ def version() -> str:
     return lib().rtp_version().decode()
 
 
-def _p(t: Optional[torch.Tensor]):
-    if t is None:
-        return None
+def device_ptr(t: torch.Tensor) -> int:
+    """Raw device address of a contiguous device tensor (raises otherwise)."""
     if not t.is_cuda or not t.is_contiguous():
         raise ValueError("librtp arguments must be contiguous device tensors")
     return t.data_ptr()
+
+
+def nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def check(fn: str, st: int) -> None:
+    if st != RTP_OK:
+        raise RTPError(fn, st)
+
+
+# ---- HIP events for ordering the step's two streams (plumbing only)
+_hip = None
+
+
+def _hip_lib() -> ctypes.CDLL:
+    global _hip
+    if _hip is None:
+        lib()  # librtp.so links the HIP runtime; load the same copy
+        h = ctypes.CDLL("libamdhip64.so")
+        h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        h.hipEventCreateWithFlags.restype = ctypes.c_int
+        h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        h.hipEventRecord.restype = ctypes.c_int
+        h.hipStreamWaitEvent.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
+        h.hipStreamWaitEvent.restype = ctypes.c_int
+        h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        h.hipEventDestroy.restype = ctypes.c_int
+        _hip = h
+    return _hip
+
+
+def event_create() -> int:
+    ev = ctypes.c_void_p()
+    st = _hip_lib().hipEventCreateWithFlags(ctypes.byref(ev), 0x2)  # hipEventDisableTiming
+    if st != 0:
+        raise RuntimeError(f"hipEventCreateWithFlags failed ({st})")
+    return ev.value
+
+
+def event_record(ev: int, stream: int) -> None:
+    st = _hip.hipEventRecord(ev, stream)
+    if st != 0:
+        raise RuntimeError(f"hipEventRecord failed ({st})")
+
+
+def stream_wait_event(stream: int, ev: int) -> None:
+    st = _hip.hipStreamWaitEvent(stream, ev, 0)
+    if st != 0:
+        raise RuntimeError(f"hipStreamWaitEvent failed ({st})")
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else device_ptr(t)
 
 
 def _nbytes(t: Optional[torch.Tensor]) -> int:
@@ -91,9 +144,7 @@ def _s(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _check(fn: str, st: int) -> None:
-    if st != RTP_OK:
-        raise RTPError(fn, st)
+_check = check
 
 
 def rtp_index_topp_workspace_size(B: int, n_ret: int, max_ctx: int, block: int) -> int:

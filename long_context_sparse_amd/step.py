@@ -63,8 +63,10 @@ class DecodeStep:
         self.ws_local = torch.zeros(max(ws2, 256), dtype=torch.uint8, device=dev)
         self.overlap = overlap and s.n_loc > 0 and s.n_ret > 0
         self.side = torch.cuda.Stream(device=dev) if self.overlap else None
-        self._fork = torch.cuda.Event() if self.overlap else None
-        self._join = torch.cuda.Event() if self.overlap else None
+        self._fork = abi.event_create() if self.overlap else None
+        self._join = abi.event_create() if self.overlap else None
+        self._key = None
+        self._vals = None
 
     # -- the four calls -------------------------------------------------------------
     def index_topp(self, t: Dict[str, torch.Tensor], stream=None) -> None:
@@ -90,20 +92,56 @@ class DecodeStep:
                                   s.B, s.Hq, s.Hkv, s.n_loc, s.max_ctx, s.window, s.sinks, self.out,
                                   self.ws_local, stream)
 
+    # -- the whole step -------------------------------------------------------------
+    def _plan(self, t: Dict[str, torch.Tensor], main: int):
+        """Argument tuples of the four calls for these tensors and this stream, converted
+        once (the C functions take raw pointers and sizes)."""
+        s = self.s
+        p = abi.device_ptr
+        side = self.side.cuda_stream if self.overlap else main
+        L = abi.lib()
+        plan_side, plan_main = [], []
+        if s.n_loc:
+            plan_side.append(("rtp_local_window_attn", L.rtp_local_window_attn, (
+                p(t["q"]), p(t["k_cache"]), p(t["v_cache"]), p(t["seq_lens"]), p(t["loc_heads"]), s.B, s.Hq,
+                s.Hkv, s.n_loc, s.max_ctx, s.window, s.sinks, p(self.out), p(self.ws_local),
+                abi.nbytes(self.ws_local), side)))
+        if s.n_ret:
+            plan_main.append(("rtp_index_topp", L.rtp_index_topp, (
+                p(t["q_pre"]), p(t["w_q"]), p(t["k_idx"]), p(t["seq_lens"]), p(t["ret_heads"]), p(t["top_p"]),
+                s.B, s.Hq, s.n_ret, s.max_ctx, s.block, p(self.sel_idx), p(self.sel_cnt), p(self.ws_index),
+                abi.nbytes(self.ws_index), main)))
+            plan_main.append(("rtp_sparse_attn_split", L.rtp_sparse_attn_split, (
+                p(t["q"]), p(t["k_cache"]), p(t["v_cache"]), p(t["seq_lens"]), p(t["ret_heads"]),
+                p(self.sel_idx), p(self.sel_cnt), s.B, s.Hq, s.Hkv, s.n_ret, s.max_ctx, s.block,
+                s.split_tokens, p(self.o_part), p(self.lse_part), main)))
+            plan_main.append(("rtp_split_reduce", L.rtp_split_reduce, (
+                p(self.o_part), p(self.lse_part), p(t["ret_heads"]), s.B, s.Hq, s.n_ret, s.n_split,
+                p(self.out), main)))
+        return plan_side, plan_main
+
     def __call__(self, t: Dict[str, torch.Tensor]) -> torch.Tensor:
-        """Enqueue one decode step on the current stream; returns the fp32 [B, Hq, 128] output."""
-        main = torch.cuda.current_stream(self.device)
+        """Enqueue one decode step on the current stream; returns the fp32 [B, Hq, 128] output.
+
+        The local heads' call goes to a second stream (forked from and joined back into
+        the current one with events) so it overlaps the retrieval heads' three calls.
+        The calls' argument tuples are converted once per (set of tensors, stream)."""
+        main = torch.cuda.current_stream(self.device).cuda_stream
+        vals = tuple(t.values())
+        key = (main,) + tuple(map(id, vals))
+        if self._key != key:
+            self._plan_side, self._plan_main = self._plan(t, main)
+            self._key = key
+            self._vals = vals  # the plan's tensors stay alive, so their ids stay theirs
         if self.overlap:
-            self._fork.record(main)
-            self.side.wait_event(self._fork)
-            self.local(t, self.side)
-            self._join.record(self.side)
-        elif self.s.n_loc:
-            self.local(t, main)
-        if self.s.n_ret:
-            self.index_topp(t, main)
-            self.sparse_attn(t, main)
-            self.reduce(t, main)
+            abi.event_record(self._fork, main)
+            abi.stream_wait_event(self.side.cuda_stream, self._fork)
+        for name, fn, args in self._plan_side:
+            abi.check(name, fn(*args))
         if self.overlap:
-            main.wait_event(self._join)
+            abi.event_record(self._join, self.side.cuda_stream)
+        for name, fn, args in self._plan_main:
+            abi.check(name, fn(*args))
+        if self.overlap:
+            abi.stream_wait_event(main, self._join)
         return self.out
