@@ -28,14 +28,15 @@
 //   threshold exactly: a key = (fp32
 //   mass bits, inverted block id) orders blocks by mass with ties by ascending id;
 //   masses are summed as fixed-point integers (2^-62 units) so every cumulative sum
-//   is exact and order-independent.  While more than 64 candidates of unequal mass
-//   remain, a 256-bin LDS histogram of (count, mass) over (bits - lo) >> shift (bins
-//   about log-uniform in mass) finds the bin where the cumulative mass crosses p, whose
-//   bit range becomes the new candidate range (>= 128x narrower); the last <= 64
-//   candidates are ranked exactly by one wave, and a run of equal masses is resolved by
-//   count in ascending block order.  The selected ids are written in ascending order by
-//   a ballot-based ordered compaction; the arrival counter is reset and the tag
-//   advanced.
+//   is exact and order-independent.  The pass that writes the masses also builds the
+//   first 256-bin LDS histogram of (count, mass), half an octave per bin (bits >> 22);
+//   one wave scans it for the bin where the cumulative mass from the top crosses p.
+//   While more than 64 candidates of unequal mass remain, a further level bins the
+//   candidates by (bits - lo) >> shift (>= 128x narrower each time); the last <= 64
+//   candidates are gathered (the same pass counts the blocks above them) and ranked
+//   exactly by one wave, and a run of equal masses is resolved by count in ascending
+//   block order.  The selected ids are written in ascending order by a ballot-based
+//   ordered compaction; the arrival counter is reset and the tag advanced.
 
 #include "rtp_common.hpp"
 
@@ -112,8 +113,15 @@ __device__ __forceinline__ uint64_t settle(const uint64_t* p, uint64_t w, uint32
 __device__ __forceinline__ uint64_t key_of(float m, int j) {
   return ((uint64_t)__float_as_uint(m) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
 }
-// Mass in fixed point, 2^-62 units: integer sums are exact and order-independent.
-__device__ __forceinline__ uint64_t fixed_mass(float m) { return (uint64_t)((double)m * 0x1p62); }
+// Mass in fixed point, 2^-62 units, from the bits of a non-negative fp32 mass (< 2):
+// floor(m * 2^62) = mantissa * 2^(exponent - 88), truncated.  Integer sums of these are
+// exact and independent of order.
+__device__ __forceinline__ uint64_t fixed_bits(uint32_t bits) {
+  const int e = min((int)(bits >> 23) & 0xFF, 127);
+  const uint64_t mant = (bits & 0x7FFFFFu) | 0x800000u;
+  if (e >= 88) return mant << (e - 88);
+  return e > 64 ? mant >> (88 - e) : 0ull;
+}
 
 // A wave-uniform 64-bit value moved to scalar registers.
 __device__ __forceinline__ uint64_t uni64(uint64_t v) {
@@ -126,69 +134,12 @@ struct TailSmem {
   uint64_t bmass[kBins];          // per bin: fixed-point mass
   uint32_t bcnt[kBins];           // per bin: candidate count
   int rowtab[kMaxRows * kWaves];  // per (row, wave) counts, then exclusive prefixes
-  uint64_t u64[kWaves];
   double f64[kWaves], f64b[kWaves];
-  uint32_t u32a[kWaves], u32b[kWaves];
   uint64_t ckey[kFinal], cfm[kFinal];  // final candidates (any order)
   uint64_t cab, thr;
   uint32_t lo, hi;
-  int cnt, nfin, total;
+  int cnt, nfin, total, found, ready;
 };
-
-template <class T, class Op>
-__device__ __forceinline__ T wave_reduce(T v, Op op) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = op(v, __shfl_xor(v, o));
-  return v;
-}
-
-// Reduction over the workgroup; every thread gets the result.
-template <class T, class Op>
-__device__ __forceinline__ T block_reduce(T v, T* red, Op op) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  v = wave_reduce(v, op);
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  T t = red[0];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) t = op(t, red[w]);
-  __syncthreads();
-  return t;
-}
-
-struct SumOp {
-  template <class T>
-  __device__ T operator()(T a, T b) const { return a + b; }
-};
-struct MinOp {
-  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; }
-};
-struct MaxOp {
-  __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; }
-};
-
-// Exclusive prefix sum over the workgroup in thread order; `total` gets the sum.
-template <class T>
-__device__ __forceinline__ T block_excl_scan(T v, T* red, T& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  T incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const T y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
-  if (lane == 63) red[wave] = incl;
-  __syncthreads();
-  T base = 0;
-  total = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    base += w < wave ? red[w] : T(0);
-    total += red[w];
-  }
-  __syncthreads();
-  return base + incl - v;
-}
 
 // Selection rows: block j = row * kThreads + thread, row < rows, masses in LDS (< 0 for
 // no block).  Every pass reads a thread's masses kRowBatch rows at a time so the LDS
@@ -208,10 +159,39 @@ __device__ __forceinline__ void for_rows(const float* __restrict__ sm_m, int row
   }
 }
 
+// One wave: turns rowtab[0 .. rows * kWaves) of per-(row, wave) counts into exclusive
+// prefixes in ascending block order and stores their total in sm.total.
+__device__ __forceinline__ void rowtab_scan(int rows, TailSmem& sm) {
+  const int lane = threadIdx.x & 63;
+  constexpr int R = (kMaxRows * kWaves + 63) / 64;  // table entries a lane
+  const int n = rows * kWaves;
+  int v[R], tot = 0;
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int idx = lane * R + k;
+    v[k] = idx < n ? sm.rowtab[idx] : 0;
+    tot += v[k];
+  }
+  int incl = tot;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  int run = incl - tot;
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int idx = lane * R + k;
+    if (idx < n) sm.rowtab[idx] = run;
+    run += v[k];
+  }
+  if (lane == 63) sm.total = incl;
+}
+
 // For a predicate on (row, mass), fills rowtab with the exclusive prefix, in ascending
 // block order, of the satisfying blocks per (row, wave) and returns their total; the
 // ordinal of a satisfying block is then rowtab[row * kWaves + wave] + (satisfying
-// lanes below it in its wave).  One wave scans the table.
+// lanes below it in its wave).
 template <class Pred>
 __device__ __forceinline__ int rows_prefix(const float* __restrict__ sm_m, int rows, Pred pred,
                                            TailSmem& sm) {
@@ -221,31 +201,7 @@ __device__ __forceinline__ int rows_prefix(const float* __restrict__ sm_m, int r
     if (lane == 0) sm.rowtab[i * kWaves + wave] = __popcll(bal);
   });
   __syncthreads();
-  if (wave == 0) {
-    constexpr int R = (kMaxRows * kWaves + 63) / 64;  // table entries a lane
-    const int n = rows * kWaves;
-    int v[R], tot = 0;
-#pragma unroll
-    for (int k = 0; k < R; ++k) {
-      const int idx = lane * R + k;
-      v[k] = idx < n ? sm.rowtab[idx] : 0;
-      tot += v[k];
-    }
-    int incl = tot;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
-    int run = incl - tot;
-#pragma unroll
-    for (int k = 0; k < R; ++k) {
-      const int idx = lane * R + k;
-      if (idx < n) sm.rowtab[idx] = run;
-      run += v[k];
-    }
-    if (lane == 63) sm.total = incl;
-  }
+  if (wave == 0) rowtab_scan(rows, sm);
   __syncthreads();
   return sm.total;
 }
@@ -259,26 +215,80 @@ __device__ __forceinline__ uint64_t key_at(int i, float m) {
   return key_of(m, i * kThreads + (int)threadIdx.x);
 }
 
-// Exact greedy top-p threshold over the masses in LDS.  Returns the key of the last
-// admitted block: the selected set is every block whose key is >= it.  Preconditions:
-// the total fixed-point mass reaches P; [lo, hi] spans the mass bits of all blocks;
-// the bins and the final-candidate count are zero.
+// One wave: scans the bins from the top for the bin where cab + (mass of the bins above
+// it) + (its own mass) first reaches P, and records that bin's mass above (sm.cab), count
+// (sm.cnt) and bit range [sm.lo, sm.hi]; sets sm.found.  Bin b of a level over [lo, hi]
+// holds the bits lo + (b << shift) ..; the top bin also takes everything above.  The bins
+// are cleared for the next level.
+__device__ __forceinline__ void scan_level(uint64_t cab, uint64_t P, uint32_t lo, uint32_t hi, int shift,
+                                           TailSmem& sm) {
+  const int lane = threadIdx.x & 63;
+  // lane l holds bins kBins-1-4l .. kBins-4-4l (descending mass)
+  uint64_t bm[4];
+  uint32_t bc[4];
+  uint64_t tot = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int bin = kBins - 1 - 4 * lane - k;
+    bm[k] = sm.bmass[bin];
+    bc[k] = sm.bcnt[bin];
+    tot += bm[k];
+    sm.bmass[bin] = 0;
+    sm.bcnt[bin] = 0;
+  }
+  uint64_t incl = tot;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint64_t y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  uint64_t run = cab + incl - tot;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (bm[k] > 0 && run < P && run + bm[k] >= P) {
+      const uint32_t bin = kBins - 1 - 4 * lane - k;
+      const uint32_t blo = lo + (bin << shift);
+      sm.cab = run;
+      sm.cnt = (int)bc[k];
+      sm.lo = blo;
+      sm.hi = bin == kBins - 1 ? hi : min(hi, blo + ((1u << shift) - 1u));
+      sm.found = 1;
+    }
+    run += bm[k];
+  }
+}
+
+__device__ __forceinline__ int level_bin(uint32_t bits, uint32_t lo, int shift) {
+  return (int)min((bits - lo) >> shift, (uint32_t)(kBins - 1));
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t a = __builtin_amdgcn_readlane((uint32_t)v, l);
+  const uint32_t b = __builtin_amdgcn_readlane((uint32_t)(v >> 32), l);
+  return ((uint64_t)b << 32) | a;
+}
+
+// Exact greedy top-p threshold over the masses in LDS, after a first level whose result
+// (sm.cab, sm.cnt, sm.lo, sm.hi) is in place.  Returns the key of the last admitted
+// block: the selected set is every block whose key is >= it.  When sm.ready is set on
+// return, sm.rowtab already holds the exclusive prefix per (row, wave) of the selected
+// blocks and sm.total their number.  Preconditions: the bins and sm.nfin are zero.
 //
 // Candidates are the blocks whose mass bits lie in [lo, hi], with fixed mass `cab`
 // strictly above them, and cab < P <= cab + mass(candidates) holds throughout.  A
 // level puts every candidate into one of kBins bins by (bits - lo) >> shift, a
 // monotone map, so bins are contiguous ranges of mass (about log-uniform, since fp32
 // bits grow with log2 of the value); one wave scans the bins from the top, finds the
-// bin where cab + cumulative mass crosses P, takes its bit range as the new candidate
-// range (at least kBins/2 times narrower) and clears the bins.  It ends when <= kFinal
-// candidates remain (ranked exactly by one wave), or when the range is a single mass
-// value: the threshold is then the k-th candidate in ascending block order,
-// k = ceil((P - cab) / mass).
-__device__ uint64_t select_threshold(const float* __restrict__ sm_m, int rows, int nblk, uint64_t P,
-                                     uint32_t lo, uint32_t hi, TailSmem& sm) {
+// bin where cab + cumulative mass crosses P and takes its bit range as the new candidate
+// range (at least kBins/2 times narrower).  It ends when <= kFinal candidates remain
+// (ranked exactly by one wave), or when the range is a single mass value: the threshold
+// is then the k-th candidate in ascending block order, k = ceil((P - cab) / mass).
+__device__ uint64_t select_threshold(const float* __restrict__ sm_m, int rows, uint64_t P, TailSmem& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint64_t cab = 0;
-  int cnt = nblk;
+  uint64_t cab = uni64(sm.cab);
+  int cnt = __builtin_amdgcn_readfirstlane(sm.cnt);
+  uint32_t lo = __builtin_amdgcn_readfirstlane(sm.lo);
+  uint32_t hi = __builtin_amdgcn_readfirstlane(sm.hi);
   auto cand = [&](float m) {
     const uint32_t bits = __float_as_uint(m);
     return m >= 0.f && bits >= lo && bits <= hi;
@@ -288,58 +298,28 @@ __device__ uint64_t select_threshold(const float* __restrict__ sm_m, int rows, i
     const int shift = max(0, 32 - (int)__clz(span) - 8);  // (span >> shift) < kBins
     for_rows(sm_m, rows, [&](int i, float m) {
       if (cand(m)) {
-        const int bin = (int)((__float_as_uint(m) - lo) >> shift);
-        atomicAdd((unsigned long long*)&sm.bmass[bin], (unsigned long long)fixed_mass(m));
+        const int bin = level_bin(__float_as_uint(m), lo, shift);
+        atomicAdd((unsigned long long*)&sm.bmass[bin], (unsigned long long)fixed_bits(__float_as_uint(m)));
         atomicAdd(&sm.bcnt[bin], 1u);
       }
     });
     __syncthreads();
-    if (wave == 0) {
-      // lane l holds bins kBins-1-4l .. kBins-4-4l (descending mass)
-      uint64_t bm[4], run;
-      uint32_t bc[4];
-      uint64_t tot = 0;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int bin = kBins - 1 - 4 * lane - k;
-        bm[k] = sm.bmass[bin];
-        bc[k] = sm.bcnt[bin];
-        tot += bm[k];
-        sm.bmass[bin] = 0;  // cleared for the next level
-        sm.bcnt[bin] = 0;
-      }
-      uint64_t incl = tot;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint64_t y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
-      }
-      run = cab + incl - tot;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if (bm[k] > 0 && run < P && run + bm[k] >= P) {
-          const uint32_t bin = kBins - 1 - 4 * lane - k;
-          const uint32_t blo = lo + (bin << shift);
-          sm.cab = run;
-          sm.cnt = (int)bc[k];
-          sm.lo = blo;
-          sm.hi = min(hi, blo + ((1u << shift) - 1u));
-        }
-        run += bm[k];
-      }
-    }
+    if (wave == 0) scan_level(cab, P, lo, hi, shift, sm);
     __syncthreads();
     cab = uni64(sm.cab);
     cnt = __builtin_amdgcn_readfirstlane(sm.cnt);
     lo = __builtin_amdgcn_readfirstlane(sm.lo);
     hi = __builtin_amdgcn_readfirstlane(sm.hi);
   }
-  if (tid == 0) sm.thr = 0;
   if (cnt > kFinal) {
     // every candidate has mass bits lo: admit them in ascending block order
+    if (tid == 0) {
+      sm.thr = 0;
+      sm.ready = 0;
+    }
     auto tie = [&](int i, float m) { return m >= 0.f && __float_as_uint(m) == lo; };
     rows_prefix(sm_m, rows, tie, sm);
-    const uint64_t f = fixed_mass(__uint_as_float(lo));
+    const uint64_t f = fixed_bits(lo);
     if (f == 0) return 0;  // cannot happen while the invariant holds
     const uint64_t k = (P - cab + f - 1) / f;  // >= 1, <= cnt
     for_rows(sm_m, rows, [&](int i, float m) {
@@ -350,24 +330,46 @@ __device__ uint64_t select_threshold(const float* __restrict__ sm_m, int rows, i
     __syncthreads();
     return uni64(sm.thr);
   }
-  // the last <= kFinal candidates: gathered in any order, ranked by key in one wave
-  // (keys are distinct, so the order is unique), then scanned from the top
+  // the last <= kFinal candidates are gathered in any order; the same pass counts, per
+  // (row, wave), the blocks above the candidates' range (all selected)
   for_rows(sm_m, rows, [&](int i, float m) {
+    const uint32_t bits = __float_as_uint(m);
     if (cand(m)) {
       const int slot = atomicAdd(&sm.nfin, 1);
-      sm.ckey[slot] = key_at(i, m);
-      sm.cfm[slot] = fixed_mass(m);
+      if (slot < kFinal) {
+        sm.ckey[slot] = key_at(i, m);
+        sm.cfm[slot] = fixed_bits(bits);
+      }
     }
+    const uint64_t bal = __ballot(m >= 0.f && bits > hi);
+    if (lane == 0) sm.rowtab[i * kWaves + wave] = __popcll(bal);
   });
   __syncthreads();
   if (wave == 0) {
-    const int nf = sm.nfin;
+    // rank by key (keys are distinct): the crossing candidate has cab + (mass of the
+    // larger keys) < P <= that + its own mass
+    const int nf = min(sm.nfin, kFinal);
     const uint64_t my = lane < nf ? sm.ckey[lane] : 0ull;
     const uint64_t f = lane < nf ? sm.cfm[lane] : 0ull;
-    uint64_t above = 0;  // mass of the candidates with a larger key
-    for (int i = 0; i < nf; ++i) above += sm.ckey[i] > my ? sm.cfm[i] : 0ull;
-    if (lane < nf && cab + above < P && cab + above + f >= P) sm.thr = my;
-    if (lane == 0) sm.nfin = 0;
+    uint64_t above = 0;
+    for (int i = 0; i < nf; ++i) {
+      const uint64_t ki = readlane_u64(my, i), fi = readlane_u64(f, i);
+      above += ki > my ? fi : 0ull;
+    }
+    const uint64_t cb = __ballot(lane < nf && cab + above < P && cab + above + f >= P);
+    const uint64_t thr = cb ? readlane_u64(my, __ffsll((long long)cb) - 1) : 0ull;
+    // the selected candidates join the per-(row, wave) counts (LDS operations of one
+    // wave complete in order, so the scan below sees them)
+    if (cb && lane < nf && my >= thr) {
+      const int j = (int)(0xFFFFFFFFu - (uint32_t)my);
+      atomicAdd(&sm.rowtab[(j / kThreads) * kWaves + (j % kThreads) / kWave], 1);
+    }
+    if (cb) rowtab_scan(rows, sm);
+    if (lane == 0) {
+      sm.thr = thr;
+      sm.ready = cb != 0;
+      sm.nfin = 0;
+    }
   }
   __syncthreads();
   return uni64(sm.thr);
@@ -548,7 +550,12 @@ __global__ __launch_bounds__(kThreads) void index_topp_kernel(
     sm.bmass[tid] = 0;
     sm.bcnt[tid] = 0;
   }
-  if (tid == 0) sm.nfin = 0;
+  if (tid == 0) {
+    sm.nfin = 0;
+    sm.found = 0;
+  }
+  const float p = top_p[head];
+  const bool pick = p < 1.0f && nblk > 1;  // else every block is selected
   const int rows = (nblk + kThreads - 1) / kThreads;
   constexpr int LB = 16;  // global reads in flight per thread
   uint64_t w[LB];         // the first LB rows' words go out before the reductions below
@@ -569,23 +576,38 @@ __global__ __launch_bounds__(kThreads) void index_topp_kernel(
       cz[k] = untag(settle(cs + 2 * i + 1, z, tag, budget));
     }
   }
-  const double M = block_reduce(fmax(cm[0], cm[1]), sm.f64, [](double a, double b) { return fmax(a, b); });
+  {
+    const double mw = wave_max(fmax(cm[0], cm[1]));
+    if (lane == 0) sm.f64[wave] = mw;
+  }
+  __syncthreads();
+  double M = sm.f64[0];
+#pragma unroll
+  for (int w2 = 1; w2 < kWaves; ++w2) M = fmax(M, sm.f64[w2]);
   double f[2], zloc = 0.0;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     f[k] = cm[k] == -INFINITY ? 0.0 : exp(cm[k] - M);
     zloc += cz[k] * f[k];
   }
-  const double invZ = 1.0 / block_reduce(zloc, sm.f64b, SumOp());
+  {
+    const double zw = wave_sum(zloc);
+    if (lane == 0) sm.f64b[wave] = zw;
+  }
+  __syncthreads();
+  double Z = sm.f64b[0];
+#pragma unroll
+  for (int w2 = 1; w2 < kWaves; ++w2) Z += sm.f64b[w2];
+  const double invZ = 1.0 / Z;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int i = tid + k * kThreads;
     if (i < nch) s_f[i] = f[k] * invZ;
   }
   __syncthreads();
+  // masses into LDS; the same pass builds the first threshold level: 256 bins of half an
+  // octave each over the mass bits (bin = bits >> 22, the top bin also takes any larger)
   const int cshift = __ffs(chunk_blocks) - 1;
-  uint64_t fsum = 0;
-  uint32_t bmin = 0xFFFFFFFFu, bmax = 0;
   for (int i0 = 0; i0 < rows; i0 += LB) {
     if (i0 > 0) {
 #pragma unroll
@@ -594,62 +616,67 @@ __global__ __launch_bounds__(kThreads) void index_topp_kernel(
         w[u] = (i0 + u < rows && j < nblk) ? ld_dev(e_io + j) : 0ull;
       }
     }
+    bool ok = true;
+#pragma unroll
+    for (int u = 0; u < LB; ++u) {
+      const int j = (i0 + u) * kThreads + tid;
+      if (i0 + u < rows && j < nblk) ok = ok && (uint32_t)(w[u] & kTagBits) == tag;
+    }
+    if (!ok) {
+#pragma unroll
+      for (int u = 0; u < LB; ++u) {
+        const int j = (i0 + u) * kThreads + tid;
+        if (i0 + u < rows && j < nblk) w[u] = settle(e_io + j, w[u], tag, budget);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < LB; ++u) {
       const int j = (i0 + u) * kThreads + tid;
       if (i0 + u < rows) {
         float m = -1.0f;  // no block
         if (j < nblk) {
-          const uint64_t x = settle(e_io + j, w[u], tag, budget);
-          m = (float)((double)__uint_as_float((uint32_t)(x >> 32)) * s_f[j >> cshift]);
-          fsum += fixed_mass(m);
-          bmin = min(bmin, __float_as_uint(m));
-          bmax = max(bmax, __float_as_uint(m));
+          m = (float)((double)__uint_as_float((uint32_t)(w[u] >> 32)) * s_f[j >> cshift]);
+          if (pick) {
+            const uint32_t bits = __float_as_uint(m);
+            const int bin = level_bin(bits, 0u, 22);
+            atomicAdd((unsigned long long*)&sm.bmass[bin], (unsigned long long)fixed_bits(bits));
+            atomicAdd(&sm.bcnt[bin], 1u);
+          }
         }
         s_mass[j] = m;
       }
     }
   }
-  // one reduction for (sum, min, max)
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    fsum += __shfl_xor(fsum, o);
-    bmin = min(bmin, (uint32_t)__shfl_xor((int)bmin, o));
-    bmax = max(bmax, (uint32_t)__shfl_xor((int)bmax, o));
-  }
-  if (lane == 0) {
-    sm.u64[wave] = fsum;
-    sm.u32a[wave] = bmin;
-    sm.u32b[wave] = bmax;
-  }
   __syncthreads();
-  fsum = 0;
-#pragma unroll
-  for (int w2 = 0; w2 < kWaves; ++w2) {
-    fsum += sm.u64[w2];
-    bmin = min(bmin, sm.u32a[w2]);
-    bmax = max(bmax, sm.u32b[w2]);
-  }
 
-  // threshold key: block j is selected iff key_of(m_j, j) >= thr
+  // ---- threshold key: block j is selected iff key_of(m_j, j) >= thr
   uint64_t thr = 0;
-  const float p = top_p[head];
-  if (p < 1.0f && nblk > 1) {
+  bool all = true, ready = false;
+  if (pick) {
     const uint64_t P = (uint64_t)ceil(ldexp((double)p, 62));
-    if (fsum >= P)
-      thr = select_threshold(s_mass, rows, nblk, P, __builtin_amdgcn_readfirstlane(bmin),
-                             __builtin_amdgcn_readfirstlane(bmax), sm);
+    if (wave == 0) scan_level(0, P, 0u, 0xFFFFFFFFu, 22, sm);
+    __syncthreads();
+    if (sm.found) {  // else the total mass is below p: every block
+      all = false;
+      thr = select_threshold(s_mass, rows, P, sm);
+      ready = sm.ready;
+    }
   }
 
   // ---- ordered compaction of the selected ids (ascending)
-  auto sel = [&](int i, float m) { return m >= 0.f && key_at(i, m) >= thr; };
-  const int total = rows_prefix(s_mass, rows, sel, sm);
   int* out = sel_idx + head * nblk_max;
-  for_rows(s_mass, rows, [&](int i, float m) {
-    const bool sl = sel(i, m);
-    const int ord = ordinal(sl, i, sm);
-    if (sl) out[ord] = i * kThreads + tid;
-  });
+  int total = nblk;
+  if (all) {
+    for (int j = tid; j < nblk; j += kThreads) out[j] = j;
+  } else {
+    auto sel = [&](int i, float m) { return m >= 0.f && key_at(i, m) >= thr; };
+    total = ready ? sm.total : rows_prefix(s_mass, rows, sel, sm);
+    for_rows(s_mass, rows, [&](int i, float m) {
+      const bool sl = sel(i, m);
+      const int ord = ordinal(sl, i, sm);
+      if (sl) out[ord] = i * kThreads + tid;
+    });
+  }
   if (tid == 0) {
     sel_cnt[head] = total;
     __hip_atomic_store(&counters[head], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call

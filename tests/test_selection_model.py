@@ -3,9 +3,10 @@ oracle with the acceptance rule on large, tied and near-tied mass vectors.
 
 The model restates the algorithm the index kernel runs in its last workgroup
 (fp32 block masses, composite keys (mass bits, inverted block id), fixed-point
-masses in 2^-62 units, refinement by 256-bin histograms over the mass bits while
-more than 64 candidates of unequal mass remain, exact ranking of the rest, and the
-equal-mass case resolved by count in ascending block order).  It exercises the algorithm's logic at sizes and
+masses in 2^-62 units, a first 256-bin level of half-octave bins over all blocks, then
+refinement by 256-bin histograms over the mass bits while more than 64 candidates of
+unequal mass remain, exact ranking of the rest, and the equal-mass case resolved by
+count in ascending block order).  It exercises the algorithm's logic at sizes and
 distributions the device sees (up to 16384 blocks) without a GPU; the device code
 itself is covered by the GPU parity tests.
 """
@@ -24,6 +25,27 @@ def _fixed(mf):
     return [int(np.float64(x) * 2.0 ** 62) for x in mf.astype(np.float32)]
 
 
+def _level(bits, fm, lo, hi, shift, cab, P):
+    """One histogram level over the candidates in [lo, hi]: bin = min((bits - lo) >> shift,
+    255); returns (mass above, count, lo, hi) of the bin where the cumulative mass from the
+    top reaches P, or None."""
+    bm = [0] * BINS
+    bc = [0] * BINS
+    for b_, f in zip(bits, fm):
+        if lo <= b_ <= hi:
+            k = min((b_ - lo) >> shift, BINS - 1)
+            bm[k] += f
+            bc[k] += 1
+    above = cab
+    for k in range(BINS - 1, -1, -1):
+        if bm[k] > 0 and above < P <= above + bm[k]:
+            nlo = lo + (k << shift)
+            nhi = hi if k == BINS - 1 else min(hi, nlo + (1 << shift) - 1)
+            return above, bc[k], nlo, nhi
+        above += bm[k]
+    return None
+
+
 def model_select(m64, p):
     """Blocks the device algorithm selects for fp64 masses m64 and threshold p (fp32).
 
@@ -37,34 +59,22 @@ def model_select(m64, p):
     keys = [(bits[j] << 32) | (0xFFFFFFFF - j) for j in range(n)]
     fm = _fixed(mf)
     P = int(np.ceil(np.ldexp(p, 62)))
-    if sum(fm) < P:
+    # first level: half-octave bins over all blocks, built in the same pass as the masses
+    r = _level(bits, fm, 0, 0xFFFFFFFF, 22, 0, P)
+    if r is None:  # the total mass is below p
+        assert sum(fm) < P
         return np.arange(n), 0
-    lo, hi, cab, cnt = min(bits), max(bits), 0, n
-    levels = 0
+    cab, cnt, lo, hi = r
+    levels = 1
     while cnt > FINAL and lo < hi:
         span = hi - lo
         shift = max(0, span.bit_length() - 8)
-        bm = [0] * BINS
-        bc = [0] * BINS
-        bmin = [None] * BINS
-        bmax = [None] * BINS
-        for j in range(n):
-            if lo <= bits[j] <= hi:
-                b = (bits[j] - lo) >> shift
-                assert 0 <= b < BINS
-                bm[b] += fm[j]
-                bc[b] += 1
-                bmin[b] = bits[j] if bmin[b] is None else min(bmin[b], bits[j])
-                bmax[b] = bits[j] if bmax[b] is None else max(bmax[b], bits[j])
-        above = cab
-        for b in range(BINS - 1, -1, -1):
-            if bm[b] > 0 and above < P <= above + bm[b]:
-                new = (above, bc[b], bmin[b], bmax[b])
-                break
-            above += bm[b]
-        cab, nc, nlo, nhi = new
-        assert nhi - nlo < max(1, span) or span == 0
-        cnt, lo, hi = nc, nlo, nhi
+        assert (span >> shift) < BINS
+        r = _level(bits, fm, lo, hi, shift, cab, P)
+        assert r is not None
+        ncab, nc, nlo, nhi = r
+        assert nhi - nlo < span
+        cab, cnt, lo, hi = ncab, nc, nlo, nhi
         levels += 1
     cands = [j for j in range(n) if lo <= bits[j] <= hi]
     assert len(cands) == cnt
@@ -82,6 +92,10 @@ def model_select(m64, p):
                 break
             run += fm[j]
         assert thr is not None
+        # the compaction's count: blocks above the range plus the admitted candidates
+        n_above = sum(1 for j in range(n) if bits[j] > hi)
+        n_cand = sum(1 for j in cands if keys[j] >= thr)
+        assert n_above + n_cand == sum(1 for j in range(n) if keys[j] >= thr)
     return np.array([j for j in range(n) if keys[j] >= thr]), levels
 
 
@@ -117,7 +131,7 @@ def test_model_matches_oracle(kind, n, p):
     sel = O.select_top_p(m, float(np.float32(p)))
     ok, why = A.accept_selection(m, float(np.float32(p)), G, sel)
     assert ok, why
-    assert levels <= 5
+    assert levels <= 4
 
 
 def test_model_ties_follow_block_order():
