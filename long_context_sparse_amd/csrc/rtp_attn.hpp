@@ -45,28 +45,31 @@ struct SubTile {
   uint4 k[4], v[4];
 };
 
-// Loads rows [row0, row0 + 16) of kg/vg (row stride 128); rows at or beyond row_end
-// are never read and come back as zeros.
+// Loads rows [row0, row0 + 16) of kg/vg (row stride 128).  A row at or beyond row_end
+// reads row min(row, row_end - 1) instead (row 0 when row_end <= 0), so every load is
+// unconditional and in bounds; attn_subtile masks those rows.  Branch-free loads let
+// the compiler count them, so the next sub-tile's loads stay in flight while the
+// current one is computed.
 __device__ __forceinline__ void load_subtile(SubTile& t, const uint16_t* __restrict__ kg,
                                              const uint16_t* __restrict__ vg, int row0, int row_end,
                                              int lane) {
   const int R = lane >> 4, c16 = lane & 15;
-  const bool full = row0 + 16 <= row_end;
+  const int last = max(row_end - 1, 0);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int row = row0 + 4 * i + R;
-    const bool ok = full || row < row_end;
+    const int row = min(row0 + 4 * i + R, last);
     const size_t off = (size_t)row * kHeadDim + c16 * 8;
-    t.k[i] = ok ? ld16(kg + off) : make_uint4(0, 0, 0, 0);
-    t.v[i] = ok ? ld16(vg + off) : make_uint4(0, 0, 0, 0);
+    t.k[i] = ld16(kg + off);
+    t.v[i] = ld16(vg + off);
   }
 }
 
 // Online-softmax update with one loaded sub-tile.  Rows at or beyond row_end are
-// masked; hmask picks the heads (bit h) that attend to these rows and must be 0 unless
+// masked (their logits are -inf and their V rows zero, whatever was loaded for them);
+// hmask picks the heads (bit h) that attend to these rows and must be 0 unless
 // row0 < row_end.  qk[h] holds head h's 8 query dims of this lane.
 template <int G>
-__device__ __forceinline__ void attn_subtile(AttnState<G>& s, const SubTile& t, int row0,
+__device__ __forceinline__ void attn_subtile(AttnState<G>& s, const SubTile& tile, int row0,
                                              int row_end, uint32_t hmask, const uint4 (&qk)[G],
                                              float scale_log2, int lane) {
   const int R = lane >> 4;
@@ -74,6 +77,13 @@ __device__ __forceinline__ void attn_subtile(AttnState<G>& s, const SubTile& t, 
   const bool myvalid = row0 + 4 * isel + R < row_end;
   const bool b3 = (lane >> 3) & 1, b2 = (lane >> 2) & 1;
   const bool counted = (lane & 3) == 0;
+  SubTile t;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    t.k[i] = tile.k[i];
+    const bool ok = row0 + 4 * i + R < row_end;
+    t.v[i] = ok ? tile.v[i] : make_uint4(0, 0, 0, 0);
+  }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     if (!((hmask >> h) & 1u)) continue;
@@ -145,12 +155,12 @@ __device__ __forceinline__ void attn_stream(AttnState<G>& s, const uint16_t* __r
     const int i2 = i + WAVES;
     const bool more = i2 < nitems;
     SubTile nxt;
-    int row2 = 0;
-    uint32_t hm2 = 0;
-    if (more) {
-      item(i2, row2, hm2);
-      load_subtile(nxt, kg, vg, row2, hm2 ? row_end : row2, lane);
-    }
+    int row2 = row0;
+    uint32_t hm2 = hm;
+    if (more) item(i2, row2, hm2);
+    // unconditional, so the compiler keeps these loads in flight over the compute below;
+    // past the last item they re-read the current rows (cache hits)
+    load_subtile(nxt, kg, vg, row2, hm2 ? row_end : row2, lane);
     attn_subtile<G>(s, cur, row0, row_end, hm, qk, scale_log2, lane);
     if (!more) break;
     cur = nxt;

@@ -92,6 +92,60 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 // 16-byte global load of 8 bf16 values.
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// A wave-uniform 64-bit value moved to scalar registers; a 64-bit value of one lane.
+__device__ __forceinline__ uint64_t uni64(uint64_t v) {
+  const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t b = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)b << 32) | a;
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t a = __builtin_amdgcn_readlane((uint32_t)v, l);
+  const uint32_t b = __builtin_amdgcn_readlane((uint32_t)(v >> 32), l);
+  return ((uint64_t)b << 32) | a;
+}
+
+// ------------------------------------------------------------------ published words
+// Values passed between workgroups of one launch without fences: every published
+// 64-bit word carries the call's tag (1..4095, advanced by every call) in its low 12
+// bits, words are written and read with relaxed device-scope atomics, and a reader
+// re-reads a word until it carries the current tag.  An fp64 keeps its top 52 bits
+// (relative precision 2^-40); an fp32 or an int sits in the high half.
+constexpr uint64_t kTagBits = 0xFFFull;
+constexpr int kSpinBudget = 1 << 12;  // re-reads a thread may spend waiting for one tag
+
+__device__ __forceinline__ uint64_t tagged(double x, uint32_t tag) {
+  return ((uint64_t)__double_as_longlong(x) & ~kTagBits) | tag;
+}
+__device__ __forceinline__ double untag(uint64_t w) { return __longlong_as_double((long long)(w & ~kTagBits)); }
+__device__ __forceinline__ uint64_t tagged_f32(float x, uint32_t tag) {
+  return ((uint64_t)__float_as_uint(x) << 32) | tag;
+}
+__device__ __forceinline__ float untag_f32(uint64_t w) { return __uint_as_float((uint32_t)(w >> 32)); }
+__device__ __forceinline__ uint64_t ld_dev(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool has_tag(uint64_t w, uint32_t tag) { return (uint32_t)(w & kTagBits) == tag; }
+// Re-read a published word until it carries `tag` (bounded by the thread's budget).
+__device__ __forceinline__ uint64_t settle(const uint64_t* p, uint64_t w, uint32_t tag, int& budget) {
+  while (!has_tag(w, tag) && budget > 0) {
+    --budget;
+    __builtin_amdgcn_s_sleep(1);
+    w = ld_dev(p);
+  }
+  return w;
+}
+// The tag a call uses, from the word that holds it (0 in a fresh workspace reads as 1),
+// and the tag of the next call.
+__device__ __forceinline__ uint32_t load_tag(const uint32_t* p) {
+  const uint32_t t = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return t == 0 ? 1u : t;
+}
+__device__ __forceinline__ uint32_t next_tag(uint32_t t) { return t % 4095u + 1u; }
 
 }  // namespace rtp
