@@ -96,13 +96,17 @@ size_t rtp_index_topp_workspace_size(int B, int n_ret, int max_ctx, int block);
  *   sel_idx   out int32 [B, n_ret, ceil(max_ctx / block)]  selected block ids,
  *             ascending, in the first sel_cnt[b, r] entries (the rest untouched)
  *   sel_cnt   out int32 [B, n_ret]      number of selected blocks (>= 1)
+ *   sel_mask  optional out uint8 [B, n_ret, ceil(max_ctx / block)]: the same set as a block
+ *             mask (Review, Hardware-aware top-p decoding kernel: the last workgroup writes
+ *             the block mask), 1 = selected, 0 = not, for blocks < ceil(N_b / block) (the
+ *             rest untouched); NULL to skip it
  *   workspace device scratch of >= rtp_index_topp_workspace_size(B, n_ret, max_ctx, block)
  *             bytes, zero-filled before first use
  */
 rtp_status rtp_index_topp(const void* q_pre, const void* w_q, const void* k_idx,
                           const int* seq_lens, const int* ret_heads, const float* top_p,
                           int B, int Hq, int n_ret, int max_ctx, int block,
-                          int* sel_idx, int* sel_cnt,
+                          int* sel_idx, int* sel_cnt, unsigned char* sel_mask,
                           void* workspace, size_t ws_bytes, void* stream);
 
 /*
@@ -123,13 +127,17 @@ rtp_status rtp_index_topp(const void* q_pre, const void* w_q, const void* k_idx,
  *   v_cache    bf16 [B, Hkv, max_ctx, 128]
  *   seq_lens, ret_heads as in rtp_index_topp
  *   sel_idx, sel_cnt    as written by rtp_index_topp for the same B, n_ret, max_ctx, block
+ *   sel_mask   optional: the block masks rtp_index_topp wrote for the same sizes.  When it is
+ *              not NULL the union of a split's blocks is read from it in one round of loads
+ *              (sel_idx and sel_cnt are then not read and may be NULL); otherwise each
+ *              head's ascending list is searched for the split's range.
  *   split_tokens  multiple of block; split_tokens / block <= 2048
  *   o_part     out fp32 [B, n_ret, n_split, 128], n_split = ceil(max_ctx / split_tokens)
  *   lse_part   out fp32 [B, n_ret, n_split]
  */
 rtp_status rtp_sparse_attn_split(const void* q, const void* k_cache, const void* v_cache,
                                  const int* seq_lens, const int* ret_heads,
-                                 const int* sel_idx, const int* sel_cnt,
+                                 const int* sel_idx, const int* sel_cnt, const unsigned char* sel_mask,
                                  int B, int Hq, int Hkv, int n_ret, int max_ctx, int block,
                                  int split_tokens, float* o_part, float* lse_part, void* stream);
 

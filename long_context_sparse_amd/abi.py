@@ -34,8 +34,8 @@ _SIGS = {
     "rtp_status_string": ([_i], ctypes.c_char_p),
     "rtp_version": ([], ctypes.c_char_p),
     "rtp_index_topp_workspace_size": ([_i, _i, _i, _i], _sz),
-    "rtp_index_topp": ([_vp] * 6 + [_i] * 5 + [_vp, _vp, _vp, _sz, _vp], _i),
-    "rtp_sparse_attn_split": ([_vp] * 7 + [_i] * 7 + [_vp, _vp, _vp], _i),
+    "rtp_index_topp": ([_vp] * 6 + [_i] * 5 + [_vp, _vp, _vp, _vp, _sz, _vp], _i),
+    "rtp_sparse_attn_split": ([_vp] * 8 + [_i] * 7 + [_vp, _vp, _vp], _i),
     "rtp_split_reduce": ([_vp] * 3 + [_i] * 4 + [_vp, _vp], _i),
     "rtp_local_window_workspace_size": ([_i] * 7, _sz),
     "rtp_local_window_attn": ([_vp] * 5 + [_i] * 7 + [_vp, _vp, _sz, _vp], _i),
@@ -157,17 +157,17 @@ def rtp_local_window_workspace_size(B: int, Hq: int, Hkv: int, n_loc: int, max_c
 
 
 def rtp_index_topp(q_pre, w_q, k_idx, seq_lens, ret_heads, top_p, B, Hq, n_ret, max_ctx, block,
-                   sel_idx, sel_cnt, workspace, stream=None) -> None:
+                   sel_idx, sel_cnt, workspace, stream=None, sel_mask=None) -> None:
     st = lib().rtp_index_topp(_p(q_pre), _p(w_q), _p(k_idx), _p(seq_lens), _p(ret_heads), _p(top_p),
-                              B, Hq, n_ret, max_ctx, block, _p(sel_idx), _p(sel_cnt), _p(workspace),
+                              B, Hq, n_ret, max_ctx, block, _p(sel_idx), _p(sel_cnt), _p(sel_mask), _p(workspace),
                               _nbytes(workspace), _s(stream))
     _check("rtp_index_topp", st)
 
 
 def rtp_sparse_attn_split(q, k_cache, v_cache, seq_lens, ret_heads, sel_idx, sel_cnt, B, Hq, Hkv,
-                          n_ret, max_ctx, block, split_tokens, o_part, lse_part, stream=None) -> None:
+                          n_ret, max_ctx, block, split_tokens, o_part, lse_part, stream=None, sel_mask=None) -> None:
     st = lib().rtp_sparse_attn_split(_p(q), _p(k_cache), _p(v_cache), _p(seq_lens), _p(ret_heads),
-                                     _p(sel_idx), _p(sel_cnt), B, Hq, Hkv, n_ret, max_ctx, block,
+                                     _p(sel_idx), _p(sel_cnt), _p(sel_mask), B, Hq, Hkv, n_ret, max_ctx, block,
                                      split_tokens, _p(o_part), _p(lse_part), _s(stream))
     _check("rtp_sparse_attn_split", st)
 

@@ -55,7 +55,8 @@ extern "C" size_t rtp_index_topp_workspace_size(int B, int n_ret, int max_ctx, i
 extern "C" rtp_status rtp_index_topp(const void* q_pre, const void* w_q, const void* k_idx,
                                      const int* seq_lens, const int* ret_heads, const float* top_p,
                                      int B, int Hq, int n_ret, int max_ctx, int block, int* sel_idx,
-                                     int* sel_cnt, void* workspace, size_t ws_bytes, void* stream) {
+                                     int* sel_cnt, unsigned char* sel_mask, void* workspace, size_t ws_bytes,
+                                     void* stream) {
   if (B <= 0 || Hq <= 0 || n_ret < 0 || n_ret > Hq || max_ctx <= 0) return RTP_EINVAL;
   if (block != 64 && block != 128) return RTP_EUNSUPPORTED;
   if (ceil_div(max_ctx, block) > kIdxMaxBlocks) return RTP_EUNSUPPORTED;
@@ -71,7 +72,7 @@ extern "C" rtp_status rtp_index_topp(const void* q_pre, const void* w_q, const v
   char* ws = static_cast<char*>(workspace);
   IndexArgs args{static_cast<const uint16_t*>(q_pre), static_cast<const uint16_t*>(w_q),
                  static_cast<const uint16_t*>(k_idx), seq_lens, ret_heads, top_p, Hq, n_ret, max_ctx,
-                 L.g.nblk_max, L.g.chunk_blocks, L.g.n_chunk, sel_idx, sel_cnt,
+                 L.g.nblk_max, L.g.chunk_blocks, L.g.n_chunk, sel_idx, sel_cnt, sel_mask,
                  reinterpret_cast<int*>(ws + L.off_counters), reinterpret_cast<uint64_t*>(ws + L.off_cmax),
                  reinterpret_cast<uint64_t*>(ws + L.off_e)};
   uint32_t* tags = reinterpret_cast<uint32_t*>(ws + L.off_tag);

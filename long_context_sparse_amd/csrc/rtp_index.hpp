@@ -104,6 +104,7 @@ struct IndexArgs {
   int Hq, n_ret, max_ctx, nblk_max, chunk_blocks, n_chunk_max;
   int* sel_idx;
   int* sel_cnt;
+  uint8_t* sel_mask;  // [B * n_ret, nblk_max] 1 = selected (blocks < nblk), or null
   int* counters;   // [B * n_ret] arrival counters, zero between calls
   uint64_t* cmax;  // [B * n_ret, n_chunk_max, 2] tagged (M_c, Z_c)
   uint64_t* blk_e; // [B * n_ret, nblk_max] tagged e_j
@@ -524,7 +525,8 @@ __device__ __forceinline__ bool index_chunk(const IndexArgs& a, int c, int r, in
 }
 
 // The selection of head (b, r), run by the workgroup index_chunk picked: writes the
-// ascending selected block ids and their count, and resets the head's arrival counter.
+// ascending selected block ids and their count (and, if asked, one byte per block:
+// 1 = selected), and resets the head's arrival counter.
 template <int T>
 __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int r, int b, IndexSmem<T>* S) {
   constexpr int W = T / kWave;
@@ -661,16 +663,22 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int r, 
 
   // ---- ordered compaction of the selected ids (ascending)
   int* out = a.sel_idx + head * a.nblk_max;
+  uint8_t* mask = a.sel_mask ? a.sel_mask + head * a.nblk_max : nullptr;
   int total = nblk;
   if (all) {
-    for (int j = tid; j < nblk; j += T) out[j] = j;
+    for (int j = tid; j < nblk; j += T) {
+      out[j] = j;
+      if (mask) mask[j] = 1;
+    }
   } else {
     auto sel = [&](int i, float m) { return m >= 0.f && key_at<T>(i, m) >= thr; };
     total = ready ? sm.total : rows_prefix<T>(s_mass, rows, sel, sm);
     for_rows<T>(s_mass, rows, [&](int i, float m) {
       const bool sl = sel(i, m);
       const int ord = ordinal<T>(sl, i, sm);
-      if (sl) out[ord] = i * T + tid;
+      const int j = i * T + tid;
+      if (sl) out[ord] = j;
+      if (mask && j < nblk) mask[j] = sl;
     });
   }
   if (tid == 0) {

@@ -7,7 +7,8 @@
 // (split, KV group, sequence); it builds the union of its retrieval heads' selected
 // blocks inside the split (binary search into each ascending list, LDS head-mask per
 // block, ordered compaction), so a block picked by several heads of the group is read
-// from HBM once, then streams the union's 16-token sub-tiles through the shared
+// from HBM once (with the index kernel's per-head block masks the union is one round of
+// byte loads), then streams the union's 16-token sub-tiles through the shared
 // attention core (rtp_attn.hpp) and emits per-head (o, lse) partials.
 //
 // Local heads: the same core over attention sinks + the sliding window (RTPurbo
@@ -53,6 +54,7 @@ struct SparseArgs {
   const int* ret_heads;
   const int* sel_idx;
   const int* sel_cnt;
+  const uint8_t* sel_mask;  // [B, n_ret, nblk_max] 1 = selected, or null (then the lists)
   int Hq, Hkv, n_ret, max_ctx, nblk_max, split_blocks;
 };
 struct LocalArgs {
@@ -111,13 +113,15 @@ __device__ __forceinline__ bool sparse_split(const SparseArgs& a, int c, int g, 
   const int* __restrict__ ret_heads = a.ret_heads;
   const int* __restrict__ sel_idx = a.sel_idx;
   const int* __restrict__ sel_cnt = a.sel_cnt;
-  // the first 64 selected counts go out with the head list (one memory round trip)
-  const int cnt_l = lane < n_ret ? sel_cnt[(size_t)b * n_ret + lane] : 0;
+  const uint8_t* __restrict__ sel_mask = a.sel_mask;
+  // the sequence length and (for the lists) the first 64 selected counts go out with the
+  // head list: one memory round trip
+  const int N = a.seq_lens[b];
+  const int cnt_l = (!sel_mask && lane < n_ret) ? sel_cnt[(size_t)b * n_ret + lane] : 0;
   int rbeg, rend;
   group_range(ret_heads, n_ret, g, G, rbeg, rend);
   const int nh = rend - rbeg;
   if (nh == 0) return false;
-  const int N = a.seq_lens[b];
   const int nblk = (N + BK - 1) / BK;
   const int jlo = c * split_blocks, jhi = min(jlo + split_blocks, nblk);
   uint32_t* s_hm = S->hm;
@@ -127,45 +131,64 @@ __device__ __forceinline__ bool sparse_split(const SparseArgs& a, int c, int g, 
   int nL = 0;
   if (jlo < jhi) {
     const int nb = jhi - jlo;
-    for (int i = tid; i < (nb + 3) / 4; i += kThreads) s_hm[i] = 0;
-    __syncthreads();
-    // mark each head's selected blocks in [jlo, jhi): one wave per head.  A list of at
-    // most 64 entries is read in one round; a longer one is searched for its range.
-    for (int h = wave; h < nh; h += kWaves) {
-      const int hh = rbeg + h;
-      const size_t hr = (size_t)b * n_ret + hh;
-      const int cnt = hh < 64 ? __shfl(cnt_l, hh) : sel_cnt[hr];
-      const int* sl = sel_idx + hr * nblk_max;
-      const uint32_t bit = 1u << h;
-      if (cnt <= 64) {
-        const int v = lane < cnt ? sl[lane] : -1;
-        if (v >= jlo && v < jhi) atomicOr(&s_hm[(v - jlo) >> 2], bit << (((v - jlo) & 3) * 8));
-      } else {
-        const int a = lower_bound_wave(sl, cnt, jlo);
-        const int e = lower_bound_wave(sl, cnt, jhi);
-        for (int i = a + lane; i < e; i += 64) {
-          const int off = sl[i] - jlo;
-          atomicOr(&s_hm[off >> 2], bit << ((off & 3) * 8));
-        }
-      }
-    }
-    __syncthreads();
-    // ordered compaction of the blocks some head selected: entry = (offset << 8) | mask
+    // per block of the split, the mask of the group's heads that selected it (one byte
+    // per block in s_hm); each wave then takes a contiguous segment of blocks
     const int seg = ((nb + kWaves - 1) / kWaves + 63) / 64 * 64;
     const int sb = wave * seg, se = min(nb, sb + seg);
+    uint8_t* hm8 = reinterpret_cast<uint8_t*>(s_hm);
     int cnt = 0;
-    for (int base = sb; base < se; base += 64) {
-      const int off = base + lane;
-      const uint32_t mk = off < se ? (s_hm[off >> 2] >> ((off & 3) * 8)) & 0xffu : 0u;
-      cnt += __popcll(__ballot(mk != 0));
+    if (sel_mask) {
+      // block masks: each lane ORs the group's heads' bytes of its blocks (one round trip)
+      const uint8_t* mrow = sel_mask + ((size_t)b * n_ret + rbeg) * nblk_max + jlo;
+      for (int base = sb; base < se; base += 64) {
+        const int off = base + lane;
+        uint32_t mk = 0;
+        if (off < se) {
+#pragma unroll
+          for (int h = 0; h < G; ++h)
+            if (h < nh && mrow[(size_t)h * nblk_max + off]) mk |= 1u << h;
+          hm8[off] = (uint8_t)mk;
+        }
+        cnt += __popcll(__ballot(mk != 0));
+      }
+    } else {
+      for (int i = tid; i < (nb + 3) / 4; i += kThreads) s_hm[i] = 0;
+      __syncthreads();
+      // mark each head's selected blocks in [jlo, jhi): one wave per head.  A list of at
+      // most 64 entries is read in one round; a longer one is searched for its range.
+      for (int h = wave; h < nh; h += kWaves) {
+        const int hh = rbeg + h;
+        const size_t hr = (size_t)b * n_ret + hh;
+        const int cnt_h = hh < 64 ? __shfl(cnt_l, hh) : sel_cnt[hr];
+        const int* sl = sel_idx + hr * nblk_max;
+        const uint32_t bit = 1u << h;
+        if (cnt_h <= 64) {
+          const int v = lane < cnt_h ? sl[lane] : -1;
+          if (v >= jlo && v < jhi) atomicOr(&s_hm[(v - jlo) >> 2], bit << (((v - jlo) & 3) * 8));
+        } else {
+          const int a0 = lower_bound_wave(sl, cnt_h, jlo);
+          const int e0 = lower_bound_wave(sl, cnt_h, jhi);
+          for (int i = a0 + lane; i < e0; i += 64) {
+            const int off = sl[i] - jlo;
+            atomicOr(&s_hm[off >> 2], bit << ((off & 3) * 8));
+          }
+        }
+      }
+      __syncthreads();
+      for (int base = sb; base < se; base += 64) {
+        const int off = base + lane;
+        const uint32_t mk = off < se ? hm8[off] : 0u;
+        cnt += __popcll(__ballot(mk != 0));
+      }
     }
+    // ordered compaction of the blocks some head selected: entry = (offset << 8) | mask
     if (lane == 0) s_wcnt[wave] = cnt;
     __syncthreads();
     int pos = 0;
     for (int w = 0; w < wave; ++w) pos += s_wcnt[w];
     for (int base = sb; base < se; base += 64) {
       const int off = base + lane;
-      const uint32_t mk = off < se ? (s_hm[off >> 2] >> ((off & 3) * 8)) & 0xffu : 0u;
+      const uint32_t mk = off < se ? hm8[off] : 0u;
       const uint64_t bal = __ballot(mk != 0);
       if (mk) s_list[pos + __popcll(bal & lanemask_lt())] = ((uint32_t)off << 8) | mk;
       pos += __popcll(bal);

@@ -152,7 +152,8 @@ using namespace rtp;
 
 extern "C" rtp_status rtp_sparse_attn_split(const void* q, const void* k_cache, const void* v_cache,
                                             const int* seq_lens, const int* ret_heads,
-                                            const int* sel_idx, const int* sel_cnt, int B, int Hq,
+                                            const int* sel_idx, const int* sel_cnt,
+                                            const unsigned char* sel_mask, int B, int Hq,
                                             int Hkv, int n_ret, int max_ctx, int block,
                                             int split_tokens, float* o_part, float* lse_part,
                                             void* stream) {
@@ -163,9 +164,8 @@ extern "C" rtp_status rtp_sparse_attn_split(const void* q, const void* k_cache, 
   if (split_tokens <= 0 || split_tokens % block) return RTP_EINVAL;
   if (split_tokens / block > kMaxSplitBlocks) return RTP_EUNSUPPORTED;
   if (n_ret == 0) return RTP_OK;
-  if (!q || !k_cache || !v_cache || !seq_lens || !ret_heads || !sel_idx || !sel_cnt || !o_part ||
-      !lse_part)
-    return RTP_EINVAL;
+  if (!q || !k_cache || !v_cache || !seq_lens || !ret_heads || !o_part || !lse_part) return RTP_EINVAL;
+  if (!sel_mask && (!sel_idx || !sel_cnt)) return RTP_EINVAL;
   if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache) & 15) return RTP_EINVAL;
   const int nblk_max = ceil_div(max_ctx, block);
   const int sb = split_tokens / block;
@@ -174,7 +174,7 @@ extern "C" rtp_status rtp_sparse_attn_split(const void* q, const void* k_cache, 
   dim3 grid(n_split, Hkv, B);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const SparseArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
-                     static_cast<const uint16_t*>(v_cache), seq_lens, ret_heads, sel_idx, sel_cnt, Hq, Hkv,
+                     static_cast<const uint16_t*>(v_cache), seq_lens, ret_heads, sel_idx, sel_cnt, sel_mask, Hq, Hkv,
                      n_ret, max_ctx, nblk_max, sb};
   const int G = Hq / Hkv;
   if (block == 64)

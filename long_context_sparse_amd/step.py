@@ -44,7 +44,7 @@ class StepShape:
 
 
 class DecodeStep:
-    def __init__(self, shape: StepShape, device: str = "cuda", overlap: bool = True):
+    def __init__(self, shape: StepShape, device: str = "cuda", overlap: bool = True, use_mask: bool = True):
         self.s = shape
         dev = torch.device(device)
         self.device = dev
@@ -53,6 +53,10 @@ class DecodeStep:
         f32 = dict(dtype=torch.float32, device=dev)
         self.sel_idx = torch.zeros((s.B, max(s.n_ret, 1), s.nblk_max), **i32)
         self.sel_cnt = torch.zeros((s.B, max(s.n_ret, 1)), **i32)
+        # per-head block masks: the index call writes them and the split attention reads
+        # its union from them in one round of loads (use_mask=False: the lists are searched)
+        self.sel_mask = (torch.zeros((s.B, max(s.n_ret, 1), s.nblk_max), dtype=torch.uint8, device=dev)
+                         if use_mask else None)
         self.o_part = torch.zeros((s.B, max(s.n_ret, 1), s.n_split, HEAD_DIM), **f32)
         self.lse_part = torch.zeros((s.B, max(s.n_ret, 1), s.n_split), **f32)
         self.out = torch.zeros((s.B, s.Hq, HEAD_DIM), **f32)
@@ -73,13 +77,14 @@ class DecodeStep:
         s = self.s
         abi.rtp_index_topp(t["q_pre"], t["w_q"], t["k_idx"], t["seq_lens"], t["ret_heads"], t["top_p"],
                            s.B, s.Hq, s.n_ret, s.max_ctx, s.block, self.sel_idx, self.sel_cnt,
-                           self.ws_index, stream)
+                           self.ws_index, stream, sel_mask=self.sel_mask)
 
     def sparse_attn(self, t: Dict[str, torch.Tensor], stream=None) -> None:
         s = self.s
         abi.rtp_sparse_attn_split(t["q"], t["k_cache"], t["v_cache"], t["seq_lens"], t["ret_heads"],
                                   self.sel_idx, self.sel_cnt, s.B, s.Hq, s.Hkv, s.n_ret, s.max_ctx,
-                                  s.block, s.split_tokens, self.o_part, self.lse_part, stream)
+                                  s.block, s.split_tokens, self.o_part, self.lse_part, stream,
+                                  sel_mask=self.sel_mask)
 
     def reduce(self, t: Dict[str, torch.Tensor], stream=None) -> None:
         s = self.s
@@ -100,6 +105,7 @@ class DecodeStep:
         p = abi.device_ptr
         side = self.side.cuda_stream if self.overlap else main
         L = abi.lib()
+        mk = p(self.sel_mask) if self.sel_mask is not None else None
         plan_side, plan_main = [], []
         if s.n_loc:
             plan_side.append(("rtp_local_window_attn", L.rtp_local_window_attn, (
@@ -109,11 +115,11 @@ class DecodeStep:
         if s.n_ret:
             plan_main.append(("rtp_index_topp", L.rtp_index_topp, (
                 p(t["q_pre"]), p(t["w_q"]), p(t["k_idx"]), p(t["seq_lens"]), p(t["ret_heads"]), p(t["top_p"]),
-                s.B, s.Hq, s.n_ret, s.max_ctx, s.block, p(self.sel_idx), p(self.sel_cnt), p(self.ws_index),
+                s.B, s.Hq, s.n_ret, s.max_ctx, s.block, p(self.sel_idx), p(self.sel_cnt), mk, p(self.ws_index),
                 abi.nbytes(self.ws_index), main)))
             plan_main.append(("rtp_sparse_attn_split", L.rtp_sparse_attn_split, (
                 p(t["q"]), p(t["k_cache"]), p(t["v_cache"]), p(t["seq_lens"]), p(t["ret_heads"]),
-                p(self.sel_idx), p(self.sel_cnt), s.B, s.Hq, s.Hkv, s.n_ret, s.max_ctx, s.block,
+                p(self.sel_idx), p(self.sel_cnt), mk, s.B, s.Hq, s.Hkv, s.n_ret, s.max_ctx, s.block,
                 s.split_tokens, p(self.o_part), p(self.lse_part), main)))
             plan_main.append(("rtp_split_reduce", L.rtp_split_reduce, (
                 p(self.o_part), p(self.lse_part), p(t["ret_heads"]), s.B, s.Hq, s.n_ret, s.n_split,

@@ -27,14 +27,15 @@ class Run:
     """One GPU decode step on a workload, with host copies of its outputs."""
 
     def __init__(self, inp: W.DecodeInputs, tensors=None, overlap: bool = True,
-                 split_tokens: Optional[int] = None, tag: str = ""):
+                 split_tokens: Optional[int] = None, tag: str = "", use_mask: bool = True):
         cfg = inp.cfg
         self.inp = inp
         say(f"[gpu] {tag or cfg.name}: B={cfg.B} Hq={cfg.Hq} Hkv={cfg.Hkv} n_ret={cfg.n_ret} "
             f"ctx={cfg.ctx[:4]}{'...' if len(cfg.ctx) > 4 else ''} block={cfg.block} "
-            f"split={split_tokens or cfg.split_tokens} window={cfg.window} sinks={cfg.sinks} seed={cfg.seed}")
+            f"split={split_tokens or cfg.split_tokens} window={cfg.window} sinks={cfg.sinks} seed={cfg.seed} "
+            f"{'masks' if use_mask else 'lists'}")
         self.t = tensors if tensors is not None else W.to_device(inp)
-        self.step = DecodeStep(shape_of(cfg, split_tokens), overlap=overlap)
+        self.step = DecodeStep(shape_of(cfg, split_tokens), overlap=overlap, use_mask=use_mask)
         self.out = self.step(self.t)
         torch.cuda.synchronize()
         self.out_h = self.out.cpu().numpy().astype(np.float64)

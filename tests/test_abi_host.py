@@ -36,13 +36,14 @@ def test_workspace_sizes():
 
 def _topp(**kw):
     a = dict(q_pre=FAKE, w_q=FAKE, k_idx=FAKE, seq_lens=FAKE, ret_heads=FAKE, top_p=FAKE, B=1, Hq=4,
-             n_ret=2, max_ctx=1024, block=64, sel_idx=FAKE, sel_cnt=FAKE, ws=FAKE, ws_bytes=0, stream=None)
+             n_ret=2, max_ctx=1024, block=64, sel_idx=FAKE, sel_cnt=FAKE, sel_mask=None, ws=FAKE, ws_bytes=0,
+             stream=None)
     a.update(kw)
     if a["ws_bytes"] == 0 and "ws_bytes" not in kw:
         a["ws_bytes"] = abi.rtp_index_topp_workspace_size(a["B"], a["n_ret"], a["max_ctx"], a["block"]) - 1
     return abi.lib().rtp_index_topp(a["q_pre"], a["w_q"], a["k_idx"], a["seq_lens"], a["ret_heads"], a["top_p"],
                                     a["B"], a["Hq"], a["n_ret"], a["max_ctx"], a["block"], a["sel_idx"],
-                                    a["sel_cnt"], a["ws"], a["ws_bytes"], a["stream"])
+                                    a["sel_cnt"], a["sel_mask"], a["ws"], a["ws_bytes"], a["stream"])
 
 
 def test_index_topp_rejects():
@@ -59,11 +60,13 @@ def test_index_topp_rejects():
 
 
 def _sparse(**kw):
-    a = dict(B=1, Hq=8, Hkv=2, n_ret=2, max_ctx=4096, block=64, split=1024)
+    a = dict(B=1, Hq=8, Hkv=2, n_ret=2, max_ctx=4096, block=64, split=1024, sel_idx=FAKE, sel_cnt=FAKE,
+             sel_mask=None)
     a.update(kw)
     ptr = kw.get("ptr", FAKE)
-    return abi.lib().rtp_sparse_attn_split(ptr, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["B"], a["Hq"], a["Hkv"],
-                                           a["n_ret"], a["max_ctx"], a["block"], a["split"], FAKE, FAKE, None)
+    return abi.lib().rtp_sparse_attn_split(ptr, FAKE, FAKE, FAKE, FAKE, a["sel_idx"], a["sel_cnt"], a["sel_mask"],
+                                           a["B"], a["Hq"], a["Hkv"], a["n_ret"], a["max_ctx"], a["block"],
+                                           a["split"], FAKE, FAKE, None)
 
 
 def test_sparse_attn_rejects():
@@ -74,6 +77,8 @@ def test_sparse_attn_rejects():
     assert _sparse(Hq=48, Hkv=2) == abi.RTP_EUNSUPPORTED  # 24 query heads per KV head
     assert _sparse(split=64 * 4096) == abi.RTP_EUNSUPPORTED
     assert _sparse(ptr=None) == abi.RTP_EINVAL
+    assert _sparse(sel_idx=None) == abi.RTP_EINVAL          # no lists and no masks
+    assert _sparse(sel_cnt=None) == abi.RTP_EINVAL
     assert _sparse(n_ret=0) == abi.RTP_OK
 
 

@@ -220,3 +220,26 @@ def test_workspace_reuse_across_inputs():
     rb = Run(b_, tensors=tb, tag="reuse B fresh")
     assert np.array_equal(outs[0].cpu().numpy().astype(np.float64), rb.out_h)
     assert np.array_equal(outs[2].cpu().numpy().astype(np.float64), rb.out_h)
+
+
+def test_block_masks_match_lists_and_give_the_same_partials():
+    """The index call's block masks hold exactly the listed blocks, and the split attention
+    reading its union from the masks writes bit-identical partials to the list search."""
+    cfg = W.custom_config(name="masks", B=3, Hkv=2, Hq=8, n_ret=6, ctx=(9000, 4097, 70), block=64, window=64,
+                          sinks=4, split_tokens=512, kind="peaked_diffuse")
+    inp = W.make_inputs(cfg)
+    t = W.to_device(inp)
+    m = Run(inp, tensors=t, tag="masks")
+    ls = Run(inp, tensors=t, tag="lists", use_mask=False)
+    mask = m.step.sel_mask.cpu().numpy()
+    for b in range(cfg.B):
+        nblk = -(-int(inp.seq_lens[b]) // cfg.block)
+        for r in range(cfg.n_ret):
+            G = m.gpu_blocks(b, r)
+            assert np.array_equal(G, ls.gpu_blocks(b, r))
+            want = np.zeros(nblk, np.uint8)
+            want[G] = 1
+            assert np.array_equal(mask[b, r, :nblk], want), (b, r)
+    assert torch.equal(m.step.o_part, ls.step.o_part)
+    assert torch.equal(m.step.lse_part, ls.step.lse_part)
+    assert np.array_equal(m.out_h, ls.out_h)
