@@ -33,12 +33,16 @@ if ROOT not in sys.path:
 
 METRIC = "sparse-decode step latency (µs) + effective HBM GB/s at 128K and 1M ctx"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, vendor figure
-KERNEL_NAMES = {
+KERNEL_NAMES = {                # call -> the kernel it launches (the local call also merges)
     "index_topp": "index_topp_kernel",
     "sparse_attn": "sparse_attn_kernel",
-    "split_reduce": "split_reduce_kernel",
+    "split_reduce": "merge_kernel",
     "local_window": "local_window_kernel",
 }
+
+
+CALL_NAMES = {"index_topp": "rtp_index_topp", "sparse_attn": "rtp_sparse_attn_split",
+              "split_reduce": "rtp_split_reduce", "local_window": "rtp_local_window_attn"}
 
 
 def log(*a) -> None:
@@ -173,7 +177,7 @@ def measure(name: str, steps: int, warmup: int, cold_iters: int, calib_copy: boo
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms_per_step = ev0.elapsed_time(ev1) / steps
-    log(f"[bench] {name}: {steps} steps, {ms_per_step * 1e3:.1f} us/step (wall {wall * 1e3 / steps:.1f} us/step)")
+    log(f"[bench] {name}: {steps} steps, {ms_per_step * 1e3:.1f} us/step (host {wall * 1e6 / steps:.1f} us/step)")
 
     # per-call durations: the four calls one after another on the main stream, with
     # events around each call on that stream
@@ -305,7 +309,7 @@ def main(argv: Optional[List[str]] = None) -> int:
                 "frac_of_peak": round(r["gbs"] / PEAK_HBM_GBS, 4), "alg_bytes": int(r["alg"]["step"]),
                 "cold_latency_us": None if r["cold_us"] is None else round(r["cold_us"], 2),
                 "cold_effective_gbs": None if not r["cold_us"] else round(r["alg"]["step"] / r["cold_us"] / 1e3, 1),
-                "kernel_us": {KERNEL_NAMES[k]: round(v, 2) for k, v in r["kern_us"].items()},
+                "call_us": {CALL_NAMES[k]: round(v, 2) for k, v in r["kern_us"].items()},
                 "mean_selected_block_fraction": round(r["sel_frac"], 4),
                 "roofline": roofline_of(r), "config": config_of(r["cfg"])}
 
