@@ -554,6 +554,10 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int r, 
   }
   const float p = a.top_p[head];
   const bool pick = p < 1.0f && nblk > 1;  // else every block is selected
+  // Every block of mass below (1 - p) / (2 nblk) is outside the selection and below its
+  // threshold: with total mass ~1 the threshold exceeds (total - p) / nblk.  Such blocks
+  // stay out of the histograms (peaked heads have thousands of them).
+  const uint32_t lbits = __float_as_uint(fmaxf(0.f, 0.5f * (1.0f - p - 1e-6f) / (float)nblk));
   const int rows = (nblk + T - 1) / T;
   constexpr int LB = 16;  // global reads in flight per thread
   uint64_t w[LB];         // the first LB rows' words go out before the reductions below
@@ -634,8 +638,8 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int r, 
         float m = -1.0f;  // no block
         if (j < nblk) {
           m = (float)((double)untag_f32(w[u]) * S->f[j >> cshift]);
-          if (pick) {
-            const uint32_t bits = __float_as_uint(m);
+          const uint32_t bits = __float_as_uint(m);
+          if (pick && bits >= lbits) {
             const int bin = level_bin(bits, 0u, 22);
             atomicAdd((unsigned long long*)&sm.bmass[bin], (unsigned long long)fixed_bits(bits));
             atomicAdd(&sm.bcnt[bin], 1u);
@@ -652,7 +656,11 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int r, 
   bool all = true, ready = false;
   if (pick) {
     const uint64_t P = (uint64_t)ceil(ldexp((double)p, 62));
-    if (wave == 0) scan_level<T>(0, P, 0u, 0xFFFFFFFFu, 22, sm);
+    if (wave == 0) {
+      scan_level<T>(0, P, 0u, 0xFFFFFFFFu, 22, sm);
+      // the pruned blocks were not counted: the candidates start at the floor
+      if (lane == 0 && sm.found) sm.lo = min(max(sm.lo, lbits), sm.hi);
+    }
     __syncthreads();
     if (sm.found) {  // else the total mass is below p: every block
       all = false;

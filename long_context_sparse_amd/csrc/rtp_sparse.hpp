@@ -24,6 +24,7 @@ namespace rtp {
 constexpr int kAttnThreads = 256;
 constexpr int kAttnWaves = kAttnThreads / kWave;
 constexpr int kMaxSplitBlocks = 2048;
+constexpr int kOrderMax = 256;  // KV groups (sequences x KV heads) kernel 2 orders by weight
 
 template <int G>
 struct SparseSmem {
@@ -32,6 +33,8 @@ struct SparseSmem {
   int wcnt[kAttnWaves];
   float m[kAttnWaves * G], l[kAttnWaves * G];
   float acc[kAttnWaves * G * kHeadDim];
+  int gw[kOrderMax];  // per KV group: selected blocks summed over its retrieval heads
+  int pick;
 };
 template <int G>
 struct LocalSmem {
@@ -98,6 +101,36 @@ __device__ __forceinline__ int lower_bound_wave(const int* __restrict__ a, int n
     lo += (k - 1) * step + 1;
   }
   return lo;
+}
+
+// Kernel 2's dispatch order of KV groups: the group of rank `rank` when groups are taken
+// heaviest first (most selected blocks summed over their retrieval heads, ties by
+// index), so the grid ends with its lightest workgroups and drains quickly.  Returns
+// b * Hkv + g.  Without the counts (block masks only) or with more than kOrderMax
+// groups, the natural order.  Every thread of the workgroup calls it.
+template <int G>
+__device__ __forceinline__ int group_of_rank(const SparseArgs& a, int B, int rank, SparseSmem<G>* S) {
+  const int ngrp = B * a.Hkv;
+  if (!a.sel_cnt || ngrp > kOrderMax) return rank;
+  const int tid = threadIdx.x;
+  for (int k = tid; k < ngrp; k += kAttnThreads) S->gw[k] = 0;
+  __syncthreads();
+  for (int i = tid; i < B * a.n_ret; i += kAttnThreads) {
+    const int b = i / a.n_ret, r = i - b * a.n_ret;
+    atomicAdd(&S->gw[b * a.Hkv + a.ret_heads[r] / G], a.sel_cnt[i]);
+  }
+  __syncthreads();
+  for (int k = tid; k < ngrp; k += kAttnThreads) {
+    const int wk = S->gw[k];
+    int rk = 0;
+    for (int k2 = 0; k2 < ngrp; ++k2) {
+      const int w2 = S->gw[k2];
+      rk += (w2 > wk) || (w2 == wk && k2 < k);
+    }
+    if (rk == rank) S->pick = k;
+  }
+  __syncthreads();
+  return S->pick;
 }
 
 // Split c of KV group g of sequence b.  emit(i, d, o, lse) takes retrieval head i's dim d

@@ -1,8 +1,9 @@
 // Kernel 2 of the decode path, the local heads' kernel and the log-sum-exp merge, as
 // launches (their attention device code and its description are in rtp_sparse.hpp).
 //
-// Kernel 2: grid (split, KV group, sequence), 256 threads; each workgroup writes per-head
-// (o, lse) partials of its split, which rtp_split_reduce merges.  Local heads: grid
+// Kernel 2: grid (split, KV group rank), 256 threads; each workgroup writes per-head
+// (o, lse) partials of its split, which rtp_split_reduce merges.  KV groups are ranked
+// by their selected-block counts, heaviest first, so the grid drains on light work.  Local heads: grid
 // (window split, KV group, sequence); the partials go to the workspace and the merge
 // kernel (one workgroup per output row, the same kernel as the cross-split reduce)
 // combines them with the log-sum-exp rule on the same stream.
@@ -18,7 +19,10 @@ template <int BK, int G>
 __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(SparseArgs a, int n_split, float* __restrict__ o_part,
                                                                float* __restrict__ lse_part) {
   __shared__ SparseSmem<G> S;
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // workgroups are dispatched in blockIdx order: (split, group rank), heaviest group first
+  const int c = blockIdx.x;
+  const int bg = group_of_rank<G>(a, gridDim.z, blockIdx.y + a.Hkv * blockIdx.z, &S);
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int n_ret = a.n_ret;
   sparse_split<BK, G>(a, c, g, b, &S, [&](int i, int d, float o, float lse) {
     const size_t hr = (size_t)b * n_ret + i;

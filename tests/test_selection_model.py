@@ -25,14 +25,14 @@ def _fixed(mf):
     return [int(np.float64(x) * 2.0 ** 62) for x in mf.astype(np.float32)]
 
 
-def _level(bits, fm, lo, hi, shift, cab, P):
-    """One histogram level over the candidates in [lo, hi]: bin = min((bits - lo) >> shift,
-    255); returns (mass above, count, lo, hi) of the bin where the cumulative mass from the
-    top reaches P, or None."""
+def _level(bits, fm, lo, hi, shift, cab, P, floor=0):
+    """One histogram level over the candidates in [lo, hi] (and >= floor): bin =
+    min((bits - lo) >> shift, 255); returns (mass above, count, lo, hi) of the bin where
+    the cumulative mass from the top reaches P, or None."""
     bm = [0] * BINS
     bc = [0] * BINS
     for b_, f in zip(bits, fm):
-        if lo <= b_ <= hi:
+        if lo <= b_ <= hi and b_ >= floor:
             k = min((b_ - lo) >> shift, BINS - 1)
             bm[k] += f
             bc[k] += 1
@@ -46,7 +46,15 @@ def _level(bits, fm, lo, hi, shift, cab, P):
     return None
 
 
-def model_select(m64, p):
+def prune_floor(p: float, n: int) -> int:
+    """Bits of the device's pruning floor (1 - p - 1e-6) / (2 n), in fp32 as the device
+    computes it: blocks below it stay out of the histograms."""
+    f32 = np.float32
+    x = f32(0.5) * (f32(1.0) - f32(p) - f32(1e-6)) / f32(n)
+    return int(np.array(max(f32(0.0), x), dtype=np.float32).view(np.uint32))
+
+
+def model_select(m64, p, prune=True):
     """Blocks the device algorithm selects for fp64 masses m64 and threshold p (fp32).
 
     Returns (blocks, levels)."""
@@ -59,12 +67,15 @@ def model_select(m64, p):
     keys = [(bits[j] << 32) | (0xFFFFFFFF - j) for j in range(n)]
     fm = _fixed(mf)
     P = int(np.ceil(np.ldexp(p, 62)))
-    # first level: half-octave bins over all blocks, built in the same pass as the masses
-    r = _level(bits, fm, 0, 0xFFFFFFFF, 22, 0, P)
+    # first level: half-octave bins over all blocks above the pruning floor, built in the
+    # same pass as the masses
+    floor = prune_floor(p, n) if prune else 0
+    r = _level(bits, fm, 0, 0xFFFFFFFF, 22, 0, P, floor)
     if r is None:  # the total mass is below p
         assert sum(fm) < P
         return np.arange(n), 0
     cab, cnt, lo, hi = r
+    lo = min(max(lo, floor), hi)
     levels = 1
     while cnt > FINAL and lo < hi:
         span = hi - lo
@@ -132,6 +143,9 @@ def test_model_matches_oracle(kind, n, p):
     ok, why = A.accept_selection(m, float(np.float32(p)), G, sel)
     assert ok, why
     assert levels <= 4
+    # pruning the negligible blocks never changes the set
+    G0, _ = model_select(m, p, prune=False)
+    assert np.array_equal(G, G0)
 
 
 def test_model_ties_follow_block_order():
