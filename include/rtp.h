@@ -184,6 +184,32 @@ rtp_status rtp_local_window_attn(const void* q, const void* k_cache, const void*
                                  int window, int sinks, float* out,
                                  void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * One decode step in one host call: the four calls above, enqueued in their order for
+ * the same arguments (Strikes-Back architecture paragraph: Kernel 1, Kernel 2 and the
+ * reduce; Review, Adaptive sparse attention: local heads).  rtp_local_window_attn goes to
+ * side_stream, forked from `stream` by recording ev_fork on it and joined back by
+ * recording ev_join on side_stream and making `stream` wait for it, so the local heads
+ * overlap the retrieval heads' calls; with side_stream, ev_fork or ev_join NULL (or
+ * n_ret == 0 or n_loc == 0) everything runs on `stream`.  The caller owns the streams
+ * and the events (hipEvent_t as void*, created without timing); the library creates
+ * nothing.  Returns the first failing call's status.
+ *
+ *   o_part, lse_part   split partials as in rtp_sparse_attn_split (n_split =
+ *                      ceil(max_ctx / split_tokens))
+ *   ws_index           workspace of rtp_index_topp; ws_local of rtp_local_window_attn
+ *   every other argument as in the four calls
+ */
+rtp_status rtp_decode_step(const void* q_pre, const void* w_q, const void* k_idx, const void* q,
+                           const void* k_cache, const void* v_cache, const int* seq_lens,
+                           const int* ret_heads, const int* loc_heads, const float* top_p,
+                           int B, int Hq, int Hkv, int n_ret, int n_loc, int max_ctx, int block,
+                           int split_tokens, int window, int sinks,
+                           int* sel_idx, int* sel_cnt, unsigned char* sel_mask,
+                           float* o_part, float* lse_part, float* out,
+                           void* ws_index, size_t ws_index_bytes, void* ws_local, size_t ws_local_bytes,
+                           void* stream, void* side_stream, void* ev_fork, void* ev_join);
+
 #ifdef __cplusplus
 }
 #endif

@@ -39,6 +39,7 @@ _SIGS = {
     "rtp_split_reduce": ([_vp] * 3 + [_i] * 4 + [_vp, _vp], _i),
     "rtp_local_window_workspace_size": ([_i] * 7, _sz),
     "rtp_local_window_attn": ([_vp] * 5 + [_i] * 7 + [_vp, _vp, _sz, _vp], _i),
+    "rtp_decode_step": ([_vp] * 10 + [_i] * 10 + [_vp] * 6 + [_vp, _sz, _vp, _sz] + [_vp] * 4, _i),
 }
 
 

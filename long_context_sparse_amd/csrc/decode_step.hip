@@ -1,0 +1,42 @@
+// One decode step as a single host call: the four calls of the path enqueued in order
+// from C, so the host pays one call instead of four plus the event calls (the step's
+// enqueue cost decides the latency when the device work is short, as at 1M tokens).
+
+#include "rtp_common.hpp"
+
+extern "C" rtp_status rtp_decode_step(
+    const void* q_pre, const void* w_q, const void* k_idx, const void* q, const void* k_cache,
+    const void* v_cache, const int* seq_lens, const int* ret_heads, const int* loc_heads, const float* top_p,
+    int B, int Hq, int Hkv, int n_ret, int n_loc, int max_ctx, int block, int split_tokens, int window,
+    int sinks, int* sel_idx, int* sel_cnt, unsigned char* sel_mask, float* o_part, float* lse_part, float* out,
+    void* ws_index, size_t ws_index_bytes, void* ws_local, size_t ws_local_bytes, void* stream,
+    void* side_stream, void* ev_fork, void* ev_join) {
+  if (B <= 0 || Hq <= 0 || n_ret < 0 || n_loc < 0 || n_ret + n_loc > Hq) return RTP_EINVAL;
+  const int n_split = split_tokens > 0 ? (max_ctx + split_tokens - 1) / split_tokens : 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool fork = n_loc > 0 && n_ret > 0 && side_stream && ev_fork && ev_join;
+  rtp_status st = RTP_OK;
+  if (n_loc > 0) {
+    hipStream_t ls = s;
+    if (fork) {
+      ls = static_cast<hipStream_t>(side_stream);
+      if (hipEventRecord(static_cast<hipEvent_t>(ev_fork), s) != hipSuccess ||
+          hipStreamWaitEvent(ls, static_cast<hipEvent_t>(ev_fork), 0) != hipSuccess)
+        return RTP_ELAUNCH;
+    }
+    st = rtp_local_window_attn(q, k_cache, v_cache, seq_lens, loc_heads, B, Hq, Hkv, n_loc, max_ctx, window,
+                               sinks, out, ws_local, ws_local_bytes, ls);
+    if (st != RTP_OK) return st;
+    if (fork && hipEventRecord(static_cast<hipEvent_t>(ev_join), ls) != hipSuccess) return RTP_ELAUNCH;
+  }
+  if (n_ret > 0) {
+    st = rtp_index_topp(q_pre, w_q, k_idx, seq_lens, ret_heads, top_p, B, Hq, n_ret, max_ctx, block, sel_idx,
+                        sel_cnt, sel_mask, ws_index, ws_index_bytes, stream);
+    if (st == RTP_OK)
+      st = rtp_sparse_attn_split(q, k_cache, v_cache, seq_lens, ret_heads, sel_idx, sel_cnt, sel_mask, B, Hq, Hkv,
+                                 n_ret, max_ctx, block, split_tokens, o_part, lse_part, stream);
+    if (st == RTP_OK) st = rtp_split_reduce(o_part, lse_part, ret_heads, B, Hq, n_ret, n_split, out, stream);
+  }
+  if (fork && hipStreamWaitEvent(s, static_cast<hipEvent_t>(ev_join), 0) != hipSuccess) return RTP_ELAUNCH;
+  return st;
+}

@@ -1,7 +1,7 @@
 """One decode step of the sparse attention path, as four librtp calls.
 
-DecodeStep owns the device buffers the calls need (selected-block lists, split
-partials, workspaces, output) and issues
+DecodeStep owns the device buffers the calls need (selected-block lists and masks,
+split partials, workspaces, output) and issues them through one rtp_decode_step call:
 
   retrieval heads:  rtp_index_topp -> rtp_sparse_attn_split -> rtp_split_reduce
   local heads:      rtp_local_window_attn (on a second stream, overlapping the above)
@@ -71,6 +71,7 @@ class DecodeStep:
         self._join = abi.event_create() if self.overlap else None
         self._key = None
         self._vals = None
+        self._step_fn = abi.lib().rtp_decode_step
 
     # -- the four calls -------------------------------------------------------------
     def index_topp(self, t: Dict[str, torch.Tensor], stream=None) -> None:
@@ -98,56 +99,35 @@ class DecodeStep:
                                   self.ws_local, stream)
 
     # -- the whole step -------------------------------------------------------------
-    def _plan(self, t: Dict[str, torch.Tensor], main: int):
-        """Argument tuples of the four calls for these tensors and this stream, converted
-        once (the C functions take raw pointers and sizes)."""
+    def _plan(self, t: Dict[str, torch.Tensor], main: int) -> tuple:
+        """Arguments of rtp_decode_step for these tensors and this stream, converted once
+        (the C function takes raw pointers and sizes)."""
         s = self.s
         p = abi.device_ptr
-        side = self.side.cuda_stream if self.overlap else main
-        L = abi.lib()
-        mk = p(self.sel_mask) if self.sel_mask is not None else None
-        plan_side, plan_main = [], []
-        if s.n_loc:
-            plan_side.append(("rtp_local_window_attn", L.rtp_local_window_attn, (
-                p(t["q"]), p(t["k_cache"]), p(t["v_cache"]), p(t["seq_lens"]), p(t["loc_heads"]), s.B, s.Hq,
-                s.Hkv, s.n_loc, s.max_ctx, s.window, s.sinks, p(self.out), p(self.ws_local),
-                abi.nbytes(self.ws_local), side)))
-        if s.n_ret:
-            plan_main.append(("rtp_index_topp", L.rtp_index_topp, (
-                p(t["q_pre"]), p(t["w_q"]), p(t["k_idx"]), p(t["seq_lens"]), p(t["ret_heads"]), p(t["top_p"]),
-                s.B, s.Hq, s.n_ret, s.max_ctx, s.block, p(self.sel_idx), p(self.sel_cnt), mk, p(self.ws_index),
-                abi.nbytes(self.ws_index), main)))
-            plan_main.append(("rtp_sparse_attn_split", L.rtp_sparse_attn_split, (
-                p(t["q"]), p(t["k_cache"]), p(t["v_cache"]), p(t["seq_lens"]), p(t["ret_heads"]),
-                p(self.sel_idx), p(self.sel_cnt), mk, s.B, s.Hq, s.Hkv, s.n_ret, s.max_ctx, s.block,
-                s.split_tokens, p(self.o_part), p(self.lse_part), main)))
-            plan_main.append(("rtp_split_reduce", L.rtp_split_reduce, (
-                p(self.o_part), p(self.lse_part), p(t["ret_heads"]), s.B, s.Hq, s.n_ret, s.n_split,
-                p(self.out), main)))
-        return plan_side, plan_main
+        z = lambda name: p(t[name]) if t[name].numel() else None  # noqa: E731
+        side = self.side.cuda_stream if self.overlap else None
+        return (z("q_pre") if s.n_ret else None, z("w_q") if s.n_ret else None, z("k_idx") if s.n_ret else None,
+                p(t["q"]), p(t["k_cache"]), p(t["v_cache"]), p(t["seq_lens"]),
+                z("ret_heads") if s.n_ret else None, z("loc_heads") if s.n_loc else None,
+                z("top_p") if s.n_ret else None, s.B, s.Hq, s.Hkv, s.n_ret, s.n_loc, s.max_ctx, s.block,
+                s.split_tokens, s.window, s.sinks, p(self.sel_idx), p(self.sel_cnt),
+                p(self.sel_mask) if self.sel_mask is not None else None, p(self.o_part), p(self.lse_part),
+                p(self.out), p(self.ws_index), abi.nbytes(self.ws_index), p(self.ws_local),
+                abi.nbytes(self.ws_local), main, side, self._fork, self._join)
 
     def __call__(self, t: Dict[str, torch.Tensor]) -> torch.Tensor:
         """Enqueue one decode step on the current stream; returns the fp32 [B, Hq, 128] output.
 
-        The local heads' call goes to a second stream (forked from and joined back into
-        the current one with events) so it overlaps the retrieval heads' three calls.
-        The calls' argument tuples are converted once per (set of tensors, stream)."""
+        One rtp_decode_step call: the local heads' call goes to a second stream (forked
+        from and joined back into the current one with events) so it overlaps the
+        retrieval heads' three calls.  The arguments are converted once per (set of
+        tensors, stream)."""
         main = torch.cuda.current_stream(self.device).cuda_stream
         vals = tuple(t.values())
         key = (main,) + tuple(map(id, vals))
         if self._key != key:
-            self._plan_side, self._plan_main = self._plan(t, main)
+            self._args = self._plan(t, main)
             self._key = key
             self._vals = vals  # the plan's tensors stay alive, so their ids stay theirs
-        if self.overlap:
-            abi.event_record(self._fork, main)
-            abi.stream_wait_event(self.side.cuda_stream, self._fork)
-        for name, fn, args in self._plan_side:
-            abi.check(name, fn(*args))
-        if self.overlap:
-            abi.event_record(self._join, self.side.cuda_stream)
-        for name, fn, args in self._plan_main:
-            abi.check(name, fn(*args))
-        if self.overlap:
-            abi.stream_wait_event(main, self._join)
+        abi.check("rtp_decode_step", self._step_fn(*self._args))
         return self.out
