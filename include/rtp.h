@@ -193,7 +193,8 @@ rtp_status rtp_local_window_attn(const void* q, const void* k_cache, const void*
  * overlap the retrieval heads' calls; with side_stream, ev_fork or ev_join NULL (or
  * n_ret == 0 or n_loc == 0) everything runs on `stream`.  The caller owns the streams
  * and the events (hipEvent_t as void*, created without timing); the library creates
- * nothing.  Returns the first failing call's status.
+ * nothing.  Every argument is checked (as by each call) before anything is enqueued;
+ * after that it returns the first failing call's status.
  *
  *   o_part, lse_part   split partials as in rtp_sparse_attn_split (n_split =
  *                      ceil(max_ctx / split_tokens))

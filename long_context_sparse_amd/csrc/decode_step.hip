@@ -4,6 +4,8 @@
 
 #include "rtp_common.hpp"
 
+using rtp::ceil_div;
+
 extern "C" rtp_status rtp_decode_step(
     const void* q_pre, const void* w_q, const void* k_idx, const void* q, const void* k_cache,
     const void* v_cache, const int* seq_lens, const int* ret_heads, const int* loc_heads, const float* top_p,
@@ -11,8 +13,32 @@ extern "C" rtp_status rtp_decode_step(
     int sinks, int* sel_idx, int* sel_cnt, unsigned char* sel_mask, float* o_part, float* lse_part, float* out,
     void* ws_index, size_t ws_index_bytes, void* ws_local, size_t ws_local_bytes, void* stream,
     void* side_stream, void* ev_fork, void* ev_join) {
-  if (B <= 0 || Hq <= 0 || n_ret < 0 || n_loc < 0 || n_ret + n_loc > Hq) return RTP_EINVAL;
-  const int n_split = split_tokens > 0 ? (max_ctx + split_tokens - 1) / split_tokens : 0;
+  // every argument is checked before anything is enqueued
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_ctx <= 0 || n_ret < 0 || n_loc < 0 || n_ret + n_loc > Hq)
+    return RTP_EINVAL;
+  if (Hq % Hkv) return RTP_EINVAL;
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return RTP_EUNSUPPORTED;
+  if (!q || !k_cache || !v_cache || !seq_lens || !out) return RTP_EINVAL;
+  if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache) & 15) return RTP_EINVAL;
+  if (n_ret > 0) {
+    if (block != 64 && block != 128) return RTP_EUNSUPPORTED;
+    if (split_tokens <= 0 || split_tokens % block) return RTP_EINVAL;
+    if (split_tokens / block > 2048 || ceil_div(max_ctx, split_tokens) > 65535) return RTP_EUNSUPPORTED;
+    if (!q_pre || !w_q || !k_idx || !ret_heads || !top_p || !sel_idx || !sel_cnt || !o_part || !lse_part ||
+        !ws_index)
+      return RTP_EINVAL;
+    if (((uintptr_t)q_pre | (uintptr_t)w_q | (uintptr_t)k_idx) & 15) return RTP_EINVAL;
+    const size_t need = rtp_index_topp_workspace_size(B, n_ret, max_ctx, block);
+    if (need == 0) return RTP_EUNSUPPORTED;  // more blocks than one selection holds
+    if (ws_index_bytes < need || ((uintptr_t)ws_index & 255)) return RTP_EINVAL;
+  }
+  if (n_loc > 0) {
+    if (window < 0 || sinks < 0 || window + sinks < 1 || !loc_heads || !ws_local) return RTP_EINVAL;
+    const size_t need = rtp_local_window_workspace_size(B, Hq, Hkv, n_loc, max_ctx, window, sinks);
+    if (need == 0 || ws_local_bytes < need || ((uintptr_t)ws_local & 255)) return RTP_EINVAL;
+  }
+  const int n_split = n_ret > 0 ? ceil_div(max_ctx, split_tokens) : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool fork = n_loc > 0 && n_ret > 0 && side_stream && ev_fork && ev_join;
   rtp_status st = RTP_OK;

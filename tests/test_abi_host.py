@@ -97,3 +97,18 @@ def test_reduce_and_local_reject():
                                    1 << 30, None) == abi.RTP_EINVAL
     assert L.rtp_local_window_attn(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 0, 4096, 16, 4, FAKE, FAKE,
                                    0, None) == abi.RTP_OK
+
+
+def test_decode_step_rejects():
+    L = abi.lib()
+    args = [FAKE] * 10 + [1, 8, 2, 2, 6, 4096, 64, 1024, 1024, 4] + [FAKE] * 6 + [FAKE, 1 << 30, FAKE, 1 << 30] + \
+        [None] * 4
+    bad = list(args)
+    bad[10] = 0                                        # B = 0
+    assert L.rtp_decode_step(*bad) == abi.RTP_EINVAL
+    bad = list(args)
+    bad[13], bad[14] = 5, 6                            # more heads than query heads
+    assert L.rtp_decode_step(*bad) == abi.RTP_EINVAL
+    bad = list(args)
+    bad[16] = 96                                       # block size outside {64, 128}
+    assert L.rtp_decode_step(*bad) == abi.RTP_EUNSUPPORTED

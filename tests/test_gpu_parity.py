@@ -243,3 +243,17 @@ def test_block_masks_match_lists_and_give_the_same_partials():
     assert torch.equal(m.step.o_part, ls.step.o_part)
     assert torch.equal(m.step.lse_part, ls.step.lse_part)
     assert np.array_equal(m.out_h, ls.out_h)
+
+
+def test_one_stream_matches_two_streams():
+    """rtp_decode_step without a side stream (everything in order on one stream) gives the
+    same bits as the forked step."""
+    cfg = W.custom_config(name="streams", B=2, Hkv=2, Hq=8, n_ret=3, ctx=(7000, 3001), block=64, window=600,
+                          sinks=4, split_tokens=512, kind="peaked_diffuse")
+    inp = W.make_inputs(cfg)
+    t = W.to_device(inp)
+    two = Run(inp, tensors=t, tag="two streams")
+    one = Run(inp, tensors=t, tag="one stream", overlap=False)
+    assert not one.step.overlap and two.step.overlap
+    assert np.array_equal(one.out_h, two.out_h)
+    assert np.array_equal(one.sel_cnt, two.sel_cnt)
