@@ -23,9 +23,10 @@
 // block's mass m_j = e_j exp(M_c - M) / Z in fp32 into LDS, then the greedy threshold
 // exactly: a key = (fp32 mass bits, inverted block id) orders blocks by mass with ties
 // by ascending id; masses are summed as fixed-point integers (2^-62 units) so every
-// cumulative sum is exact and order-independent.  The pass that writes the masses also
-// builds the first 256-bin LDS histogram of (count, mass), half an octave per bin
-// (bits >> 22); one wave scans it for the bin where the cumulative mass from the top
+// cumulative sum is exact and order-independent.  Blocks below (1 - p) / (2 nblk) can
+// never be selected and stay out; the pass that writes the masses also builds the first
+// 256-bin LDS histogram of (count, mass) of the others, an eighth of an octave per bin
+// from that floor; one wave scans it for the bin where the cumulative mass from the top
 // crosses p.  While more than 64 candidates of unequal mass remain, a further level bins
 // the candidates by (bits - lo) >> shift (>= 128x narrower each time); the last <= 64
 // candidates are gathered (the same pass counts the blocks above them) and ranked
@@ -558,6 +559,10 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int r, 
   // threshold: with total mass ~1 the threshold exceeds (total - p) / nblk.  Such blocks
   // stay out of the histograms (peaked heads have thousands of them).
   const uint32_t lbits = __float_as_uint(fmaxf(0.f, 0.5f * (1.0f - p - 1e-6f) / (float)nblk));
+  // first level: 1/8-octave bins (bits >> 20) from the floor up, which span 32 octaves
+  // (everything above goes to the top bin); without a floor, half-octave bins from 0
+  const int shift1 = lbits ? 20 : 22;
+  const uint32_t lo1 = lbits & ~((1u << shift1) - 1u);
   const int rows = (nblk + T - 1) / T;
   constexpr int LB = 16;  // global reads in flight per thread
   uint64_t w[LB];         // the first LB rows' words go out before the reductions below
@@ -607,8 +612,8 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int r, 
     if (i < nch) S->f[i] = f[k] * invZ;
   }
   __syncthreads();
-  // masses into LDS; the same pass builds the first threshold level: 256 bins of half an
-  // octave each over the mass bits (bin = bits >> 22, the top bin also takes any larger)
+  // masses into LDS; the same pass builds the first threshold level over the blocks above
+  // the floor: bin = (bits - lo1) >> shift1, the top bin also takes any larger
   const int cshift = __ffs(a.chunk_blocks) - 1;
   for (int i0 = 0; i0 < rows; i0 += LB) {
     if (i0 > 0) {
@@ -640,7 +645,7 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int r, 
           m = (float)((double)untag_f32(w[u]) * S->f[j >> cshift]);
           const uint32_t bits = __float_as_uint(m);
           if (pick && bits >= lbits) {
-            const int bin = level_bin(bits, 0u, 22);
+            const int bin = level_bin(bits, lo1, shift1);
             atomicAdd((unsigned long long*)&sm.bmass[bin], (unsigned long long)fixed_bits(bits));
             atomicAdd(&sm.bcnt[bin], 1u);
           }
@@ -657,7 +662,7 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int r, 
   if (pick) {
     const uint64_t P = (uint64_t)ceil(ldexp((double)p, 62));
     if (wave == 0) {
-      scan_level<T>(0, P, 0u, 0xFFFFFFFFu, 22, sm);
+      scan_level<T>(0, P, lo1, 0xFFFFFFFFu, shift1, sm);
       // the pruned blocks were not counted: the candidates start at the floor
       if (lane == 0 && sm.found) sm.lo = min(max(sm.lo, lbits), sm.hi);
     }

@@ -67,10 +67,12 @@ def model_select(m64, p, prune=True):
     keys = [(bits[j] << 32) | (0xFFFFFFFF - j) for j in range(n)]
     fm = _fixed(mf)
     P = int(np.ceil(np.ldexp(p, 62)))
-    # first level: half-octave bins over all blocks above the pruning floor, built in the
-    # same pass as the masses
+    # first level: over the blocks above the pruning floor, built in the same pass as the
+    # masses
     floor = prune_floor(p, n) if prune else 0
-    r = _level(bits, fm, 0, 0xFFFFFFFF, 22, 0, P, floor)
+    shift1 = 20 if floor else 22     # eighth-octave bins from the floor, else half-octave from 0
+    lo1 = floor & ~((1 << shift1) - 1)
+    r = _level(bits, fm, lo1, 0xFFFFFFFF, shift1, 0, P, floor)
     if r is None:  # the total mass is below p
         assert sum(fm) < P
         return np.arange(n), 0
