@@ -45,11 +45,11 @@ struct SubTile {
   uint4 k[4], v[4];
 };
 
-// Loads rows [row0, row0 + 16) of kg/vg (row stride 128).  A row at or beyond row_end
-// reads row min(row, row_end - 1) instead (row 0 when row_end <= 0), so every load is
-// unconditional and in bounds; attn_subtile masks those rows.  Branch-free loads let
-// the compiler count them, so the next sub-tile's loads stay in flight while the
-// current one is computed.
+// Loads rows [row0, row0 + 16) of kg/vg (row stride 128) with streaming loads (each K/V
+// byte is read once).  A row at or beyond row_end reads row min(row, row_end - 1)
+// instead (row 0 when row_end <= 0), so every load is unconditional and in bounds;
+// attn_subtile masks those rows.  Branch-free loads let the compiler count them, so the
+// next sub-tile's loads stay in flight while the current one is computed.
 __device__ __forceinline__ void load_subtile(SubTile& t, const uint16_t* __restrict__ kg,
                                              const uint16_t* __restrict__ vg, int row0, int row_end,
                                              int lane) {
@@ -59,8 +59,8 @@ __device__ __forceinline__ void load_subtile(SubTile& t, const uint16_t* __restr
   for (int i = 0; i < 4; ++i) {
     const int row = min(row0 + 4 * i + R, last);
     const size_t off = (size_t)row * kHeadDim + c16 * 8;
-    t.k[i] = ld16(kg + off);
-    t.v[i] = ld16(vg + off);
+    t.k[i] = ld16_nt(kg + off);
+    t.v[i] = ld16_nt(vg + off);
   }
 }
 
@@ -68,6 +68,10 @@ __device__ __forceinline__ void load_subtile(SubTile& t, const uint16_t* __restr
 // masked (their logits are -inf and their V rows zero, whatever was loaded for them);
 // hmask picks the heads (bit h) that attend to these rows and must be 0 unless
 // row0 < row_end.  qk[h] holds head h's 8 query dims of this lane.
+//
+// The running maximum changes only when a logit exceeds it (a wave-wide ballot); most
+// sub-tiles then skip the maximum reduction and the rescaling of the accumulators, with
+// the same result as the unconditional update (their rescale factor would be exactly 1).
 template <int G>
 __device__ __forceinline__ void attn_subtile(AttnState<G>& s, const SubTile& tile, int row0,
                                              int row_end, uint32_t hmask, const uint4 (&qk)[G],
@@ -77,12 +81,11 @@ __device__ __forceinline__ void attn_subtile(AttnState<G>& s, const SubTile& til
   const bool myvalid = row0 + 4 * isel + R < row_end;
   const bool b3 = (lane >> 3) & 1, b2 = (lane >> 2) & 1;
   const bool counted = (lane & 3) == 0;
-  SubTile t;
+  SubTile t = tile;
+  if (row0 + 16 > row_end) {  // wave-uniform: only a sequence's last sub-tile is ragged
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    t.k[i] = tile.k[i];
-    const bool ok = row0 + 4 * i + R < row_end;
-    t.v[i] = ok ? tile.v[i] : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 4; ++i)
+      if (row0 + 4 * i + R >= row_end) t.v[i] = make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -109,19 +112,22 @@ __device__ __forceinline__ void attn_subtile(AttnState<G>& s, const SubTile& til
     v += dpp_f32<kDppXor2>(v);
     v += dpp_f32<kDppXor1>(v);
     const float lg = myvalid ? v * scale_log2 : -INFINITY;
-    const float mnew = fmaxf(s.m[h], wave_maxf(lg));
-    const float alpha = fast_exp2(s.m[h] - mnew);
-    const float p = fast_exp2(lg - mnew);
-    s.l[h] = s.l[h] * alpha + (counted ? p : 0.f);
-    s.m[h] = mnew;
+    if (__ballot(lg > s.m[h]) != 0ull) {
+      const float mnew = fmaxf(s.m[h], wave_maxf(lg));
+      const float alpha = fast_exp2(s.m[h] - mnew);
+      s.l[h] *= alpha;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) s.acc[h][k] *= alpha;
+      s.m[h] = mnew;
+    }
+    const float p = fast_exp2(lg - s.m[h]);
+    s.l[h] += counted ? p : 0.f;
     // p of row 4 * i + R sits in lane 4 * i of this lane's DPP row
     float pi[4];
     pi[0] = dpp_f32<kDppRowBcast0>(p);
     pi[1] = dpp_f32<kDppRowBcast0 + 4>(p);
     pi[2] = dpp_f32<kDppRowBcast0 + 8>(p);
     pi[3] = dpp_f32<kDppRowBcast0 + 12>(p);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) s.acc[h][k] *= alpha;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       s.acc[h][0] = fmaf(pi[i], bf_lo(t.v[i].x), s.acc[h][0]);
@@ -137,8 +143,9 @@ __device__ __forceinline__ void attn_subtile(AttnState<G>& s, const SubTile& til
 }
 
 // Streams this wave's items i = wave, wave + WAVES, ... through attn_subtile with the
-// next item's loads in flight while the current one is computed.  item(i, row0, hmask)
-// gives the first row and the head mask of item i (hmask 0 skips it).
+// next item's loads in flight while the current one is computed (two sub-tile buffers
+// used in turn, so no registers are copied).  item(i, row0, hmask) gives the first row
+// and the head mask of item i (hmask 0 skips it).
 template <int G, int WAVES, class ItemFn>
 __device__ __forceinline__ void attn_stream(AttnState<G>& s, const uint16_t* __restrict__ kg,
                                             const uint16_t* __restrict__ vg, int nitems, int row_end,
@@ -146,27 +153,28 @@ __device__ __forceinline__ void attn_stream(AttnState<G>& s, const uint16_t* __r
                                             int wave, int lane) {
   int i = wave;
   if (i >= nitems) return;
-  SubTile cur;
-  int row0;
-  uint32_t hm;
-  item(i, row0, hm);
-  load_subtile(cur, kg, vg, row0, hm ? row_end : row0, lane);
+  SubTile ta, tb;
+  int ra, rb;
+  uint32_t ha, hb;
+  item(i, ra, ha);
+  load_subtile(ta, kg, vg, ra, ha ? row_end : ra, lane);
+  // issues the loads of item j into t (unconditional, so the compiler keeps them in flight
+  // over the compute that follows); past the last item, or for an item no head needs,
+  // every lane reads one row (512 B)
+  auto next = [&](int j, SubTile& t, int& r, uint32_t& h, int rcur) {
+    r = rcur;
+    h = 0;
+    if (j < nitems) item(j, r, h);
+    load_subtile(t, kg, vg, r, h ? row_end : r, lane);
+  };
   while (true) {
-    const int i2 = i + WAVES;
-    const bool more = i2 < nitems;
-    SubTile nxt;
-    int row2 = row0;
-    uint32_t hm2 = hm;
-    if (more) item(i2, row2, hm2);
-    // unconditional, so the compiler keeps these loads in flight over the compute below;
-    // past the last item they re-read the current rows (cache hits)
-    load_subtile(nxt, kg, vg, row2, hm2 ? row_end : row2, lane);
-    attn_subtile<G>(s, cur, row0, row_end, hm, qk, scale_log2, lane);
-    if (!more) break;
-    cur = nxt;
-    row0 = row2;
-    hm = hm2;
-    i = i2;
+    next(i + WAVES, tb, rb, hb, ra);
+    attn_subtile<G>(s, ta, ra, row_end, ha, qk, scale_log2, lane);
+    if (i + WAVES >= nitems) break;
+    next(i + 2 * WAVES, ta, ra, ha, rb);
+    attn_subtile<G>(s, tb, rb, row_end, hb, qk, scale_log2, lane);
+    if (i + 2 * WAVES >= nitems) break;
+    i += 2 * WAVES;
   }
 }
 

@@ -33,7 +33,9 @@ struct SparseSmem {
   int wcnt[kAttnWaves];
   float m[kAttnWaves * G], l[kAttnWaves * G];
   float acc[kAttnWaves * G * kHeadDim];
-  int gw[kOrderMax];  // per KV group: selected blocks summed over its retrieval heads
+  // kernel 2's ordering of KV groups: per group, selected blocks summed over its
+  // retrieval heads and its number of retrieval heads; the head list; the lengths
+  int gw[kOrderMax], gn[kOrderMax], rh[kOrderMax], sl[kOrderMax];
   int pick;
 };
 template <int G>
@@ -103,58 +105,109 @@ __device__ __forceinline__ int lower_bound_wave(const int* __restrict__ a, int n
   return lo;
 }
 
+// Kernel 2's workgroup: sequence b, KV group g, the range [rbeg, rbeg + nh) of the
+// ascending retrieval-head list that falls in g, their query-head ids (hid[h] for h >=
+// nh repeats the last one, so loads through it stay valid) and the sequence length.
+template <int G>
+struct SparseGroup {
+  int b, g, N, rbeg, nh;
+  int hid[G];
+};
+
 // Kernel 2's dispatch order of KV groups: the group of rank `rank` when groups are taken
 // heaviest first (most selected blocks summed over their retrieval heads, ties by
-// index), so the grid ends with its lightest workgroups and drains quickly.  Returns
-// b * Hkv + g.  Without the counts (block masks only) or with more than kOrderMax
-// groups, the natural order.  Every thread of the workgroup calls it.
+// index), so the grid ends with its lightest workgroups and drains quickly.  The
+// selected counts, the head list and the lengths come in one round of loads, so the
+// group's heads and length are known without a further round trip.  Without the counts
+// (block masks only), or with more than kOrderMax groups or retrieval heads, the natural
+// order.  Every thread of the workgroup calls it.
 template <int G>
-__device__ __forceinline__ int group_of_rank(const SparseArgs& a, int B, int rank, SparseSmem<G>* S) {
-  const int ngrp = B * a.Hkv;
-  if (!a.sel_cnt || ngrp > kOrderMax) return rank;
+__device__ __forceinline__ SparseGroup<G> sparse_group(const SparseArgs& a, int B, int rank, SparseSmem<G>* S) {
+  const int Hkv = a.Hkv, n_ret = a.n_ret;
+  const int ngrp = B * Hkv;
   const int tid = threadIdx.x;
-  for (int k = tid; k < ngrp; k += kAttnThreads) S->gw[k] = 0;
-  __syncthreads();
-  for (int i = tid; i < B * a.n_ret; i += kAttnThreads) {
-    const int b = i / a.n_ret, r = i - b * a.n_ret;
-    atomicAdd(&S->gw[b * a.Hkv + a.ret_heads[r] / G], a.sel_cnt[i]);
-  }
-  __syncthreads();
-  for (int k = tid; k < ngrp; k += kAttnThreads) {
-    const int wk = S->gw[k];
-    int rk = 0;
-    for (int k2 = 0; k2 < ngrp; ++k2) {
-      const int w2 = S->gw[k2];
-      rk += (w2 > wk) || (w2 == wk && k2 < k);
+  SparseGroup<G> r;
+  int beg, nh;
+  if (a.sel_cnt && ngrp <= kOrderMax && n_ret <= kOrderMax) {
+    // the first (head, count) of every thread and the lengths: unconditional loads at
+    // clamped indices, all in flight while the tables are cleared
+    const int nbr = B * n_ret;
+    const int i0 = min(tid, nbr - 1), b0 = i0 / n_ret, r0 = i0 - b0 * n_ret;
+    const int h0 = a.ret_heads[r0], c0 = a.sel_cnt[i0];
+    const int len0 = a.seq_lens[min(tid, B - 1)];  // B <= kOrderMax == kAttnThreads
+    for (int k = tid; k < ngrp; k += kAttnThreads) S->gw[k] = 0;
+    for (int k = tid; k < Hkv; k += kAttnThreads) S->gn[k] = 0;
+    __syncthreads();
+    if (tid < B) S->sl[tid] = len0;
+    auto add = [&](int b, int rr, int h, int cnt) {
+      if (h >= 0 && h < a.Hq) {
+        atomicAdd(&S->gw[b * Hkv + h / G], cnt);
+        if (b == 0) atomicAdd(&S->gn[h / G], 1);
+      }
+      if (b == 0) S->rh[rr] = h;
+    };
+    if (tid < nbr) add(b0, r0, h0, c0);
+    for (int i = tid + kAttnThreads; i < nbr; i += kAttnThreads) {
+      const int b = i / n_ret, rr = i - b * n_ret;
+      add(b, rr, a.ret_heads[rr], a.sel_cnt[i]);
     }
-    if (rk == rank) S->pick = k;
+    __syncthreads();
+    for (int k = tid; k < ngrp; k += kAttnThreads) {
+      const int wk = S->gw[k];
+      int rk = 0;
+      for (int k2 = 0; k2 < ngrp; ++k2) {
+        const int w2 = S->gw[k2];
+        rk += (w2 > wk) || (w2 == wk && k2 < k);
+      }
+      if (rk == rank) S->pick = k;
+    }
+    __syncthreads();
+    const int k = S->pick;
+    r.b = k / Hkv;
+    r.g = k - r.b * Hkv;
+    beg = 0;
+    for (int g2 = 0; g2 < r.g; ++g2) beg += S->gn[g2];
+    nh = S->gn[r.g];
+    r.N = S->sl[r.b];
+#pragma unroll
+    for (int h = 0; h < G; ++h) r.hid[h] = nh > 0 ? S->rh[beg + min(h, nh - 1)] : 0;
+  } else {
+    r.b = rank / Hkv;
+    r.g = rank - r.b * Hkv;
+    r.N = a.seq_lens[r.b];
+    int end;
+    group_range(a.ret_heads, n_ret, r.g, G, beg, end);
+    nh = end - beg;
+#pragma unroll
+    for (int h = 0; h < G; ++h) r.hid[h] = nh > 0 ? a.ret_heads[beg + min(h, nh - 1)] : 0;
   }
-  __syncthreads();
-  return S->pick;
+  r.rbeg = beg;
+  r.nh = nh;
+  return r;
 }
 
-// Split c of KV group g of sequence b.  emit(i, d, o, lse) takes retrieval head i's dim d
-// (lse once, at d == 0); a split past the sequence's end emits o = 0, lse = -inf.  A
-// group without retrieval heads emits nothing and returns false.
+// Split c of the workgroup's KV group (sparse_group).  emit(i, d, o, lse) takes retrieval
+// head i's dim d (lse once, at d == 0); a split past the sequence's end emits o = 0,
+// lse = -inf.  A group without retrieval heads emits nothing and returns false.
 template <int BK, int G, class Emit>
-__device__ __forceinline__ bool sparse_split(const SparseArgs& a, int c, int g, int b, SparseSmem<G>* S,
-                                             Emit emit) {
+__device__ __forceinline__ bool sparse_split(const SparseArgs& a, int c, const SparseGroup<G>& grp,
+                                             SparseSmem<G>* S, Emit emit) {
   constexpr int ST = BK / 16;  // sub-tiles per block
   constexpr int kWaves = kAttnWaves, kThreads = kAttnThreads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n_ret = a.n_ret, Hq = a.Hq, nblk_max = a.nblk_max, split_blocks = a.split_blocks;
-  const int* __restrict__ ret_heads = a.ret_heads;
   const int* __restrict__ sel_idx = a.sel_idx;
   const int* __restrict__ sel_cnt = a.sel_cnt;
   const uint8_t* __restrict__ sel_mask = a.sel_mask;
-  // the sequence length and (for the lists) the first 64 selected counts go out with the
-  // head list: one memory round trip
-  const int N = a.seq_lens[b];
-  const int cnt_l = (!sel_mask && lane < n_ret) ? sel_cnt[(size_t)b * n_ret + lane] : 0;
-  int rbeg, rend;
-  group_range(ret_heads, n_ret, g, G, rbeg, rend);
-  const int nh = rend - rbeg;
+  const int b = grp.b, g = grp.g, N = grp.N, rbeg = grp.rbeg, nh = grp.nh;
   if (nh == 0) return false;
+  // the query rows go out first (unconditional loads: a head slot past nh reads the last
+  // head's row), in flight while the split's blocks are gathered
+  uint4 qk[G];
+  const int c16 = lane & 15;
+#pragma unroll
+  for (int h = 0; h < G; ++h) qk[h] = ld16(a.q + ((size_t)b * Hq + grp.hid[h]) * kHeadDim + c16 * 8);
+  const int cnt_l = (!sel_mask && lane < n_ret) ? sel_cnt[(size_t)b * n_ret + lane] : 0;
   const int nblk = (N + BK - 1) / BK;
   const int jlo = c * split_blocks, jhi = min(jlo + split_blocks, nblk);
   uint32_t* s_hm = S->hm;
@@ -171,17 +224,20 @@ __device__ __forceinline__ bool sparse_split(const SparseArgs& a, int c, int g, 
     uint8_t* hm8 = reinterpret_cast<uint8_t*>(s_hm);
     int cnt = 0;
     if (sel_mask) {
-      // block masks: each lane ORs the group's heads' bytes of its blocks (one round trip)
+      // block masks: each lane ORs the group's heads' bytes of its blocks.  The loads are
+      // unconditional (clamped to the last head and block), so all G are in flight at once.
       const uint8_t* mrow = sel_mask + ((size_t)b * n_ret + rbeg) * nblk_max + jlo;
       for (int base = sb; base < se; base += 64) {
         const int off = base + lane;
-        uint32_t mk = 0;
-        if (off < se) {
+        const int offc = min(off, se - 1);
+        uint32_t v[G];
 #pragma unroll
-          for (int h = 0; h < G; ++h)
-            if (h < nh && mrow[(size_t)h * nblk_max + off]) mk |= 1u << h;
-          hm8[off] = (uint8_t)mk;
-        }
+        for (int h = 0; h < G; ++h) v[h] = mrow[(size_t)min(h, nh - 1) * nblk_max + offc];
+        uint32_t mk = 0;
+#pragma unroll
+        for (int h = 0; h < G; ++h) mk |= (h < nh && v[h] != 0u) ? 1u << h : 0u;
+        if (off >= se) mk = 0;
+        if (off < se) hm8[off] = (uint8_t)mk;
         cnt += __popcll(__ballot(mk != 0));
       }
     } else {
@@ -232,12 +288,6 @@ __device__ __forceinline__ bool sparse_split(const SparseArgs& a, int c, int g, 
 
   AttnState<G> st;
   attn_init(st);
-  uint4 qk[G];
-  const int c16 = lane & 15;
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-    qk[h] = h < nh ? ld16(a.q + ((size_t)b * Hq + ret_heads[rbeg + h]) * kHeadDim + c16 * 8)
-                   : make_uint4(0, 0, 0, 0);
   const size_t kvoff = ((size_t)b * a.Hkv + g) * (size_t)a.max_ctx * kHeadDim;
   const float scale = (float)(kLog2e / 11.313708498984761);  // log2(e) / sqrt(128)
   auto item = [&](int i, int& row0, uint32_t& hm) {

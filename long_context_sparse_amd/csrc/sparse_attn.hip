@@ -21,10 +21,10 @@ __global__ __launch_bounds__(kThreads) void sparse_attn_kernel(SparseArgs a, int
   __shared__ SparseSmem<G> S;
   // workgroups are dispatched in blockIdx order: (split, group rank), heaviest group first
   const int c = blockIdx.x;
-  const int bg = group_of_rank<G>(a, gridDim.z, blockIdx.y + a.Hkv * blockIdx.z, &S);
-  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const SparseGroup<G> grp = sparse_group<G>(a, gridDim.z, blockIdx.y + a.Hkv * blockIdx.z, &S);
+  const int b = grp.b;
   const int n_ret = a.n_ret;
-  sparse_split<BK, G>(a, c, g, b, &S, [&](int i, int d, float o, float lse) {
+  sparse_split<BK, G>(a, c, grp, &S, [&](int i, int d, float o, float lse) {
     const size_t hr = (size_t)b * n_ret + i;
     o_part[(hr * n_split + c) * kHeadDim + d] = o;
     if (d == 0) lse_part[hr * n_split + c] = lse;

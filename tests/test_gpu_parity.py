@@ -243,6 +243,17 @@ def test_block_masks_match_lists_and_give_the_same_partials():
     assert torch.equal(m.step.o_part, ls.step.o_part)
     assert torch.equal(m.step.lse_part, ls.step.lse_part)
     assert np.array_equal(m.out_h, ls.out_h)
+    # masks alone (no lists, no counts): the KV groups go in their natural order and every
+    # split's partials are the same bits
+    o2 = torch.full_like(m.step.o_part, float("nan"))
+    l2 = torch.full_like(m.step.lse_part, float("nan"))
+    s = m.step.s
+    abi.rtp_sparse_attn_split(t["q"], t["k_cache"], t["v_cache"], t["seq_lens"], t["ret_heads"], None, None,
+                              s.B, s.Hq, s.Hkv, s.n_ret, s.max_ctx, s.block, s.split_tokens, o2, l2,
+                              sel_mask=m.step.sel_mask)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, m.step.o_part)
+    assert torch.equal(l2, m.step.lse_part)
 
 
 def test_one_stream_matches_two_streams():
