@@ -81,11 +81,27 @@ __device__ __forceinline__ void attn_subtile(AttnState<G>& s, const SubTile& til
   const bool myvalid = row0 + 4 * isel + R < row_end;
   const bool b3 = (lane >> 3) & 1, b2 = (lane >> 2) & 1;
   const bool counted = (lane & 3) == 0;
-  SubTile t = tile;
+  // V rows in fp32, unpacked once for all heads; rows past row_end are zero
+  float vf[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 v = tile.v[i];
+    vf[i][0] = bf_lo(v.x);
+    vf[i][1] = bf_hi(v.x);
+    vf[i][2] = bf_lo(v.y);
+    vf[i][3] = bf_hi(v.y);
+    vf[i][4] = bf_lo(v.z);
+    vf[i][5] = bf_hi(v.z);
+    vf[i][6] = bf_lo(v.w);
+    vf[i][7] = bf_hi(v.w);
+  }
   if (row0 + 16 > row_end) {  // wave-uniform: only a sequence's last sub-tile is ragged
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (row0 + 4 * i + R >= row_end) t.v[i] = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = row0 + 4 * i + R < row_end;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) vf[i][k] = ok ? vf[i][k] : 0.f;
+    }
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -93,10 +109,10 @@ __device__ __forceinline__ void attn_subtile(AttnState<G>& s, const SubTile& til
     float part[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float a = dot2(t.k[i].x, qk[h].x, 0.f);
-      a = dot2(t.k[i].y, qk[h].y, a);
-      a = dot2(t.k[i].z, qk[h].z, a);
-      part[i] = dot2(t.k[i].w, qk[h].w, a);
+      float a = dot2(tile.k[i].x, qk[h].x, 0.f);
+      a = dot2(tile.k[i].y, qk[h].y, a);
+      a = dot2(tile.k[i].z, qk[h].z, a);
+      part[i] = dot2(tile.k[i].w, qk[h].w, a);
     }
     // transpose-reduce over the 16 lanes that share R (one DPP row), on DPP lane moves:
     // the row mirror (partner l ^ 15) exchanges parts by bit 3, the half-row mirror
@@ -129,16 +145,9 @@ __device__ __forceinline__ void attn_subtile(AttnState<G>& s, const SubTile& til
     pi[2] = dpp_f32<kDppRowBcast0 + 8>(p);
     pi[3] = dpp_f32<kDppRowBcast0 + 12>(p);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s.acc[h][0] = fmaf(pi[i], bf_lo(t.v[i].x), s.acc[h][0]);
-      s.acc[h][1] = fmaf(pi[i], bf_hi(t.v[i].x), s.acc[h][1]);
-      s.acc[h][2] = fmaf(pi[i], bf_lo(t.v[i].y), s.acc[h][2]);
-      s.acc[h][3] = fmaf(pi[i], bf_hi(t.v[i].y), s.acc[h][3]);
-      s.acc[h][4] = fmaf(pi[i], bf_lo(t.v[i].z), s.acc[h][4]);
-      s.acc[h][5] = fmaf(pi[i], bf_hi(t.v[i].z), s.acc[h][5]);
-      s.acc[h][6] = fmaf(pi[i], bf_lo(t.v[i].w), s.acc[h][6]);
-      s.acc[h][7] = fmaf(pi[i], bf_hi(t.v[i].w), s.acc[h][7]);
-    }
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) s.acc[h][k] = fmaf(pi[i], vf[i][k], s.acc[h][k]);
   }
 }
 

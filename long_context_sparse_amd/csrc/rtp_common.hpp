@@ -27,15 +27,16 @@ constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within each 8 lanes
 constexpr int kDppMirror = 0x140;     // lane i <- lane 15-i within each 16 lanes
 constexpr int kDppRowBcast0 = 0x150;  // + n: every lane <- lane n of its 16-lane row
 
+// (every lane is written, so the destination's old value is never needed)
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {
   const long long b = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)b, CTRL, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, 0xF, 0xF, false);
+  const int lo = __builtin_amdgcn_mov_dpp((int)b, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(b >> 32), CTRL, 0xF, 0xF, false);
   return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
 }
 __device__ __forceinline__ float readlane_f32(float v, int l) {

@@ -389,25 +389,26 @@ __device__ __forceinline__ bool index_chunk(const IndexArgs& a, int c, int r, in
   const uint16_t* kb = a.k_idx + head * (size_t)a.max_ctx * kIndexDim + half * 8;
   const int j0 = c * a.chunk_blocks;
   const int j1 = min(j0 + a.chunk_blocks, nblk);
-  // Every load is unconditional: a token past the sequence's end (or of a block past the
-  // chunk's end) reads token N - 1 instead and its score is masked (or the block skipped)
-  // below.  Branch-free loads let the compiler count them, so the next blocks' loads stay
-  // in flight while the current ones are reduced.
-  auto load = [&](uint4 (&v)[U][NL], int jj) {
+  // Every load is unconditional and streaming (the keys are read once): a token past the
+  // sequence's end (or of a block past the chunk's end) reads token `last` instead and its
+  // score is masked (or the block skipped) below.  Branch-free loads let the compiler
+  // count them, so the next blocks' loads stay in flight while the current ones are
+  // reduced.
+  auto load = [&](uint4 (&v)[U][NL], int jj, int last) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = jj + u * W;
 #pragma unroll
       for (int t = 0; t < NL; ++t) {
-        const int tok = min(j * BK + 32 * t + (lane >> 1), N - 1);
-        v[u][t] = ld16(kb + (size_t)tok * kIndexDim);
+        const int tok = min(j * BK + 32 * t + (lane >> 1), last);
+        v[u][t] = ld16_nt(kb + (size_t)tok * kIndexDim);
       }
     }
   };
   // the first blocks' loads go out before q_idx is formed
   int jj = j0 + wave;
   uint4 cur[U][NL];
-  if (jj < j1) load(cur, jj);
+  if (jj < j1) load(cur, jj, N - 1);
 
   // ---- this call's tag; q_idx = W^Q_r q_pre[b, hq] in fp64 (16 outputs x 16 partial dots)
   if (tid == 0) S->tag = load_tag(tag_word);
@@ -438,7 +439,8 @@ __device__ __forceinline__ bool index_chunk(const IndexArgs& a, int c, int r, in
     while (true) {
       const int jn = jj + W * U;
       uint4 nxt[U][NL];
-      load(nxt, jn < j1 ? jn : jj);  // past the end: the current blocks again (cache hits)
+      // past the chunk's end every lane reads the current block's first token (32 B)
+      load(nxt, jn < j1 ? jn : jj, jn < j1 ? N - 1 : jj * BK);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int j = jj + u * W;
