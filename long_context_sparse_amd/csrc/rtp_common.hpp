@@ -69,6 +69,31 @@ __device__ __forceinline__ T wave_reduce_dpp(T v, Op op) {
   }
 }
 
+// Inclusive prefix sums over the 64 lanes of a wave: a Hillis-Steele scan inside each
+// 16-lane row on DPP row shifts (a lane whose source lies before its row's start adds
+// 0), then each row adds the totals of the rows below it, read from lanes 15, 31, 47.
+constexpr int kDppRowShr = 0x110;  // + n: lane i <- lane i - n of its row (n = 1..15)
+
+template <int N>
+__device__ __forceinline__ uint32_t dpp_shr_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppRowShr + N, 0xF, 0xF, false);
+}
+template <int N>
+__device__ __forceinline__ uint64_t dpp_shr_u64(uint64_t v) {
+  const uint32_t lo = dpp_shr_u32<N>((uint32_t)v), hi = dpp_shr_u32<N>((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
+  x += dpp_shr_u32<1>(x);
+  x += dpp_shr_u32<2>(x);
+  x += dpp_shr_u32<4>(x);
+  x += dpp_shr_u32<8>(x);
+  const uint32_t t0 = __builtin_amdgcn_readlane(x, 15), t1 = __builtin_amdgcn_readlane(x, 31),
+                 t2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row >= 1 ? t0 : 0u) + (row >= 2 ? t1 : 0u) + (row >= 3 ? t2 : 0u);
+}
+
 __device__ __forceinline__ double wave_max(double v) {
   return wave_reduce_dpp(v, [](double a, double b) { return fmax(a, b); });
 }
@@ -114,6 +139,15 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
   const uint32_t a = __builtin_amdgcn_readlane((uint32_t)v, l);
   const uint32_t b = __builtin_amdgcn_readlane((uint32_t)(v >> 32), l);
   return ((uint64_t)b << 32) | a;
+}
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t x) {
+  x += dpp_shr_u64<1>(x);
+  x += dpp_shr_u64<2>(x);
+  x += dpp_shr_u64<4>(x);
+  x += dpp_shr_u64<8>(x);
+  const uint64_t t0 = readlane_u64(x, 15), t1 = readlane_u64(x, 31), t2 = readlane_u64(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row >= 1 ? t0 : 0ull) + (row >= 2 ? t1 : 0ull) + (row >= 3 ? t2 : 0ull);
 }
 
 // ------------------------------------------------------------------ published words

@@ -44,6 +44,7 @@ constexpr int kIdxMaxBlocks = 16384;            // blocks per sequence the selec
 constexpr int kBins = 256;                      // histogram bins per refinement level
 constexpr int kFinal = kWave;                   // candidates ranked directly (one per lane)
 constexpr int kRowTab = kIdxMaxBlocks / kWave;  // (row, wave) entries of the selection
+constexpr int kRowBatch = 4;                    // selection rows read together (see for_rows)
 
 template <int T>
 struct TailSmem {
@@ -51,10 +52,11 @@ struct TailSmem {
   uint32_t bcnt[kBins];   // per bin: candidate count
   int rowtab[kRowTab];    // per (row, wave) counts, then exclusive prefixes
   double f64[T / kWave], f64b[T / kWave];
-  uint64_t ckey[kFinal], cfm[kFinal];  // final candidates (any order)
+  uint64_t above[kFinal];  // final candidates: fixed-point mass of the larger keys
+  int wn[T / kWave];       // final candidates gathered by each wave
   uint64_t cab, thr;
   uint32_t lo, hi;
-  int cnt, nfin, total, found, ready;
+  int cnt, total, found, ready;
 };
 
 // LDS of the index role; the per-block masses (rows * T floats) follow it.
@@ -62,7 +64,9 @@ template <int T>
 struct IndexSmem {
   double qidx[kIndexDim];
   double mx[kIdxMaxChunkBlocks], sum[kIdxMaxChunkBlocks];  // scoring: per-block max, sum
-  double f[2 * T];  // selection: per-chunk factor exp(M_c - M) / Z
+  // selection: per-chunk factor exp(M_c - M) / Z; after the masses are formed, the
+  // final candidates each wave gathers (2 * kFinal words a wave)
+  double f[2 * T];
   TailSmem<T> sm;
   int flag;
   uint32_t tag;
@@ -77,7 +81,8 @@ __device__ __forceinline__ float* index_masses(IndexSmem<T>* S) {
 }
 
 // Chunking of the index role: at least `target` workgroups over the batch, 8..128 blocks
-// a chunk, at most 2 * T chunks per head.  rows = blocks per thread in the selection.
+// a chunk, at most 2 * T chunks per head.  rows = blocks per thread in the selection,
+// rounded up to a multiple of kRowBatch.
 struct IndexGeom {
   int nblk_max, chunk_blocks, n_chunk, rows;
 };
@@ -90,7 +95,7 @@ inline IndexGeom index_geom(int B, int n_ret, int max_ctx, int block, int T, int
   while (ceil_div(g.nblk_max, cb) > 2 * T && cb < kIdxMaxChunkBlocks) cb <<= 1;
   g.chunk_blocks = cb;
   g.n_chunk = ceil_div(g.nblk_max, cb);
-  g.rows = ceil_div(g.nblk_max, T);
+  g.rows = ceil_div(ceil_div(g.nblk_max, T), kRowBatch) * kRowBatch;
   return g;
 }
 
@@ -133,21 +138,30 @@ __device__ __forceinline__ int level_bin(uint32_t bits, uint32_t lo, int shift) 
 }
 
 // Selection rows: block j = row * T + thread, row < rows, masses in LDS (< 0 for no
-// block).  Every pass reads a thread's masses kRowBatch rows at a time so the LDS
-// latencies overlap.
-constexpr int kRowBatch = 8;
-
+// block; rows is a multiple of kRowBatch and the rows past the sequence's blocks hold
+// -1).  Every pass reads a thread's masses kRowBatch rows at a time, unconditionally,
+// so the LDS latencies overlap.
 template <int T, class F>
 __device__ __forceinline__ void for_rows(const float* __restrict__ sm_m, int rows, F f) {
   const int tid = threadIdx.x;
   for (int i0 = 0; i0 < rows; i0 += kRowBatch) {
     float mm[kRowBatch];
 #pragma unroll
-    for (int u = 0; u < kRowBatch; ++u) mm[u] = i0 + u < rows ? sm_m[(i0 + u) * T + tid] : -1.0f;
+    for (int u = 0; u < kRowBatch; ++u) mm[u] = sm_m[(i0 + u) * T + tid];
 #pragma unroll
-    for (int u = 0; u < kRowBatch; ++u)
-      if (i0 + u < rows) f(i0 + u, mm[u]);
+    for (int u = 0; u < kRowBatch; ++u) f(i0 + u, mm[u]);
   }
+}
+
+// A wave's count of a per-row predicate ballot, kept in lane `row` of one register (rows
+// <= 64) and stored to rowtab once after the pass.
+__device__ __forceinline__ int count_into_lane(int cntv, uint64_t bal, int row) {
+  return (int)(threadIdx.x & 63) == row ? (int)__popcll(bal) : cntv;
+}
+template <int T>
+__device__ __forceinline__ void store_row_counts(int cntv, int rows, TailSmem<T>& sm) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane < rows) sm.rowtab[lane * (T / kWave) + wave] = cntv;
 }
 
 // One wave: turns rowtab[0 .. rows * waves) of per-(row, wave) counts into exclusive
@@ -164,12 +178,7 @@ __device__ __forceinline__ void rowtab_scan(int rows, TailSmem<T>& sm) {
     v[k] = idx < n ? sm.rowtab[idx] : 0;
     tot += v[k];
   }
-  int incl = tot;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
+  const int incl = (int)wave_incl_scan_u32((uint32_t)tot);
   int run = incl - tot;
 #pragma unroll
   for (int k = 0; k < R; ++k) {
@@ -187,11 +196,10 @@ __device__ __forceinline__ void rowtab_scan(int rows, TailSmem<T>& sm) {
 template <int T, class Pred>
 __device__ __forceinline__ int rows_prefix(const float* __restrict__ sm_m, int rows, Pred pred,
                                            TailSmem<T>& sm) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for_rows<T>(sm_m, rows, [&](int i, float m) {
-    const uint64_t bal = __ballot(pred(i, m));
-    if (lane == 0) sm.rowtab[i * (T / kWave) + wave] = __popcll(bal);
-  });
+  const int wave = threadIdx.x >> 6;
+  int cntv = 0;
+  for_rows<T>(sm_m, rows, [&](int i, float m) { cntv = count_into_lane(cntv, __ballot(pred(i, m)), i); });
+  store_row_counts<T>(cntv, rows, sm);
   __syncthreads();
   if (wave == 0) rowtab_scan<T>(rows, sm);
   __syncthreads();
@@ -231,12 +239,7 @@ __device__ __forceinline__ void scan_level(uint64_t cab, uint64_t P, uint32_t lo
     sm.bmass[bin] = 0;
     sm.bcnt[bin] = 0;
   }
-  uint64_t incl = tot;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint64_t y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
+  const uint64_t incl = wave_incl_scan_u64(tot);
   uint64_t run = cab + incl - tot;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -257,7 +260,8 @@ __device__ __forceinline__ void scan_level(uint64_t cab, uint64_t P, uint32_t lo
 // (sm.cab, sm.cnt, sm.lo, sm.hi) is in place.  Returns the key of the last admitted
 // block: the selected set is every block whose key is >= it.  When sm.ready is set on
 // return, sm.rowtab already holds the exclusive prefix per (row, wave) of the selected
-// blocks and sm.total their number.  Preconditions: the bins and sm.nfin are zero.
+// blocks and sm.total their number.  Preconditions: the bins are zero.  wbuf: LDS for
+// the final candidates, 2 * kFinal words per wave.
 //
 // Candidates are the blocks whose mass bits lie in [lo, hi], with fixed mass `cab`
 // strictly above them, and cab < P <= cab + mass(candidates) holds throughout.  A
@@ -266,11 +270,12 @@ __device__ __forceinline__ void scan_level(uint64_t cab, uint64_t P, uint32_t lo
 // bits grow with log2 of the value); one wave scans the bins from the top, finds the
 // bin where cab + cumulative mass crosses P and takes its bit range as the new candidate
 // range (at least kBins/2 times narrower).  It ends when <= kFinal candidates remain
-// (ranked exactly by one wave), or when the range is a single mass value: the threshold
-// is then the k-th candidate in ascending block order, k = ceil((P - cab) / mass).
+// (ranked exactly: every wave compares each candidate with a share of the others), or
+// when the range is a single mass value: the threshold is then the k-th candidate in
+// ascending block order, k = ceil((P - cab) / mass).
 template <int T>
 __device__ __noinline__ uint64_t select_threshold(const float* __restrict__ sm_m, int rows, uint64_t P,
-                                                  TailSmem<T>& sm) {
+                                                  TailSmem<T>& sm, uint64_t* __restrict__ wbuf) {
   constexpr int W = T / kWave;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint64_t cab = uni64(sm.cab);
@@ -318,32 +323,54 @@ __device__ __noinline__ uint64_t select_threshold(const float* __restrict__ sm_m
     __syncthreads();
     return uni64(sm.thr);
   }
-  // the last <= kFinal candidates are gathered in any order; the same pass counts, per
-  // (row, wave), the blocks above the candidates' range (all selected)
+  // the last <= kFinal candidates: each wave gathers its own in wbuf (slots from a
+  // wave-uniform running count, no atomics); the same pass counts, per (row, wave), the
+  // blocks above the candidates' range (all selected)
+  uint64_t* wk = wbuf + wave * 2 * kFinal;
+  int nw = 0, cntv = 0;
   for_rows<T>(sm_m, rows, [&](int i, float m) {
     const uint32_t bits = __float_as_uint(m);
-    if (cand(m)) {
-      const int slot = atomicAdd(&sm.nfin, 1);
+    const bool c = cand(m);
+    const uint64_t bc = __ballot(c);
+    if (c) {
+      const int slot = nw + (int)__popcll(bc & lanemask_lt());
       if (slot < kFinal) {
-        sm.ckey[slot] = key_at<T>(i, m);
-        sm.cfm[slot] = fixed_bits(bits);
+        wk[slot] = key_at<T>(i, m);
+        wk[kFinal + slot] = fixed_bits(bits);
       }
     }
-    const uint64_t bal = __ballot(m >= 0.f && bits > hi);
-    if (lane == 0) sm.rowtab[i * W + wave] = __popcll(bal);
+    nw += (int)__popcll(bc);
+    cntv = count_into_lane(cntv, __ballot(m >= 0.f && bits > hi), i);
   });
+  store_row_counts<T>(cntv, rows, sm);
+  if (lane == 0) sm.wn[wave] = min(nw, kFinal);
+  if (wave == 0) sm.above[lane] = 0;
+  __syncthreads();
+  // every wave holds the candidates one per lane (lane < nf), in wave order
+  int nf = 0, sw = 0, sk = 0;
+  for (int w2 = 0; w2 < W; ++w2) {
+    const int c2 = sm.wn[w2];
+    if (lane >= nf && lane < nf + c2) {
+      sw = w2;
+      sk = lane - nf;
+    }
+    nf += c2;
+  }
+  nf = min(nf, kFinal);
+  const uint64_t my = lane < nf ? wbuf[sw * 2 * kFinal + sk] : 0ull;
+  const uint64_t f = lane < nf ? wbuf[sw * 2 * kFinal + kFinal + sk] : 0ull;
+  // rank by key (keys are distinct): wave w sums the masses of the larger keys among
+  // candidates w, w + W, ...
+  uint64_t part = 0;
+  for (int i = wave; i < nf; i += W) {
+    const uint64_t ki = readlane_u64(my, i), fi = readlane_u64(f, i);
+    part += ki > my ? fi : 0ull;
+  }
+  if (lane < nf && part) atomicAdd((unsigned long long*)&sm.above[lane], (unsigned long long)part);
   __syncthreads();
   if (wave == 0) {
-    // rank by key (keys are distinct): the crossing candidate has cab + (mass of the
-    // larger keys) < P <= that + its own mass
-    const int nf = min(sm.nfin, kFinal);
-    const uint64_t my = lane < nf ? sm.ckey[lane] : 0ull;
-    const uint64_t f = lane < nf ? sm.cfm[lane] : 0ull;
-    uint64_t above = 0;
-    for (int i = 0; i < nf; ++i) {
-      const uint64_t ki = readlane_u64(my, i), fi = readlane_u64(f, i);
-      above += ki > my ? fi : 0ull;
-    }
+    // the crossing candidate has cab + (mass of the larger keys) < P <= that + its own
+    const uint64_t above = lane < nf ? sm.above[lane] : 0ull;
     const uint64_t cb = __ballot(lane < nf && cab + above < P && cab + above + f >= P);
     const uint64_t thr = cb ? readlane_u64(my, __ffsll((long long)cb) - 1) : 0ull;
     // the selected candidates join the per-(row, wave) counts (LDS operations of one
@@ -356,7 +383,6 @@ __device__ __noinline__ uint64_t select_threshold(const float* __restrict__ sm_m
     if (lane == 0) {
       sm.thr = thr;
       sm.ready = cb != 0;
-      sm.nfin = 0;
     }
   }
   __syncthreads();
@@ -551,10 +577,7 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int r, 
     sm.bmass[tid] = 0;
     sm.bcnt[tid] = 0;
   }
-  if (tid == 0) {
-    sm.nfin = 0;
-    sm.found = 0;
-  }
+  if (tid == 0) sm.found = 0;
   const float p = a.top_p[head];
   const bool pick = p < 1.0f && nblk > 1;  // else every block is selected
   // Every block of mass below (1 - p) / (2 nblk) is outside the selection and below its
@@ -565,7 +588,7 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int r, 
   // (everything above goes to the top bin); without a floor, half-octave bins from 0
   const int shift1 = lbits ? 20 : 22;
   const uint32_t lo1 = lbits & ~((1u << shift1) - 1u);
-  const int rows = (nblk + T - 1) / T;
+  const int rows = ceil_div(ceil_div(nblk, T), kRowBatch) * kRowBatch;  // rows past nblk hold -1
   constexpr int LB = 16;  // global reads in flight per thread
   uint64_t w[LB];         // the first LB rows' words go out before the reductions below
 #pragma unroll
@@ -671,7 +694,7 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int r, 
     __syncthreads();
     if (sm.found) {  // else the total mass is below p: every block
       all = false;
-      thr = select_threshold<T>(s_mass, rows, P, sm);
+      thr = select_threshold<T>(s_mass, rows, P, sm, reinterpret_cast<uint64_t*>(S->f));
       ready = sm.ready;
     }
   }
