@@ -1,30 +1,51 @@
 // Kernel 1 of the decode path as its own launch: low-rank index scoring and exact
 // block top-p (the device code and its description are in rtp_index.hpp).
 //
-// gfx950 launch: grid (chunk, retrieval head, sequence), 512 threads = 8 wave64, at
-// least 512 workgroups over the batch.  Each head's tag word lives in the workspace and
-// is advanced by the head's selecting workgroup at the end of every call.
+// gfx950 launch: grid (chunk, retrieval head, sequence), 1024 threads = 16 wave64, one
+// workgroup per compute unit at a time (its registers and LDS allow one), so the chunks
+// are sized for about one workgroup per compute unit and the scoring runs in a single
+// wave of workgroups; the selecting workgroup of each head then has 16 waves for the
+// threshold search.  Each head's tag word lives in the workspace and is advanced by the
+// head's selecting workgroup at the end of every call.
 
 #include "rtp_index.hpp"
 
 namespace rtp {
 namespace {
 
-constexpr int kIdxThreads = 512;
+constexpr int kIdxThreads = 1024;
+
+constexpr int kIdxMaxChunks = 2 * kIdxThreads;  // chunks per head the selection combines
 
 struct K1Layout {
   IndexGeom g;
   size_t off_counters, off_tag, off_cmax, off_e, total;
 };
 
-K1Layout k1_layout(int B, int n_ret, int max_ctx, int block) {
+// Compute units of the current device (cached per device; 256, MI355X's count, if it
+// cannot be queried).
+int compute_units() {
+  static thread_local int cached_dev = -1, cached_n = 256;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev != cached_dev) {
+    int n = 0;
+    cached_n = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+    cached_dev = dev;
+  }
+  return cached_n;
+}
+
+// The workspace has room for the most chunks a head can have, so its size does not
+// depend on the device; `target` (workgroups wanted) sets one launch's chunking.
+K1Layout k1_layout(int B, int n_ret, int max_ctx, int block, int target) {
   K1Layout L{};
-  L.g = index_geom(B, n_ret, max_ctx, block, kIdxThreads, 512);
+  L.g = index_geom(B, n_ret, max_ctx, block, kIdxThreads, target);
   const size_t heads = (size_t)B * n_ret;
   L.off_counters = 0;
   L.off_tag = align_up(heads * sizeof(int), 256);
   L.off_cmax = L.off_tag + align_up(heads * sizeof(uint32_t), 256);
-  L.off_e = L.off_cmax + align_up(heads * L.g.n_chunk * 2 * sizeof(uint64_t), 256);
+  L.off_e = L.off_cmax + align_up(heads * kIdxMaxChunks * 2 * sizeof(uint64_t), 256);
   L.total = L.off_e + align_up(heads * (size_t)L.g.nblk_max * sizeof(uint64_t), 256);
   return L;
 }
@@ -49,7 +70,7 @@ using namespace rtp;
 extern "C" size_t rtp_index_topp_workspace_size(int B, int n_ret, int max_ctx, int block) {
   if (B <= 0 || n_ret <= 0 || max_ctx <= 0 || (block != 64 && block != 128)) return 0;
   if (ceil_div(max_ctx, block) > kIdxMaxBlocks) return 0;
-  return k1_layout(B, n_ret, max_ctx, block).total;
+  return k1_layout(B, n_ret, max_ctx, block, 1).total;
 }
 
 extern "C" rtp_status rtp_index_topp(const void* q_pre, const void* w_q, const void* k_idx,
@@ -67,12 +88,12 @@ extern "C" rtp_status rtp_index_topp(const void* q_pre, const void* w_q, const v
     return RTP_EINVAL;
   if (((uintptr_t)q_pre | (uintptr_t)w_q | (uintptr_t)k_idx) & 15) return RTP_EINVAL;
   if ((uintptr_t)workspace & 255) return RTP_EINVAL;
-  const K1Layout L = k1_layout(B, n_ret, max_ctx, block);
-  if (ws_bytes < L.total) return RTP_EINVAL;
+  if (ws_bytes < k1_layout(B, n_ret, max_ctx, block, 1).total) return RTP_EINVAL;
+  const K1Layout L = k1_layout(B, n_ret, max_ctx, block, compute_units());
   char* ws = static_cast<char*>(workspace);
   IndexArgs args{static_cast<const uint16_t*>(q_pre), static_cast<const uint16_t*>(w_q),
                  static_cast<const uint16_t*>(k_idx), seq_lens, ret_heads, top_p, Hq, n_ret, max_ctx,
-                 L.g.nblk_max, L.g.chunk_blocks, L.g.n_chunk, sel_idx, sel_cnt, sel_mask,
+                 L.g.nblk_max, L.g.chunk_blocks, kIdxMaxChunks, sel_idx, sel_cnt, sel_mask,
                  reinterpret_cast<int*>(ws + L.off_counters), reinterpret_cast<uint64_t*>(ws + L.off_cmax),
                  reinterpret_cast<uint64_t*>(ws + L.off_e)};
   uint32_t* tags = reinterpret_cast<uint32_t*>(ws + L.off_tag);

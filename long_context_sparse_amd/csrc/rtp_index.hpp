@@ -39,7 +39,7 @@
 
 namespace rtp {
 
-constexpr int kIdxMaxChunkBlocks = 128;
+constexpr int kIdxMaxChunkBlocks = 256;
 constexpr int kIdxMaxBlocks = 16384;            // blocks per sequence the selection holds
 constexpr int kBins = 256;                      // histogram bins per refinement level
 constexpr int kFinal = kWave;                   // candidates ranked directly (one per lane)
@@ -80,8 +80,8 @@ __device__ __forceinline__ float* index_masses(IndexSmem<T>* S) {
   return reinterpret_cast<float*>(reinterpret_cast<char*>(S) + (sizeof(IndexSmem<T>) + 15) / 16 * 16);
 }
 
-// Chunking of the index role: at least `target` workgroups over the batch, 8..128 blocks
-// a chunk, at most 2 * T chunks per head.  rows = blocks per thread in the selection,
+// Chunking of the index role: at least `target` workgroups over the batch where the
+// blocks allow, 8..256 blocks (a power of two) a chunk, at most 2 * T chunks per head.  rows = blocks per thread in the selection,
 // rounded up to a multiple of kRowBatch.
 struct IndexGeom {
   int nblk_max, chunk_blocks, n_chunk, rows;
@@ -528,20 +528,27 @@ __device__ __forceinline__ bool index_chunk(const IndexArgs& a, int c, int r, in
   // the last workgroup of (b, r) to arrive selects
   uint64_t* e_io = a.blk_e + head * a.nblk_max;
   if (wave == 0) {
+    constexpr int PL = kIdxMaxChunkBlocks / kWave;  // blocks of the chunk per lane
     const int nb = j1 - j0;
-    const double x0 = lane < nb ? S->mx[lane] : -INFINITY;
-    const double x1 = lane + 64 < nb ? S->mx[lane + 64] : -INFINITY;
-    const double mc = wave_max(fmax(x0, x1));
-    float e0 = 0.f, e1 = 0.f;
-    if (lane < nb) {
-      e0 = (float)(S->sum[lane] * (double)fast_exp2((float)((x0 - mc) * kLog2e)));
-      st_dev(e_io + j0 + lane, tagged_f32(e0, tag));
+    double x[PL];
+    double xm = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < PL; ++q) {
+      x[q] = lane + kWave * q < nb ? S->mx[lane + kWave * q] : -INFINITY;
+      xm = fmax(xm, x[q]);
     }
-    if (lane + 64 < nb) {
-      e1 = (float)(S->sum[lane + 64] * (double)fast_exp2((float)((x1 - mc) * kLog2e)));
-      st_dev(e_io + j0 + lane + 64, tagged_f32(e1, tag));
+    const double mc = wave_max(xm);
+    double zl = 0.0;
+#pragma unroll
+    for (int q = 0; q < PL; ++q) {
+      const int k = lane + kWave * q;
+      if (k < nb) {
+        const float e = (float)(S->sum[k] * (double)fast_exp2((float)((x[q] - mc) * kLog2e)));
+        st_dev(e_io + j0 + k, tagged_f32(e, tag));
+        zl += (double)e;
+      }
     }
-    const double zc = wave_sum((double)e0 + (double)e1);
+    const double zc = wave_sum(zl);
     if (lane == 0) {
       uint64_t* cs = a.cmax + (head * a.n_chunk_max + c) * 2;
       st_dev(cs, tagged(mc, tag));
