@@ -187,6 +187,18 @@ __device__ __forceinline__ void attn_stream(AttnState<G>& s, const uint16_t* __r
   }
 }
 
+// Sum over the four 16-lane rows of a wave (lanes l, l ^ 16, l ^ 32, l ^ 48): gfx950's
+// row-swap moves (v_permlane16_swap: rows 0 <-> 1 and 2 <-> 3; v_permlane32_swap:
+// halves) on the VALU, without the LDS crossbar.  Every lane gets the same sum.
+__device__ __forceinline__ float sum_rows(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float s16 = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);  // row pair sum
+  const uint32_t w = __float_as_uint(s16);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+}
+
 // Combine the per-lane state of every wave of the workgroup through LDS and leave,
 // for head h and dim d, the normalised output and the natural-log LSE.
 // sm/sl: [waves][G]; sacc: [waves][G][128].
@@ -198,12 +210,7 @@ __device__ __forceinline__ void attn_publish_wave(const AttnState<G>& s, float* 
     const float lt = wave_sumf(s.l[h]);
     float a[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      float v = s.acc[h][k];
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      a[k] = v;
-    }
+    for (int k = 0; k < 8; ++k) a[k] = sum_rows(s.acc[h][k]);
     if (lane < 16) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) sacc[(wave * G + h) * kHeadDim + lane * 8 + k] = a[k];
