@@ -15,6 +15,10 @@ admitted block and cumulative mass C* at that block (eps = 1e-6) when:
   R3  sum_{G} m >= p - eps            (coverage);
   R4  sum_{G} m - min_{G} m < p + eps (minimality).
 
+Static top-k block sets (budget of kb = ceil(k / block) blocks) are accepted when G
+has exactly min(kb, nblk) blocks, every block with m_j > tau + eps is in G and every
+block in G has m_j >= tau - eps (tau = the oracle's kb-th largest mass).
+
 Outputs.  max |g - o| <= 1e-2 and sum |g - o| / sum |o| <= 1e-3 over every
 output element of a workload, with bf16 inputs and fp32 accumulation.
 """
@@ -24,7 +28,7 @@ from typing import Iterable, List, Tuple
 
 import numpy as np
 
-from .rtp_oracle import Selection, select_top_p
+from .rtp_oracle import Selection, select_top_k, select_top_p
 
 EPS_MASS = 1e-6
 TOL_MAX_ABS = 1e-2
@@ -69,6 +73,34 @@ def accept_selection(m: np.ndarray, p: float, gpu_blocks: Iterable[int],
         why.append(f"R3: coverage {tot!r} < p - eps")
     if G.size and tot - float(m[G].min()) >= p + eps:
         why.append(f"R4: not minimal: {tot!r} - {float(m[G].min())!r} >= p + eps")
+    return not why, why
+
+
+def accept_topk(m: np.ndarray, k_tokens: int, block: int, gpu_blocks: Iterable[int],
+                sel: Selection = None, eps: float = EPS_MASS) -> Tuple[bool, List[str]]:
+    m = np.asarray(m, dtype=np.float64)
+    n = m.shape[0]
+    G = np.asarray(sorted(int(j) for j in gpu_blocks), dtype=np.int64)
+    why: List[str] = []
+    if G.size != np.unique(G).size:
+        why.append("duplicate block ids")
+    if G.size and (G.min() < 0 or G.max() >= n):
+        why.append("block id out of range")
+    if why:
+        return False, why
+    if sel is None:
+        sel = select_top_k(m, k_tokens, block)
+    if G.size != sel.k_star:
+        why.append(f"size: {G.size} blocks, the budget keeps {sel.k_star}")
+    inG = np.zeros(n, dtype=bool)
+    inG[G] = True
+    must = np.nonzero(m > sel.tau + eps)[0]
+    missing = must[~inG[must]]
+    if missing.size:
+        why.append(f"{missing.size} blocks above tau+eps missing (e.g. {missing[:5].tolist()})")
+    low = G[m[G] < sel.tau - eps]
+    if low.size:
+        why.append(f"{low.size} blocks below tau-eps selected (e.g. {low[:5].tolist()})")
     return not why, why
 
 

@@ -27,6 +27,11 @@ Readings taken where the pages are silent or garbled:
 * Greedy top-p: blocks by mass descending, ties by ascending block id; the
   smallest prefix whose cumulative mass reaches p; every block when no prefix
   does; p >= 1 selects every block.
+* Static top-k (the Review's Experiments paragraph: a fixed-budget variant with
+  k = 4096 built to isolate the dynamic budget; its Insight item 3 counts the
+  budget in tokens): a budget of k tokens keeps ceil(k / block) blocks, the
+  same order (mass descending, ties by ascending id); every block when the
+  budget covers them.
 * Strikes-Back's printed O_h(m) has lost its value vector; the output is the
   usual softmax(q K^T / sqrt(128)) V over the selected tokens.
 * Retrieval heads attend to the selected tokens only (no forced sink/window).
@@ -133,6 +138,26 @@ def select_top_p(m: np.ndarray, p: float) -> Selection:
     c_prev = float(csum[k - 2]) if k >= 2 else 0.0
     return Selection(blocks=blocks, order=order, k_star=k, tau=tau, c_prev=c_prev,
                      c_star=c_star, all_blocks=all_blocks)
+
+
+def select_top_k(m: np.ndarray, k_tokens: int, block: int) -> Selection:
+    """Static top-k at block granularity: a budget of k_tokens keeps the
+    ceil(k_tokens / block) blocks of largest mass, ties by ascending id (Review,
+    Experiments: the static top-k variant, k = 4096; Insight item 3: a fixed k
+    counted in tokens); every block when there are no more than that."""
+    m = np.asarray(m, dtype=np.float64)
+    n = m.shape[0]
+    assert n >= 1
+    assert k_tokens >= 1 and block >= 1
+    kb = -(-int(k_tokens) // int(block))
+    ids = np.arange(n)
+    order = np.lexsort((ids, -m))
+    k = min(kb, n)
+    csum = np.cumsum(m[order])
+    blocks = np.sort(order[:k])
+    return Selection(blocks=blocks, order=order, k_star=k, tau=float(m[order[k - 1]]),
+                     c_prev=float(csum[k - 2]) if k >= 2 else 0.0, c_star=float(csum[k - 1]),
+                     all_blocks=k == n)
 
 
 def block_tokens(blocks: Sequence[int], block: int, n: int) -> np.ndarray:

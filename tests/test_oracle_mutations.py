@@ -10,7 +10,7 @@ from oracle import rtp_oracle as O
 import test_oracle_pins as P
 
 _orig = {name: getattr(O, name) for name in
-         ("block_masses", "token_softmax", "select_top_p", "attend", "local_tokens",
+         ("block_masses", "token_softmax", "select_top_p", "select_top_k", "attend", "local_tokens",
           "merge_partials", "index_query", "retrieval_head")}
 
 
@@ -45,6 +45,19 @@ def _select_generic(m, p, tie_desc=False, strict=False, extra=0):
     cs = np.cumsum(m[order])
     hit = np.nonzero(cs > p if strict else cs >= p)[0]
     k = n if (p >= 1.0 or not hit.size) else min(n, int(hit[0]) + 1 + extra)
+    return O.Selection(blocks=np.sort(order[:k]), order=order, k_star=k, tau=float(m[order[k - 1]]),
+                       c_prev=float(cs[k - 2]) if k > 1 else 0.0, c_star=float(cs[k - 1]),
+                       all_blocks=k == n)
+
+
+def _topk_generic(m, k_tokens, block, tie_desc=False, floor_blocks=False):
+    m = np.asarray(m, np.float64)
+    n = m.shape[0]
+    ids = np.arange(n)
+    order = np.lexsort(((-ids if tie_desc else ids), -m))
+    kb = max(1, k_tokens // block) if floor_blocks else -(-k_tokens // block)
+    k = min(kb, n)
+    cs = np.cumsum(m[order])
     return O.Selection(blocks=np.sort(order[:k]), order=order, k_star=k, tau=float(m[order[k - 1]]),
                        c_prev=float(cs[k - 2]) if k > 1 else 0.0, c_star=float(cs[k - 1]),
                        all_blocks=k == n)
@@ -109,6 +122,9 @@ MUTANTS = [
     ("select_top_p", lambda m, p: _select_generic(m, p, strict=True), [P.check_tie_break_worked]),
     ("select_top_p", lambda m, p: _select_generic(m, p, extra=1),
      [P.check_block_mass_worked, P.check_selection_bruteforce]),
+    ("select_top_k", lambda m, k, b: _topk_generic(m, k, b, tie_desc=True), [P.check_topk_worked]),
+    ("select_top_k", lambda m, k, b: _topk_generic(m, k, b, floor_blocks=True),
+     [P.check_topk_worked, P.check_topk_bruteforce]),
     ("attend", _attend_no_scale, [P.check_attention_vs_sdpa]),
     ("attend", _attend_lost_value, [P.check_attention_vs_sdpa, P.check_attention_closed_forms]),
     ("local_tokens", _local_off_by_one, [P.check_local_tokens_worked]),

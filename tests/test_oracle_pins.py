@@ -162,6 +162,53 @@ def check_dominant_needle():
             assert res.masses[inp1.needles[(b, r)][0]] > 0.95
 
 
+# ------------------------------------------------------- static top-k (next row f1)
+def check_topk_worked():
+    """Hand-worked: masses [0.1, 0.4, 0.4, 0.1] at block 64; the budget is counted in
+    tokens and rounded up to whole blocks; ties go to the lower block id."""
+    m = np.array([0.1, 0.4, 0.4, 0.1])
+    assert O.select_top_k(m, 64, 64).blocks.tolist() == [1]           # 1 block: tie 1/2 -> 1
+    assert O.select_top_k(m, 65, 64).blocks.tolist() == [1, 2]        # 2 blocks
+    assert O.select_top_k(m, 129, 64).blocks.tolist() == [0, 1, 2]   # 3 blocks: tie 0/3 -> 0
+    assert O.select_top_k(m, 10000, 64).blocks.tolist() == [0, 1, 2, 3]
+    assert O.select_top_k(m, 10000, 64).all_blocks
+    assert O.select_top_k(m, 128, 128).blocks.tolist() == [1]         # block 128: 1 block
+    assert O.select_top_k(m, 4096, 64).k_star == 4
+
+
+def check_topk_bruteforce(trials=300, seed=11):
+    """Against exhaustive search on tiny inputs: the kept set is a subset of the budget's
+    size with the largest mass, and among those the one a pure-Python sort by (mass
+    descending, id ascending) picks."""
+    g = np.random.default_rng(seed)
+    for t in range(trials):
+        n = int(g.integers(1, 11))
+        m = g.dirichlet(np.ones(n) * 0.5) if t % 2 else g.integers(1, 4, size=n) / 10.0
+        block = int(g.choice([64, 128]))
+        k_tokens = int(g.integers(1, (n + 2) * block))
+        kb = -(-k_tokens // block)
+        sel = O.select_top_k(m, k_tokens, block)
+        k = min(kb, n)
+        want = sorted(sorted(range(n), key=lambda j: (-m[j], j))[:k])
+        assert sel.blocks.tolist() == want, (m, k_tokens, block)
+        best = max(sum(m[list(sub)]) for sub in itertools.combinations(range(n), k))
+        assert abs(m[sel.blocks].sum() - best) < 1e-12
+
+
+def check_topk_matches_topp_prefix(trials=200, seed=12):
+    """Both rules take a prefix of the same order: a budget of exactly the top-p set's
+    size (in tokens) keeps the top-p set."""
+    g = np.random.default_rng(seed)
+    for _ in range(trials):
+        n = int(g.integers(1, 200))
+        m = g.dirichlet(np.ones(n) * float(g.choice([0.05, 0.5, 5.0])))
+        p = float(g.uniform(0.1, 0.999))
+        sp = O.select_top_p(m, p)
+        block = 64
+        sk = O.select_top_k(m, sp.k_star * block - int(g.integers(0, block)), block)
+        assert sk.blocks.tolist() == sp.blocks.tolist()
+
+
 # ------------------------------------------------------------ attention (a6-a8)
 def _sdpa(q, K, V):
     qt = torch.from_numpy(O.bf16_to_f64(q))[None, None, None, :]
@@ -283,10 +330,20 @@ def check_acceptance_rule():
     assert A.accept_selection(m3, 0.9, [0, 1, 2])[0]
     assert A.accept_selection(m, 1.0, [0, 1, 2, 3, 4])[0]
     assert not A.accept_selection(m, 1.0, [0, 1, 2, 3])[0]
+    # static top-k: exact size, no lower block in place of a higher one; ties either way
+    mk = np.array([0.1, 0.4, 0.4, 0.1])
+    assert A.accept_topk(mk, 65, 64, [1, 2])[0]
+    assert not A.accept_topk(mk, 65, 64, [1])[0]                 # too few
+    assert not A.accept_topk(mk, 65, 64, [0, 1, 2])[0]           # too many
+    assert not A.accept_topk(mk, 65, 64, [0, 1])[0]              # 0.1 in place of 0.4
+    assert A.accept_topk(mk, 64, 64, [2])[0]                     # tie at the threshold
+    assert A.accept_topk(mk, 129, 64, [1, 2, 3])[0]
+    assert A.accept_topk(mk, 9999, 64, [0, 1, 2, 3])[0]
 
 
 CHECKS = [check_index_worked, check_block_mass_worked, check_tie_break_worked, check_mass_vs_library,
           check_selection_bruteforce, check_p_one_selects_all, check_dominant_needle,
+          check_topk_worked, check_topk_bruteforce, check_topk_matches_topp_prefix,
           check_attention_vs_sdpa, check_attention_closed_forms, check_merge_is_union,
           check_local_tokens_worked, check_local_reduces_to_dense, check_p_one_is_dense,
           check_gqa_mapping, check_acceptance_rule]
