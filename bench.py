@@ -4,7 +4,11 @@ One step = the whole hot path for one decode token of every sequence and query
 head of a workload: rtp_index_topp -> rtp_sparse_attn_split -> rtp_split_reduce for
 the retrieval heads, rtp_local_window_attn (second stream) for the local heads.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ctx128k] [--also ctx1m]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ctx128k]
+                    [--also ctx1m,ctx128k@topk4096]
+
+A workload name with "@topkK" runs the step with the static top-k rule (a budget of K
+tokens, rtp_index_topk) in place of top-p.
 
 Prints ONE JSON line.  `value` is the effective HBM bandwidth of the step,
 algorithmic bytes / step latency, with every input resident in HBM before the
@@ -35,13 +39,14 @@ METRIC = "sparse-decode step latency (µs) + effective HBM GB/s at 128K and 1M c
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, vendor figure
 KERNEL_NAMES = {                # call -> the kernel it launches (the local call also merges)
     "index_topp": "index_topp_kernel",
+    "index_topk": "index_topp_kernel",
     "sparse_attn": "sparse_attn_kernel",
     "split_reduce": "merge_kernel",
     "local_window": "local_window_kernel",
 }
 
 
-CALL_NAMES = {"index_topp": "rtp_index_topp", "sparse_attn": "rtp_sparse_attn_split",
+CALL_NAMES = {"index_topp": "rtp_index_topp", "index_topk": "rtp_index_topk", "sparse_attn": "rtp_sparse_attn_split",
               "split_reduce": "rtp_split_reduce", "local_window": "rtp_local_window_attn"}
 
 
@@ -142,26 +147,34 @@ def read_traffic(workload: str, kernel: str) -> Optional[float]:
 
 
 # ------------------------------------------------------------------ GPU measurement
-def measure(name: str, steps: int, warmup: int, cold_iters: int, calib_copy: bool) -> Dict:
+def measure(label: str, steps: int, warmup: int, cold_iters: int, calib_copy: bool) -> Dict:
+    """One workload; label = a workload name, optionally with "@topkK" (static top-k rule,
+    budget K tokens)."""
     import torch
 
     import workloads as W
     from long_context_sparse_amd import DecodeStep, StepShape
 
+    name, _, rule = label.partition("@")
+    k_tokens = int(rule[4:]) if rule.startswith("topk") else 0
+    if rule and not k_tokens:
+        raise ValueError(f"unknown selection rule in {label!r}")
     cfg = W.get_config(name)
     t0 = time.time()
     inp = W.make_inputs(cfg)
-    log(f"[bench] {name}: inputs built in {time.time() - t0:.1f}s")
+    log(f"[bench] {label}: inputs built in {time.time() - t0:.1f}s")
     dev = torch.device("cuda:0")
     t = W.to_device(inp, dev)
     shape = StepShape(B=cfg.B, Hq=cfg.Hq, Hkv=cfg.Hkv, n_ret=cfg.n_ret, n_loc=cfg.n_loc, max_ctx=cfg.max_ctx,
                       block=cfg.block, split_tokens=cfg.split_tokens, window=cfg.window, sinks=cfg.sinks)
-    step = DecodeStep(shape, device=dev)
+    step = DecodeStep(shape, device=dev, k_tokens=k_tokens)
     step(t)
     torch.cuda.synchronize()
     sel_idx = step.sel_idx.cpu().numpy()
     sel_cnt = step.sel_cnt.cpu().numpy()
     alg = algorithmic_bytes(cfg, inp, sel_idx, sel_cnt)
+    if k_tokens:
+        alg["index_topk"] = alg.pop("index_topp")
 
     # timed region: `steps` back-to-back decode steps, inputs resident in HBM
     main = torch.cuda.current_stream(dev)
@@ -177,11 +190,12 @@ def measure(name: str, steps: int, warmup: int, cold_iters: int, calib_copy: boo
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms_per_step = ev0.elapsed_time(ev1) / steps
-    log(f"[bench] {name}: {steps} steps, {ms_per_step * 1e3:.1f} us/step (host {wall * 1e6 / steps:.1f} us/step)")
+    log(f"[bench] {label}: {steps} steps, {ms_per_step * 1e3:.1f} us/step (host {wall * 1e6 / steps:.1f} us/step)")
 
     # per-call durations: the four calls one after another on the main stream, with
     # events around each call on that stream
-    calls = [("index_topp", step.index_topp), ("sparse_attn", step.sparse_attn),
+    calls = [("index_topk", step.index_topk) if k_tokens else ("index_topp", step.index_topp),
+             ("sparse_attn", step.sparse_attn),
              ("split_reduce", step.reduce), ("local_window", step.local)]
     calls = [(k, f) for k, f in calls if (cfg.n_ret if k != "local_window" else cfg.n_loc)]
     per = {k: [] for k, _ in calls}
@@ -223,7 +237,7 @@ def measure(name: str, steps: int, warmup: int, cold_iters: int, calib_copy: boo
     lat_us = ms_per_step * 1e3
     dom = max(kern_us, key=kern_us.get)
     res = dict(
-        workload=name, cfg=cfg, inp=inp, alg=alg, latency_us=lat_us, wall_us=wall * 1e6 / steps,
+        workload=name, label=label, k_tokens=k_tokens, cfg=cfg, inp=inp, alg=alg, latency_us=lat_us, wall_us=wall * 1e6 / steps,
         kern_us=kern_us, dominant=dom, cold_us=float(np.median(cold)) if cold else None,
         gbs=alg["step"] / (lat_us * 1e-6) / 1e9,
         sel_frac=float(np.mean([sel_cnt[b, r] / -(-int(inp.seq_lens[b]) // cfg.block)
@@ -234,11 +248,12 @@ def measure(name: str, steps: int, warmup: int, cold_iters: int, calib_copy: boo
     return res
 
 
-def config_of(cfg) -> Dict:
+def config_of(cfg, k_tokens: int = 0) -> Dict:
     ctx = sorted(set(cfg.ctx))
+    sel = {"top_k_tokens": k_tokens} if k_tokens else {"top_p": sorted(set(cfg.top_p))}
     return {"workload": cfg.name, "batch": cfg.B, "ctx": ctx[0] if len(ctx) == 1 else [min(ctx), max(ctx)],
             "kv_heads": cfg.Hkv, "q_heads": cfg.Hq, "retrieval_heads": cfg.n_ret, "head_dim": 128,
-            "index_dim": 16, "block": cfg.block, "top_p": sorted(set(cfg.top_p)), "window": cfg.window,
+            "index_dim": 16, "block": cfg.block, **sel, "window": cfg.window,
             "sinks": cfg.sinks, "split_tokens": cfg.split_tokens}
 
 
@@ -248,7 +263,7 @@ def roofline_of(r: Dict) -> Dict:
     ach = r["alg"][k] / (us * 1e-6) / 1e9
     return {"bound": "hbm", "kernel": KERNEL_NAMES[k], "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
             "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-            "traffic": read_traffic(r["workload"], k),
+            "traffic": read_traffic(r["label"], k),
             "alg_bytes_per_launch": int(r["alg"][k]), "avg_launch_us": round(us, 2)}
 
 
@@ -279,7 +294,8 @@ def main(argv: Optional[List[str]] = None) -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="ctx128k")
-    ap.add_argument("--also", default="ctx1m", help="comma-separated extra workloads ('' for none)")
+    ap.add_argument("--also", default="ctx1m,ctx128k@topk4096",
+                    help="comma-separated extra workloads ('' for none); name@topkK: static top-k rule")
     ap.add_argument("--cold-iters", type=int, default=20)
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -311,13 +327,13 @@ def main(argv: Optional[List[str]] = None) -> int:
                 "cold_effective_gbs": None if not r["cold_us"] else round(r["alg"]["step"] / r["cold_us"] / 1e3, 1),
                 "call_us": {CALL_NAMES[k]: round(v, 2) for k, v in r["kern_us"].items()},
                 "mean_selected_block_fraction": round(r["sel_frac"], 4),
-                "roofline": roofline_of(r), "config": config_of(r["cfg"])}
+                "roofline": roofline_of(r), "config": config_of(r["cfg"], r["k_tokens"])}
 
     line = {
         "metric": METRIC, "value": round(head["gbs"], 1), "unit": "GB/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": round(head["latency_us"] / 1e3, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": config_of(head["cfg"]),
+        "config": config_of(head["cfg"], head["k_tokens"]),
         "latency_us": round(head["latency_us"], 2),
         "frac_of_peak": round(head["gbs"] / PEAK_HBM_GBS, 4),
         "roofline": roofline_of(head),

@@ -110,6 +110,23 @@ rtp_status rtp_index_topp(const void* q_pre, const void* w_q, const void* k_idx,
                           void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Kernel 1 with the static top-k rule instead of top-p (Review, Experiments: the
+ * fixed-budget variant with k = 4096 built to isolate the dynamic budget; Insight item 3
+ * counts the budget in tokens): the same scores and block masses, and
+ *   S = the ceil(k_tokens / block) blocks of largest m_j (ties by ascending j); every
+ *       block when there are no more than that.
+ * The same exact radix select finds the set, every block weighing 1.
+ *
+ *   k_tokens  budget in tokens, >= 1 (RTP_EINVAL otherwise)
+ *   every other argument as in rtp_index_topp (same workspace)
+ */
+rtp_status rtp_index_topk(const void* q_pre, const void* w_q, const void* k_idx,
+                          const int* seq_lens, const int* ret_heads, int k_tokens,
+                          int B, int Hq, int n_ret, int max_ctx, int block,
+                          int* sel_idx, int* sel_cnt, unsigned char* sel_mask,
+                          void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * Kernel 2: block-sparse exact attention over the selected blocks, split along the
  * context (Strikes-Back method item 2, O_h(m) with the value vector; architecture
  * paragraph, Kernel 2 at D128).
@@ -196,6 +213,8 @@ rtp_status rtp_local_window_attn(const void* q, const void* k_cache, const void*
  * nothing.  Every argument is checked (as by each call) before anything is enqueued;
  * after that it returns the first failing call's status.
  *
+ *   k_tokens           0: the top-p rule with top_p (rtp_index_topp); > 0: the static top-k
+ *                      rule with this budget (rtp_index_topk; top_p may then be NULL)
  *   o_part, lse_part   split partials as in rtp_sparse_attn_split (n_split =
  *                      ceil(max_ctx / split_tokens))
  *   ws_index           workspace of rtp_index_topp; ws_local of rtp_local_window_attn
@@ -203,7 +222,7 @@ rtp_status rtp_local_window_attn(const void* q, const void* k_cache, const void*
  */
 rtp_status rtp_decode_step(const void* q_pre, const void* w_q, const void* k_idx, const void* q,
                            const void* k_cache, const void* v_cache, const int* seq_lens,
-                           const int* ret_heads, const int* loc_heads, const float* top_p,
+                           const int* ret_heads, const int* loc_heads, const float* top_p, int k_tokens,
                            int B, int Hq, int Hkv, int n_ret, int n_loc, int max_ctx, int block,
                            int split_tokens, int window, int sinks,
                            int* sel_idx, int* sel_cnt, unsigned char* sel_mask,

@@ -35,11 +35,12 @@ _SIGS = {
     "rtp_version": ([], ctypes.c_char_p),
     "rtp_index_topp_workspace_size": ([_i, _i, _i, _i], _sz),
     "rtp_index_topp": ([_vp] * 6 + [_i] * 5 + [_vp, _vp, _vp, _vp, _sz, _vp], _i),
+    "rtp_index_topk": ([_vp] * 5 + [_i] * 6 + [_vp, _vp, _vp, _vp, _sz, _vp], _i),
     "rtp_sparse_attn_split": ([_vp] * 8 + [_i] * 7 + [_vp, _vp, _vp], _i),
     "rtp_split_reduce": ([_vp] * 3 + [_i] * 4 + [_vp, _vp], _i),
     "rtp_local_window_workspace_size": ([_i] * 7, _sz),
     "rtp_local_window_attn": ([_vp] * 5 + [_i] * 7 + [_vp, _vp, _sz, _vp], _i),
-    "rtp_decode_step": ([_vp] * 10 + [_i] * 10 + [_vp] * 6 + [_vp, _sz, _vp, _sz] + [_vp] * 4, _i),
+    "rtp_decode_step": ([_vp] * 10 + [_i] * 11 + [_vp] * 6 + [_vp, _sz, _vp, _sz] + [_vp] * 4, _i),
 }
 
 
@@ -163,6 +164,14 @@ def rtp_index_topp(q_pre, w_q, k_idx, seq_lens, ret_heads, top_p, B, Hq, n_ret, 
                               B, Hq, n_ret, max_ctx, block, _p(sel_idx), _p(sel_cnt), _p(sel_mask), _p(workspace),
                               _nbytes(workspace), _s(stream))
     _check("rtp_index_topp", st)
+
+
+def rtp_index_topk(q_pre, w_q, k_idx, seq_lens, ret_heads, k_tokens, B, Hq, n_ret, max_ctx, block,
+                   sel_idx, sel_cnt, workspace, stream=None, sel_mask=None) -> None:
+    st = lib().rtp_index_topk(_p(q_pre), _p(w_q), _p(k_idx), _p(seq_lens), _p(ret_heads), int(k_tokens),
+                              B, Hq, n_ret, max_ctx, block, _p(sel_idx), _p(sel_cnt), _p(sel_mask), _p(workspace),
+                              _nbytes(workspace), _s(stream))
+    _check("rtp_index_topk", st)
 
 
 def rtp_sparse_attn_split(q, k_cache, v_cache, seq_lens, ret_heads, sel_idx, sel_cnt, B, Hq, Hkv,

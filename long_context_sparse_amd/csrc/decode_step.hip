@@ -9,7 +9,7 @@ using rtp::ceil_div;
 extern "C" rtp_status rtp_decode_step(
     const void* q_pre, const void* w_q, const void* k_idx, const void* q, const void* k_cache,
     const void* v_cache, const int* seq_lens, const int* ret_heads, const int* loc_heads, const float* top_p,
-    int B, int Hq, int Hkv, int n_ret, int n_loc, int max_ctx, int block, int split_tokens, int window,
+    int k_tokens, int B, int Hq, int Hkv, int n_ret, int n_loc, int max_ctx, int block, int split_tokens, int window,
     int sinks, int* sel_idx, int* sel_cnt, unsigned char* sel_mask, float* o_part, float* lse_part, float* out,
     void* ws_index, size_t ws_index_bytes, void* ws_local, size_t ws_local_bytes, void* stream,
     void* side_stream, void* ev_fork, void* ev_join) {
@@ -25,8 +25,9 @@ extern "C" rtp_status rtp_decode_step(
     if (block != 64 && block != 128) return RTP_EUNSUPPORTED;
     if (split_tokens <= 0 || split_tokens % block) return RTP_EINVAL;
     if (split_tokens / block > 2048 || ceil_div(max_ctx, split_tokens) > 65535) return RTP_EUNSUPPORTED;
-    if (!q_pre || !w_q || !k_idx || !ret_heads || !top_p || !sel_idx || !sel_cnt || !o_part || !lse_part ||
-        !ws_index)
+    if (k_tokens < 0) return RTP_EINVAL;
+    if (!q_pre || !w_q || !k_idx || !ret_heads || (k_tokens == 0 && !top_p) || !sel_idx || !sel_cnt || !o_part ||
+        !lse_part || !ws_index)
       return RTP_EINVAL;
     if (((uintptr_t)q_pre | (uintptr_t)w_q | (uintptr_t)k_idx) & 15) return RTP_EINVAL;
     const size_t need = rtp_index_topp_workspace_size(B, n_ret, max_ctx, block);
@@ -56,8 +57,10 @@ extern "C" rtp_status rtp_decode_step(
     if (fork && hipEventRecord(static_cast<hipEvent_t>(ev_join), ls) != hipSuccess) return RTP_ELAUNCH;
   }
   if (n_ret > 0) {
-    st = rtp_index_topp(q_pre, w_q, k_idx, seq_lens, ret_heads, top_p, B, Hq, n_ret, max_ctx, block, sel_idx,
-                        sel_cnt, sel_mask, ws_index, ws_index_bytes, stream);
+    st = k_tokens > 0 ? rtp_index_topk(q_pre, w_q, k_idx, seq_lens, ret_heads, k_tokens, B, Hq, n_ret, max_ctx,
+                                       block, sel_idx, sel_cnt, sel_mask, ws_index, ws_index_bytes, stream)
+                      : rtp_index_topp(q_pre, w_q, k_idx, seq_lens, ret_heads, top_p, B, Hq, n_ret, max_ctx, block,
+                                       sel_idx, sel_cnt, sel_mask, ws_index, ws_index_bytes, stream);
     if (st == RTP_OK)
       st = rtp_sparse_attn_split(q, k_cache, v_cache, seq_lens, ret_heads, sel_idx, sel_cnt, sel_mask, B, Hq, Hkv,
                                  n_ret, max_ctx, block, split_tokens, o_part, lse_part, stream);

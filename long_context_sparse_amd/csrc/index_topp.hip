@@ -73,18 +73,21 @@ extern "C" size_t rtp_index_topp_workspace_size(int B, int n_ret, int max_ctx, i
   return k1_layout(B, n_ret, max_ctx, block, 1).total;
 }
 
-extern "C" rtp_status rtp_index_topp(const void* q_pre, const void* w_q, const void* k_idx,
-                                     const int* seq_lens, const int* ret_heads, const float* top_p,
-                                     int B, int Hq, int n_ret, int max_ctx, int block, int* sel_idx,
-                                     int* sel_cnt, unsigned char* sel_mask, void* workspace, size_t ws_bytes,
-                                     void* stream) {
+namespace {
+
+// Checks the arguments and enqueues kernel 1 with either selection rule: top_p per head
+// (topk_blocks == 0) or a fixed number of blocks per head (topk_blocks > 0).
+rtp_status index_launch(const void* q_pre, const void* w_q, const void* k_idx, const int* seq_lens,
+                        const int* ret_heads, const float* top_p, int topk_blocks, int B, int Hq, int n_ret,
+                        int max_ctx, int block, int* sel_idx, int* sel_cnt, unsigned char* sel_mask,
+                        void* workspace, size_t ws_bytes, void* stream) {
   if (B <= 0 || Hq <= 0 || n_ret < 0 || n_ret > Hq || max_ctx <= 0) return RTP_EINVAL;
   if (block != 64 && block != 128) return RTP_EUNSUPPORTED;
   if (ceil_div(max_ctx, block) > kIdxMaxBlocks) return RTP_EUNSUPPORTED;
   if (B > 65535 || n_ret > 65535) return RTP_EUNSUPPORTED;
   if (n_ret == 0) return RTP_OK;
-  if (!q_pre || !w_q || !k_idx || !seq_lens || !ret_heads || !top_p || !sel_idx || !sel_cnt ||
-      !workspace)
+  if (!q_pre || !w_q || !k_idx || !seq_lens || !ret_heads || (topk_blocks == 0 && !top_p) || !sel_idx ||
+      !sel_cnt || !workspace)
     return RTP_EINVAL;
   if (((uintptr_t)q_pre | (uintptr_t)w_q | (uintptr_t)k_idx) & 15) return RTP_EINVAL;
   if ((uintptr_t)workspace & 255) return RTP_EINVAL;
@@ -92,9 +95,9 @@ extern "C" rtp_status rtp_index_topp(const void* q_pre, const void* w_q, const v
   const K1Layout L = k1_layout(B, n_ret, max_ctx, block, compute_units());
   char* ws = static_cast<char*>(workspace);
   IndexArgs args{static_cast<const uint16_t*>(q_pre), static_cast<const uint16_t*>(w_q),
-                 static_cast<const uint16_t*>(k_idx), seq_lens, ret_heads, top_p, Hq, n_ret, max_ctx,
-                 L.g.nblk_max, L.g.chunk_blocks, kIdxMaxChunks, sel_idx, sel_cnt, sel_mask,
-                 reinterpret_cast<int*>(ws + L.off_counters), reinterpret_cast<uint64_t*>(ws + L.off_cmax),
+                 static_cast<const uint16_t*>(k_idx), seq_lens, ret_heads, topk_blocks ? nullptr : top_p,
+                 topk_blocks, Hq, n_ret, max_ctx, L.g.nblk_max, L.g.chunk_blocks, kIdxMaxChunks, sel_idx, sel_cnt,
+                 sel_mask, reinterpret_cast<int*>(ws + L.off_counters), reinterpret_cast<uint64_t*>(ws + L.off_cmax),
                  reinterpret_cast<uint64_t*>(ws + L.off_e)};
   uint32_t* tags = reinterpret_cast<uint32_t*>(ws + L.off_tag);
   dim3 grid(L.g.n_chunk, n_ret, B);
@@ -105,4 +108,27 @@ extern "C" rtp_status rtp_index_topp(const void* q_pre, const void* w_q, const v
   else
     hipLaunchKernelGGL(index_topp_kernel<128>, grid, dim3(kIdxThreads), dyn, s, args, tags);
   return hipGetLastError() == hipSuccess ? RTP_OK : RTP_ELAUNCH;
+}
+
+}  // namespace
+
+extern "C" rtp_status rtp_index_topp(const void* q_pre, const void* w_q, const void* k_idx,
+                                     const int* seq_lens, const int* ret_heads, const float* top_p,
+                                     int B, int Hq, int n_ret, int max_ctx, int block, int* sel_idx,
+                                     int* sel_cnt, unsigned char* sel_mask, void* workspace, size_t ws_bytes,
+                                     void* stream) {
+  return index_launch(q_pre, w_q, k_idx, seq_lens, ret_heads, top_p, 0, B, Hq, n_ret, max_ctx, block, sel_idx,
+                      sel_cnt, sel_mask, workspace, ws_bytes, stream);
+}
+
+extern "C" rtp_status rtp_index_topk(const void* q_pre, const void* w_q, const void* k_idx,
+                                     const int* seq_lens, const int* ret_heads, int k_tokens,
+                                     int B, int Hq, int n_ret, int max_ctx, int block, int* sel_idx,
+                                     int* sel_cnt, unsigned char* sel_mask, void* workspace, size_t ws_bytes,
+                                     void* stream) {
+  if (k_tokens <= 0) return RTP_EINVAL;
+  if (block != 64 && block != 128) return RTP_EUNSUPPORTED;
+  const int kb = (int)(((long long)k_tokens + block - 1) / block);
+  return index_launch(q_pre, w_q, k_idx, seq_lens, ret_heads, nullptr, kb, B, Hq, n_ret, max_ctx, block, sel_idx,
+                      sel_cnt, sel_mask, workspace, ws_bytes, stream);
 }

@@ -106,7 +106,8 @@ struct IndexArgs {
   const uint16_t* k_idx;  // bf16 [B, n_ret, max_ctx, 16]
   const int* seq_lens;
   const int* ret_heads;
-  const float* top_p;
+  const float* top_p;     // [B * n_ret] top-p of each head (top-p rule)
+  int topk_blocks;        // > 0: static top-k, keep this many blocks (top_p unused)
   int Hq, n_ret, max_ctx, nblk_max, chunk_blocks, n_chunk_max;
   int* sel_idx;
   int* sel_cnt;
@@ -275,7 +276,10 @@ __device__ __forceinline__ void scan_level(uint64_t cab, uint64_t P, uint32_t lo
 // ascending block order, k = ceil((P - cab) / mass).
 template <int T>
 __device__ __noinline__ uint64_t select_threshold(const float* __restrict__ sm_m, int rows, uint64_t P,
-                                                  TailSmem<T>& sm, uint64_t* __restrict__ wbuf) {
+                                                  TailSmem<T>& sm, uint64_t* __restrict__ wbuf, bool count) {
+  // a block's weight: its fixed-point mass (top-p), or 1 (static top-k: P is then the
+  // number of blocks to keep)
+  auto wgt = [&](uint32_t bits) { return count ? 1ull : fixed_bits(bits); };
   constexpr int W = T / kWave;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint64_t cab = uni64(sm.cab);
@@ -292,7 +296,7 @@ __device__ __noinline__ uint64_t select_threshold(const float* __restrict__ sm_m
     for_rows<T>(sm_m, rows, [&](int i, float m) {
       if (cand(m)) {
         const int bin = level_bin(__float_as_uint(m), lo, shift);
-        atomicAdd((unsigned long long*)&sm.bmass[bin], (unsigned long long)fixed_bits(__float_as_uint(m)));
+        atomicAdd((unsigned long long*)&sm.bmass[bin], (unsigned long long)wgt(__float_as_uint(m)));
         atomicAdd(&sm.bcnt[bin], 1u);
       }
     });
@@ -312,7 +316,7 @@ __device__ __noinline__ uint64_t select_threshold(const float* __restrict__ sm_m
     }
     auto tie = [&](int i, float m) { return m >= 0.f && __float_as_uint(m) == lo; };
     rows_prefix<T>(sm_m, rows, tie, sm);
-    const uint64_t f = fixed_bits(lo);
+    const uint64_t f = wgt(lo);
     if (f == 0) return 0;  // cannot happen while the invariant holds
     const uint64_t k = (P - cab + f - 1) / f;  // >= 1, <= cnt
     for_rows<T>(sm_m, rows, [&](int i, float m) {
@@ -336,7 +340,7 @@ __device__ __noinline__ uint64_t select_threshold(const float* __restrict__ sm_m
       const int slot = nw + (int)__popcll(bc & lanemask_lt());
       if (slot < kFinal) {
         wk[slot] = key_at<T>(i, m);
-        wk[kFinal + slot] = fixed_bits(bits);
+        wk[kFinal + slot] = wgt(bits);
       }
     }
     nw += (int)__popcll(bc);
@@ -585,12 +589,16 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int r, 
     sm.bcnt[tid] = 0;
   }
   if (tid == 0) sm.found = 0;
-  const float p = a.top_p[head];
-  const bool pick = p < 1.0f && nblk > 1;  // else every block is selected
-  // Every block of mass below (1 - p) / (2 nblk) is outside the selection and below its
-  // threshold: with total mass ~1 the threshold exceeds (total - p) / nblk.  Such blocks
-  // stay out of the histograms (peaked heads have thousands of them).
-  const uint32_t lbits = __float_as_uint(fmaxf(0.f, 0.5f * (1.0f - p - 1e-6f) / (float)nblk));
+  // static top-k keeps topk_blocks blocks: the same search with every block weighing 1
+  // and P = the number of blocks
+  const int kb = a.topk_blocks;
+  const bool count = kb > 0;
+  const float p = count ? 1.0f : a.top_p[head];
+  const bool pick = count ? kb < nblk : (p < 1.0f && nblk > 1);  // else every block is selected
+  // Top-p: every block of mass below (1 - p) / (2 nblk) is outside the selection and
+  // below its threshold: with total mass ~1 the threshold exceeds (total - p) / nblk.
+  // Such blocks stay out of the histograms (peaked heads have thousands of them).
+  const uint32_t lbits = count ? 0u : __float_as_uint(fmaxf(0.f, 0.5f * (1.0f - p - 1e-6f) / (float)nblk));
   // first level: 1/8-octave bins (bits >> 20) from the floor up, which span 32 octaves
   // (everything above goes to the top bin); without a floor, half-octave bins from 0
   const int shift1 = lbits ? 20 : 22;
@@ -678,7 +686,7 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int r, 
           const uint32_t bits = __float_as_uint(m);
           if (pick && bits >= lbits) {
             const int bin = level_bin(bits, lo1, shift1);
-            atomicAdd((unsigned long long*)&sm.bmass[bin], (unsigned long long)fixed_bits(bits));
+            atomicAdd((unsigned long long*)&sm.bmass[bin], count ? 1ull : (unsigned long long)fixed_bits(bits));
             atomicAdd(&sm.bcnt[bin], 1u);
           }
         }
@@ -692,7 +700,7 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int r, 
   uint64_t thr = 0;
   bool all = true, ready = false;
   if (pick) {
-    const uint64_t P = (uint64_t)ceil(ldexp((double)p, 62));
+    const uint64_t P = count ? (uint64_t)kb : (uint64_t)ceil(ldexp((double)p, 62));
     if (wave == 0) {
       scan_level<T>(0, P, lo1, 0xFFFFFFFFu, shift1, sm);
       // the pruned blocks were not counted: the candidates start at the floor
@@ -701,7 +709,7 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int r, 
     __syncthreads();
     if (sm.found) {  // else the total mass is below p: every block
       all = false;
-      thr = select_threshold<T>(s_mass, rows, P, sm, reinterpret_cast<uint64_t*>(S->f));
+      thr = select_threshold<T>(s_mass, rows, P, sm, reinterpret_cast<uint64_t*>(S->f), count);
       ready = sm.ready;
     }
   }

@@ -3,7 +3,7 @@
 DecodeStep owns the device buffers the calls need (selected-block lists and masks,
 split partials, workspaces, output) and issues them through one rtp_decode_step call:
 
-  retrieval heads:  rtp_index_topp -> rtp_sparse_attn_split -> rtp_split_reduce
+  retrieval heads:  rtp_index_topp (or rtp_index_topk) -> rtp_sparse_attn_split -> rtp_split_reduce
   local heads:      rtp_local_window_attn (on a second stream, overlapping the above)
 
 PyTorch provides the memory and the streams; every step runs in librtp.so.
@@ -44,8 +44,12 @@ class StepShape:
 
 
 class DecodeStep:
-    def __init__(self, shape: StepShape, device: str = "cuda", overlap: bool = True, use_mask: bool = True):
+    def __init__(self, shape: StepShape, device: str = "cuda", overlap: bool = True, use_mask: bool = True,
+                 k_tokens: int = 0):
+        """k_tokens = 0: the top-p rule (the inputs' top_p); > 0: the static top-k rule
+        with this budget in tokens."""
         self.s = shape
+        self.k_tokens = int(k_tokens)
         dev = torch.device(device)
         self.device = dev
         s = shape
@@ -74,6 +78,12 @@ class DecodeStep:
         self._step_fn = abi.lib().rtp_decode_step
 
     # -- the four calls -------------------------------------------------------------
+    def index_topk(self, t: Dict[str, torch.Tensor], stream=None) -> None:
+        s = self.s
+        abi.rtp_index_topk(t["q_pre"], t["w_q"], t["k_idx"], t["seq_lens"], t["ret_heads"], self.k_tokens,
+                           s.B, s.Hq, s.n_ret, s.max_ctx, s.block, self.sel_idx, self.sel_cnt, self.ws_index,
+                           stream, sel_mask=self.sel_mask)
+
     def index_topp(self, t: Dict[str, torch.Tensor], stream=None) -> None:
         s = self.s
         abi.rtp_index_topp(t["q_pre"], t["w_q"], t["k_idx"], t["seq_lens"], t["ret_heads"], t["top_p"],
@@ -109,7 +119,7 @@ class DecodeStep:
         return (z("q_pre") if s.n_ret else None, z("w_q") if s.n_ret else None, z("k_idx") if s.n_ret else None,
                 p(t["q"]), p(t["k_cache"]), p(t["v_cache"]), p(t["seq_lens"]),
                 z("ret_heads") if s.n_ret else None, z("loc_heads") if s.n_loc else None,
-                z("top_p") if s.n_ret else None, s.B, s.Hq, s.Hkv, s.n_ret, s.n_loc, s.max_ctx, s.block,
+                z("top_p") if s.n_ret else None, self.k_tokens, s.B, s.Hq, s.Hkv, s.n_ret, s.n_loc, s.max_ctx, s.block,
                 s.split_tokens, s.window, s.sinks, p(self.sel_idx), p(self.sel_cnt),
                 p(self.sel_mask) if self.sel_mask is not None else None, p(self.o_part), p(self.lse_part),
                 p(self.out), p(self.ws_index), abi.nbytes(self.ws_index), p(self.ws_local),

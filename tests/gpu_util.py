@@ -27,15 +27,16 @@ class Run:
     """One GPU decode step on a workload, with host copies of its outputs."""
 
     def __init__(self, inp: W.DecodeInputs, tensors=None, overlap: bool = True,
-                 split_tokens: Optional[int] = None, tag: str = "", use_mask: bool = True):
+                 split_tokens: Optional[int] = None, tag: str = "", use_mask: bool = True, k_tokens: int = 0):
         cfg = inp.cfg
         self.inp = inp
+        self.k_tokens = k_tokens
         say(f"[gpu] {tag or cfg.name}: B={cfg.B} Hq={cfg.Hq} Hkv={cfg.Hkv} n_ret={cfg.n_ret} "
             f"ctx={cfg.ctx[:4]}{'...' if len(cfg.ctx) > 4 else ''} block={cfg.block} "
             f"split={split_tokens or cfg.split_tokens} window={cfg.window} sinks={cfg.sinks} seed={cfg.seed} "
-            f"{'masks' if use_mask else 'lists'}")
+            f"{'masks' if use_mask else 'lists'}{f' top-k {k_tokens}' if k_tokens else ''}")
         self.t = tensors if tensors is not None else W.to_device(inp)
-        self.step = DecodeStep(shape_of(cfg, split_tokens), overlap=overlap, use_mask=use_mask)
+        self.step = DecodeStep(shape_of(cfg, split_tokens), overlap=overlap, use_mask=use_mask, k_tokens=k_tokens)
         self.out = self.step(self.t)
         torch.cuda.synchronize()
         self.out_h = self.out.cpu().numpy().astype(np.float64)
@@ -67,6 +68,27 @@ def check_selection(run: Run, pairs: Optional[Iterable[Tuple[int, int]]] = None)
         assert ok, f"selection {(b, r)} rejected: {why}"
         if not np.array_equal(G, sel.blocks):
             differ[(b, r)] = G
+    return differ
+
+
+def check_selection_topk(run: Run) -> Dict[Tuple[int, int], np.ndarray]:
+    """Static top-k acceptance on every (b, r); returns the GPU sets that differ from the
+    oracle's (ties at the threshold)."""
+    inp = run.inp
+    cfg = inp.cfg
+    differ = {}
+    for b in range(cfg.B):
+        for r in range(cfg.n_ret):
+            G = run.gpu_blocks(b, r)
+            nblk = -(-int(inp.seq_lens[b]) // cfg.block)
+            assert np.all(np.diff(G) > 0), f"sel_idx not strictly ascending for {(b, r)}"
+            assert G.size >= 1 and G[0] >= 0 and G[-1] < nblk
+            m = O.retrieval_masses(inp, b, r)
+            sel = O.select_top_k(m, run.k_tokens, cfg.block)
+            ok, why = A.accept_topk(m, run.k_tokens, cfg.block, G, sel)
+            assert ok, f"top-k selection {(b, r)} rejected: {why}"
+            if not np.array_equal(G, sel.blocks):
+                differ[(b, r)] = G
     return differ
 
 

@@ -59,6 +59,28 @@ def test_index_topp_rejects():
     assert _topp(n_ret=0) == abi.RTP_OK                 # no-op
 
 
+def _topk(k_tokens=4096, **kw):
+    a = dict(q_pre=FAKE, w_q=FAKE, k_idx=FAKE, seq_lens=FAKE, ret_heads=FAKE, B=1, Hq=4,
+             n_ret=2, max_ctx=1024, block=64, sel_idx=FAKE, sel_cnt=FAKE, sel_mask=None, ws=FAKE, ws_bytes=0)
+    a.update(kw)
+    if "ws_bytes" not in kw:
+        a["ws_bytes"] = abi.rtp_index_topp_workspace_size(a["B"], a["n_ret"], a["max_ctx"], a["block"]) - 1
+    return abi.lib().rtp_index_topk(a["q_pre"], a["w_q"], a["k_idx"], a["seq_lens"], a["ret_heads"], k_tokens,
+                                    a["B"], a["Hq"], a["n_ret"], a["max_ctx"], a["block"], a["sel_idx"],
+                                    a["sel_cnt"], a["sel_mask"], a["ws"], a["ws_bytes"], None)
+
+
+def test_index_topk_rejects():
+    assert _topk() == abi.RTP_EINVAL                    # workspace one byte short
+    assert _topk(k_tokens=0, ws_bytes=1 << 30) == abi.RTP_EINVAL
+    assert _topk(k_tokens=-5, ws_bytes=1 << 30) == abi.RTP_EINVAL
+    assert _topk(block=32, ws_bytes=1 << 30) == abi.RTP_EUNSUPPORTED
+    assert _topk(B=0, ws_bytes=1 << 30) == abi.RTP_EINVAL
+    assert _topk(q_pre=None, ws_bytes=1 << 30) == abi.RTP_EINVAL
+    assert _topk(k_idx=FAKE + 2, ws_bytes=1 << 30) == abi.RTP_EINVAL
+    assert _topk(n_ret=0) == abi.RTP_OK                 # no-op
+
+
 def _sparse(**kw):
     a = dict(B=1, Hq=8, Hkv=2, n_ret=2, max_ctx=4096, block=64, split=1024, sel_idx=FAKE, sel_cnt=FAKE,
              sel_mask=None)
@@ -101,14 +123,20 @@ def test_reduce_and_local_reject():
 
 def test_decode_step_rejects():
     L = abi.lib()
-    args = [FAKE] * 10 + [1, 8, 2, 2, 6, 4096, 64, 1024, 1024, 4] + [FAKE] * 6 + [FAKE, 1 << 30, FAKE, 1 << 30] + \
-        [None] * 4
+    args = [FAKE] * 10 + [0] + [1, 8, 2, 2, 6, 4096, 64, 1024, 1024, 4] + [FAKE] * 6 + \
+        [FAKE, 1 << 30, FAKE, 1 << 30] + [None] * 4
     bad = list(args)
-    bad[10] = 0                                        # B = 0
+    bad[11] = 0                                        # B = 0
     assert L.rtp_decode_step(*bad) == abi.RTP_EINVAL
     bad = list(args)
-    bad[13], bad[14] = 5, 6                            # more heads than query heads
+    bad[14], bad[15] = 5, 6                            # more heads than query heads
     assert L.rtp_decode_step(*bad) == abi.RTP_EINVAL
     bad = list(args)
-    bad[16] = 96                                       # block size outside {64, 128}
+    bad[17] = 96                                       # block size outside {64, 128}
     assert L.rtp_decode_step(*bad) == abi.RTP_EUNSUPPORTED
+    bad = list(args)
+    bad[10] = -1                                       # negative top-k budget
+    assert L.rtp_decode_step(*bad) == abi.RTP_EINVAL
+    bad = list(args)
+    bad[9] = None                                      # top-p rule without top_p
+    assert L.rtp_decode_step(*bad) == abi.RTP_EINVAL
