@@ -36,6 +36,10 @@ Readings taken where the pages are silent or garbled:
   usual softmax(q K^T / sqrt(128)) V over the selected tokens.
 * Retrieval heads attend to the selected tokens only (no forced sink/window).
 * Local heads: tokens [0, min(S, N)) union [max(0, N - W), N), no double count.
+* Cache append (the decode step before the path): the new token is the last of the
+  N_b tokens (row N_b - 1); its index key for retrieval head h is W^K_h k^pre of
+  the head's KV head, the exact dot products rounded once to bf16 (nearest, ties to
+  even); its K and V rows are stored as given.
 
 Parity of every function here is pinned by tests/test_oracle_pins.py (closed
 forms, brute force, library routines, hand-worked golden fixtures).
@@ -43,6 +47,8 @@ forms, brute force, library routines, hand-worked golden fixtures).
 from __future__ import annotations
 
 import dataclasses
+import math
+from fractions import Fraction
 from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
@@ -58,6 +64,47 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- index (Kernel 1)
+def bf16_round(x) -> int:
+    """bf16 bit pattern of the real number x (a float or an exact Fraction), rounded
+    once to nearest with ties to even: 8 significant bits, float32's exponent range,
+    subnormals (quantum 2^-133) below 2^-126, infinity beyond the largest finite value."""
+    if isinstance(x, float) and math.isnan(x):
+        return 0x7FC0
+    if isinstance(x, float) and math.isinf(x):
+        return (0x8000 if x < 0 else 0) | 0x7F80
+    neg = (x < 0) or (isinstance(x, float) and x == 0.0 and math.copysign(1.0, x) < 0)
+    sign = 0x8000 if neg else 0
+    a = abs(Fraction(x))
+    if a == 0:
+        return sign
+    e = a.numerator.bit_length() - a.denominator.bit_length()   # 2^e <= a < 2^(e+2)
+    if a < Fraction(2) ** e:
+        e -= 1
+    elif a >= Fraction(2) ** (e + 1):
+        e += 1                                                   # now 2^e <= a < 2^(e+1)
+    if e < -126:
+        return sign | round(a * Fraction(2) ** 133)              # 128 = the smallest normal
+    n = round(a * Fraction(2) ** (7 - e))                        # in [128, 256], ties to even
+    if n == 256:
+        n, e = 128, e + 1
+    if e + 127 >= 255:
+        return sign | 0x7F80
+    return sign | ((e + 127) << 7) | (n - 128)
+
+
+def index_key(w_k_h: np.ndarray, k_pre: np.ndarray) -> np.ndarray:
+    """k_idx = bf16(W^K_h k^pre): 16 dot products over 128 dims, each summed exactly
+    (rationals) and rounded once (Review, Adaptive sparse attention equation: the key
+    side of s_h(m, n)).  Returns uint16 bf16 bit patterns [16]."""
+    w = bf16_to_f64(w_k_h).reshape(INDEX_DIM, HEAD_DIM)
+    k = bf16_to_f64(k_pre).reshape(HEAD_DIM)
+    out = np.zeros(INDEX_DIM, dtype=np.uint16)
+    for i in range(INDEX_DIM):
+        exact = sum((Fraction(float(w[i, d])) * Fraction(float(k[d])) for d in range(HEAD_DIM)), Fraction(0))
+        out[i] = bf16_round(exact)
+    return out
+
+
 def index_query(w_q_h: np.ndarray, q_pre: np.ndarray) -> np.ndarray:
     """q_idx = W^Q_h q^pre  (Review, Adaptive sparse attention equation).
 

@@ -11,6 +11,7 @@ import test_oracle_pins as P
 
 _orig = {name: getattr(O, name) for name in
          ("block_masses", "token_softmax", "select_top_p", "select_top_k", "attend", "local_tokens",
+          "bf16_round", "index_key",
           "merge_partials", "index_query", "retrieval_head")}
 
 
@@ -61,6 +62,20 @@ def _topk_generic(m, k_tokens, block, tie_desc=False, floor_blocks=False):
     return O.Selection(blocks=np.sort(order[:k]), order=order, k_star=k, tau=float(m[order[k - 1]]),
                        c_prev=float(cs[k - 2]) if k > 1 else 0.0, c_star=float(cs[k - 1]),
                        all_blocks=k == n)
+
+
+def _bf16_truncate(x):
+    from fractions import Fraction
+    v = float(Fraction(x))
+    return int(np.float32(v).view(np.uint32) >> 16)
+
+
+def _index_key_drops_last_dim(w_k_h, k_pre):
+    from fractions import Fraction
+    w = O.bf16_to_f64(w_k_h).reshape(16, 128)
+    k = O.bf16_to_f64(k_pre).reshape(128)
+    return np.array([O.bf16_round(sum((Fraction(float(w[i, d])) * Fraction(float(k[d])) for d in range(127)),
+                                      Fraction(0))) for i in range(16)], dtype=np.uint16)
 
 
 def _attend_no_scale(q, K, V, tokens):
@@ -125,6 +140,8 @@ MUTANTS = [
     ("select_top_k", lambda m, k, b: _topk_generic(m, k, b, tie_desc=True), [P.check_topk_worked]),
     ("select_top_k", lambda m, k, b: _topk_generic(m, k, b, floor_blocks=True),
      [P.check_topk_worked, P.check_topk_bruteforce]),
+    ("bf16_round", _bf16_truncate, [P.check_bf16_round]),
+    ("index_key", _index_key_drops_last_dim, [P.check_index_key_vs_float64]),
     ("attend", _attend_no_scale, [P.check_attention_vs_sdpa]),
     ("attend", _attend_lost_value, [P.check_attention_vs_sdpa, P.check_attention_closed_forms]),
     ("local_tokens", _local_off_by_one, [P.check_local_tokens_worked]),

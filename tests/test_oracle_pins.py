@@ -209,6 +209,60 @@ def check_topk_matches_topp_prefix(trials=200, seed=12):
         assert sk.blocks.tolist() == sp.blocks.tolist()
 
 
+# ---------------------------------------------------- cache append (next row f2)
+def check_bf16_round():
+    """Against torch's float32 -> bfloat16 conversion (nearest-even) on float32 values,
+    and hand cases: ties to even, the subnormal range, overflow, signed zero."""
+    x = np.random.default_rng(21).standard_normal(5000).astype(np.float32) * np.float32(7.0)
+    x = np.concatenate([x, np.float32([1e-39, -3e-40, 1e-45, 3.3e38, -3.38e38, 1.17549435e-38])])
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
+    got = np.array([O.bf16_round(float(v)) for v in x], dtype=np.uint16)
+    assert np.array_equal(got, want)
+    assert O.bf16_round(1.0 + 2.0 ** -8) == 0x3F80          # tie -> even mantissa 0
+    assert O.bf16_round(1.0 + 3 * 2.0 ** -8) == 0x3F82      # tie -> even mantissa 2
+    assert O.bf16_round(-(1.0 + 2.0 ** -8 + 2.0 ** -40)) == 0xBF81   # above the tie
+    assert O.bf16_round(2.0 ** -130) == 0x0008              # subnormal: 8 quanta of 2^-133
+    assert O.bf16_round(2.0 ** -126 * (1 - 2.0 ** -20)) == 0x0080   # rounds up to the smallest normal
+    assert O.bf16_round(3.5e38) == 0x7F80 and O.bf16_round(-0.0) == 0x8000
+    # a tie carried only by a term far below float64 precision of the sum: exact input
+    from fractions import Fraction
+    assert O.bf16_round(Fraction(1) + Fraction(1, 256) + Fraction(1, 2 ** 90)) == 0x3F81
+
+
+def check_index_key_worked():
+    """Hand-worked: k_pre = (1, 1, 0, ...); row i of W^K = (1, (i + 1) 2^-8, 0, ...), so
+    key i = 1 + (i + 1) 2^-8, which bf16 (spacing 2^-7 at 1) rounds to 1 + 2 j 2^-8
+    with j the even neighbour at the odd (tied) values."""
+    def bits(v):
+        return np.float32(v).view(np.uint32) >> 16
+    k = np.zeros(128, np.uint16)
+    k[0] = k[1] = bits(1.0)
+    w = np.zeros((16, 128), np.uint16)
+    for i in range(16):
+        w[i, 0] = bits(1.0)
+        w[i, 1] = bits((i + 1) * 2.0 ** -8)
+    j = [0, 1, 2, 2, 2, 3, 4, 4, 4, 5, 6, 6, 6, 7, 8, 8]
+    assert O.index_key(w, k).tolist() == [0x3F80 + v for v in j]
+    # sign and scale: negating k negates every key; scaling k by 2 adds one to each exponent
+    assert (O.index_key(w, k ^ np.uint16(0x8000) * (k != 0)) == (O.index_key(w, k) | 0x8000)).all()
+    k2 = k.copy()
+    k2[:2] = bits(2.0)
+    assert (O.index_key(w, k2) == O.index_key(w, k) + 0x80).all()
+
+
+def check_index_key_vs_float64():
+    """On random bf16 inputs whose products span well under 53 bits, the exact sum equals
+    the float64 sum, so the key equals torch's rounding of the float64 matvec (through
+    float32 only where that cannot double-round: checked against the exact rounding)."""
+    g = np.random.default_rng(22)
+    w = (np.float32(g.standard_normal((16, 128)) / np.sqrt(128)).view(np.uint32) >> 16).astype(np.uint16)
+    k = (np.float32(g.standard_normal(128)).view(np.uint32) >> 16).astype(np.uint16)
+    wf = O.bf16_to_f64(w)
+    kf = O.bf16_to_f64(k)
+    ref = [O.bf16_round(float(np.dot(wf[i], kf))) for i in range(16)]
+    assert O.index_key(w, k).tolist() == ref
+
+
 # ------------------------------------------------------------ attention (a6-a8)
 def _sdpa(q, K, V):
     qt = torch.from_numpy(O.bf16_to_f64(q))[None, None, None, :]
@@ -344,6 +398,7 @@ def check_acceptance_rule():
 CHECKS = [check_index_worked, check_block_mass_worked, check_tie_break_worked, check_mass_vs_library,
           check_selection_bruteforce, check_p_one_selects_all, check_dominant_needle,
           check_topk_worked, check_topk_bruteforce, check_topk_matches_topp_prefix,
+          check_bf16_round, check_index_key_worked, check_index_key_vs_float64,
           check_attention_vs_sdpa, check_attention_closed_forms, check_merge_is_union,
           check_local_tokens_worked, check_local_reduces_to_dense, check_p_one_is_dense,
           check_gqa_mapping, check_acceptance_rule]
