@@ -225,6 +225,26 @@ def measure(label: str, steps: int, warmup: int, cold_iters: int, calib_copy: bo
         cold.append(a.elapsed_time(b_) * 1e3)
     del flush
 
+    # the decode-side cache append before the step (not part of the step): the last
+    # token's K/V rows and index keys rewritten from the token itself
+    from long_context_sparse_amd import abi
+    lens = [int(n) for n in inp.seq_lens]
+    k_new = torch.stack([t["k_cache"][b, :, n - 1] for b, n in enumerate(lens)]).contiguous()
+    v_new = torch.stack([t["v_cache"][b, :, n - 1] for b, n in enumerate(lens)]).contiguous()
+    w_k = torch.from_numpy(np.ascontiguousarray(inp.w_k)).view(torch.bfloat16).to(dev) if cfg.n_ret else None
+    append = lambda: abi.rtp_cache_append(k_new, v_new, k_new, w_k, t["seq_lens"], t["ret_heads"], cfg.B,  # noqa
+                                          cfg.Hq, cfg.Hkv, cfg.n_ret, cfg.max_ctx, t["k_cache"], t["v_cache"],
+                                          t["k_idx"], main)
+    for _ in range(5):
+        append()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(main)
+    for _ in range(50):
+        append()
+    a1.record(main)
+    torch.cuda.synchronize()
+    append_us = a0.elapsed_time(a1) * 1e3 / 50
+
     if calib_copy:
         # plain device copy of known size, for scaling HBM counters (1 GiB read + 1 GiB written)
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -238,7 +258,7 @@ def measure(label: str, steps: int, warmup: int, cold_iters: int, calib_copy: bo
     dom = max(kern_us, key=kern_us.get)
     res = dict(
         workload=name, label=label, k_tokens=k_tokens, cfg=cfg, inp=inp, alg=alg, latency_us=lat_us, wall_us=wall * 1e6 / steps,
-        kern_us=kern_us, dominant=dom, cold_us=float(np.median(cold)) if cold else None,
+        kern_us=kern_us, dominant=dom, append_us=append_us, cold_us=float(np.median(cold)) if cold else None,
         gbs=alg["step"] / (lat_us * 1e-6) / 1e9,
         sel_frac=float(np.mean([sel_cnt[b, r] / -(-int(inp.seq_lens[b]) // cfg.block)
                                 for b in range(cfg.B) for r in range(cfg.n_ret)])) if cfg.n_ret else 0.0,
@@ -326,6 +346,7 @@ def main(argv: Optional[List[str]] = None) -> int:
                 "cold_latency_us": None if r["cold_us"] is None else round(r["cold_us"], 2),
                 "cold_effective_gbs": None if not r["cold_us"] else round(r["alg"]["step"] / r["cold_us"] / 1e3, 1),
                 "call_us": {CALL_NAMES[k]: round(v, 2) for k, v in r["kern_us"].items()},
+                "cache_append_us": round(r["append_us"], 2),
                 "mean_selected_block_fraction": round(r["sel_frac"], 4),
                 "roofline": roofline_of(r), "config": config_of(r["cfg"], r["k_tokens"])}
 

@@ -202,6 +202,29 @@ rtp_status rtp_local_window_attn(const void* q, const void* k_cache, const void*
                                  void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Decode-side cache maintenance, the step before the path: stores the decode token of
+ * every sequence b at row pos = seq_lens[b] - 1 (the token is the last of the N_b tokens
+ * the step attends to) (Review, Adaptive sparse attention equation, the key side of
+ * s_h(m, n); Review, Method overview: retrieval heads keep the full KV cache):
+ *   k_cache[b, g, pos] = k_new[b, g],  v_cache[b, g, pos] = v_new[b, g]   for every KV head g
+ *   k_idx[b, r, pos, i] = bf16(sum_d W^K[r, i, d] k_pre[b, g_r, d])        for every retrieval
+ *       head r (g_r = ret_heads[r] / (Hq / Hkv)) and i < 16, rounded once to nearest-even
+ *       (the products are exact and summed in fp64)
+ *
+ *   k_new, v_new  bf16 [B, Hkv, 128]   the token's key (as the attention reads it) and value
+ *   k_pre         bf16 [B, Hkv, 128]   the token's pre-RoPE key (the index projection's input)
+ *   w_k           bf16 [n_ret, 16, 128] W^K of each retrieval head
+ *   seq_lens      int32 [B]            N_b including the token, 1 <= N_b <= max_ctx
+ *   k_cache, v_cache, k_idx            the caches of rtp_index_topp / rtp_sparse_attn_split;
+ *                                      only row pos of each is written
+ * k_pre, w_k, ret_heads and k_idx may be NULL when n_ret == 0.  Device pointers 16-byte
+ * aligned (k_idx 2-byte).
+ */
+rtp_status rtp_cache_append(const void* k_new, const void* v_new, const void* k_pre, const void* w_k,
+                            const int* seq_lens, const int* ret_heads, int B, int Hq, int Hkv, int n_ret,
+                            int max_ctx, void* k_cache, void* v_cache, void* k_idx, void* stream);
+
+/*
  * One decode step in one host call: the four calls above, enqueued in their order for
  * the same arguments (Strikes-Back architecture paragraph: Kernel 1, Kernel 2 and the
  * reduce; Review, Adaptive sparse attention: local heads).  rtp_local_window_attn goes to

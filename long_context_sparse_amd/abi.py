@@ -41,6 +41,7 @@ _SIGS = {
     "rtp_local_window_workspace_size": ([_i] * 7, _sz),
     "rtp_local_window_attn": ([_vp] * 5 + [_i] * 7 + [_vp, _vp, _sz, _vp], _i),
     "rtp_decode_step": ([_vp] * 10 + [_i] * 11 + [_vp] * 6 + [_vp, _sz, _vp, _sz] + [_vp] * 4, _i),
+    "rtp_cache_append": ([_vp] * 6 + [_i] * 5 + [_vp] * 4, _i),
 }
 
 
@@ -180,6 +181,13 @@ def rtp_sparse_attn_split(q, k_cache, v_cache, seq_lens, ret_heads, sel_idx, sel
                                      _p(sel_idx), _p(sel_cnt), _p(sel_mask), B, Hq, Hkv, n_ret, max_ctx, block,
                                      split_tokens, _p(o_part), _p(lse_part), _s(stream))
     _check("rtp_sparse_attn_split", st)
+
+
+def rtp_cache_append(k_new, v_new, k_pre, w_k, seq_lens, ret_heads, B, Hq, Hkv, n_ret, max_ctx,
+                     k_cache, v_cache, k_idx, stream=None) -> None:
+    st = lib().rtp_cache_append(_p(k_new), _p(v_new), _p(k_pre), _p(w_k), _p(seq_lens), _p(ret_heads), B, Hq,
+                                Hkv, n_ret, max_ctx, _p(k_cache), _p(v_cache), _p(k_idx), _s(stream))
+    _check("rtp_cache_append", st)
 
 
 def rtp_split_reduce(o_part, lse_part, heads, B, Hq, n_heads, n_split, out, stream=None) -> None:

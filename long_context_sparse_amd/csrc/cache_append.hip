@@ -1,0 +1,115 @@
+// Decode-side cache maintenance, the step before the path: the decode token's K and V
+// rows go into the caches and its low-rank index key k_idx = W^K_h k^pre of every
+// retrieval head h into the index-key cache (Review, Adaptive sparse attention
+// equation, the key side of s_h(m, n); Review, Method overview: retrieval heads keep
+// the full KV cache).  The token is the last of the sequence's N_b tokens (row N_b - 1).
+//
+// gfx950 launch: one 256-thread workgroup per sequence.  The K/V rows are 16-byte
+// copies; each index key is 16 lanes x 8 dims of bf16 products summed in fp64 (the
+// products are exact, the sum carries < 2^-50 relative error) and rounded once to
+// bf16, nearest-even.
+
+#include "rtp_common.hpp"
+
+namespace rtp {
+namespace {
+
+constexpr int kAppendThreads = 256;
+
+struct AppendArgs {
+  const uint4* k_new;  // bf16 [B, Hkv, 128]
+  const uint4* v_new;  // bf16 [B, Hkv, 128]
+  const uint16_t* k_pre;  // bf16 [B, Hkv, 128]
+  const uint16_t* w_k;    // bf16 [n_ret, 16, 128]
+  const int* seq_lens;
+  const int* ret_heads;
+  int Hq, Hkv, n_ret, max_ctx;
+  uint4* kc;           // bf16 [B, Hkv, max_ctx, 128]
+  uint4* vc;
+  uint16_t* kidx;      // bf16 [B, n_ret, max_ctx, 16]
+};
+
+// bf16 bit pattern of a double rounded once to nearest, ties to even: 8 significant
+// bits, float32's exponent range, subnormals (quantum 2^-133) below 2^-126, infinity
+// on overflow.
+__device__ __forceinline__ uint32_t bf16_rne(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const uint32_t sign = (uint32_t)(u >> 48) & 0x8000u;
+  const int e = (int)((u >> 52) & 0x7FF);
+  const uint64_t mant = u & ((1ull << 52) - 1ull);
+  if (e == 0x7FF) return sign | 0x7F80u | (mant ? 0x40u : 0u);
+  if (e == 0) return sign;                 // float64 subnormals: far below bf16's range
+  const int eb = e - 1023 + 127;           // bf16 biased exponent of 1.m x 2^(e - 1023)
+  const int s = eb > 0 ? 45 : 46 - eb;     // significant bits dropped (more when subnormal)
+  if (s > 63) return sign;
+  const uint64_t sig = (1ull << 52) | mant;
+  uint32_t q = (uint32_t)(sig >> s);
+  const uint64_t rem = sig & ((1ull << s) - 1ull), half = 1ull << (s - 1);
+  if (rem > half || (rem == half && (q & 1u))) ++q;
+  if (eb <= 0) return sign | q;            // q == 128 is the smallest normal's pattern
+  int ebb = eb;
+  if (q == 256u) {
+    q = 128u;
+    ++ebb;
+  }
+  if (ebb >= 255) return sign | 0x7F80u;
+  return sign | ((uint32_t)ebb << 7) | (q - 128u);
+}
+
+__global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int pos = a.seq_lens[b] - 1;
+  // K and V rows: 16 loads of 16 bytes each per KV head
+  for (int i = tid; i < a.Hkv * 32; i += kAppendThreads) {
+    const int g = i >> 5, part = i & 31, c = part & 15;
+    const size_t row = (size_t)b * a.Hkv + g;
+    const uint4 v = (part < 16 ? a.k_new : a.v_new)[row * 16 + c];
+    (part < 16 ? a.kc : a.vc)[(row * a.max_ctx + pos) * 16 + c] = v;
+  }
+  // index keys: 16 lanes per (retrieval head, key dim); every pass of the workgroup
+  // takes 16 of them, so all lanes of a wave run the same number of passes
+  const int G = a.Hq / a.Hkv, part = tid & 15;
+  for (int w = tid >> 4; w < a.n_ret * kIndexDim; w += kAppendThreads / 16) {
+    const int r = w >> 4, i = w & 15;
+    const int kv = a.ret_heads[r] / G;
+    const uint4 wv = ld16(a.w_k + ((size_t)r * kIndexDim + i) * kHeadDim + part * 8);
+    const uint4 kq = ld16(a.k_pre + ((size_t)b * a.Hkv + kv) * kHeadDim + part * 8);
+    double x = (double)bf_lo(wv.x) * (double)bf_lo(kq.x);
+    x = fma((double)bf_hi(wv.x), (double)bf_hi(kq.x), x);
+    x = fma((double)bf_lo(wv.y), (double)bf_lo(kq.y), x);
+    x = fma((double)bf_hi(wv.y), (double)bf_hi(kq.y), x);
+    x = fma((double)bf_lo(wv.z), (double)bf_lo(kq.z), x);
+    x = fma((double)bf_hi(wv.z), (double)bf_hi(kq.z), x);
+    x = fma((double)bf_lo(wv.w), (double)bf_lo(kq.w), x);
+    x = fma((double)bf_hi(wv.w), (double)bf_hi(kq.w), x);
+    // sum over the 16 lanes of this (head, dim): DPP moves inside the 16-lane row
+    x += dpp_f64<kDppXor1>(x);
+    x += dpp_f64<kDppXor2>(x);
+    x += dpp_f64<kDppHalfMirror>(x);
+    x += dpp_f64<kDppMirror>(x);
+    if (part == 0) a.kidx[(((size_t)b * a.n_ret + r) * a.max_ctx + pos) * kIndexDim + i] = (uint16_t)bf16_rne(x);
+  }
+}
+
+}  // namespace
+}  // namespace rtp
+
+using namespace rtp;
+
+extern "C" rtp_status rtp_cache_append(const void* k_new, const void* v_new, const void* k_pre, const void* w_k,
+                                       const int* seq_lens, const int* ret_heads, int B, int Hq, int Hkv, int n_ret,
+                                       int max_ctx, void* k_cache, void* v_cache, void* k_idx, void* stream) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || n_ret < 0 || n_ret > Hq || max_ctx <= 0) return RTP_EINVAL;
+  if (Hq % Hkv) return RTP_EINVAL;
+  if (!k_new || !v_new || !seq_lens || !k_cache || !v_cache) return RTP_EINVAL;
+  if (n_ret > 0 && (!k_pre || !w_k || !ret_heads || !k_idx)) return RTP_EINVAL;
+  if (((uintptr_t)k_new | (uintptr_t)v_new | (uintptr_t)k_cache | (uintptr_t)v_cache) & 15) return RTP_EINVAL;
+  if (n_ret > 0 && (((uintptr_t)k_pre | (uintptr_t)w_k) & 15)) return RTP_EINVAL;
+  if ((uintptr_t)k_idx & 1) return RTP_EINVAL;
+  const AppendArgs a{static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new),
+                     static_cast<const uint16_t*>(k_pre), static_cast<const uint16_t*>(w_k), seq_lens, ret_heads,
+                     Hq, Hkv, n_ret, max_ctx, static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache),
+                     static_cast<uint16_t*>(k_idx)};
+  hipLaunchKernelGGL(append_kernel, dim3(B), dim3(kAppendThreads), 0, static_cast<hipStream_t>(stream), a);
+  return hipGetLastError() == hipSuccess ? RTP_OK : RTP_ELAUNCH;
+}

@@ -121,6 +121,22 @@ def test_reduce_and_local_reject():
                                    0, None) == abi.RTP_OK
 
 
+def test_cache_append_rejects():
+    L = abi.lib()
+
+    def call(B=2, Hq=8, Hkv=2, n_ret=2, max_ctx=256, k_new=FAKE, k_pre=FAKE, k_idx=FAKE):
+        return L.rtp_cache_append(k_new, FAKE, k_pre, FAKE, FAKE, FAKE, B, Hq, Hkv, n_ret, max_ctx,
+                                  FAKE, FAKE, k_idx, None)
+    assert call(B=0) == abi.RTP_EINVAL
+    assert call(Hkv=3) == abi.RTP_EINVAL                 # heads not divisible
+    assert call(n_ret=9) == abi.RTP_EINVAL               # more retrieval heads than heads
+    assert call(max_ctx=0) == abi.RTP_EINVAL
+    assert call(k_new=None) == abi.RTP_EINVAL
+    assert call(k_pre=None) == abi.RTP_EINVAL            # needed for the index keys
+    assert call(k_new=FAKE + 8) == abi.RTP_EINVAL        # misaligned
+    assert call(k_idx=FAKE + 1) == abi.RTP_EINVAL
+
+
 def test_decode_step_rejects():
     L = abi.lib()
     args = [FAKE] * 10 + [0] + [1, 8, 2, 2, 6, 4096, 64, 1024, 1024, 4] + [FAKE] * 6 + \
