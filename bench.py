@@ -234,7 +234,8 @@ def measure(label: str, steps: int, warmup: int, cold_iters: int, calib_copy: bo
     w_k = torch.from_numpy(np.ascontiguousarray(inp.w_k)).view(torch.bfloat16).to(dev) if cfg.n_ret else None
     append = lambda: abi.rtp_cache_append(k_new, v_new, k_new, w_k, t["seq_lens"], t["ret_heads"], cfg.B,  # noqa
                                           cfg.Hq, cfg.Hkv, cfg.n_ret, cfg.max_ctx, t["k_cache"], t["v_cache"],
-                                          t["k_idx"], main)
+                                          t["k_idx"], main, sinks=cfg.sinks, window=cfg.window,
+                                          **DecodeStep.placement(t))
     for _ in range(5):
         append()
     a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -127,6 +127,22 @@ rtp_status rtp_index_topk(const void* q_pre, const void* w_q, const void* k_idx,
                           void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * KV placement (Review, Method overview: only the retrieval heads need the full KV cache;
+ * the other heads safely drop remote tokens).  With kv_slot (int32 [Hkv], device) the
+ * KV groups live in two places:
+ *   kv_slot[g] = s >= 0   full caches k_cache, v_cache  bf16 [B, n_full, max_ctx, 128],
+ *                         group index s, position p at row p;
+ *   kv_slot[g] = -1 - s   sink + window rings k_ring, v_ring  bf16 [B, n_ring, sinks + window,
+ *                         128], group index s: position p < sinks at row p, a later position at
+ *                         row sinks + (p - sinks) mod window (the last `window` positions are
+ *                         kept; with window 0 nothing past the sinks).
+ * The rings suit KV groups whose query heads are all local: their attention reads
+ * exactly the sinks and the window.  n_full + n_ring <= Hkv (else RTP_EINVAL).  Slots
+ * must be distinct and in range (device values, not checked).  kv_slot NULL: every group
+ * is in the full caches at its own index.
+ */
+
+/*
  * Kernel 2: block-sparse exact attention over the selected blocks, split along the
  * context (Strikes-Back method item 2, O_h(m) with the value vector; architecture
  * paragraph, Kernel 2 at D128).
@@ -151,12 +167,16 @@ rtp_status rtp_index_topk(const void* q_pre, const void* w_q, const void* k_idx,
  *   split_tokens  multiple of block; split_tokens / block <= 2048
  *   o_part     out fp32 [B, n_ret, n_split, 128], n_split = ceil(max_ctx / split_tokens)
  *   lse_part   out fp32 [B, n_ret, n_split]
+ *   kv_slot, n_full  KV placement (see "KV placement" below); NULL: k_cache and v_cache
+ *              hold every KV head ([B, Hkv, max_ctx, 128]).  A KV group with retrieval heads
+ *              must be in the full caches (kv_slot[g] >= 0).
  */
 rtp_status rtp_sparse_attn_split(const void* q, const void* k_cache, const void* v_cache,
                                  const int* seq_lens, const int* ret_heads,
                                  const int* sel_idx, const int* sel_cnt, const unsigned char* sel_mask,
                                  int B, int Hq, int Hkv, int n_ret, int max_ctx, int block,
-                                 int split_tokens, float* o_part, float* lse_part, void* stream);
+                                 int split_tokens, float* o_part, float* lse_part,
+                                 const int* kv_slot, int n_full, void* stream);
 
 /*
  * Cross-split log-sum-exp reduce (Strikes-Back architecture paragraph):
@@ -194,12 +214,16 @@ size_t rtp_local_window_workspace_size(int B, int Hq, int Hkv, int n_loc, int ma
  *   workspace >= rtp_local_window_workspace_size(B, Hq, Hkv, n_loc, max_ctx, window, sinks)
  *             bytes,
  *             zero-filled before first use
+ *   kv_slot, n_full, k_ring, v_ring, n_ring  KV placement (above); NULL kv_slot: every group
+ *             in k_cache / v_cache ([B, Hkv, max_ctx, 128]).  A ring group attends to its
+ *             rows [0, min(N, sinks + window)): the same token set T.
  */
 rtp_status rtp_local_window_attn(const void* q, const void* k_cache, const void* v_cache,
                                  const int* seq_lens, const int* loc_heads,
                                  int B, int Hq, int Hkv, int n_loc, int max_ctx,
                                  int window, int sinks, float* out,
-                                 void* workspace, size_t ws_bytes, void* stream);
+                                 void* workspace, size_t ws_bytes, const int* kv_slot, int n_full,
+                                 const void* k_ring, const void* v_ring, int n_ring, void* stream);
 
 /*
  * Decode-side cache maintenance, the step before the path: stores the decode token of
@@ -217,12 +241,17 @@ rtp_status rtp_local_window_attn(const void* q, const void* k_cache, const void*
  *   seq_lens      int32 [B]            N_b including the token, 1 <= N_b <= max_ctx
  *   k_cache, v_cache, k_idx            the caches of rtp_index_topp / rtp_sparse_attn_split;
  *                                      only row pos of each is written
+ *   kv_slot, n_full, k_ring, v_ring, n_ring, sinks, window  KV placement (above): a ring
+ *                                      group's token goes to its ring row; NULL kv_slot: every
+ *                                      group in k_cache / v_cache ([B, Hkv, max_ctx, 128])
  * k_pre, w_k, ret_heads and k_idx may be NULL when n_ret == 0.  Device pointers 16-byte
  * aligned (k_idx 2-byte).
  */
 rtp_status rtp_cache_append(const void* k_new, const void* v_new, const void* k_pre, const void* w_k,
                             const int* seq_lens, const int* ret_heads, int B, int Hq, int Hkv, int n_ret,
-                            int max_ctx, void* k_cache, void* v_cache, void* k_idx, void* stream);
+                            int max_ctx, void* k_cache, void* v_cache, void* k_idx, const int* kv_slot,
+                            int n_full, void* k_ring, void* v_ring, int n_ring, int sinks, int window,
+                            void* stream);
 
 /*
  * One decode step in one host call: the four calls above, enqueued in their order for
@@ -241,6 +270,8 @@ rtp_status rtp_cache_append(const void* k_new, const void* v_new, const void* k_
  *   o_part, lse_part   split partials as in rtp_sparse_attn_split (n_split =
  *                      ceil(max_ctx / split_tokens))
  *   ws_index           workspace of rtp_index_topp; ws_local of rtp_local_window_attn
+ *   kv_slot, n_full, k_ring, v_ring, n_ring   KV placement (above), passed to the split
+ *                      attention and the local heads' call
  *   every other argument as in the four calls
  */
 rtp_status rtp_decode_step(const void* q_pre, const void* w_q, const void* k_idx, const void* q,
@@ -251,6 +282,7 @@ rtp_status rtp_decode_step(const void* q_pre, const void* w_q, const void* k_idx
                            int* sel_idx, int* sel_cnt, unsigned char* sel_mask,
                            float* o_part, float* lse_part, float* out,
                            void* ws_index, size_t ws_index_bytes, void* ws_local, size_t ws_local_bytes,
+                           const int* kv_slot, int n_full, const void* k_ring, const void* v_ring, int n_ring,
                            void* stream, void* side_stream, void* ev_fork, void* ev_join);
 
 #ifdef __cplusplus

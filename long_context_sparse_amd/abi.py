@@ -36,12 +36,13 @@ _SIGS = {
     "rtp_index_topp_workspace_size": ([_i, _i, _i, _i], _sz),
     "rtp_index_topp": ([_vp] * 6 + [_i] * 5 + [_vp, _vp, _vp, _vp, _sz, _vp], _i),
     "rtp_index_topk": ([_vp] * 5 + [_i] * 6 + [_vp, _vp, _vp, _vp, _sz, _vp], _i),
-    "rtp_sparse_attn_split": ([_vp] * 8 + [_i] * 7 + [_vp, _vp, _vp], _i),
+    "rtp_sparse_attn_split": ([_vp] * 8 + [_i] * 7 + [_vp, _vp, _vp, _i, _vp], _i),
     "rtp_split_reduce": ([_vp] * 3 + [_i] * 4 + [_vp, _vp], _i),
     "rtp_local_window_workspace_size": ([_i] * 7, _sz),
-    "rtp_local_window_attn": ([_vp] * 5 + [_i] * 7 + [_vp, _vp, _sz, _vp], _i),
-    "rtp_decode_step": ([_vp] * 10 + [_i] * 11 + [_vp] * 6 + [_vp, _sz, _vp, _sz] + [_vp] * 4, _i),
-    "rtp_cache_append": ([_vp] * 6 + [_i] * 5 + [_vp] * 4, _i),
+    "rtp_local_window_attn": ([_vp] * 5 + [_i] * 7 + [_vp, _vp, _sz, _vp, _i, _vp, _vp, _i, _vp], _i),
+    "rtp_decode_step": ([_vp] * 10 + [_i] * 11 + [_vp] * 6 + [_vp, _sz, _vp, _sz] + [_vp, _i, _vp, _vp, _i]
+                        + [_vp] * 4, _i),
+    "rtp_cache_append": ([_vp] * 6 + [_i] * 5 + [_vp] * 3 + [_vp, _i, _vp, _vp, _i, _i, _i, _vp], _i),
 }
 
 
@@ -176,17 +177,20 @@ def rtp_index_topk(q_pre, w_q, k_idx, seq_lens, ret_heads, k_tokens, B, Hq, n_re
 
 
 def rtp_sparse_attn_split(q, k_cache, v_cache, seq_lens, ret_heads, sel_idx, sel_cnt, B, Hq, Hkv,
-                          n_ret, max_ctx, block, split_tokens, o_part, lse_part, stream=None, sel_mask=None) -> None:
+                          n_ret, max_ctx, block, split_tokens, o_part, lse_part, stream=None, sel_mask=None,
+                          kv_slot=None, n_full=0) -> None:
     st = lib().rtp_sparse_attn_split(_p(q), _p(k_cache), _p(v_cache), _p(seq_lens), _p(ret_heads),
                                      _p(sel_idx), _p(sel_cnt), _p(sel_mask), B, Hq, Hkv, n_ret, max_ctx, block,
-                                     split_tokens, _p(o_part), _p(lse_part), _s(stream))
+                                     split_tokens, _p(o_part), _p(lse_part), _p(kv_slot), n_full, _s(stream))
     _check("rtp_sparse_attn_split", st)
 
 
 def rtp_cache_append(k_new, v_new, k_pre, w_k, seq_lens, ret_heads, B, Hq, Hkv, n_ret, max_ctx,
-                     k_cache, v_cache, k_idx, stream=None) -> None:
+                     k_cache, v_cache, k_idx, stream=None, kv_slot=None, n_full=0, k_ring=None, v_ring=None,
+                     n_ring=0, sinks=0, window=0) -> None:
     st = lib().rtp_cache_append(_p(k_new), _p(v_new), _p(k_pre), _p(w_k), _p(seq_lens), _p(ret_heads), B, Hq,
-                                Hkv, n_ret, max_ctx, _p(k_cache), _p(v_cache), _p(k_idx), _s(stream))
+                                Hkv, n_ret, max_ctx, _p(k_cache), _p(v_cache), _p(k_idx), _p(kv_slot), n_full,
+                                _p(k_ring), _p(v_ring), n_ring, sinks, window, _s(stream))
     _check("rtp_cache_append", st)
 
 
@@ -197,8 +201,10 @@ def rtp_split_reduce(o_part, lse_part, heads, B, Hq, n_heads, n_split, out, stre
 
 
 def rtp_local_window_attn(q, k_cache, v_cache, seq_lens, loc_heads, B, Hq, Hkv, n_loc, max_ctx,
-                          window, sinks, out, workspace, stream=None) -> None:
+                          window, sinks, out, workspace, stream=None, kv_slot=None, n_full=0, k_ring=None,
+                          v_ring=None, n_ring=0) -> None:
     st = lib().rtp_local_window_attn(_p(q), _p(k_cache), _p(v_cache), _p(seq_lens), _p(loc_heads), B, Hq,
                                      Hkv, n_loc, max_ctx, window, sinks, _p(out), _p(workspace),
-                                     _nbytes(workspace), _s(stream))
+                                     _nbytes(workspace), _p(kv_slot), n_full, _p(k_ring), _p(v_ring), n_ring,
+                                     _s(stream))
     _check("rtp_local_window_attn", st)

@@ -24,9 +24,18 @@ struct AppendArgs {
   const int* seq_lens;
   const int* ret_heads;
   int Hq, Hkv, n_ret, max_ctx;
-  uint4* kc;           // bf16 [B, Hkv, max_ctx, 128]
+  uint4* kc;           // bf16 [B, n_full, max_ctx, 128]
   uint4* vc;
   uint16_t* kidx;      // bf16 [B, n_ret, max_ctx, 16]
+  // KV placement (as the local heads' call reads it): kv_slot[g] >= 0: group g in kc/vc
+  // at index kv_slot[g]; < 0: in the sink + window ring kr/vr at index -1 - kv_slot[g]
+  // ([B, n_ring, sinks + window, 128]), position p at row p (p < sinks) or
+  // sinks + (p - sinks) mod window (a position past the sinks with window 0 is dropped).
+  // Null: identity.
+  const int* kv_slot;
+  uint4* kr;
+  uint4* vr;
+  int n_full, n_ring, sinks, window;
 };
 
 // bf16 bit pattern of a double rounded once to nearest, ties to even: 8 significant
@@ -62,9 +71,15 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   // K and V rows: 16 loads of 16 bytes each per KV head
   for (int i = tid; i < a.Hkv * 32; i += kAppendThreads) {
     const int g = i >> 5, part = i & 31, c = part & 15;
-    const size_t row = (size_t)b * a.Hkv + g;
-    const uint4 v = (part < 16 ? a.k_new : a.v_new)[row * 16 + c];
-    (part < 16 ? a.kc : a.vc)[(row * a.max_ctx + pos) * 16 + c] = v;
+    const uint4 v = (part < 16 ? a.k_new : a.v_new)[((size_t)b * a.Hkv + g) * 16 + c];
+    const int slot = a.kv_slot ? a.kv_slot[g] : g;
+    if (slot >= 0) {
+      (part < 16 ? a.kc : a.vc)[(((size_t)b * a.n_full + slot) * a.max_ctx + pos) * 16 + c] = v;
+    } else {
+      const int row = pos < a.sinks ? pos : (a.window > 0 ? a.sinks + (pos - a.sinks) % a.window : -1);
+      if (row >= 0)
+        (part < 16 ? a.kr : a.vr)[(((size_t)b * a.n_ring + (-1 - slot)) * (a.sinks + a.window) + row) * 16 + c] = v;
+    }
   }
   // index keys: 16 lanes per (retrieval head, key dim); every pass of the workgroup
   // takes 16 of them, so all lanes of a wave run the same number of passes
@@ -98,10 +113,22 @@ using namespace rtp;
 
 extern "C" rtp_status rtp_cache_append(const void* k_new, const void* v_new, const void* k_pre, const void* w_k,
                                        const int* seq_lens, const int* ret_heads, int B, int Hq, int Hkv, int n_ret,
-                                       int max_ctx, void* k_cache, void* v_cache, void* k_idx, void* stream) {
+                                       int max_ctx, void* k_cache, void* v_cache, void* k_idx, const int* kv_slot,
+                                       int n_full, void* k_ring, void* v_ring, int n_ring, int sinks, int window,
+                                       void* stream) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || n_ret < 0 || n_ret > Hq || max_ctx <= 0) return RTP_EINVAL;
   if (Hq % Hkv) return RTP_EINVAL;
-  if (!k_new || !v_new || !seq_lens || !k_cache || !v_cache) return RTP_EINVAL;
+  if (!k_new || !v_new || !seq_lens) return RTP_EINVAL;
+  if (kv_slot) {
+    if (n_full < 0 || n_full > Hkv || n_ring < 0 || n_ring > Hkv || n_full + n_ring < 1 ||
+        n_full + n_ring > Hkv)
+      return RTP_EINVAL;
+    if (n_full > 0 && (!k_cache || !v_cache)) return RTP_EINVAL;
+    if (n_ring > 0 && (!k_ring || !v_ring || sinks < 0 || window < 0 || sinks + window < 1)) return RTP_EINVAL;
+    if (((uintptr_t)k_ring | (uintptr_t)v_ring) & 15) return RTP_EINVAL;
+  } else if (!k_cache || !v_cache) {
+    return RTP_EINVAL;
+  }
   if (n_ret > 0 && (!k_pre || !w_k || !ret_heads || !k_idx)) return RTP_EINVAL;
   if (((uintptr_t)k_new | (uintptr_t)v_new | (uintptr_t)k_cache | (uintptr_t)v_cache) & 15) return RTP_EINVAL;
   if (n_ret > 0 && (((uintptr_t)k_pre | (uintptr_t)w_k) & 15)) return RTP_EINVAL;
@@ -109,7 +136,8 @@ extern "C" rtp_status rtp_cache_append(const void* k_new, const void* v_new, con
   const AppendArgs a{static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new),
                      static_cast<const uint16_t*>(k_pre), static_cast<const uint16_t*>(w_k), seq_lens, ret_heads,
                      Hq, Hkv, n_ret, max_ctx, static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache),
-                     static_cast<uint16_t*>(k_idx)};
+                     static_cast<uint16_t*>(k_idx), kv_slot, static_cast<uint4*>(k_ring), static_cast<uint4*>(v_ring),
+                     kv_slot ? n_full : Hkv, kv_slot ? n_ring : 0, sinks, window};
   hipLaunchKernelGGL(append_kernel, dim3(B), dim3(kAppendThreads), 0, static_cast<hipStream_t>(stream), a);
   return hipGetLastError() == hipSuccess ? RTP_OK : RTP_ELAUNCH;
 }

@@ -11,15 +11,26 @@ extern "C" rtp_status rtp_decode_step(
     const void* v_cache, const int* seq_lens, const int* ret_heads, const int* loc_heads, const float* top_p,
     int k_tokens, int B, int Hq, int Hkv, int n_ret, int n_loc, int max_ctx, int block, int split_tokens, int window,
     int sinks, int* sel_idx, int* sel_cnt, unsigned char* sel_mask, float* o_part, float* lse_part, float* out,
-    void* ws_index, size_t ws_index_bytes, void* ws_local, size_t ws_local_bytes, void* stream,
-    void* side_stream, void* ev_fork, void* ev_join) {
+    void* ws_index, size_t ws_index_bytes, void* ws_local, size_t ws_local_bytes, const int* kv_slot,
+    int n_full, const void* k_ring, const void* v_ring, int n_ring, void* stream, void* side_stream, void* ev_fork,
+    void* ev_join) {
   // every argument is checked before anything is enqueued
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_ctx <= 0 || n_ret < 0 || n_loc < 0 || n_ret + n_loc > Hq)
     return RTP_EINVAL;
   if (Hq % Hkv) return RTP_EINVAL;
   const int G = Hq / Hkv;
   if (G != 1 && G != 2 && G != 4 && G != 8) return RTP_EUNSUPPORTED;
-  if (!q || !k_cache || !v_cache || !seq_lens || !out) return RTP_EINVAL;
+  if (!q || !seq_lens || !out) return RTP_EINVAL;
+  if (kv_slot) {
+    if (n_full < 0 || n_full > Hkv || n_ring < 0 || n_ring > Hkv || n_full + n_ring < 1 ||
+        n_full + n_ring > Hkv)
+      return RTP_EINVAL;
+    if ((n_full > 0 || n_ret > 0) && (!k_cache || !v_cache || n_full < 1)) return RTP_EINVAL;
+    if (n_ring > 0 && (!k_ring || !v_ring)) return RTP_EINVAL;
+    if (((uintptr_t)k_ring | (uintptr_t)v_ring) & 15) return RTP_EINVAL;
+  } else if (!k_cache || !v_cache) {
+    return RTP_EINVAL;
+  }
   if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache) & 15) return RTP_EINVAL;
   if (n_ret > 0) {
     if (block != 64 && block != 128) return RTP_EUNSUPPORTED;
@@ -52,7 +63,7 @@ extern "C" rtp_status rtp_decode_step(
         return RTP_ELAUNCH;
     }
     st = rtp_local_window_attn(q, k_cache, v_cache, seq_lens, loc_heads, B, Hq, Hkv, n_loc, max_ctx, window,
-                               sinks, out, ws_local, ws_local_bytes, ls);
+                               sinks, out, ws_local, ws_local_bytes, kv_slot, n_full, k_ring, v_ring, n_ring, ls);
     if (st != RTP_OK) return st;
     if (fork && hipEventRecord(static_cast<hipEvent_t>(ev_join), ls) != hipSuccess) return RTP_ELAUNCH;
   }
@@ -63,7 +74,7 @@ extern "C" rtp_status rtp_decode_step(
                                        sel_idx, sel_cnt, sel_mask, ws_index, ws_index_bytes, stream);
     if (st == RTP_OK)
       st = rtp_sparse_attn_split(q, k_cache, v_cache, seq_lens, ret_heads, sel_idx, sel_cnt, sel_mask, B, Hq, Hkv,
-                                 n_ret, max_ctx, block, split_tokens, o_part, lse_part, stream);
+                                 n_ret, max_ctx, block, split_tokens, o_part, lse_part, kv_slot, n_full, stream);
     if (st == RTP_OK) st = rtp_split_reduce(o_part, lse_part, ret_heads, B, Hq, n_ret, n_split, out, stream);
   }
   if (fork && hipStreamWaitEvent(s, static_cast<hipEvent_t>(ev_join), 0) != hipSuccess) return RTP_ELAUNCH;

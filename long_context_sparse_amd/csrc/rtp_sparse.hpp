@@ -35,7 +35,7 @@ struct SparseSmem {
   float acc[kAttnWaves * G * kHeadDim];
   // kernel 2's ordering of KV groups: per group, selected blocks summed over its
   // retrieval heads and its number of retrieval heads; the head list; the lengths
-  int gw[kOrderMax], gn[kOrderMax], rh[kOrderMax], sl[kOrderMax];
+  int gw[kOrderMax], gn[kOrderMax], rh[kOrderMax], sl[kOrderMax], slot[kOrderMax];
   int pick;
 };
 template <int G>
@@ -60,13 +60,21 @@ struct SparseArgs {
   const int* sel_idx;
   const int* sel_cnt;
   const uint8_t* sel_mask;  // [B, n_ret, nblk_max] 1 = selected, or null (then the lists)
+  const int* kv_slot;       // [Hkv] KV group -> its index in the caches (>= 0), or null (identity)
   int Hq, Hkv, n_ret, max_ctx, nblk_max, split_blocks;
+  int n_full;               // groups in the caches (Hkv when kv_slot is null)
 };
 struct LocalArgs {
   const uint16_t *q, *kc, *vc;
   const int* seq_lens;
   const int* loc_heads;
   int Hq, Hkv, n_loc, max_ctx, window, sinks, split_tokens;
+  // KV placement: kv_slot[g] >= 0: group g's rows are in kc/vc at group index kv_slot[g]
+  // ([B, n_full, max_ctx, 128]); < 0: in the sink + window ring kr/vr at group index
+  // -1 - kv_slot[g] ([B, n_ring, sinks + window, 128]).  Null: identity, all in kc/vc.
+  const int* kv_slot;
+  const uint16_t *kr, *vr;
+  int n_full, n_ring;
 };
 
 // Contiguous range [beg, end) of an ascending head list that falls in KV group g,
@@ -110,7 +118,7 @@ __device__ __forceinline__ int lower_bound_wave(const int* __restrict__ a, int n
 // nh repeats the last one, so loads through it stay valid) and the sequence length.
 template <int G>
 struct SparseGroup {
-  int b, g, N, rbeg, nh;
+  int b, g, N, rbeg, nh, slot;
   int hid[G];
 };
 
@@ -135,10 +143,13 @@ __device__ __forceinline__ SparseGroup<G> sparse_group(const SparseArgs& a, int 
     const int i0 = min(tid, nbr - 1), b0 = i0 / n_ret, r0 = i0 - b0 * n_ret;
     const int h0 = a.ret_heads[r0], c0 = a.sel_cnt[i0];
     const int len0 = a.seq_lens[min(tid, B - 1)];  // B <= kOrderMax == kAttnThreads
+    const int* slot_src = a.kv_slot ? a.kv_slot : a.seq_lens;  // any readable word without a table
+    const int slot0 = slot_src[a.kv_slot ? min(tid, Hkv - 1) : 0];
     for (int k = tid; k < ngrp; k += kAttnThreads) S->gw[k] = 0;
     for (int k = tid; k < Hkv; k += kAttnThreads) S->gn[k] = 0;
     __syncthreads();
     if (tid < B) S->sl[tid] = len0;
+    if (tid < Hkv) S->slot[tid] = a.kv_slot ? slot0 : tid;
     auto add = [&](int b, int rr, int h, int cnt) {
       if (h >= 0 && h < a.Hq) {
         atomicAdd(&S->gw[b * Hkv + h / G], cnt);
@@ -169,12 +180,14 @@ __device__ __forceinline__ SparseGroup<G> sparse_group(const SparseArgs& a, int 
     for (int g2 = 0; g2 < r.g; ++g2) beg += S->gn[g2];
     nh = S->gn[r.g];
     r.N = S->sl[r.b];
+    r.slot = S->slot[r.g];
 #pragma unroll
     for (int h = 0; h < G; ++h) r.hid[h] = nh > 0 ? S->rh[beg + min(h, nh - 1)] : 0;
   } else {
     r.b = rank / Hkv;
     r.g = rank - r.b * Hkv;
     r.N = a.seq_lens[r.b];
+    r.slot = a.kv_slot ? a.kv_slot[r.g] : r.g;
     int end;
     group_range(a.ret_heads, n_ret, r.g, G, beg, end);
     nh = end - beg;
@@ -288,7 +301,10 @@ __device__ __forceinline__ bool sparse_split(const SparseArgs& a, int c, const S
 
   AttnState<G> st;
   attn_init(st);
-  const size_t kvoff = ((size_t)b * a.Hkv + g) * (size_t)a.max_ctx * kHeadDim;
+  // a group whose rows are not in the full caches (a caller error: it has retrieval
+  // heads) reads nothing and emits empty partials
+  if (grp.slot < 0) nL = 0;
+  const size_t kvoff = ((size_t)b * a.n_full + max(grp.slot, 0)) * (size_t)a.max_ctx * kHeadDim;
   const float scale = (float)(kLog2e / 11.313708498984761);  // log2(e) / sqrt(128)
   auto item = [&](int i, int& row0, uint32_t& hm) {
     const uint32_t ent = s_list[i / ST];
@@ -322,15 +338,22 @@ __device__ __forceinline__ bool local_split(const LocalArgs& a, int c, int g, in
   const int nh = iend - ibeg;
   if (nh == 0) return false;
   const int N = a.seq_lens[b];
+  const int slot = a.kv_slot ? a.kv_slot[g] : g;
   const int s_end = min(sinks, N);
-  const int w0 = max(s_end, N - window);
+  // the window's rows: positions [max(s_end, N - window), N) of the full cache, or every
+  // stored ring row past the sinks: the ring holds positions < sinks at their own row and
+  // the last `window` positions at rows sinks + (p - sinks) mod window, so its rows
+  // [s_end, min(N, sinks + window)) are exactly the window (in another order)
+  const bool ring = slot < 0;
+  const int w0 = ring ? s_end : max(s_end, N - window);
+  const int w1 = ring ? min(N, sinks + window) : N;
   int t0, t1;
   if (c == 0) {
     t0 = 0;
     t1 = s_end;
   } else {
     t0 = w0 + (c - 1) * split_tokens;
-    t1 = min(N, t0 + split_tokens);
+    t1 = min(w1, t0 + split_tokens);
   }
   const int nitems = t1 > t0 ? (t1 - t0 + 15) / 16 : 0;
 
@@ -342,14 +365,17 @@ __device__ __forceinline__ bool local_split(const LocalArgs& a, int c, int g, in
   for (int h = 0; h < G; ++h)
     qk[h] = h < nh ? ld16(a.q + ((size_t)b * a.Hq + loc_heads[ibeg + h]) * kHeadDim + c16 * 8)
                    : make_uint4(0, 0, 0, 0);
-  const size_t kvoff = ((size_t)b * a.Hkv + g) * (size_t)a.max_ctx * kHeadDim;
+  const size_t kvoff = ring ? ((size_t)b * a.n_ring + (-1 - slot)) * (size_t)(sinks + window) * kHeadDim
+                            : ((size_t)b * a.n_full + slot) * (size_t)a.max_ctx * kHeadDim;
+  const uint16_t* kbase = ring ? a.kr : a.kc;
+  const uint16_t* vbase = ring ? a.vr : a.vc;
   const float scale = (float)(kLog2e / 11.313708498984761);
   const uint32_t allh = (1u << nh) - 1u;
   auto item = [&](int i, int& row0, uint32_t& hm) {
     row0 = t0 + 16 * i;
     hm = allh;
   };
-  attn_stream<G, kWaves>(st, a.kc + kvoff, a.vc + kvoff, nitems, t1, item, qk, scale, wave, lane);
+  attn_stream<G, kWaves>(st, kbase + kvoff, vbase + kvoff, nitems, t1, item, qk, scale, wave, lane);
   attn_publish_wave<G, kWaves>(st, S->m, S->l, S->acc, wave, lane);
   __syncthreads();
   for (int idx = tid; idx < nh * kHeadDim; idx += kThreads) {

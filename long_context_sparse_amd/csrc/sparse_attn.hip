@@ -160,7 +160,7 @@ extern "C" rtp_status rtp_sparse_attn_split(const void* q, const void* k_cache, 
                                             const unsigned char* sel_mask, int B, int Hq,
                                             int Hkv, int n_ret, int max_ctx, int block,
                                             int split_tokens, float* o_part, float* lse_part,
-                                            void* stream) {
+                                            const int* kv_slot, int n_full, void* stream) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || n_ret < 0 || n_ret > Hq || max_ctx <= 0) return RTP_EINVAL;
   if (Hq % Hkv) return RTP_EINVAL;
   if (!group_ok(Hq, Hkv)) return RTP_EUNSUPPORTED;
@@ -170,6 +170,7 @@ extern "C" rtp_status rtp_sparse_attn_split(const void* q, const void* k_cache, 
   if (n_ret == 0) return RTP_OK;
   if (!q || !k_cache || !v_cache || !seq_lens || !ret_heads || !o_part || !lse_part) return RTP_EINVAL;
   if (!sel_mask && (!sel_idx || !sel_cnt)) return RTP_EINVAL;
+  if (kv_slot && (n_full <= 0 || n_full > Hkv)) return RTP_EINVAL;
   if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache) & 15) return RTP_EINVAL;
   const int nblk_max = ceil_div(max_ctx, block);
   const int sb = split_tokens / block;
@@ -178,8 +179,8 @@ extern "C" rtp_status rtp_sparse_attn_split(const void* q, const void* k_cache, 
   dim3 grid(n_split, Hkv, B);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const SparseArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
-                     static_cast<const uint16_t*>(v_cache), seq_lens, ret_heads, sel_idx, sel_cnt, sel_mask, Hq, Hkv,
-                     n_ret, max_ctx, nblk_max, sb};
+                     static_cast<const uint16_t*>(v_cache), seq_lens, ret_heads, sel_idx, sel_cnt, sel_mask, kv_slot,
+                     Hq, Hkv, n_ret, max_ctx, nblk_max, sb, kv_slot ? n_full : Hkv};
   const int G = Hq / Hkv;
   if (block == 64)
     launch_sparse<64>(G, grid, s, a, n_split, o_part, lse_part);
@@ -213,12 +214,24 @@ extern "C" rtp_status rtp_local_window_attn(const void* q, const void* k_cache, 
                                             const int* seq_lens, const int* loc_heads, int B, int Hq,
                                             int Hkv, int n_loc, int max_ctx, int window, int sinks,
                                             float* out, void* workspace, size_t ws_bytes,
-                                            void* stream) {
+                                            const int* kv_slot, int n_full, const void* k_ring,
+                                            const void* v_ring, int n_ring, void* stream) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || n_loc < 0 || n_loc > Hq || max_ctx <= 0) return RTP_EINVAL;
   if (Hq % Hkv || window < 0 || sinks < 0 || window + sinks < 1) return RTP_EINVAL;
   if (!group_ok(Hq, Hkv)) return RTP_EUNSUPPORTED;
   if (n_loc == 0) return RTP_OK;
-  if (!q || !k_cache || !v_cache || !seq_lens || !loc_heads || !out || !workspace) return RTP_EINVAL;
+  if (!q || !seq_lens || !loc_heads || !out || !workspace) return RTP_EINVAL;
+  if (kv_slot) {
+    // full caches may be absent when every group is in the ring, and the reverse
+    if (n_full < 0 || n_full > Hkv || n_ring < 0 || n_ring > Hkv || n_full + n_ring < 1 ||
+        n_full + n_ring > Hkv)
+      return RTP_EINVAL;
+    if (n_full > 0 && (!k_cache || !v_cache)) return RTP_EINVAL;
+    if (n_ring > 0 && (!k_ring || !v_ring)) return RTP_EINVAL;
+    if (((uintptr_t)k_ring | (uintptr_t)v_ring) & 15) return RTP_EINVAL;
+  } else if (!k_cache || !v_cache) {
+    return RTP_EINVAL;
+  }
   if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache) & 15) return RTP_EINVAL;
   if ((uintptr_t)workspace & 255) return RTP_EINVAL;
   const LocalLayout L = local_layout(B, Hkv, n_loc, window < max_ctx ? window : max_ctx);
@@ -231,7 +244,8 @@ extern "C" rtp_status rtp_local_window_attn(const void* q, const void* k_cache, 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const LocalArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
                     static_cast<const uint16_t*>(v_cache), seq_lens, loc_heads, Hq, Hkv, n_loc, max_ctx,
-                    window, sinks, L.split_tokens};
+                    window, sinks, L.split_tokens, kv_slot, static_cast<const uint16_t*>(k_ring),
+                    static_cast<const uint16_t*>(v_ring), kv_slot ? n_full : Hkv, kv_slot ? n_ring : 0};
 #define RTP_LOCAL(GG) \
   hipLaunchKernelGGL(local_window_kernel<GG>, grid, dim3(kThreads), 0, s, a, L.n_split, ws_o, ws_lse)
   switch (Hq / Hkv) {

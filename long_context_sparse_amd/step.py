@@ -6,6 +6,10 @@ split partials, workspaces, output) and issues them through one rtp_decode_step 
   retrieval heads:  rtp_index_topp (or rtp_index_topk) -> rtp_sparse_attn_split -> rtp_split_reduce
   local heads:      rtp_local_window_attn (on a second stream, overlapping the above)
 
+The inputs may place KV groups in sink + window rings (keys "kv_slot", "k_ring",
+"v_ring"; see the KV placement note in include/rtp.h): the full caches then hold only
+the groups with kv_slot >= 0.
+
 PyTorch provides the memory and the streams; every step runs in librtp.so.
 """
 from __future__ import annotations
@@ -77,6 +81,15 @@ class DecodeStep:
         self._vals = None
         self._step_fn = abi.lib().rtp_decode_step
 
+    @staticmethod
+    def placement(t: Dict[str, torch.Tensor]) -> dict:
+        """KV placement arguments of these inputs: none (every group in the full caches)
+        unless they carry a kv_slot table and the ring caches."""
+        if t.get("kv_slot") is None:
+            return dict(kv_slot=None, n_full=0, k_ring=None, v_ring=None, n_ring=0)
+        return dict(kv_slot=t["kv_slot"], n_full=int(t["k_cache"].shape[1]), k_ring=t["k_ring"],
+                    v_ring=t["v_ring"], n_ring=int(t["k_ring"].shape[1]))
+
     # -- the four calls -------------------------------------------------------------
     def index_topk(self, t: Dict[str, torch.Tensor], stream=None) -> None:
         s = self.s
@@ -95,7 +108,8 @@ class DecodeStep:
         abi.rtp_sparse_attn_split(t["q"], t["k_cache"], t["v_cache"], t["seq_lens"], t["ret_heads"],
                                   self.sel_idx, self.sel_cnt, s.B, s.Hq, s.Hkv, s.n_ret, s.max_ctx,
                                   s.block, s.split_tokens, self.o_part, self.lse_part, stream,
-                                  sel_mask=self.sel_mask)
+                                  sel_mask=self.sel_mask, kv_slot=t.get("kv_slot"),
+                                  n_full=self.placement(t)["n_full"])
 
     def reduce(self, t: Dict[str, torch.Tensor], stream=None) -> None:
         s = self.s
@@ -106,7 +120,7 @@ class DecodeStep:
         s = self.s
         abi.rtp_local_window_attn(t["q"], t["k_cache"], t["v_cache"], t["seq_lens"], t["loc_heads"],
                                   s.B, s.Hq, s.Hkv, s.n_loc, s.max_ctx, s.window, s.sinks, self.out,
-                                  self.ws_local, stream)
+                                  self.ws_local, stream, **self.placement(t))
 
     # -- the whole step -------------------------------------------------------------
     def _plan(self, t: Dict[str, torch.Tensor], main: int) -> tuple:
@@ -116,6 +130,8 @@ class DecodeStep:
         p = abi.device_ptr
         z = lambda name: p(t[name]) if t[name].numel() else None  # noqa: E731
         side = self.side.cuda_stream if self.overlap else None
+        pl = self.placement(t)
+        o = lambda x: None if x is None else p(x)  # noqa: E731
         return (z("q_pre") if s.n_ret else None, z("w_q") if s.n_ret else None, z("k_idx") if s.n_ret else None,
                 p(t["q"]), p(t["k_cache"]), p(t["v_cache"]), p(t["seq_lens"]),
                 z("ret_heads") if s.n_ret else None, z("loc_heads") if s.n_loc else None,
@@ -123,7 +139,8 @@ class DecodeStep:
                 s.split_tokens, s.window, s.sinks, p(self.sel_idx), p(self.sel_cnt),
                 p(self.sel_mask) if self.sel_mask is not None else None, p(self.o_part), p(self.lse_part),
                 p(self.out), p(self.ws_index), abi.nbytes(self.ws_index), p(self.ws_local),
-                abi.nbytes(self.ws_local), main, side, self._fork, self._join)
+                abi.nbytes(self.ws_local), o(pl["kv_slot"]), pl["n_full"], o(pl["k_ring"]), o(pl["v_ring"]),
+                pl["n_ring"], main, side, self._fork, self._join)
 
     def __call__(self, t: Dict[str, torch.Tensor]) -> torch.Tensor:
         """Enqueue one decode step on the current stream; returns the fp32 [B, Hq, 128] output.

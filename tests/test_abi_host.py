@@ -83,12 +83,12 @@ def test_index_topk_rejects():
 
 def _sparse(**kw):
     a = dict(B=1, Hq=8, Hkv=2, n_ret=2, max_ctx=4096, block=64, split=1024, sel_idx=FAKE, sel_cnt=FAKE,
-             sel_mask=None)
+             sel_mask=None, kv_slot=None, n_full=0)
     a.update(kw)
     ptr = kw.get("ptr", FAKE)
     return abi.lib().rtp_sparse_attn_split(ptr, FAKE, FAKE, FAKE, FAKE, a["sel_idx"], a["sel_cnt"], a["sel_mask"],
                                            a["B"], a["Hq"], a["Hkv"], a["n_ret"], a["max_ctx"], a["block"],
-                                           a["split"], FAKE, FAKE, None)
+                                           a["split"], FAKE, FAKE, a["kv_slot"], a["n_full"], None)
 
 
 def test_sparse_attn_rejects():
@@ -101,6 +101,8 @@ def test_sparse_attn_rejects():
     assert _sparse(ptr=None) == abi.RTP_EINVAL
     assert _sparse(sel_idx=None) == abi.RTP_EINVAL          # no lists and no masks
     assert _sparse(sel_cnt=None) == abi.RTP_EINVAL
+    assert _sparse(kv_slot=FAKE, n_full=0) == abi.RTP_EINVAL   # placement without full caches
+    assert _sparse(kv_slot=FAKE, n_full=3) == abi.RTP_EINVAL   # more full slots than groups
     assert _sparse(n_ret=0) == abi.RTP_OK
 
 
@@ -111,22 +113,30 @@ def test_reduce_and_local_reject():
     assert L.rtp_split_reduce(None, FAKE, FAKE, 1, 4, 2, 2, FAKE, None) == abi.RTP_EINVAL
     assert L.rtp_split_reduce(FAKE, FAKE, FAKE, 1, 4, 0, 2, FAKE, None) == abi.RTP_OK
     ws = abi.rtp_local_window_workspace_size(1, 8, 2, 6, 4096, 1024, 4)
-    assert L.rtp_local_window_attn(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 6, 4096, 1024, 4, FAKE, FAKE,
-                                   ws - 1, None) == abi.RTP_EINVAL
-    assert L.rtp_local_window_attn(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 6, 4096, 0, 0, FAKE, FAKE,
-                                   1 << 30, None) == abi.RTP_EINVAL
-    assert L.rtp_local_window_attn(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 6, 4096, -1, 4, FAKE, FAKE,
-                                   1 << 30, None) == abi.RTP_EINVAL
-    assert L.rtp_local_window_attn(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 0, 4096, 16, 4, FAKE, FAKE,
-                                   0, None) == abi.RTP_OK
+    nop = [None, 0, None, None, 0, None]            # no placement table; default stream
+
+    def loc(window=1024, sinks=4, n_loc=6, ws_bytes=1 << 30, kc=FAKE, tail=nop):
+        return L.rtp_local_window_attn(FAKE, kc, kc, FAKE, FAKE, 1, 8, 2, n_loc, 4096, window, sinks, FAKE,
+                                       FAKE, ws_bytes, *tail)
+    assert loc(ws_bytes=ws - 1) == abi.RTP_EINVAL
+    assert loc(window=0, sinks=0) == abi.RTP_EINVAL
+    assert loc(window=-1) == abi.RTP_EINVAL
+    assert loc(kc=None) == abi.RTP_EINVAL                         # no caches at all
+    assert loc(tail=[FAKE, 0, None, None, 0, None]) == abi.RTP_EINVAL      # placement with no groups
+    assert loc(tail=[FAKE, 1, None, None, 1, None]) == abi.RTP_EINVAL      # rings missing
+    assert loc(tail=[FAKE, 1, FAKE + 4, FAKE, 1, None]) == abi.RTP_EINVAL  # ring misaligned
+    assert loc(kc=None, tail=[FAKE, 1, FAKE, FAKE, 1, None]) == abi.RTP_EINVAL  # full slots, no caches
+    assert loc(tail=[FAKE, 3, None, None, 0, None]) == abi.RTP_EINVAL      # more full slots than groups
+    assert loc(n_loc=0, window=16, ws_bytes=0) == abi.RTP_OK
 
 
 def test_cache_append_rejects():
     L = abi.lib()
 
-    def call(B=2, Hq=8, Hkv=2, n_ret=2, max_ctx=256, k_new=FAKE, k_pre=FAKE, k_idx=FAKE):
+    def call(B=2, Hq=8, Hkv=2, n_ret=2, max_ctx=256, k_new=FAKE, k_pre=FAKE, k_idx=FAKE,
+             place=(None, 0, None, None, 0, 0, 0)):
         return L.rtp_cache_append(k_new, FAKE, k_pre, FAKE, FAKE, FAKE, B, Hq, Hkv, n_ret, max_ctx,
-                                  FAKE, FAKE, k_idx, None)
+                                  FAKE, FAKE, k_idx, *place, None)
     assert call(B=0) == abi.RTP_EINVAL
     assert call(Hkv=3) == abi.RTP_EINVAL                 # heads not divisible
     assert call(n_ret=9) == abi.RTP_EINVAL               # more retrieval heads than heads
@@ -135,12 +145,16 @@ def test_cache_append_rejects():
     assert call(k_pre=None) == abi.RTP_EINVAL            # needed for the index keys
     assert call(k_new=FAKE + 8) == abi.RTP_EINVAL        # misaligned
     assert call(k_idx=FAKE + 1) == abi.RTP_EINVAL
+    assert call(place=(FAKE, 1, FAKE, FAKE, 1, 0, 0)) == abi.RTP_EINVAL      # ring of no rows
+    assert call(place=(FAKE, 1, None, FAKE, 1, 4, 16)) == abi.RTP_EINVAL     # ring missing
+    assert call(place=(FAKE, 2, FAKE, FAKE, 1, 4, 16)) == abi.RTP_EINVAL     # 3 slots for 2 groups
+    assert call(place=(FAKE, 1, FAKE, FAKE, 1, -1, 16)) == abi.RTP_EINVAL
 
 
 def test_decode_step_rejects():
     L = abi.lib()
     args = [FAKE] * 10 + [0] + [1, 8, 2, 2, 6, 4096, 64, 1024, 1024, 4] + [FAKE] * 6 + \
-        [FAKE, 1 << 30, FAKE, 1 << 30] + [None] * 4
+        [FAKE, 1 << 30, FAKE, 1 << 30] + [None, 0, None, None, 0] + [None] * 4
     bad = list(args)
     bad[11] = 0                                        # B = 0
     assert L.rtp_decode_step(*bad) == abi.RTP_EINVAL
@@ -155,4 +169,13 @@ def test_decode_step_rejects():
     assert L.rtp_decode_step(*bad) == abi.RTP_EINVAL
     bad = list(args)
     bad[9] = None                                      # top-p rule without top_p
+    assert L.rtp_decode_step(*bad) == abi.RTP_EINVAL
+    bad = list(args)
+    bad[31:36] = [FAKE, 0, FAKE, FAKE, 2]              # retrieval heads but no full caches
+    assert L.rtp_decode_step(*bad) == abi.RTP_EINVAL
+    bad = list(args)
+    bad[31:36] = [FAKE, 1, None, None, 1]              # ring groups but no rings
+    assert L.rtp_decode_step(*bad) == abi.RTP_EINVAL
+    bad = list(args)
+    bad[31:36] = [FAKE, 2, FAKE, FAKE, 1]              # three slots for two groups
     assert L.rtp_decode_step(*bad) == abi.RTP_EINVAL
