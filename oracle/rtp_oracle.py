@@ -40,6 +40,10 @@ Readings taken where the pages are silent or garbled:
   N_b tokens (row N_b - 1); its index key for retrieval head h is W^K_h k^pre of
   the head's KV head, the exact dot products rounded once to bf16 (nearest, ties to
   even); its K and V rows are stored as given.
+* Prefill (the Review's Adaptive sparse attention paragraph): causal; a local head's
+  query at position i sees the decode rule's token set for N = i + 1, a retrieval
+  head's sees every position up to i.  The prompt's index keys are each computed as
+  in the cache append.
 
 Parity of every function here is pinned by tests/test_oracle_pins.py (closed
 forms, brute force, library routines, hand-worked golden fixtures).
@@ -324,3 +328,43 @@ def decode_step(inp, items: Optional[Sequence[Tuple[int, int]]] = None) -> Dict[
         else:
             res[(b, h)] = local_head(inp, b, h)
     return res
+
+
+# ------------------------------------------------------------------------ prefill
+def prefill_tokens(i: int, retrieval: bool, window: int, sinks: int) -> np.ndarray:
+    """Keys the query at prompt position i attends to during prefill.
+
+    Review, Adaptive sparse attention: local heads apply the sliding window + sink rule
+    in prefill as in decode, and retrieval heads run full dense attention in prefill;
+    Review, Efficiency & ultra-long robustness: prefill sparsity is fixed in advance
+    (local heads see only sink 4 + window 8192).  Prefill is causal, so position i sees
+    positions 0..i: the decode rule with N = i + 1 tokens (all of them for a retrieval
+    head, local_tokens(i + 1, W, S) for a local head).
+    """
+    n = i + 1
+    if retrieval:
+        return np.arange(n, dtype=np.int64)
+    return local_tokens(n, window, sinks)
+
+
+def prefill_row(q_i: np.ndarray, K: np.ndarray, V: np.ndarray, i: int, retrieval: bool, window: int,
+                sinks: int) -> Tuple[np.ndarray, float]:
+    """Prefill output (fp64 [128], lse) of the query at position i: exact attention over
+    prefill_tokens(i, ...).  q_i: bf16 bits [128]; K, V: bf16 bits [>= i + 1, 128], the
+    prompt's rows of the head's KV group (row n = position n)."""
+    return attend(q_i, K, V, prefill_tokens(i, retrieval, window, sinks))
+
+
+def prefill_head(pin, b: int, hq: int, rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Prefill outputs (fp64 [len(rows), 128]) of query head hq of sequence b for the
+    given prompt positions (default: all N_b of them).  pin carries q [B, Hq, T, 128],
+    k, v [B, Hkv, T, 128] (bf16 bits), seq_lens, ret_heads and the config's window,
+    sinks and head counts; the head's KV group is hq // (Hq / Hkv)."""
+    cfg = pin.cfg
+    n = int(pin.seq_lens[b])
+    kv = hq // (cfg.Hq // cfg.Hkv)
+    ret = hq in {int(h) for h in pin.ret_heads}
+    if rows is None:
+        rows = range(n)
+    return np.stack([prefill_row(pin.q[b, hq, i], pin.k[b, kv], pin.v[b, kv], int(i), ret, cfg.window,
+                                 cfg.sinks)[0] for i in rows])

@@ -12,7 +12,7 @@ import test_oracle_pins as P
 _orig = {name: getattr(O, name) for name in
          ("block_masses", "token_softmax", "select_top_p", "select_top_k", "attend", "local_tokens",
           "bf16_round", "index_key",
-          "merge_partials", "index_query", "retrieval_head")}
+          "merge_partials", "index_query", "retrieval_head", "prefill_tokens")}
 
 
 def _masses_per_block_softmax(s, block):
@@ -129,6 +129,18 @@ def _retrieval_wrong_group(inp, b, r):
     return O.HeadResult(out=o, lse=lse, tokens=toks, masses=m, selection=sel)
 
 
+def _prefill_excludes_self(i, retrieval, window, sinks):
+    return _orig["prefill_tokens"](i - 1, retrieval, window, sinks) if i > 0 else np.zeros(1, np.int64)
+
+
+def _prefill_sees_next(i, retrieval, window, sinks):
+    return np.arange(i + 2, dtype=np.int64) if retrieval else _orig["prefill_tokens"](i, retrieval, window, sinks)
+
+
+def _prefill_no_sinks(i, retrieval, window, sinks):
+    return _orig["prefill_tokens"](i, retrieval, window, 0)
+
+
 MUTANTS = [
     ("block_masses", _masses_per_block_softmax, [P.check_block_mass_worked, P.check_mass_vs_library]),
     ("block_masses", _masses_drop_partial, [P.check_block_mass_worked, P.check_mass_vs_library]),
@@ -148,6 +160,10 @@ MUTANTS = [
     ("merge_partials", _merge_unweighted, [P.check_merge_is_union]),
     ("retrieval_head", _retrieval_uses_wk, [P.check_dominant_needle]),
     ("retrieval_head", _retrieval_wrong_group, [P.check_gqa_mapping]),
+    ("prefill_tokens", _prefill_excludes_self, [P.check_prefill_tokens_worked, P.check_prefill_one_hot_values]),
+    ("prefill_tokens", _prefill_sees_next, [P.check_prefill_tokens_worked, P.check_prefill_vs_sdpa]),
+    ("prefill_tokens", _prefill_no_sinks, [P.check_prefill_tokens_worked, P.check_prefill_vs_sdpa,
+                                           P.check_prefill_one_hot_values]),
 ]
 
 

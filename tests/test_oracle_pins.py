@@ -367,6 +367,65 @@ def check_gqa_mapping():
                        rtol=0, atol=1e-12)
 
 
+# --------------------------------------------------------------------- prefill
+def check_prefill_tokens_worked():
+    # worked by hand from the rule (Review, Adaptive sparse attention: window + sink in
+    # prefill for local heads, dense for retrieval heads; causal): W = 3, S = 2
+    want = {0: [0], 1: [0, 1], 2: [0, 1, 2], 3: [0, 1, 2, 3], 4: [0, 1, 2, 3, 4], 5: [0, 1, 3, 4, 5],
+            9: [0, 1, 7, 8, 9]}
+    for i, t in want.items():
+        assert O.prefill_tokens(i, False, 3, 2).tolist() == t, i
+        assert O.prefill_tokens(i, True, 3, 2).tolist() == list(range(i + 1)), i
+    assert O.prefill_tokens(5, False, 0, 2).tolist() == [0, 1]        # sinks only
+    assert O.prefill_tokens(5, False, 1, 0).tolist() == [5]           # the token itself
+    assert O.prefill_tokens(1, False, 0, 4).tolist() == [0, 1]        # sinks beyond the prompt so far
+
+
+def _prefill_pin_inputs(N, Hq, Hkv, ret_heads, window, sinks, seed):
+    # a second, longer prompt gives the first one rows past its end (a rule that looks
+    # past position i then reads them instead of failing on an index)
+    cfg = W.custom_config(B=2, Hkv=Hkv, Hq=Hq, n_ret=len(ret_heads), ret_heads=tuple(ret_heads), ctx=(N, N + 5),
+                          window=window, sinks=sinks, seed=seed)
+    return W.make_prefill_inputs(cfg)
+
+
+def check_prefill_vs_sdpa():
+    """Every row of every head against torch's attention in float64 with the causal /
+    window + sink mask written as an elementwise predicate on (query i, key j)."""
+    pin = _prefill_pin_inputs(70, 4, 2, (1,), 9, 3, 21)
+    N, S, Wn = 70, 3, 9
+    i = np.arange(N)[:, None]
+    j = np.arange(N)[None, :]
+    for h in range(4):
+        kv = h // 2
+        qt = torch.from_numpy(O.bf16_to_f64(pin.q[0, h, :N]))[None, None]
+        kt = torch.from_numpy(O.bf16_to_f64(pin.k[0, kv, :N]))[None, None]
+        vt = torch.from_numpy(O.bf16_to_f64(pin.v[0, kv, :N]))[None, None]
+        if h == 1:
+            ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+        else:
+            m = torch.from_numpy((j <= i) & ((j < S) | (i - j < Wn)))
+            ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m)
+        assert np.allclose(O.prefill_head(pin, 0, h), ref[0, 0].numpy(), rtol=0, atol=1e-12), h
+
+
+def check_prefill_one_hot_values():
+    """Equal keys give uniform weights; V row j = e_j then shows each row's token set
+    and weights directly: output[i, j] = 1 / |T_i| for j in T_i, else 0."""
+    pin = _prefill_pin_inputs(100, 2, 1, (0,), 7, 2, 22)
+    pin.k[0, 0, :100] = pin.k[0, 0, 0]
+    one = W.f32_to_bf16_bits(np.float32([1.0]))[0]
+    pin.v[0, 0, :100] = 0
+    pin.v[0, 0, np.arange(100), np.arange(100)] = one
+    for h, pred in ((0, lambda i, j: j <= i), (1, lambda i, j: j <= i and (j < 2 or j > i - 7))):
+        out = O.prefill_head(pin, 0, h)
+        for i in range(100):
+            T = [j for j in range(100) if pred(i, j)]
+            want = np.zeros(128)
+            want[T] = 1.0 / len(T)
+            assert np.allclose(out[i], want, rtol=0, atol=1e-15), (h, i)
+
+
 # ------------------------------------------------------------------ acceptance
 def check_acceptance_rule():
     m = np.array([0.3, 0.3, 0.2, 0.1, 0.1])
@@ -401,7 +460,8 @@ CHECKS = [check_index_worked, check_block_mass_worked, check_tie_break_worked, c
           check_bf16_round, check_index_key_worked, check_index_key_vs_float64,
           check_attention_vs_sdpa, check_attention_closed_forms, check_merge_is_union,
           check_local_tokens_worked, check_local_reduces_to_dense, check_p_one_is_dense,
-          check_gqa_mapping, check_acceptance_rule]
+          check_gqa_mapping, check_acceptance_rule,
+          check_prefill_tokens_worked, check_prefill_vs_sdpa, check_prefill_one_hot_values]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=[c.__name__ for c in CHECKS])

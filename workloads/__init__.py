@@ -36,6 +36,7 @@ INDEX_DIM = 16
 
 # tensor ids for the seed streams
 _T_Q, _T_WQ, _T_WK, _T_K, _T_V, _T_HEADS, _T_LENS, _T_PLANT, _T_P, _T_KIND = range(1, 11)
+_T_PQ = 11          # prefill queries (one per prompt position)
 
 
 # --------------------------------------------------------------------------- bf16
@@ -326,6 +327,67 @@ def make_inputs(cfg: DecodeConfig, seed: Optional[int] = None, pad_value: int = 
     return DecodeInputs(cfg=cfg, seq_lens=seq_lens, ret_heads=ret, loc_heads=loc, top_p=top_p,
                         q=q, w_q=w_q, w_k=w_k, k_cache=k_cache, v_cache=v_cache, k_idx=k_idx,
                         needles=needles, peaked=peaked)
+
+
+# ------------------------------------------------------------------ prefill inputs
+@dataclasses.dataclass
+class PrefillInputs:
+    """The prompt of a prefill pass: every position's query, key and value rows."""
+    cfg: DecodeConfig
+    seq_lens: np.ndarray      # int32 [B]: prompt lengths N_b
+    ret_heads: np.ndarray     # int32 [n_ret], ascending query-head ids
+    loc_heads: np.ndarray     # int32 [n_loc]
+    q: np.ndarray             # bf16 bits [B, Hq, T, 128]: row i = the query at position i
+    k: np.ndarray             # bf16 bits [B, Hkv, T, 128]: the prompt's keys (no RoPE here, so also k_pre)
+    v: np.ndarray             # bf16 bits [B, Hkv, T, 128]
+    w_k: np.ndarray           # bf16 bits [n_ret, 16, 128]
+
+
+def make_prefill_inputs(cfg: DecodeConfig, seed: Optional[int] = None, pad_value: int = 0,
+                        workers: Optional[int] = None) -> PrefillInputs:
+    """Seeded prompt for ``cfg``: T = max_ctx rows per head, the first N_b = ctx[b]
+    of them drawn from N(0, 1) (queries, keys and values alike), the rest
+    ``pad_value``.  Retrieval heads and W^K follow make_inputs' streams."""
+    s = cfg.seed if seed is None else seed
+    B, Hkv, Hq, R, Tm = cfg.B, cfg.Hkv, cfg.Hq, cfg.n_ret, cfg.max_ctx
+    assert Hq % Hkv == 0 and 0 <= R <= Hq and len(cfg.ctx) == B and all(1 <= n for n in cfg.ctx)
+    seq_lens = np.asarray(cfg.ctx, dtype=np.int32)
+    if cfg.ret_heads is not None:
+        ret = np.asarray(sorted(cfg.ret_heads), dtype=np.int32)
+    else:
+        ret = np.sort(_rng(s, _T_HEADS).choice(Hq, size=R, replace=False)).astype(np.int32)
+    assert len(ret) == R
+    loc = np.asarray([h for h in range(Hq) if h not in set(ret.tolist())], dtype=np.int32)
+    wscale = np.float32(1.0 / np.sqrt(HEAD_DIM))
+    w_k = np.empty((R, INDEX_DIM, HEAD_DIM), np.uint16)
+    for r in range(R):
+        w_k[r] = f32_to_bf16_bits(_rng(s, _T_WK, r).standard_normal((INDEX_DIM, HEAD_DIM), dtype=np.float32) * wscale)
+    q = np.full((B, Hq, Tm, HEAD_DIM), pad_value, np.uint16)
+    k = np.full((B, Hkv, Tm, HEAD_DIM), pad_value, np.uint16)
+    v = np.full((B, Hkv, Tm, HEAD_DIM), pad_value, np.uint16)
+    jobs = []
+    for b in range(B):
+        n = int(seq_lens[b])
+        jobs += [(q[b, h], (s, _T_PQ, b, h), n) for h in range(Hq)]
+        jobs += [(k[b, g], (s, _T_K, b, g), n) for g in range(Hkv)]
+        jobs += [(v[b, g], (s, _T_V, b, g), n) for g in range(Hkv)]
+    with ThreadPoolExecutor(workers or _workers()) as ex:
+        list(ex.map(lambda a: _fill_normal(a[0], a[1], a[2], HEAD_DIM), jobs))
+    return PrefillInputs(cfg=cfg, seq_lens=seq_lens, ret_heads=ret, loc_heads=loc, q=q, k=k, v=v, w_k=w_k)
+
+
+def prefill_to_device(pin: PrefillInputs, device="cuda") -> Dict[str, "object"]:
+    """Upload a prompt as torch tensors (bf16 tensors keep their bit patterns)."""
+    import torch
+
+    def bf(a: np.ndarray):
+        return torch.from_numpy(np.ascontiguousarray(a)).view(torch.bfloat16).to(device)
+
+    def i32(a: np.ndarray):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+
+    return {"q": bf(pin.q), "k": bf(pin.k), "v": bf(pin.v), "w_k": bf(pin.w_k),
+            "seq_lens": i32(pin.seq_lens), "ret_heads": i32(pin.ret_heads)}
 
 
 def custom_config(name: str = "custom", **kw) -> DecodeConfig:
