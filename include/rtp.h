@@ -285,6 +285,46 @@ rtp_status rtp_decode_step(const void* q_pre, const void* w_q, const void* k_idx
                            const int* kv_slot, int n_full, const void* k_ring, const void* v_ring, int n_ring,
                            void* stream, void* side_stream, void* ev_fork, void* ev_join);
 
+/*
+ * Prefill attention over whole prompts (Review, Adaptive sparse attention: local heads
+ * apply the sliding window + sink rule in prefill as in decode; retrieval heads run full
+ * dense attention; Review, Efficiency & ultra-long robustness: the prefill sparsity is
+ * fixed in advance).  Causal: the query at prompt position i of query head h attends to
+ *   retrieval head (h in ret_heads):  every position 0..i;
+ *   local head:                       [0, min(S, i + 1)) union [max(0, i + 1 - W), i + 1).
+ * out[b, h, i] = softmax(q_i K^T / sqrt(128)) V over that set, for i < seq_lens[b].
+ *
+ *   q          bf16 [B, Hq, max_ctx, 128]   row i = the query at position i
+ *   k, v       bf16 [B, Hkv, max_ctx, 128]  the prompt's keys and values (e.g. the full caches);
+ *                                           query head h uses KV head h / (Hq / Hkv)
+ *   seq_lens   int32 [B]: prompt lengths, 1 <= seq_lens[b] <= max_ctx (device values, not
+ *              checked); rows at or past seq_lens[b] are neither read nor written
+ *   ret_heads  int32 [n_ret] retrieval query heads, distinct (NULL when n_ret == 0)
+ *   window, sinks  W >= 0, S >= 0, W + S >= 1 (ignored when every head is a retrieval head)
+ *   out        fp32 [B, Hq, max_ctx, 128]
+ * Precision: q.k products exact, fp32 accumulation; probabilities and V enter the PV
+ * product as fp16 (V values outside fp16's normal range, |v| < 2^-14 or > 65504, lose
+ * precision or saturate).  Device pointers 16-byte aligned.
+ */
+rtp_status rtp_prefill_attn(const void* q, const void* k, const void* v, const int* seq_lens,
+                            const int* ret_heads, int B, int Hq, int Hkv, int n_ret, int max_ctx,
+                            int window, int sinks, float* out, void* stream);
+
+/*
+ * The prompt's index keys (Review, Adaptive sparse attention equation, the key side of
+ * s_h(m, n)): k_idx[b, r, n] = bf16(W^K_r k^pre[b, g, n]) for n < seq_lens[b], every
+ * retrieval head r (g its KV head), each the exact sum of the 128 products rounded once
+ * to bf16, nearest-even, as rtp_cache_append does for one decode token.
+ *
+ *   k_pre  bf16 [B, Hkv, max_ctx, 128]   pre-RoPE keys
+ *   w_k    bf16 [n_ret, 16, 128]
+ *   k_idx  bf16 [B, n_ret, max_ctx, 16]  rows at or past seq_lens[b] untouched
+ * n_ret == 0 is a no-op.  k_pre, w_k 16-byte aligned; k_idx 2-byte aligned.
+ */
+rtp_status rtp_prefill_index_keys(const void* k_pre, const void* w_k, const int* seq_lens,
+                                  const int* ret_heads, int B, int Hq, int Hkv, int n_ret, int max_ctx,
+                                  void* k_idx, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

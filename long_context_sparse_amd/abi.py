@@ -43,6 +43,8 @@ _SIGS = {
     "rtp_decode_step": ([_vp] * 10 + [_i] * 11 + [_vp] * 6 + [_vp, _sz, _vp, _sz] + [_vp, _i, _vp, _vp, _i]
                         + [_vp] * 4, _i),
     "rtp_cache_append": ([_vp] * 6 + [_i] * 5 + [_vp] * 3 + [_vp, _i, _vp, _vp, _i, _i, _i, _vp], _i),
+    "rtp_prefill_attn": ([_vp] * 5 + [_i] * 7 + [_vp, _vp], _i),
+    "rtp_prefill_index_keys": ([_vp] * 4 + [_i] * 5 + [_vp, _vp], _i),
 }
 
 
@@ -208,3 +210,16 @@ def rtp_local_window_attn(q, k_cache, v_cache, seq_lens, loc_heads, B, Hq, Hkv, 
                                      _nbytes(workspace), _p(kv_slot), n_full, _p(k_ring), _p(v_ring), n_ring,
                                      _s(stream))
     _check("rtp_local_window_attn", st)
+
+
+def rtp_prefill_attn(q, k, v, seq_lens, ret_heads, B, Hq, Hkv, n_ret, max_ctx, window, sinks, out,
+                     stream=None) -> None:
+    st = lib().rtp_prefill_attn(_p(q), _p(k), _p(v), _p(seq_lens), _p(ret_heads) if n_ret else None, B, Hq, Hkv,
+                                n_ret, max_ctx, window, sinks, _p(out), _s(stream))
+    _check("rtp_prefill_attn", st)
+
+
+def rtp_prefill_index_keys(k_pre, w_k, seq_lens, ret_heads, B, Hq, Hkv, n_ret, max_ctx, k_idx, stream=None) -> None:
+    st = lib().rtp_prefill_index_keys(_p(k_pre), _p(w_k), _p(seq_lens), _p(ret_heads), B, Hq, Hkv, n_ret, max_ctx,
+                                      _p(k_idx), _s(stream))
+    _check("rtp_prefill_index_keys", st)

@@ -38,33 +38,6 @@ struct AppendArgs {
   int n_full, n_ring, sinks, window;
 };
 
-// bf16 bit pattern of a double rounded once to nearest, ties to even: 8 significant
-// bits, float32's exponent range, subnormals (quantum 2^-133) below 2^-126, infinity
-// on overflow.
-__device__ __forceinline__ uint32_t bf16_rne(double x) {
-  const uint64_t u = (uint64_t)__double_as_longlong(x);
-  const uint32_t sign = (uint32_t)(u >> 48) & 0x8000u;
-  const int e = (int)((u >> 52) & 0x7FF);
-  const uint64_t mant = u & ((1ull << 52) - 1ull);
-  if (e == 0x7FF) return sign | 0x7F80u | (mant ? 0x40u : 0u);
-  if (e == 0) return sign;                 // float64 subnormals: far below bf16's range
-  const int eb = e - 1023 + 127;           // bf16 biased exponent of 1.m x 2^(e - 1023)
-  const int s = eb > 0 ? 45 : 46 - eb;     // significant bits dropped (more when subnormal)
-  if (s > 63) return sign;
-  const uint64_t sig = (1ull << 52) | mant;
-  uint32_t q = (uint32_t)(sig >> s);
-  const uint64_t rem = sig & ((1ull << s) - 1ull), half = 1ull << (s - 1);
-  if (rem > half || (rem == half && (q & 1u))) ++q;
-  if (eb <= 0) return sign | q;            // q == 128 is the smallest normal's pattern
-  int ebb = eb;
-  if (q == 256u) {
-    q = 128u;
-    ++ebb;
-  }
-  if (ebb >= 255) return sign | 0x7F80u;
-  return sign | ((uint32_t)ebb << 7) | (q - 128u);
-}
-
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   const int b = blockIdx.x, tid = threadIdx.x;
   const int pos = a.seq_lens[b] - 1;

@@ -1,0 +1,339 @@
+// Prefill: causal attention over a whole prompt (Review, Adaptive sparse attention:
+// local heads keep the sliding window + sink rule in prefill as in decode, retrieval
+// heads run full dense attention and so fill the full KV cache; Review, Efficiency &
+// ultra-long robustness: the prefill sparsity is fixed in advance), and the prompt's
+// low-rank index keys bf16(W^K_h k^pre) for the decode-time retrieval (Review, Adaptive
+// sparse attention equation, the key side of s_h(m, n)).
+//
+// Attention is a flash-style MFMA kernel for gfx950.  A 256-thread workgroup takes 128
+// queries of one head (32 per wave) and walks 64-key tiles: all tiles up to the
+// diagonal for a retrieval head, the sink tiles and the window's tiles for a local head
+// (the tiles in between are never loaded).  Per tile and wave:
+//   S^T = K Q^T   16 v_mfma_f32_32x32x16_bf16 (K from LDS as the A operand, the wave's
+//                 queries held in registers as the B operand), so each lane's
+//                 accumulators belong to one query: the online softmax needs only the
+//                 lane's own values and one exchange with lane ^ 32;
+//   O^T += V^T P^T  16 v_mfma_f32_32x32x16_f16: P^T straight from the S^T accumulators
+//                 (rounded to fp16: p in [0, 1], 11 significant bits), V^T from LDS,
+//                 where the tile is stored transposed and converted to fp16 once.
+// Products of bf16 q and k are exact in the fp32 accumulators; V goes to fp16 exactly
+// for |v| in [2^-14, 65504] (smaller values keep an absolute error below 2^-25; larger
+// ones are out of range).  Rows past a prompt's end are never read (loads clamp to its
+// last row) and never written.
+
+#include "rtp_common.hpp"
+
+namespace rtp {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kPfWaves = 4;
+constexpr int kPfThreads = kPfWaves * kWave;
+constexpr int kPfM = 32 * kPfWaves;        // queries per workgroup
+constexpr int kPfN = 64;                   // keys per tile
+constexpr int kKStride = kHeadDim + 8;     // bf16 per K row in LDS (272 B: b128 reads spread over banks)
+constexpr int kVStride = kPfN + 4;         // fp16 per V^T row in LDS (136 B)
+
+struct PrefillArgs {
+  const uint16_t* q;  // bf16 [B, Hq, T, 128]
+  const uint16_t* k;  // bf16 [B, Hkv, T, 128]
+  const uint16_t* v;  // bf16 [B, Hkv, T, 128]
+  const int* seq_lens;
+  const int* ret_heads;
+  float* out;         // fp32 [B, Hq, T, 128]
+  int Hq, Hkv, n_ret, T, window, sinks, n_mtiles;
+};
+
+__device__ __forceinline__ uint32_t word(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+__device__ __forceinline__ float max_pair(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
+__device__ __forceinline__ float sum_pair(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+__global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sk[kPfN * kKStride];
+  __shared__ __attribute__((aligned(16))) _Float16 sv[kHeadDim * kVStride];
+  const int h = blockIdx.x, b = blockIdx.z;
+  const int mt = a.n_mtiles - 1 - (int)blockIdx.y;  // the late (heavy) query tiles first
+  const int N = a.seq_lens[b];
+  const int m0 = mt * kPfM;
+  if (m0 >= N) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hi = lane >> 5;
+  const int G = a.Hq / a.Hkv, g = h / G;
+  bool ret = false;  // is h a retrieval head
+  for (int i0 = 0; i0 < a.n_ret; i0 += kWave) {
+    const int i = i0 + lane;
+    ret |= __ballot(i < a.n_ret && a.ret_heads[i] == h) != 0;
+  }
+  const int S = a.sinks, W = a.window;
+
+  // key tiles: [r0b, r0e) then [r1b, r1e)
+  const int qlast = min(m0 + kPfM, N) - 1;
+  const int kt_end = qlast / kPfN + 1;
+  int r0e = kt_end, r1b = 0, r1e = 0;
+  if (!ret) {
+    const int se = min(ceil_div(S, kPfN), kt_end);  // tiles holding sinks
+    if (W == 0) {
+      r0e = se;
+    } else {
+      const int ws = max(0, m0 + 1 - W) / kPfN;       // first tile of the earliest query's window
+      if (ws > se) {
+        r0e = se;
+        r1b = ws;
+        r1e = kt_end;
+      }
+    }
+  }
+  const int n0 = r0e, ntiles = r0e + (r1e - r1b);
+
+  const size_t kvoff = ((size_t)b * a.Hkv + g) * (size_t)a.T * kHeadDim;
+  const uint16_t* __restrict__ kbase = a.k + kvoff;
+  const uint16_t* __restrict__ vbase = a.v + kvoff;
+
+  // this wave's queries; lane holds query qw0 + (lane & 31) (row clamped for loading)
+  const int qw0 = m0 + 32 * wave, qw1 = qw0 + 31;
+  const int qi = qw0 + (lane & 31);
+  uint4 qreg[8];
+  {
+    const uint16_t* qrow = a.q + (((size_t)b * a.Hq + h) * a.T + min(qi, N - 1)) * kHeadDim + 8 * hi;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) qreg[c] = ld16(qrow + 16 * c);
+  }
+
+  uint4 kreg[4], vreg[4];
+  auto gload = [&](int t) {
+    const int kt = t < n0 ? t : r1b + (t - n0);
+    const int key0 = kt * kPfN;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int ch = tid + e * kPfThreads;  // 1024 chunks of 16 B: row ch / 16, column ch % 16
+      const int key = min(key0 + (ch >> 4), N - 1);
+      kreg[e] = ld16(kbase + (size_t)key * kHeadDim + (ch & 15) * 8);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {  // keys 4 (tid / 16) + e, dims 8 (tid % 16) + 0..7
+      const int key = min(key0 + 4 * (tid >> 4) + e, N - 1);
+      vreg[e] = ld16(vbase + (size_t)key * kHeadDim + (tid & 15) * 8);
+    }
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int ch = tid + e * kPfThreads;
+      *reinterpret_cast<uint4*>(&sk[(ch >> 4) * kKStride + (ch & 15) * 8]) = kreg[e];
+    }
+    const int kg = tid >> 4, dc = tid & 15;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      f16x4_t hv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w = word(vreg[e], d >> 1);
+        hv[e] = (_Float16)((d & 1) ? bf_hi(w) : bf_lo(w));
+      }
+      *reinterpret_cast<f16x4_t*>(&sv[(dc * 8 + d) * kVStride + kg * 4]) = hv;
+    }
+  };
+
+  f32x16_t acc[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[d][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float scale = (float)(kLog2e / 11.313708498984761);  // log2(e) / sqrt(128)
+
+  if (ntiles > 0) gload(0);
+  for (int t = 0; t < ntiles; ++t) {
+    const int kt = t < n0 ? t : r1b + (t - n0);
+    const int key0 = kt * kPfN, key1 = key0 + kPfN - 1;
+    __syncthreads();  // the previous tile's LDS reads are done
+    lstore();
+    __syncthreads();
+    if (t + 1 < ntiles) gload(t + 1);  // in flight over this tile's compute
+
+    // wave-uniform: skip a tile no query of this wave attends to; mask only at edges
+    const bool skip = qw0 >= N || key0 > qw1 || (!ret && key0 >= S && key1 <= qw0 - W);
+    if (skip) continue;
+    const bool full = key1 <= qw0 && (ret || key1 < S || key0 > qw1 - W);
+
+    f32x16_t s[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
+      const uint16_t* krow = &sk[(32 * sb + (lane & 31)) * kKStride + 8 * hi];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const uint4 kv = *reinterpret_cast<const uint4*>(krow + 16 * c);
+        s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv),
+                                                         __builtin_bit_cast(bf16x8_t, qreg[c]), s[sb], 0, 0, 0);
+      }
+    }
+    // lane's scores: key key0 + 32 sb + 8 (r / 4) + 4 hi + r % 4, query qi (log2 units)
+    float mt_ = -INFINITY;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = s[sb][r] * scale;
+        if (!full) {
+          const int key = key0 + 32 * sb + 8 * (r >> 2) + 4 * hi + (r & 3);
+          const bool ok = key <= qi && (ret || key < S || key > qi - W);
+          x = ok ? x : -INFINITY;
+        }
+        s[sb][r] = x;
+        mt_ = fmaxf(mt_, x);
+      }
+    mt_ = max_pair(mt_);
+    const float m_new = fmaxf(m_run, mt_);
+    // nothing attended yet for this query: subtract 0 instead of -inf, so p = 0 and
+    // alpha = 0 without a branch (the MFMAs below run for the whole wave)
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+    float ls = 0.f;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(s[sb][r] - m_use);
+        s[sb][r] = p;
+        ls += p;
+      }
+    l_run = l_run * alpha + ls;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      f16x8_t pb;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) pb[u] = (_Float16)s[c >> 1][8 * (c & 1) + u];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const _Float16* vrow = &sv[(32 * d + (lane & 31)) * kVStride + 16 * c + 4 * hi];
+        const f16x4_t lo = *reinterpret_cast<const f16x4_t*>(vrow);
+        const f16x4_t up = *reinterpret_cast<const f16x4_t*>(vrow + 8);
+        const f16x8_t av = {lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+        acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb, acc[d], 0, 0, 0);
+      }
+    }
+  }
+
+  // lanes l and l ^ 32 hold the two halves of query qi's keys; both have m_run
+  const float lt = sum_pair(l_run);
+  if (qi >= N) return;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  float* orow = a.out + (((size_t)b * a.Hq + h) * a.T + qi) * kHeadDim;
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 o = make_float4(acc[d][4 * q4] * inv, acc[d][4 * q4 + 1] * inv, acc[d][4 * q4 + 2] * inv,
+                                   acc[d][4 * q4 + 3] * inv);
+      *reinterpret_cast<float4*>(orow + 32 * d + 8 * q4 + 4 * hi) = o;
+    }
+}
+
+// ---------------------------------------------------------------- prompt index keys
+constexpr int kKeyThreads = 256;
+constexpr int kKeyRows = 64;  // prompt rows per workgroup
+
+struct KeyArgs {
+  const uint16_t* k_pre;  // bf16 [B, Hkv, T, 128]
+  const uint16_t* w_k;    // bf16 [n_ret, 16, 128]
+  const int* seq_lens;
+  const int* ret_heads;
+  uint16_t* k_idx;        // bf16 [B, n_ret, T, 16]
+  int Hq, Hkv, n_ret, T;
+};
+
+// Thread (i, part): output dim i = tid / 16 of every row, over dims 8 part .. 8 part + 7;
+// its W^K_h slice stays in registers as doubles.  Sums in fp64 (exact products, < 2^-50
+// relative error), one rounding to bf16, as the decode-side append does.
+__global__ __launch_bounds__(kKeyThreads) void prompt_keys_kernel(KeyArgs a) {
+  const int r = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int N = a.seq_lens[b];
+  const int row0 = blockIdx.x * kKeyRows;
+  if (row0 >= N) return;
+  const int i = tid >> 4, part = tid & 15;
+  const int g = a.ret_heads[r] / (a.Hq / a.Hkv);
+  const uint4 wv = ld16(a.w_k + ((size_t)r * kIndexDim + i) * kHeadDim + part * 8);
+  const double w[8] = {bf_lo(wv.x), bf_hi(wv.x), bf_lo(wv.y), bf_hi(wv.y),
+                       bf_lo(wv.z), bf_hi(wv.z), bf_lo(wv.w), bf_hi(wv.w)};
+  const uint16_t* kp = a.k_pre + ((size_t)b * a.Hkv + g) * (size_t)a.T * kHeadDim + part * 8;
+  uint16_t* ko = a.k_idx + ((size_t)b * a.n_ret + r) * (size_t)a.T * kIndexDim + i;
+  const int row1 = min(row0 + kKeyRows, N);
+  for (int row = row0; row < row1; ++row) {  // uniform trip count: the DPP sums see every lane
+    const uint4 kv = ld16(kp + (size_t)row * kHeadDim);
+    double x = w[0] * (double)bf_lo(kv.x);
+    x = fma(w[1], (double)bf_hi(kv.x), x);
+    x = fma(w[2], (double)bf_lo(kv.y), x);
+    x = fma(w[3], (double)bf_hi(kv.y), x);
+    x = fma(w[4], (double)bf_lo(kv.z), x);
+    x = fma(w[5], (double)bf_hi(kv.z), x);
+    x = fma(w[6], (double)bf_lo(kv.w), x);
+    x = fma(w[7], (double)bf_hi(kv.w), x);
+    x += dpp_f64<kDppXor1>(x);
+    x += dpp_f64<kDppXor2>(x);
+    x += dpp_f64<kDppHalfMirror>(x);
+    x += dpp_f64<kDppMirror>(x);
+    if (part == 0) ko[(size_t)row * kIndexDim] = (uint16_t)bf16_rne(x);
+  }
+}
+
+}  // namespace
+}  // namespace rtp
+
+using namespace rtp;
+
+extern "C" rtp_status rtp_prefill_attn(const void* q, const void* k, const void* v, const int* seq_lens,
+                                       const int* ret_heads, int B, int Hq, int Hkv, int n_ret, int max_ctx,
+                                       int window, int sinks, float* out, void* stream) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || n_ret < 0 || n_ret > Hq || max_ctx <= 0) return RTP_EINVAL;
+  if (Hq % Hkv) return RTP_EINVAL;
+  if (n_ret < Hq && (window < 0 || sinks < 0 || window + sinks < 1)) return RTP_EINVAL;
+  if (!q || !k || !v || !seq_lens || !out || (n_ret > 0 && !ret_heads)) return RTP_EINVAL;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15) return RTP_EINVAL;
+  const int n_mtiles = ceil_div(max_ctx, kPfM);
+  if (n_mtiles > 65535 || Hq > 65535 || B > 65535) return RTP_EUNSUPPORTED;
+  const PrefillArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                      static_cast<const uint16_t*>(v), seq_lens, ret_heads, out, Hq, Hkv, n_ret, max_ctx,
+                      n_ret < Hq ? window : 0, n_ret < Hq ? sinks : 0, n_mtiles};
+  hipLaunchKernelGGL(prefill_kernel, dim3(Hq, n_mtiles, B), dim3(kPfThreads), 0, static_cast<hipStream_t>(stream),
+                     a);
+  return hipGetLastError() == hipSuccess ? RTP_OK : RTP_ELAUNCH;
+}
+
+extern "C" rtp_status rtp_prefill_index_keys(const void* k_pre, const void* w_k, const int* seq_lens,
+                                             const int* ret_heads, int B, int Hq, int Hkv, int n_ret, int max_ctx,
+                                             void* k_idx, void* stream) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || n_ret < 0 || n_ret > Hq || max_ctx <= 0) return RTP_EINVAL;
+  if (Hq % Hkv) return RTP_EINVAL;
+  if (n_ret == 0) return RTP_OK;
+  if (!k_pre || !w_k || !seq_lens || !ret_heads || !k_idx) return RTP_EINVAL;
+  if ((((uintptr_t)k_pre | (uintptr_t)w_k) & 15) || ((uintptr_t)k_idx & 1)) return RTP_EINVAL;
+  const int nx = ceil_div(max_ctx, kKeyRows);
+  if (n_ret > 65535 || B > 65535) return RTP_EUNSUPPORTED;
+  const KeyArgs a{static_cast<const uint16_t*>(k_pre), static_cast<const uint16_t*>(w_k), seq_lens, ret_heads,
+                  static_cast<uint16_t*>(k_idx), Hq, Hkv, n_ret, max_ctx};
+  hipLaunchKernelGGL(prompt_keys_kernel, dim3(nx, n_ret, B), dim3(kKeyThreads), 0, static_cast<hipStream_t>(stream),
+                     a);
+  return hipGetLastError() == hipSuccess ? RTP_OK : RTP_ELAUNCH;
+}

@@ -126,6 +126,33 @@ __device__ __forceinline__ uint4 ld16_nt(const uint16_t* p) {
   return make_uint4(t.x, t.y, t.z, t.w);
 }
 
+// bf16 bit pattern of a double rounded once to nearest, ties to even: 8 significant
+// bits, float32's exponent range, subnormals (quantum 2^-133) below 2^-126, infinity
+// on overflow.
+__device__ __forceinline__ uint32_t bf16_rne(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const uint32_t sign = (uint32_t)(u >> 48) & 0x8000u;
+  const int e = (int)((u >> 52) & 0x7FF);
+  const uint64_t mant = u & ((1ull << 52) - 1ull);
+  if (e == 0x7FF) return sign | 0x7F80u | (mant ? 0x40u : 0u);
+  if (e == 0) return sign;                 // float64 subnormals: far below bf16's range
+  const int eb = e - 1023 + 127;           // bf16 biased exponent of 1.m x 2^(e - 1023)
+  const int s = eb > 0 ? 45 : 46 - eb;     // significant bits dropped (more when subnormal)
+  if (s > 63) return sign;
+  const uint64_t sig = (1ull << 52) | mant;
+  uint32_t q = (uint32_t)(sig >> s);
+  const uint64_t rem = sig & ((1ull << s) - 1ull), half = 1ull << (s - 1);
+  if (rem > half || (rem == half && (q & 1u))) ++q;
+  if (eb <= 0) return sign | q;            // q == 128 is the smallest normal's pattern
+  int ebb = eb;
+  if (q == 256u) {
+    q = 128u;
+    ++ebb;
+  }
+  if (ebb >= 255) return sign | 0x7F80u;
+  return sign | ((uint32_t)ebb << 7) | (q - 128u);
+}
+
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

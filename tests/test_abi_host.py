@@ -179,3 +179,28 @@ def test_decode_step_rejects():
     bad = list(args)
     bad[31:36] = [FAKE, 2, FAKE, FAKE, 1]              # three slots for two groups
     assert L.rtp_decode_step(*bad) == abi.RTP_EINVAL
+
+
+def test_prefill_rejects():
+    L = abi.lib()
+
+    def attn(B=1, Hq=8, Hkv=2, n_ret=2, max_ctx=4096, window=1024, sinks=4, q=FAKE, rh=FAKE):
+        return L.rtp_prefill_attn(q, FAKE, FAKE, FAKE, rh, B, Hq, Hkv, n_ret, max_ctx, window, sinks, FAKE, None)
+    assert attn(B=0) == abi.RTP_EINVAL
+    assert attn(Hkv=3) == abi.RTP_EINVAL
+    assert attn(n_ret=9) == abi.RTP_EINVAL
+    assert attn(window=0, sinks=0) == abi.RTP_EINVAL       # local heads with an empty rule
+    assert attn(window=-1) == abi.RTP_EINVAL
+    assert attn(q=None) == abi.RTP_EINVAL
+    assert attn(q=FAKE + 8) == abi.RTP_EINVAL               # misaligned
+    assert attn(rh=None) == abi.RTP_EINVAL                  # retrieval heads without their list
+    assert attn(max_ctx=128 * 65536) == abi.RTP_EUNSUPPORTED
+
+    def keys(B=1, Hq=8, Hkv=2, n_ret=2, max_ctx=4096, k_pre=FAKE, k_idx=FAKE):
+        return L.rtp_prefill_index_keys(k_pre, FAKE, FAKE, FAKE, B, Hq, Hkv, n_ret, max_ctx, k_idx, None)
+    assert keys(B=0) == abi.RTP_EINVAL
+    assert keys(Hkv=3) == abi.RTP_EINVAL
+    assert keys(k_pre=None) == abi.RTP_EINVAL
+    assert keys(k_pre=FAKE + 4) == abi.RTP_EINVAL
+    assert keys(k_idx=FAKE + 1) == abi.RTP_EINVAL
+    assert keys(n_ret=0) == abi.RTP_OK                      # no-op
