@@ -269,6 +269,73 @@ def measure(label: str, steps: int, warmup: int, cold_iters: int, calib_copy: bo
     return res
 
 
+PEAK_MFMA_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 MFMA, vendor figure
+
+
+def prefill_flops(N: int, n_ret: int, n_loc: int, window: int, sinks: int) -> float:
+    """Algorithmic flops of one prefill pass: 4 x 128 per attended (query, key) pair (the
+    q.k dot product and the p.v update).  Position i attends to i + 1 keys in a
+    retrieval head and to min(i + 1, S + W) in a local head (sinks + window)."""
+    dense = N * (N + 1) // 2
+    cap = sinks + window
+    local = (min(N, cap) * (min(N, cap) + 1) // 2) + max(0, N - cap) * cap
+    return 4.0 * 128 * (n_ret * dense + n_loc * local)
+
+
+def measure_prefill(N: int, reps: int, dense_too: bool) -> Dict:
+    """rtp_prefill_attn over one N-token prompt at the pages' prefill configuration
+    (32 query heads on 8 KV heads, 5 retrieval heads ~ 15%, sink 4 + window 8192);
+    synthetic N(0, 1) rows drawn on the device from a fixed seed."""
+    import torch
+
+    from long_context_sparse_amd import abi
+
+    Hq, Hkv, W_, S_ = 32, 8, 8192, 4
+    ret = [3, 9, 15, 20, 30]
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(N)
+    q = torch.randn((1, Hq, N, 128), generator=gen, device=dev).to(torch.bfloat16)
+    k = torch.randn((1, Hkv, N, 128), generator=gen, device=dev).to(torch.bfloat16)
+    v = torch.randn((1, Hkv, N, 128), generator=gen, device=dev).to(torch.bfloat16)
+    out = torch.empty((1, Hq, N, 128), dtype=torch.float32, device=dev)
+    lens = torch.tensor([N], dtype=torch.int32, device=dev)
+
+    def run(heads):
+        rh = torch.tensor(heads, dtype=torch.int32, device=dev)
+        call = lambda: abi.rtp_prefill_attn(q, k, v, lens, rh, 1, Hq, Hkv, len(heads), N, W_, S_, out)  # noqa
+        call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms = run(ret)
+    fl = prefill_flops(N, len(ret), Hq - len(ret), W_, S_)
+    tf = fl / (ms * 1e-3) / 1e12
+    res = {"latency_ms": round(ms, 3), "tflops": round(tf, 1),
+           "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(tf, 1),
+                        "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_MFMA_TFLOPS, 4),
+                        "traffic": None, "alg_flops_per_launch": fl, "avg_launch_us": round(ms * 1e3, 1)},
+           "config": {"workload": f"prefill{N // 1024}k", "batch": 1, "ctx": N, "kv_heads": Hkv, "q_heads": Hq,
+                      "retrieval_heads": len(ret), "head_dim": 128, "window": W_, "sinks": S_}}
+    log(f"[bench] prefill {N}: {ms:.3f} ms, {tf:.1f} TFLOP/s")
+    if dense_too:
+        dms = run(list(range(Hq)))
+        dfl = prefill_flops(N, Hq, 0, W_, S_)
+        res["dense_causal_ms"] = round(dms, 3)
+        res["dense_causal_tflops"] = round(dfl / (dms * 1e-3) / 1e12, 1)
+        res["speedup_vs_dense"] = round(dms / ms, 2)
+        log(f"[bench] prefill {N} all heads dense: {dms:.3f} ms ({dms / ms:.2f}x the sparse pass)")
+    del q, k, v, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def config_of(cfg, k_tokens: int = 0) -> Dict:
     ctx = sorted(set(cfg.ctx))
     sel = {"top_k_tokens": k_tokens} if k_tokens else {"top_p": sorted(set(cfg.top_p))}
@@ -317,6 +384,8 @@ def main(argv: Optional[List[str]] = None) -> int:
     ap.add_argument("--workload", default="ctx128k")
     ap.add_argument("--also", default="ctx1m,ctx128k@topk4096",
                     help="comma-separated extra workloads ('' for none); name@topkK: static top-k rule")
+    ap.add_argument("--prefill", default="32768,131072",
+                    help="comma-separated prompt lengths for the prefill pass ('' for none)")
     ap.add_argument("--cold-iters", type=int, default=20)
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -335,6 +404,10 @@ def main(argv: Optional[List[str]] = None) -> int:
     extras = {}
     for name in [x for x in a.also.split(",") if x and x != a.workload]:
         extras[name] = measure(name, a.steps, a.warmup, a.cold_iters, False)
+
+    prefill = {}
+    for n in [int(x) for x in a.prefill.split(",") if x]:
+        prefill[f"prefill{n // 1024}k"] = measure_prefill(n, 5 if n <= 65536 else 2, dense_too=n <= 65536)
 
     cpu = None
     if not a.no_cpu_baseline:
@@ -362,6 +435,7 @@ def main(argv: Optional[List[str]] = None) -> int:
         "cpu_baseline": cpu,
         "detail": summary(head),
         "also": {k: summary(v) for k, v in extras.items()},
+        "prefill": prefill,
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -64,16 +64,19 @@ __device__ __forceinline__ float sum_pair(float v) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
-__global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sk[kPfN * kKStride];
   __shared__ __attribute__((aligned(16))) _Float16 sv[kHeadDim * kVStride];
-  const int h = blockIdx.x, b = blockIdx.z;
+  // Workgroups go to the 8 XCDs round-robin by linear id (x + Hq y + ...), so a fixed
+  // x -> head map would put a retrieval head's (heavier, causal) workgroups on the same
+  // XCD in every row; rotating the map by the row spreads them over all XCDs.
+  const int G = a.Hq / a.Hkv;
+  const int h = ((int)blockIdx.x + (int)blockIdx.y) % a.Hq, g = h / G, b = blockIdx.z;
   const int mt = a.n_mtiles - 1 - (int)blockIdx.y;  // the late (heavy) query tiles first
   const int N = a.seq_lens[b];
   const int m0 = mt * kPfM;
   if (m0 >= N) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hi = lane >> 5;
-  const int G = a.Hq / a.Hkv, g = h / G;
   bool ret = false;  // is h a retrieval head
   for (int i0 = 0; i0 < a.n_ret; i0 += kWave) {
     const int i = i0 + lane;
@@ -184,42 +187,53 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a) {
                                                          __builtin_bit_cast(bf16x8_t, qreg[c]), s[sb], 0, 0, 0);
       }
     }
-    // lane's scores: key key0 + 32 sb + 8 (r / 4) + 4 hi + r % 4, query qi (log2 units)
+    // lane's scores: key key0 + 32 sb + 8 (r / 4) + 4 hi + r % 4, query qi (raw q.k)
+    // masks as compares of the element's compile-time key offset c (key = kb + c) with
+    // three per-lane bounds: key <= qi, key < S (sink), key > qi - W (window)
     float mt_ = -INFINITY;
+    if (full) {
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
+      for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[sb][r] * scale;
-        if (!full) {
-          const int key = key0 + 32 * sb + 8 * (r >> 2) + 4 * hi + (r & 3);
-          const bool ok = key <= qi && (ret || key < S || key > qi - W);
-          x = ok ? x : -INFINITY;
+        for (int r = 0; r < 16; ++r) mt_ = fmaxf(mt_, s[sb][r]);
+    } else {
+      const int kb = key0 + 4 * hi;
+      const int d_causal = qi - kb, d_win = qi - W - kb, d_sink = S - kb;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = 32 * sb + 8 * (r >> 2) + (r & 3);
+          const bool ok = (c <= d_causal) & (ret | (c < d_sink) | (c > d_win));
+          s[sb][r] = ok ? s[sb][r] : -INFINITY;
+          mt_ = fmaxf(mt_, s[sb][r]);
         }
-        s[sb][r] = x;
-        mt_ = fmaxf(mt_, x);
-      }
+    }
     mt_ = max_pair(mt_);
-    const float m_new = fmaxf(m_run, mt_);
-    // nothing attended yet for this query: subtract 0 instead of -inf, so p = 0 and
-    // alpha = 0 without a branch (the MFMAs below run for the whole wave)
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
+    // rescale only when some query's maximum grew (wave-uniform branch); elsewhere the
+    // factor would be exactly 1
+    if (__ballot(mt_ > m_run) != 0) {
+      const float m_new = fmaxf(m_run, mt_);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * scale);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
+    }
+    // p = 2^((s - m) scale); nothing attended yet (m = -inf): p = 0 for every key
+    const float msc = m_run == -INFINITY ? 0.f : m_run * scale;
     float ls = 0.f;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(s[sb][r] - m_use);
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[sb][r], scale, -msc));
         s[sb][r] = p;
         ls += p;
       }
-    l_run = l_run * alpha + ls;
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
+    l_run += ls;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       f16x8_t pb;
