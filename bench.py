@@ -115,14 +115,33 @@ def algorithmic_bytes(cfg, inp, sel_idx: np.ndarray, sel_cnt: np.ndarray) -> Dic
 
 
 # ------------------------------------------------------------------ traffic records
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
+KERNEL_SOURCE = {"index_topp_kernel": "index_topp.hip", "sparse_attn_kernel": "sparse_attn.hip",
+                 "merge_kernel": "sparse_attn.hip", "local_window_kernel": "sparse_attn.hip",
+                 "prefill_kernel": "prefill_attn.hip"}
+
+
+def kernel_source_hash(kernel: str) -> str:
+    """sha256 (16 hex digits) of the sources `kernel` is compiled from: its .hip file and
+    every header it includes from csrc/ or include/, transitively."""
+    import re
     csrc = os.path.join(ROOT, "long_context_sparse_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode())
-                h.update(f.read())
+    inc = os.path.join(ROOT, "include")
+    seen, todo = [], [KERNEL_SOURCE[kernel]]
+    while todo:
+        name = todo.pop()
+        if name in seen:
+            continue
+        path = next((os.path.join(d, name) for d in (csrc, inc) if os.path.exists(os.path.join(d, name))), None)
+        if path is None:
+            continue
+        seen.append(name)
+        todo += re.findall(r'^\s*#include\s+"([^"]+)"', open(path).read(), flags=re.M)
+    h = hashlib.sha256()
+    for name in sorted(seen):
+        path = next(os.path.join(d, name) for d in (csrc, inc) if os.path.exists(os.path.join(d, name)))
+        with open(path, "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -138,7 +157,7 @@ def read_traffic(workload: str, kernel: str) -> Optional[float]:
             if line.startswith("- ") and ":" in line:
                 k, v = line[2:].split(":", 1)
                 vals[k.strip()] = v.strip().strip("`")
-    if vals.get("kernel_sources_sha256") != kernel_source_hash():
+    if vals.get("kernel_sources_sha256") != kernel_source_hash(KERNEL_NAMES.get(kernel, kernel)):
         return None
     try:
         return float(vals["traffic_bytes_per_launch"])
