@@ -31,7 +31,10 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kPfWaves = 4;
+#ifndef RTP_PREFILL_WAVES
+#define RTP_PREFILL_WAVES 8
+#endif
+constexpr int kPfWaves = RTP_PREFILL_WAVES;
 constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kPfM = 32 * kPfWaves;        // queries per workgroup
 constexpr int kPfN = 64;                   // keys per tile
@@ -64,7 +67,7 @@ __device__ __forceinline__ float sum_pair(float v) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
-__global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kPfThreads, 8 / kPfWaves) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sk[kPfN * kKStride];
   __shared__ __attribute__((aligned(16))) _Float16 sv[kHeadDim * kVStride];
   // Workgroups go to the 8 XCDs round-robin by linear id (x + Hq y + ...), so a fixed
@@ -117,38 +120,52 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(PrefillArgs a) {
     for (int c = 0; c < 8; ++c) qreg[c] = ld16(qrow + 16 * c);
   }
 
+  // tile copies: 256 threads move K (1024 chunks of 16 B, 4 each); with 8 waves the other
+  // 256 move V, each 4 keys x 8 dims, stored transposed in fp16 (with 4 waves every
+  // thread does both)
+  constexpr int kCopy = 256;
+  const bool do_k = kPfWaves == 4 || tid >= kCopy, do_v = kPfWaves == 4 || tid < kCopy;
+  const int ct = tid & (kCopy - 1);
   uint4 kreg[4], vreg[4];
   auto gload = [&](int t) {
     const int kt = t < n0 ? t : r1b + (t - n0);
     const int key0 = kt * kPfN;
+    if (do_k) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int ch = tid + e * kPfThreads;  // 1024 chunks of 16 B: row ch / 16, column ch % 16
-      const int key = min(key0 + (ch >> 4), N - 1);
-      kreg[e] = ld16(kbase + (size_t)key * kHeadDim + (ch & 15) * 8);
+      for (int e = 0; e < 4; ++e) {
+        const int ch = ct + e * kCopy;  // row ch / 16, column ch % 16
+        const int key = min(key0 + (ch >> 4), N - 1);
+        kreg[e] = ld16(kbase + (size_t)key * kHeadDim + (ch & 15) * 8);
+      }
     }
+    if (do_v) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {  // keys 4 (tid / 16) + e, dims 8 (tid % 16) + 0..7
-      const int key = min(key0 + 4 * (tid >> 4) + e, N - 1);
-      vreg[e] = ld16(vbase + (size_t)key * kHeadDim + (tid & 15) * 8);
+      for (int e = 0; e < 4; ++e) {  // keys 4 (ct / 16) + e, dims 8 (ct % 16) + 0..7
+        const int key = min(key0 + 4 * (ct >> 4) + e, N - 1);
+        vreg[e] = ld16(vbase + (size_t)key * kHeadDim + (ct & 15) * 8);
+      }
     }
   };
   auto lstore = [&]() {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int ch = tid + e * kPfThreads;
-      *reinterpret_cast<uint4*>(&sk[(ch >> 4) * kKStride + (ch & 15) * 8]) = kreg[e];
-    }
-    const int kg = tid >> 4, dc = tid & 15;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      f16x4_t hv;
+    if (do_k) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t w = word(vreg[e], d >> 1);
-        hv[e] = (_Float16)((d & 1) ? bf_hi(w) : bf_lo(w));
+        const int ch = ct + e * kCopy;
+        *reinterpret_cast<uint4*>(&sk[(ch >> 4) * kKStride + (ch & 15) * 8]) = kreg[e];
       }
-      *reinterpret_cast<f16x4_t*>(&sv[(dc * 8 + d) * kVStride + kg * 4]) = hv;
+    }
+    if (do_v) {
+      const int kg = ct >> 4, dc = ct & 15;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        f16x4_t hv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t w = word(vreg[e], d >> 1);
+          hv[e] = (_Float16)((d & 1) ? bf_hi(w) : bf_lo(w));
+        }
+        *reinterpret_cast<f16x4_t*>(&sv[(dc * 8 + d) * kVStride + kg * 4]) = hv;
+      }
     }
   };
 
