@@ -286,6 +286,22 @@ rtp_status rtp_decode_step(const void* q_pre, const void* w_q, const void* k_idx
                            void* stream, void* side_stream, void* ev_fork, void* ev_join);
 
 /*
+ * Ring fill after a prefill (KV placement above): for every ring group (kv_slot[g] < 0),
+ * ring row r of sequence b receives the K and V rows of the position it holds once the
+ * prompt's N = seq_lens[b] tokens are in: r < S: position r (if r < N); r = S + j: the
+ * latest position p < N with p >= max(S, N - W) and (p - S) mod W = j.  Rows no
+ * position maps to are left untouched; full groups are skipped.
+ *
+ *   k, v           bf16 [B, Hkv, max_ctx, 128]  the prompt's keys and values
+ *   kv_slot        int32 [Hkv] (device), slots in range (not checked)
+ *   k_ring, v_ring bf16 [B, n_ring, sinks + window, 128]
+ * n_ring == 0 is a no-op.  Device pointers 16-byte aligned.
+ */
+rtp_status rtp_ring_fill(const void* k, const void* v, const int* seq_lens, const int* kv_slot, int B, int Hkv,
+                         int max_ctx, void* k_ring, void* v_ring, int n_ring, int sinks, int window,
+                         void* stream);
+
+/*
  * Prefill attention over whole prompts (Review, Adaptive sparse attention: local heads
  * apply the sliding window + sink rule in prefill as in decode; retrieval heads run full
  * dense attention; Review, Efficiency & ultra-long robustness: the prefill sparsity is

@@ -45,6 +45,7 @@ _SIGS = {
     "rtp_cache_append": ([_vp] * 6 + [_i] * 5 + [_vp] * 3 + [_vp, _i, _vp, _vp, _i, _i, _i, _vp], _i),
     "rtp_prefill_attn": ([_vp] * 5 + [_i] * 7 + [_vp, _vp], _i),
     "rtp_prefill_index_keys": ([_vp] * 4 + [_i] * 5 + [_vp, _vp], _i),
+    "rtp_ring_fill": ([_vp] * 4 + [_i] * 3 + [_vp, _vp] + [_i] * 3 + [_vp], _i),
 }
 
 
@@ -223,3 +224,10 @@ def rtp_prefill_index_keys(k_pre, w_k, seq_lens, ret_heads, B, Hq, Hkv, n_ret, m
     st = lib().rtp_prefill_index_keys(_p(k_pre), _p(w_k), _p(seq_lens), _p(ret_heads), B, Hq, Hkv, n_ret, max_ctx,
                                       _p(k_idx), _s(stream))
     _check("rtp_prefill_index_keys", st)
+
+
+def rtp_ring_fill(k, v, seq_lens, kv_slot, B, Hkv, max_ctx, k_ring, v_ring, n_ring, sinks, window,
+                  stream=None) -> None:
+    st = lib().rtp_ring_fill(_p(k), _p(v), _p(seq_lens), _p(kv_slot), B, Hkv, max_ctx, _p(k_ring), _p(v_ring),
+                             n_ring, sinks, window, _s(stream))
+    _check("rtp_ring_fill", st)

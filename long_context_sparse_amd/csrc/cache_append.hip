@@ -79,10 +79,66 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   }
 }
 
+// Ring fill after a prefill: ring row r of a ring group receives the position it holds
+// once the prompt's N tokens are in (r < S: position r; r = S + j: the latest position
+// p < N with p >= max(S, N - W) and (p - S) mod W = j); rows no position maps to are
+// left untouched.  One workgroup per 16 ring rows of a (KV group, sequence): 16 lanes
+// copy a 256-byte K row and another 16 its V row.
+constexpr int kFillRows = 16;
+
+struct FillArgs {
+  const uint4* k;  // bf16 [B, Hkv, T, 128]
+  const uint4* v;
+  const int* seq_lens;
+  const int* kv_slot;
+  uint4* kr;       // bf16 [B, n_ring, S + W, 128]
+  uint4* vr;
+  int Hkv, T, n_ring, sinks, window;
+};
+
+__global__ __launch_bounds__(kAppendThreads) void ring_fill_kernel(FillArgs a) {
+  const int g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int slot = a.kv_slot[g];
+  if (slot >= 0) return;
+  const int N = a.seq_lens[b], S = a.sinks, W = a.window;
+  const int r = blockIdx.x * kFillRows + (tid >> 4);  // one ring row per 16 threads
+  if (r >= S + W) return;
+  int p;
+  if (r < S) {
+    p = r < N ? r : -1;
+  } else {
+    const int j = r - S;
+    p = N - 1 - ((((N - 1 - S - j) % W) + W) % W);
+    if (p < max(S, N - W)) p = -1;
+  }
+  if (p < 0) return;
+  const int c = tid & 15;
+  const size_t src = (((size_t)b * a.Hkv + g) * a.T + p) * 16 + c;
+  const size_t dst = (((size_t)b * a.n_ring + (-1 - slot)) * (S + W) + r) * 16 + c;
+  a.kr[dst] = a.k[src];
+  a.vr[dst] = a.v[src];
+}
+
 }  // namespace
 }  // namespace rtp
 
 using namespace rtp;
+
+extern "C" rtp_status rtp_ring_fill(const void* k, const void* v, const int* seq_lens, const int* kv_slot, int B,
+                                    int Hkv, int max_ctx, void* k_ring, void* v_ring, int n_ring, int sinks,
+                                    int window, void* stream) {
+  if (B <= 0 || Hkv <= 0 || max_ctx <= 0 || n_ring < 0 || n_ring > Hkv || sinks < 0 || window < 0) return RTP_EINVAL;
+  if (n_ring == 0) return RTP_OK;
+  if (sinks + window < 1) return RTP_EINVAL;
+  if (!k || !v || !seq_lens || !kv_slot || !k_ring || !v_ring) return RTP_EINVAL;
+  if (((uintptr_t)k | (uintptr_t)v | (uintptr_t)k_ring | (uintptr_t)v_ring) & 15) return RTP_EINVAL;
+  if (B > 65535 || Hkv > 65535) return RTP_EUNSUPPORTED;
+  const FillArgs a{static_cast<const uint4*>(k), static_cast<const uint4*>(v), seq_lens, kv_slot,
+                   static_cast<uint4*>(k_ring), static_cast<uint4*>(v_ring), Hkv, max_ctx, n_ring, sinks, window};
+  hipLaunchKernelGGL(ring_fill_kernel, dim3(ceil_div(sinks + window, kFillRows), Hkv, B), dim3(kAppendThreads), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return hipGetLastError() == hipSuccess ? RTP_OK : RTP_ELAUNCH;
+}
 
 extern "C" rtp_status rtp_cache_append(const void* k_new, const void* v_new, const void* k_pre, const void* w_k,
                                        const int* seq_lens, const int* ret_heads, int B, int Hq, int Hkv, int n_ret,

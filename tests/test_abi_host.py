@@ -194,7 +194,7 @@ def test_prefill_rejects():
     assert attn(q=None) == abi.RTP_EINVAL
     assert attn(q=FAKE + 8) == abi.RTP_EINVAL               # misaligned
     assert attn(rh=None) == abi.RTP_EINVAL                  # retrieval heads without their list
-    assert attn(max_ctx=128 * 65536) == abi.RTP_EUNSUPPORTED
+    assert attn(max_ctx=1 << 30) == abi.RTP_EUNSUPPORTED     # more query tiles than a grid holds
 
     def keys(B=1, Hq=8, Hkv=2, n_ret=2, max_ctx=4096, k_pre=FAKE, k_idx=FAKE):
         return L.rtp_prefill_index_keys(k_pre, FAKE, FAKE, FAKE, B, Hq, Hkv, n_ret, max_ctx, k_idx, None)
@@ -204,3 +204,17 @@ def test_prefill_rejects():
     assert keys(k_pre=FAKE + 4) == abi.RTP_EINVAL
     assert keys(k_idx=FAKE + 1) == abi.RTP_EINVAL
     assert keys(n_ret=0) == abi.RTP_OK                      # no-op
+
+
+def test_ring_fill_rejects():
+    L = abi.lib()
+
+    def fill(B=1, Hkv=2, max_ctx=4096, n_ring=1, sinks=4, window=16, k=FAKE, kr=FAKE):
+        return L.rtp_ring_fill(k, FAKE, FAKE, FAKE, B, Hkv, max_ctx, kr, FAKE, n_ring, sinks, window, None)
+    assert fill(B=0) == abi.RTP_EINVAL
+    assert fill(n_ring=3) == abi.RTP_EINVAL             # more rings than groups
+    assert fill(sinks=0, window=0) == abi.RTP_EINVAL    # a ring of no rows
+    assert fill(window=-1) == abi.RTP_EINVAL
+    assert fill(k=None) == abi.RTP_EINVAL
+    assert fill(kr=FAKE + 8) == abi.RTP_EINVAL          # misaligned
+    assert fill(n_ring=0) == abi.RTP_OK                 # no-op

@@ -177,3 +177,94 @@ def test_decode_loop_with_appends(window, sinks, steps):
         assert np.array_equal(vf[b, :, :n], want["v_full"][b, :, :n])
 
 
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_ring_fill_matches_placement(name):
+    """rtp_ring_fill from the prompt's full K/V gives the placement rule's ring rows bit
+    for bit; rows no position maps to keep what they held."""
+    cfg = W.custom_config(name=f"ring_{name}", **CASES[name])
+    inp = W.make_inputs(cfg)
+    rings = local_groups(inp)
+    pl = place(inp, rings)
+    say(f"[gpu] ring fill {name}: ring groups {rings}")
+    kr = torch.full(pl["k_ring"].shape, 3.0, dtype=torch.bfloat16, device="cuda")
+    vr = torch.full(pl["v_ring"].shape, 3.0, dtype=torch.bfloat16, device="cuda")
+    t = W.to_device(inp)
+    abi.rtp_ring_fill(t["k_cache"], t["v_cache"], t["seq_lens"], torch.from_numpy(pl["kv_slot"]).cuda(), cfg.B,
+                      cfg.Hkv, cfg.max_ctx, kr, vr, len(rings), cfg.sinks, cfg.window)
+    torch.cuda.synchronize()
+    got_k, got_v = _host(kr), _host(vr)
+    three = W.f32_to_bf16_bits(np.float32([3.0]))[0]
+    for b, n in enumerate(inp.seq_lens):
+        held = sorted({ring_row(int(p), cfg.sinks, cfg.window) for p in O.local_tokens(int(n), cfg.window, cfg.sinks)})
+        empty = [r for r in range(cfg.sinks + cfg.window) if r not in held]
+        assert np.array_equal(got_k[b, :, held], pl["k_ring"][b, :, held])
+        assert np.array_equal(got_v[b, :, held], pl["v_ring"][b, :, held])
+        assert (got_k[b, :, empty] == three).all() and (got_v[b, :, empty] == three).all()
+
+
+def test_prefill_then_decode():
+    """The whole cache life cycle on the device: the prompt's index keys
+    (rtp_prefill_index_keys) and rings (rtp_ring_fill) from its K/V, then decode steps
+    that append tokens and wrap the rings; every step against the oracle over the full
+    caches, whose prompt index keys the oracle computes itself."""
+    B, Hkv, Hq, n_ret, steps, window, sinks = 2, 2, 8, 2, 40, 32, 4
+    n0 = (300, 30)
+    cfg = W.custom_config(name="prefill_decode", seed=77, B=B, Hkv=Hkv, Hq=Hq, n_ret=n_ret, ret_heads=(0, 2),
+                          ctx=tuple(n + steps for n in n0), window=window, sinks=sinks, split_tokens=128)
+    inp = W.make_inputs(cfg)
+    G = cfg.gqa
+    inp.seq_lens[:] = n0
+    say(f"[gpu] prefill then decode: prompts {n0}, {steps} steps, window {window} sinks {sinks}")
+    for b, n in enumerate(n0):                         # the oracle's own prompt index keys
+        for r, h in enumerate(inp.ret_heads):
+            for i in range(n):
+                inp.k_idx[b, r, i] = O.index_key(inp.w_k[r], inp.k_cache[b, int(h) // G, i])
+    full = W.to_device(inp)                            # the prompt's K/V of every group
+    rings = local_groups(inp)
+    assert rings == [1]
+    kv_slot = torch.tensor([0, -1], dtype=torch.int32, device="cuda")
+    k_idx = torch.full_like(full["k_idx"], 5.0)
+    abi.rtp_prefill_index_keys(full["k_cache"], _bf(inp.w_k), full["seq_lens"], full["ret_heads"], B, Hq, Hkv, n_ret,
+                               cfg.max_ctx, k_idx)
+    kr = torch.zeros((B, 1, sinks + window, 128), dtype=torch.bfloat16, device="cuda")
+    vr = torch.zeros_like(kr)
+    abi.rtp_ring_fill(full["k_cache"], full["v_cache"], full["seq_lens"], kv_slot, B, Hkv, cfg.max_ctx, kr, vr, 1,
+                      sinks, window)
+    torch.cuda.synchronize()
+    ki = _host(k_idx)
+    for b, n in enumerate(n0):
+        assert np.array_equal(ki[b, :, :n], inp.k_idx[b, :, :n]), b
+    # decode state: group 0 keeps a full cache (its prompt rows, junk past them), group 1 its ring
+    kc = full["k_cache"][:, :1].clone()
+    vc = full["v_cache"][:, :1].clone()
+    for b, n in enumerate(n0):
+        kc[b, :, n:] = 30.0
+        vc[b, :, n:] = 1000.0
+    t = dict(full)
+    t.update(k_cache=kc, v_cache=vc, k_idx=k_idx, kv_slot=kv_slot, k_ring=kr, v_ring=vr)
+    step = DecodeStep(shape_of(cfg))
+    w_k = _bf(inp.w_k)
+    g = np.random.default_rng(78)
+    for i in range(steps):
+        inp.seq_lens += 1
+        lens = [int(n) for n in inp.seq_lens]
+        k_new = np.stack([inp.k_cache[b, :, n - 1] for b, n in enumerate(lens)])
+        v_new = np.stack([inp.v_cache[b, :, n - 1] for b, n in enumerate(lens)])
+        inp.q[:] = W.f32_to_bf16_bits(g.standard_normal(inp.q.shape, dtype=np.float32))
+        for b, n in enumerate(lens):
+            for r, h in enumerate(inp.ret_heads):
+                inp.k_idx[b, r, n - 1] = O.index_key(inp.w_k[r], k_new[b, int(h) // G])
+        t["seq_lens"].copy_(torch.from_numpy(inp.seq_lens.astype(np.int32)))
+        t["q"].copy_(_bf(inp.q))
+        abi.rtp_cache_append(_bf(k_new), _bf(v_new), _bf(k_new), w_k, t["seq_lens"], t["ret_heads"], B, Hq, Hkv,
+                             n_ret, cfg.max_ctx, t["k_cache"], t["v_cache"], t["k_idx"], sinks=sinks, window=window,
+                             **DecodeStep.placement(t))
+        out = step(t)
+        torch.cuda.synchronize()
+        run = types.SimpleNamespace(inp=inp, out_h=out.cpu().numpy().astype(np.float64),
+                                    sel_idx=step.sel_idx.cpu().numpy(), sel_cnt=step.sel_cnt.cpu().numpy())
+        run.gpu_blocks = lambda b, r, run=run: run.sel_idx[b, r, :run.sel_cnt[b, r]]
+        check_selection(run)
+        check_outputs(run)
