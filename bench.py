@@ -334,15 +334,29 @@ def measure_prefill(N: int, reps: int, dense_too: bool) -> Dict:
         return e0.elapsed_time(e1) / reps
 
     ms = run(ret)
+    # the prompt's index keys for the retrieval heads (rtp_prefill_index_keys)
+    w_k = torch.randn((len(ret), 16, 128), generator=gen, device=dev).to(torch.bfloat16)
+    k_idx = torch.empty((1, len(ret), N, 16), dtype=torch.bfloat16, device=dev)
+    rh = torch.tensor(ret, dtype=torch.int32, device=dev)
+    keys = lambda: abi.rtp_prefill_index_keys(k, w_k, lens, rh, 1, Hq, Hkv, len(ret), N, k_idx)  # noqa
+    keys()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        keys()
+    e1.record()
+    torch.cuda.synchronize()
+    keys_ms = e0.elapsed_time(e1) / reps
     fl = prefill_flops(N, len(ret), Hq - len(ret), W_, S_)
     tf = fl / (ms * 1e-3) / 1e12
-    res = {"latency_ms": round(ms, 3), "tflops": round(tf, 1),
+    res = {"latency_ms": round(ms, 3), "tflops": round(tf, 1), "index_keys_ms": round(keys_ms, 3),
            "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(tf, 1),
                         "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_MFMA_TFLOPS, 4),
                         "traffic": None, "alg_flops_per_launch": fl, "avg_launch_us": round(ms * 1e3, 1)},
            "config": {"workload": f"prefill{N // 1024}k", "batch": 1, "ctx": N, "kv_heads": Hkv, "q_heads": Hq,
                       "retrieval_heads": len(ret), "head_dim": 128, "window": W_, "sinks": S_}}
-    log(f"[bench] prefill {N}: {ms:.3f} ms, {tf:.1f} TFLOP/s")
+    log(f"[bench] prefill {N}: {ms:.3f} ms, {tf:.1f} TFLOP/s; prompt index keys {keys_ms:.3f} ms")
     if dense_too:
         dms = run(list(range(Hq)))
         dfl = prefill_flops(N, Hq, 0, W_, S_)
@@ -350,7 +364,7 @@ def measure_prefill(N: int, reps: int, dense_too: bool) -> Dict:
         res["dense_causal_tflops"] = round(dfl / (dms * 1e-3) / 1e12, 1)
         res["speedup_vs_dense"] = round(dms / ms, 2)
         log(f"[bench] prefill {N} all heads dense: {dms:.3f} ms ({dms / ms:.2f}x the sparse pass)")
-    del q, k, v, out
+    del q, k, v, out, k_idx
     torch.cuda.empty_cache()
     return res
 

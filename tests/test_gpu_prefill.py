@@ -80,6 +80,18 @@ def test_prefill_32k_sampled():
     _check_rows(pin, out, [(0, h, rows) for h in (3, 9, 0, 17, 31)])
 
 
+def test_prefill_128k_sampled():
+    """A 128K-token prompt (8 query heads over 2 KV heads, retrieval heads 1 and 6, sink 4
+    + window 8192): sampled rows across the whole prompt, both head kinds."""
+    cfg = W.custom_config(name="prefill128k", seed=71, B=1, Hq=8, Hkv=2, n_ret=2, ret_heads=(1, 6),
+                          ctx=(131072,), window=8192, sinks=4)
+    pin = W.make_prefill_inputs(cfg)
+    say("[gpu] prefill 128K: Hq=8 Hkv=2 ret=(1, 6) window=8192 sinks=4")
+    out, _ = _run(pin)
+    rows = [0, 5, 255, 256, 8195, 8196, 65535, 65536, 100000, 131071]
+    _check_rows(pin, out, [(0, h, rows) for h in (1, 6, 0, 7)])
+
+
 @pytest.mark.parametrize("B,Hq,Hkv,ret,ctx", [(2, 8, 2, (0, 3, 6), (500, 77)), (1, 4, 4, (2,), (1,))])
 def test_prefill_index_keys_bit_exact(B, Hq, Hkv, ret, ctx):
     cfg = W.custom_config(name="prefill_keys", seed=80, B=B, Hq=Hq, Hkv=Hkv, n_ret=len(ret), ret_heads=ret, ctx=ctx)
