@@ -426,7 +426,7 @@ def main(argv: Optional[List[str]] = None) -> int:
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}); the path shards by sequence, "
-              "KV head or context across GPUs, which this build does not run.", file=sys.stderr)
+              "KV head or context across GPUs, which is not implemented here.", file=sys.stderr)
         return 2
     import torch
     if not torch.cuda.is_available():

@@ -5,10 +5,11 @@
 // low-rank index keys bf16(W^K_h k^pre) for the decode-time retrieval (Review, Adaptive
 // sparse attention equation, the key side of s_h(m, n)).
 //
-// Attention is a flash-style MFMA kernel for gfx950.  A 256-thread workgroup takes 128
+// Attention is a flash-style MFMA kernel for gfx950.  A 512-thread workgroup takes 256
 // queries of one head (32 per wave) and walks 64-key tiles: all tiles up to the
 // diagonal for a retrieval head, the sink tiles and the window's tiles for a local head
-// (the tiles in between are never loaded).  Per tile and wave:
+// (the tiles in between are never loaded).  Each tile is copied to LDS once for all
+// eight waves (four copy K, four copy V).  Per tile and wave:
 //   S^T = K Q^T   16 v_mfma_f32_32x32x16_bf16 (K from LDS as the A operand, the wave's
 //                 queries held in registers as the B operand), so each lane's
 //                 accumulators belong to one query: the online softmax needs only the
@@ -31,10 +32,7 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-#ifndef RTP_PREFILL_WAVES
-#define RTP_PREFILL_WAVES 8
-#endif
-constexpr int kPfWaves = RTP_PREFILL_WAVES;
+constexpr int kPfWaves = 8;
 constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kPfM = 32 * kPfWaves;        // queries per workgroup
 constexpr int kPfN = 64;                   // keys per tile
@@ -67,7 +65,8 @@ __device__ __forceinline__ float sum_pair(float v) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
-__global__ __launch_bounds__(kPfThreads, 8 / kPfWaves) void prefill_kernel(PrefillArgs a) {
+// two waves per SIMD: at most 256 VGPRs a wave
+__global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sk[kPfN * kKStride];
   __shared__ __attribute__((aligned(16))) _Float16 sv[kHeadDim * kVStride];
   // Workgroups go to the 8 XCDs round-robin by linear id (x + Hq y + ...), so a fixed
@@ -120,11 +119,10 @@ __global__ __launch_bounds__(kPfThreads, 8 / kPfWaves) void prefill_kernel(Prefi
     for (int c = 0; c < 8; ++c) qreg[c] = ld16(qrow + 16 * c);
   }
 
-  // tile copies: 256 threads move K (1024 chunks of 16 B, 4 each); with 8 waves the other
-  // 256 move V, each 4 keys x 8 dims, stored transposed in fp16 (with 4 waves every
-  // thread does both)
-  constexpr int kCopy = 256;
-  const bool do_k = kPfWaves == 4 || tid >= kCopy, do_v = kPfWaves == 4 || tid < kCopy;
+  // tile copies: waves 4-7 move K (1024 chunks of 16 B, 4 a thread), waves 0-3 move V
+  // (4 keys x 8 dims a thread, stored transposed in fp16)
+  constexpr int kCopy = kPfThreads / 2;
+  const bool do_k = tid >= kCopy, do_v = tid < kCopy;
   const int ct = tid & (kCopy - 1);
   uint4 kreg[4], vreg[4];
   auto gload = [&](int t) {
