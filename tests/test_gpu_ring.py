@@ -87,6 +87,11 @@ CASES = {
                        split_tokens=256),
     "window_only": dict(seed=44, B=2, Hkv=4, Hq=8, n_ret=2, ret_heads=(2, 3), ctx=(2049, 100), window=64,
                         sinks=0, split_tokens=512),
+    # one query head per KV head, and eight
+    "gqa1": dict(seed=46, B=2, Hkv=4, Hq=4, n_ret=1, ret_heads=(2,), ctx=(1500, 70), window=128, sinks=4,
+                 split_tokens=512),
+    "gqa8": dict(seed=47, B=1, Hkv=2, Hq=16, n_ret=2, ret_heads=(3, 5), ctx=(4000,), window=512, sinks=4,
+                 split_tokens=1024),
 }
 
 
@@ -101,6 +106,17 @@ def test_ring_step_matches_oracle(name):
     run = Run(inp, tensors=placed_tensors(inp, pl), tag=f"ring {name}")
     if cfg.n_ret:
         check_selection(run)
+    check_outputs(run)
+
+
+def test_ring_step_static_topk():
+    """The ring placement under the static top-k rule (a 256-token budget)."""
+    from gpu_util import check_selection_topk
+    cfg = W.custom_config(name="ring_topk", **CASES["mixed"])
+    inp = W.make_inputs(cfg)
+    rings = local_groups(inp)
+    run = Run(inp, tensors=placed_tensors(inp, place(inp, rings)), tag="ring top-k 256", k_tokens=256)
+    check_selection_topk(run)
     check_outputs(run)
 
 
