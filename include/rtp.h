@@ -1,8 +1,11 @@
 /*
  * rtp.h - C ABI of the MI355X (gfx950) decode-time sparse attention library
- * (librtp.so): RTPurbo's retrieval-head indexer with exact block top-p, block-sparse
- * split attention with a cross-split log-sum-exp reduce, and the local heads'
- * sliding-window + sink attention.
+ * (librtp.so): RTPurbo's retrieval-head indexer with exact block top-p (or a static
+ * top-k budget), block-sparse split attention with a cross-split log-sum-exp reduce,
+ * and the local heads' sliding-window + sink attention; around that decode step, the
+ * cache maintenance it needs (appending the decode token, sink + window rings for KV
+ * groups without retrieval heads) and the prefill of a prompt (causal attention with
+ * the same head split, the prompt's index keys, the rings' first fill).
  *
  * Sources (page title, section):
  *   Review        - the Korean paper review of RTPurbo (dongryeollee1.github.io),
