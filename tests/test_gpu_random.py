@@ -1,12 +1,12 @@
 """Seeded random sweeps of small shapes, decode step and prefill, against the oracle:
 head groupings 1-8, any number of retrieval heads (none to all), ragged lengths down to
 one token, block 64 or 128, split sizes of 1-16 blocks, windows from 0 to past the
-context, 0-9 sinks, top-p from 0.5 to 1."""
+context, 0-9 sinks, top-p from 0.5 to 1 or a static top-k budget of 1-5000 tokens."""
 import numpy as np
 import pytest
 
 import workloads as W
-from gpu_util import Run, check_outputs, check_selection, say
+from gpu_util import Run, check_outputs, check_selection, check_selection_topk, say
 from test_gpu_prefill import _check_rows, _run as _prefill_run
 
 pytestmark = pytest.mark.gpu
@@ -30,8 +30,9 @@ def _decode_cases(n, seed=2024):
             sinks = 1
         top_p = tuple(float(x) for x in g.choice([0.5, 0.9, 0.99, 1.0], size=n_ret))
         kind = str(g.choice(["random", "peaked_diffuse"]))
+        k_tokens = int(g.choice([0, 0, 1, 200, 1000, 5000]))  # 0: top-p; else the static top-k budget
         out.append(dict(name=f"rand{i}", seed=100 + i, B=B, Hkv=Hkv, Hq=Hq, n_ret=n_ret, ctx=ctx, block=block,
-                        split_tokens=split, window=window, sinks=sinks, top_p=top_p, kind=kind))
+                        split_tokens=split, window=window, sinks=sinks, top_p=top_p, kind=kind, k_tokens=k_tokens))
     return out
 
 
@@ -55,18 +56,19 @@ def _prefill_cases(n, seed=2025):
     return out
 
 
-DECODE = _decode_cases(12)
-PREFILL = _prefill_cases(8)
+DECODE = _decode_cases(40)
+PREFILL = _prefill_cases(24)
 
 
 @pytest.mark.parametrize("spec", DECODE, ids=[c["name"] for c in DECODE])
 def test_random_decode_shapes(spec):
     spec = dict(spec)
     name = spec.pop("name")
+    k_tokens = spec.pop("k_tokens")
     cfg = W.custom_config(name=name, **spec)
-    run = Run(W.make_inputs(cfg), tag=f"{name} {spec}")
+    run = Run(W.make_inputs(cfg), tag=f"{name} {spec}", k_tokens=k_tokens)
     if cfg.n_ret:
-        check_selection(run)
+        (check_selection_topk if k_tokens else check_selection)(run)
     check_outputs(run)
 
 
