@@ -376,7 +376,8 @@ def measure_prefill(N: int, reps: int, dense_too: bool) -> Dict:
     res = {"latency_ms": round(ms, 3), "tflops": round(tf, 1), "index_keys_ms": round(keys_ms, 3),
            "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(tf, 1),
                         "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_MFMA_TFLOPS, 4),
-                        "traffic": None, "alg_flops_per_launch": fl, "avg_launch_us": round(ms * 1e3, 1)},
+                        "traffic": read_traffic(f"prefill{N // 1024}k", "prefill_kernel"),
+                        "alg_flops_per_launch": fl, "avg_launch_us": round(ms * 1e3, 1)},
            "config": {"workload": f"prefill{N // 1024}k", "batch": 1, "ctx": N, "kv_heads": Hkv, "q_heads": Hq,
                       "retrieval_heads": len(ret), "head_dim": 128, "window": W_, "sinks": S_}}
     log(f"[bench] prefill {N}: {ms:.3f} ms, {tf:.1f} TFLOP/s; prompt index keys {keys_ms:.3f} ms")
