@@ -38,7 +38,8 @@
  *     behaviour (a device fault surfaces at the caller's next synchronization).
  *   - Workspaces must be zero-filled once before their first use; the kernels return
  *     every counter in them to zero, so a workspace can be reused by later calls on
- *     the same stream.  Calls that share a workspace must not overlap.
+ *     the same stream (for the index workspace, see its header below).  Calls that
+ *     share a workspace must not overlap.
  *   - Return codes: RTP_OK; RTP_EINVAL for a null pointer, a non-positive size, an
  *     inconsistent shape or a workspace that is too small; RTP_EUNSUPPORTED for a block
  *     size or head grouping outside the fixed set; RTP_ELAUNCH when HIP reports a
@@ -74,6 +75,37 @@ const char* rtp_version(void);
 size_t rtp_index_topp_workspace_size(int B, int n_ret, int max_ctx, int block);
 
 /*
+ * The index workspace (rtp_index_topp, rtp_index_topk) starts with this header; the
+ * per-(sequence, retrieval head) state follows it, one region per head whose size
+ * depends only on ceil(max_ctx / block).  So a workspace sized for the largest batch
+ * serves every later call with fewer sequences or retrieval heads and the same number of
+ * blocks per sequence.  The first call after the zero-fill stores that number in
+ * `layout`; a later call with another number touches none of the state, selects every
+ * block of every head (a superset of the top-p or top-k set) and sets
+ * RTP_INDEX_LAYOUT_MISMATCH; such a call needs a freshly zero-filled workspace.
+ *
+ * The selecting workgroup of each head waits for the words the other workgroups of the
+ * launch published (no fences; each word carries a 32-bit call tag), within a bounded
+ * number of re-reads.  If a word is still stale when that bound runs out, the head's
+ * selection falls back to every block and RTP_INDEX_WAIT_EXPIRED is set.  `status` is
+ * sticky (the library never clears it) and `fallbacks` counts the heads that fell back;
+ * the caller reads them from device memory when it wants to check (the library never
+ * synchronizes), and may clear them between calls.  `inject` must stay 0: bit 0 makes
+ * every bounded wait give up at once, for tests of the fallback.
+ * A head's tag advances with every call; after 2^32 - 1 calls it restarts at 1, and
+ * the head's words are cleared first, so a word written under an old tag is never taken
+ * as current.
+ */
+#define RTP_INDEX_WAIT_EXPIRED 1u
+#define RTP_INDEX_LAYOUT_MISMATCH 2u
+typedef struct {
+  unsigned int layout;    /* ceil(max_ctx / block) of the calls served; 0 in a fresh workspace */
+  unsigned int status;    /* RTP_INDEX_* bits, sticky */
+  unsigned int fallbacks; /* heads whose selection fell back to every block */
+  unsigned int inject;    /* 0; bit 0: every bounded wait gives up (tests of the fallback) */
+} rtp_index_ws_header;
+
+/*
  * Kernel 1: low-rank index scoring + exact block top-p selection
  * (Review, Adaptive sparse attention equation and Hardware-aware top-p decoding
  * kernel; Strikes-Back architecture paragraph, Kernel 1 at D16).
@@ -104,7 +136,8 @@ size_t rtp_index_topp_workspace_size(int B, int n_ret, int max_ctx, int block);
  *             the block mask), 1 = selected, 0 = not, for blocks < ceil(N_b / block) (the
  *             rest untouched); NULL to skip it
  *   workspace device scratch of >= rtp_index_topp_workspace_size(B, n_ret, max_ctx, block)
- *             bytes, zero-filled before first use
+ *             bytes, zero-filled before first use, 256-byte aligned; it begins with an
+ *             rtp_index_ws_header (above)
  */
 rtp_status rtp_index_topp(const void* q_pre, const void* w_q, const void* k_idx,
                           const int* seq_lens, const int* ret_heads, const float* top_p,
@@ -235,8 +268,9 @@ rtp_status rtp_local_window_attn(const void* q, const void* k_cache, const void*
  * s_h(m, n); Review, Method overview: retrieval heads keep the full KV cache):
  *   k_cache[b, g, pos] = k_new[b, g],  v_cache[b, g, pos] = v_new[b, g]   for every KV head g
  *   k_idx[b, r, pos, i] = bf16(sum_d W^K[r, i, d] k_pre[b, g_r, d])        for every retrieval
- *       head r (g_r = ret_heads[r] / (Hq / Hkv)) and i < 16, rounded once to nearest-even
- *       (the products are exact and summed in fp64)
+ *       head r (g_r = ret_heads[r] / (Hq / Hkv)) and i < 16: the exact sum of the 128
+ *       products rounded once to nearest-even (an exact zero gives +0; a non-finite input
+ *       gives the IEEE result of an fp64 sum: NaN or infinity)
  *
  *   k_new, v_new  bf16 [B, Hkv, 128]   the token's key (as the attention reads it) and value
  *   k_pre         bf16 [B, Hkv, 128]   the token's pre-RoPE key (the index projection's input)

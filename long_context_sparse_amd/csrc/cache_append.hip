@@ -5,9 +5,9 @@
 // the full KV cache).  The token is the last of the sequence's N_b tokens (row N_b - 1).
 //
 // gfx950 launch: one 256-thread workgroup per sequence.  The K/V rows are 16-byte
-// copies; each index key is 16 lanes x 8 dims of bf16 products summed in fp64 (the
-// products are exact, the sum carries < 2^-50 relative error) and rounded once to
-// bf16, nearest-even.
+// copies; each index-key dim is 16 lanes x 8 dims of bf16 products whose exact sum is
+// rounded once to bf16, nearest-even (index_key_bf16: an fp64 sum when its error bound
+// cannot change the rounding, else an exact integer sum).
 
 #include "rtp_common.hpp"
 
@@ -62,20 +62,8 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
     const int kv = a.ret_heads[r] / G;
     const uint4 wv = ld16(a.w_k + ((size_t)r * kIndexDim + i) * kHeadDim + part * 8);
     const uint4 kq = ld16(a.k_pre + ((size_t)b * a.Hkv + kv) * kHeadDim + part * 8);
-    double x = (double)bf_lo(wv.x) * (double)bf_lo(kq.x);
-    x = fma((double)bf_hi(wv.x), (double)bf_hi(kq.x), x);
-    x = fma((double)bf_lo(wv.y), (double)bf_lo(kq.y), x);
-    x = fma((double)bf_hi(wv.y), (double)bf_hi(kq.y), x);
-    x = fma((double)bf_lo(wv.z), (double)bf_lo(kq.z), x);
-    x = fma((double)bf_hi(wv.z), (double)bf_hi(kq.z), x);
-    x = fma((double)bf_lo(wv.w), (double)bf_lo(kq.w), x);
-    x = fma((double)bf_hi(wv.w), (double)bf_hi(kq.w), x);
-    // sum over the 16 lanes of this (head, dim): DPP moves inside the 16-lane row
-    x += dpp_f64<kDppXor1>(x);
-    x += dpp_f64<kDppXor2>(x);
-    x += dpp_f64<kDppHalfMirror>(x);
-    x += dpp_f64<kDppMirror>(x);
-    if (part == 0) a.kidx[(((size_t)b * a.n_ret + r) * a.max_ctx + pos) * kIndexDim + i] = (uint16_t)bf16_rne(x);
+    const uint32_t key = index_key_bf16(wv, kq);  // the exact sum over the 16 lanes, rounded once
+    if (part == 0) a.kidx[(((size_t)b * a.n_ret + r) * a.max_ctx + pos) * kIndexDim + i] = (uint16_t)key;
   }
 }
 

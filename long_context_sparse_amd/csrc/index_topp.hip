@@ -5,8 +5,8 @@
 // workgroup per compute unit at a time (its registers and LDS allow one), so the chunks
 // are sized for about one workgroup per compute unit and the scoring runs in a single
 // wave of workgroups; the selecting workgroup of each head then has 16 waves for the
-// threshold search.  Each head's tag word lives in the workspace and is advanced by the
-// head's selecting workgroup at the end of every call.
+// threshold search.  Each head's tag word lives in its workspace region and is advanced
+// by the head's selecting workgroup at the end of every call.
 
 #include "rtp_index.hpp"
 
@@ -15,11 +15,11 @@ namespace {
 
 constexpr int kIdxThreads = 1024;
 
-constexpr int kIdxMaxChunks = 2 * kIdxThreads;  // chunks per head the selection combines
+static_assert(kIdxMaxChunks <= 2 * kIdxThreads, "the selection reads two chunk words per thread");
 
 struct K1Layout {
   IndexGeom g;
-  size_t off_counters, off_tag, off_cmax, off_e, total;
+  size_t stride, total;
 };
 
 // Compute units of the current device (cached per device; 256, MI355X's count, if it
@@ -36,30 +36,27 @@ int compute_units() {
   return cached_n;
 }
 
-// The workspace has room for the most chunks a head can have, so its size does not
-// depend on the device; `target` (workgroups wanted) sets one launch's chunking.
+// The workspace: the header, then one region per head whose size depends only on the
+// blocks per sequence (room for the most chunks a head can have), so neither the size
+// of a region nor where it starts depends on the device; `target` (workgroups wanted)
+// sets one launch's chunking.
 K1Layout k1_layout(int B, int n_ret, int max_ctx, int block, int target) {
   K1Layout L{};
   L.g = index_geom(B, n_ret, max_ctx, block, kIdxThreads, target);
-  const size_t heads = (size_t)B * n_ret;
-  L.off_counters = 0;
-  L.off_tag = align_up(heads * sizeof(int), 256);
-  L.off_cmax = L.off_tag + align_up(heads * sizeof(uint32_t), 256);
-  L.off_e = L.off_cmax + align_up(heads * kIdxMaxChunks * 2 * sizeof(uint64_t), 256);
-  L.total = L.off_e + align_up(heads * (size_t)L.g.nblk_max * sizeof(uint64_t), 256);
+  L.stride = index_head_stride(L.g.nblk_max);
+  L.total = kIdxWsHeaderBytes + (size_t)B * n_ret * L.stride;
   return L;
 }
 
 template <int BK>
-__global__ __launch_bounds__(kIdxThreads) void index_topp_kernel(IndexArgs a, uint32_t* __restrict__ tags) {
+__global__ __launch_bounds__(kIdxThreads) void index_topp_kernel(IndexArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   auto* S = reinterpret_cast<IndexSmem<kIdxThreads>*>(smem_raw);
   const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
   const size_t head = (size_t)b * a.n_ret + r;
-  if (!index_chunk<BK, kIdxThreads>(a, c, r, b, tags + head, S)) return;
+  if (!index_chunk<BK, kIdxThreads>(a, c, r, b, S)) return;
   index_select<kIdxThreads>(a, BK, r, b, S);
-  if (threadIdx.x == 0)
-    __hip_atomic_store(&tags[head], next_tag(S->tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  index_advance_tag<kIdxThreads>(a, head, S->tag);
 }
 
 }  // namespace
@@ -96,17 +93,16 @@ rtp_status index_launch(const void* q_pre, const void* w_q, const void* k_idx, c
   char* ws = static_cast<char*>(workspace);
   IndexArgs args{static_cast<const uint16_t*>(q_pre), static_cast<const uint16_t*>(w_q),
                  static_cast<const uint16_t*>(k_idx), seq_lens, ret_heads, topk_blocks ? nullptr : top_p,
-                 topk_blocks, Hq, n_ret, max_ctx, L.g.nblk_max, L.g.chunk_blocks, kIdxMaxChunks, sel_idx, sel_cnt,
-                 sel_mask, reinterpret_cast<int*>(ws + L.off_counters), reinterpret_cast<uint64_t*>(ws + L.off_cmax),
-                 reinterpret_cast<uint64_t*>(ws + L.off_e)};
-  uint32_t* tags = reinterpret_cast<uint32_t*>(ws + L.off_tag);
+                 topk_blocks, Hq, n_ret, max_ctx, L.g.nblk_max, L.g.chunk_blocks, index_chunk_cap(L.g.nblk_max),
+                 sel_idx, sel_cnt, sel_mask, reinterpret_cast<IndexWsHeader*>(ws), ws + kIdxWsHeaderBytes,
+                 L.stride};
   dim3 grid(L.g.n_chunk, n_ret, B);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t dyn = index_smem_bytes<kIdxThreads>(L.g.rows);
   if (block == 64)
-    hipLaunchKernelGGL(index_topp_kernel<64>, grid, dim3(kIdxThreads), dyn, s, args, tags);
+    hipLaunchKernelGGL(index_topp_kernel<64>, grid, dim3(kIdxThreads), dyn, s, args);
   else
-    hipLaunchKernelGGL(index_topp_kernel<128>, grid, dim3(kIdxThreads), dyn, s, args, tags);
+    hipLaunchKernelGGL(index_topp_kernel<128>, grid, dim3(kIdxThreads), dyn, s, args);
   return hipGetLastError() == hipSuccess ? RTP_OK : RTP_ELAUNCH;
 }
 

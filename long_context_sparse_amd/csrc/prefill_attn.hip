@@ -294,8 +294,8 @@ struct KeyArgs {
 };
 
 // Thread (i, part): output dim i = tid / 16 of every row, over dims 8 part .. 8 part + 7;
-// its W^K_h slice stays in registers as doubles.  Sums in fp64 (exact products, < 2^-50
-// relative error), one rounding to bf16, as the decode-side append does.
+// its W^K_h slice stays in registers.  The exact sum of the 128 products is rounded once
+// to bf16 (index_key_bf16), as the decode-side append does.
 __global__ __launch_bounds__(kKeyThreads) void prompt_keys_kernel(KeyArgs a) {
   const int r = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int N = a.seq_lens[b];
@@ -304,26 +304,13 @@ __global__ __launch_bounds__(kKeyThreads) void prompt_keys_kernel(KeyArgs a) {
   const int i = tid >> 4, part = tid & 15;
   const int g = a.ret_heads[r] / (a.Hq / a.Hkv);
   const uint4 wv = ld16(a.w_k + ((size_t)r * kIndexDim + i) * kHeadDim + part * 8);
-  const double w[8] = {bf_lo(wv.x), bf_hi(wv.x), bf_lo(wv.y), bf_hi(wv.y),
-                       bf_lo(wv.z), bf_hi(wv.z), bf_lo(wv.w), bf_hi(wv.w)};
   const uint16_t* kp = a.k_pre + ((size_t)b * a.Hkv + g) * (size_t)a.T * kHeadDim + part * 8;
   uint16_t* ko = a.k_idx + ((size_t)b * a.n_ret + r) * (size_t)a.T * kIndexDim + i;
   const int row1 = min(row0 + kKeyRows, N);
   for (int row = row0; row < row1; ++row) {  // uniform trip count: the DPP sums see every lane
     const uint4 kv = ld16(kp + (size_t)row * kHeadDim);
-    double x = w[0] * (double)bf_lo(kv.x);
-    x = fma(w[1], (double)bf_hi(kv.x), x);
-    x = fma(w[2], (double)bf_lo(kv.y), x);
-    x = fma(w[3], (double)bf_hi(kv.y), x);
-    x = fma(w[4], (double)bf_lo(kv.z), x);
-    x = fma(w[5], (double)bf_hi(kv.z), x);
-    x = fma(w[6], (double)bf_lo(kv.w), x);
-    x = fma(w[7], (double)bf_hi(kv.w), x);
-    x += dpp_f64<kDppXor1>(x);
-    x += dpp_f64<kDppXor2>(x);
-    x += dpp_f64<kDppHalfMirror>(x);
-    x += dpp_f64<kDppMirror>(x);
-    if (part == 0) ko[(size_t)row * kIndexDim] = (uint16_t)bf16_rne(x);
+    const uint32_t key = index_key_bf16(wv, kv);
+    if (part == 0) ko[(size_t)row * kIndexDim] = (uint16_t)key;
   }
 }
 

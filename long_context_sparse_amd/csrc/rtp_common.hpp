@@ -153,6 +153,151 @@ __device__ __forceinline__ uint32_t bf16_rne(double x) {
   return sign | ((uint32_t)ebb << 7) | (q - 128u);
 }
 
+// ------------------------------------------------------------------ exact index keys
+// One index-key dim is bf16(sum_d w_d k_d) over the 128 dims, the exact sum rounded once
+// to nearest-even.  The 16 lanes of a DPP row hold 8 (w, k) bf16 pairs each (wv, kv, in
+// the lane's order); every lane of the row gets the result, so the row must be converged.
+//
+// Fast path: every product is exact in fp64 (8 + 8 significant bits), and the fp64 sum x
+// (a chain of at most 7 FMAs per lane, then 4 row additions) is within 11 * 2^-53 * A of
+// the exact sum S, A = sum |w_d k_d|.  When x - 2^-48 A and x + 2^-48 A round to the same
+// bf16 value, S lies between them and rounds to it too (rounding is monotone).  When they
+// do not (S lies next to a rounding boundary: a tie, a tie with a tail far below fp64's
+// reach, or heavy cancellation), the products are summed exactly as integers (below).
+// Non-finite inputs give the fp64 result (NaN or infinity); an all-zero product set gives
+// +0.
+//
+// Exact path: a finite bf16 value is M * 2^(E' - 134) with the integer M = 128 + mantissa
+// (E' = E, normal) or M = mantissa (E' = 1, subnormal).  A product is then the integer
+// M1 M2 < 2^16 times 2^(t - 266), t = E1' + E2' - 2 in [0, 506], so S is an integer V
+// times 2^-266 with |V| < 2^530.  V is held in 17 signed 64-bit limbs of 32-bit digits
+// (limb j weighs 2^(32 j)); a product adds its two digits to limbs t / 32 and t / 32 + 1
+// (selected without dynamic register indexing), so no carry moves until the row sum is
+// complete; the limbs are then normalised, the sign taken, and V rounded at the bit that
+// bf16 keeps (8 significant bits, or the fixed quantum 2^-133 below 2^-126), with the
+// round and sticky bits read from V itself.
+constexpr int kKeyLimbs = 17;
+
+template <int CTRL>
+__device__ __forceinline__ long long dpp_i64(long long v) {
+  const int lo = __builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(v >> 32), CTRL, 0xF, 0xF, false);
+  return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+
+// Digits of product (w, k) bf16 bits: adds sign * M1 M2 * 2^(t mod 32) into limbs t/32, t/32+1.
+__device__ __forceinline__ void key_limbs_add(long long (&L)[kKeyLimbs], uint32_t w, uint32_t k) {
+  const uint32_t ew = (w >> 7) & 0xFFu, ek = (k >> 7) & 0xFFu;
+  const uint32_t mw = (w & 0x7Fu) | (ew ? 0x80u : 0u), mk = (k & 0x7Fu) | (ek ? 0x80u : 0u);
+  const int t = (int)(ew ? ew : 1u) + (int)(ek ? ek : 1u) - 2;
+  const uint64_t v = (uint64_t)(mw * mk) << (t & 31);
+  const bool neg = ((w ^ k) & 0x8000u) != 0;
+  const long long lo = neg ? -(long long)(v & 0xFFFFFFFFull) : (long long)(v & 0xFFFFFFFFull);
+  const long long hi = neg ? -(long long)(v >> 32) : (long long)(v >> 32);
+  const int j0 = t >> 5;
+#pragma unroll
+  for (int j = 0; j < kKeyLimbs; ++j) L[j] += (j == j0 ? lo : 0ll) + (j == j0 + 1 ? hi : 0ll);
+}
+
+// Normalises the limbs to digits in [0, 2^32) below a signed top limb.
+__device__ __forceinline__ void key_limbs_carry(long long (&L)[kKeyLimbs]) {
+#pragma unroll
+  for (int j = 0; j + 1 < kKeyLimbs; ++j) {
+    const long long c = L[j] >> 32;  // arithmetic: floor(L[j] / 2^32)
+    L[j] -= c * 4294967296ll;
+    L[j + 1] += c;
+  }
+}
+
+__device__ __noinline__ uint32_t index_key_exact(uint4 wv, uint4 kv) {
+  long long L[kKeyLimbs];
+#pragma unroll
+  for (int j = 0; j < kKeyLimbs; ++j) L[j] = 0;
+  const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w}, kd[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    key_limbs_add(L, wd[i] & 0xFFFFu, kd[i] & 0xFFFFu);
+    key_limbs_add(L, wd[i] >> 16, kd[i] >> 16);
+  }
+  // the row's sum: every limb stays below 128 * 2^32 in magnitude
+#pragma unroll
+  for (int j = 0; j < kKeyLimbs; ++j) {
+    L[j] += dpp_i64<kDppXor1>(L[j]);
+    L[j] += dpp_i64<kDppXor2>(L[j]);
+    L[j] += dpp_i64<kDppHalfMirror>(L[j]);
+    L[j] += dpp_i64<kDppMirror>(L[j]);
+  }
+  key_limbs_carry(L);
+  const bool neg = L[kKeyLimbs - 1] < 0;
+  if (neg) {
+#pragma unroll
+    for (int j = 0; j < kKeyLimbs; ++j) L[j] = -L[j];
+    key_limbs_carry(L);
+  }
+  // highest set bit of V (now >= 0, every limb a digit)
+  int top = -1;
+#pragma unroll
+  for (int j = 0; j < kKeyLimbs; ++j)
+    if (L[j] != 0) top = 32 * j + 31 - __clz((uint32_t)L[j]);
+  if (top < 0) return 0u;  // the exact sum is zero: +0
+  const uint32_t sign = neg ? 0x8000u : 0u;
+  // the kept bits start at q: 8 significant bits, or the subnormal quantum 2^-133
+  // (bit 133 of V); round bit q - 1, sticky below it
+  const int q = max(top - 7, 133);
+  const int qj = q >> 5, qs = q & 31, rb = q - 1, rj = rb >> 5, rs = rb & 31;
+  uint64_t win = 0;  // limbs qj and qj + 1
+  bool sticky = false;
+  uint32_t rbit = 0;
+#pragma unroll
+  for (int j = 0; j < kKeyLimbs; ++j) {
+    const uint32_t d = (uint32_t)L[j];
+    if (j == qj) win |= d;
+    if (j == qj + 1) win |= (uint64_t)d << 32;
+    if (j == rj) {
+      rbit = (d >> rs) & 1u;
+      sticky = sticky || (d & ((1u << rs) - 1u)) != 0u;
+    }
+    if (j < rj) sticky = sticky || d != 0u;
+  }
+  uint32_t Q = (uint32_t)(win >> qs) & 0x1FFu;
+  if (rbit && (sticky || (Q & 1u))) ++Q;
+  if (top < 140) return sign | Q;  // below 2^-126: subnormal (128 = the smallest normal)
+  int eb = top - 266 + 127;        // biased exponent of 2^(top - 266)
+  if (Q == 256u) {
+    Q = 128u;
+    ++eb;
+  }
+  if (eb >= 255) return sign | 0x7F80u;
+  return sign | ((uint32_t)eb << 7) | (Q - 128u);
+}
+
+__device__ __forceinline__ uint32_t index_key_bf16(uint4 wv, uint4 kv) {
+  const double w[8] = {bf_lo(wv.x), bf_hi(wv.x), bf_lo(wv.y), bf_hi(wv.y),
+                       bf_lo(wv.z), bf_hi(wv.z), bf_lo(wv.w), bf_hi(wv.w)};
+  const double k[8] = {bf_lo(kv.x), bf_hi(kv.x), bf_lo(kv.y), bf_hi(kv.y),
+                       bf_lo(kv.z), bf_hi(kv.z), bf_lo(kv.w), bf_hi(kv.w)};
+  double x = w[0] * k[0], A = fabs(x);
+#pragma unroll
+  for (int i = 1; i < 8; ++i) {
+    x = fma(w[i], k[i], x);
+    A = fma(fabs(w[i]), fabs(k[i]), A);
+  }
+  x += dpp_f64<kDppXor1>(x);
+  A += dpp_f64<kDppXor1>(A);
+  x += dpp_f64<kDppXor2>(x);
+  A += dpp_f64<kDppXor2>(A);
+  x += dpp_f64<kDppHalfMirror>(x);
+  A += dpp_f64<kDppHalfMirror>(A);
+  x += dpp_f64<kDppMirror>(x);
+  A += dpp_f64<kDppMirror>(A);
+  if (!isfinite(x) || !isfinite(A)) return bf16_rne(x);
+  if (A == 0.0) return 0u;
+  const double E = A * 0x1p-48;
+  const uint32_t lo = bf16_rne(x - E), hi = bf16_rne(x + E);
+  if (lo == hi) return lo;  // the same in every lane of the row
+  return index_key_exact(wv, kv);
+}
+
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -179,17 +324,12 @@ __device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t x) {
 
 // ------------------------------------------------------------------ published words
 // Values passed between workgroups of one launch without fences: every published
-// 64-bit word carries the call's tag (1..4095, advanced by every call) in its low 12
-// bits, words are written and read with relaxed device-scope atomics, and a reader
-// re-reads a word until it carries the current tag.  An fp64 keeps its top 52 bits
-// (relative precision 2^-40); an fp32 or an int sits in the high half.
-constexpr uint64_t kTagBits = 0xFFFull;
+// 64-bit word holds an fp32 value in its high half and the call's 32-bit tag in its low
+// half (tags 1 .. 2^32 - 1, advanced by every call; 0 marks a word never written), words
+// are written and read with relaxed device-scope atomics, and a reader re-reads a word
+// until it carries the current tag, within a bounded number of re-reads.
 constexpr int kSpinBudget = 1 << 12;  // re-reads a thread may spend waiting for one tag
 
-__device__ __forceinline__ uint64_t tagged(double x, uint32_t tag) {
-  return ((uint64_t)__double_as_longlong(x) & ~kTagBits) | tag;
-}
-__device__ __forceinline__ double untag(uint64_t w) { return __longlong_as_double((long long)(w & ~kTagBits)); }
 __device__ __forceinline__ uint64_t tagged_f32(float x, uint32_t tag) {
   return ((uint64_t)__float_as_uint(x) << 32) | tag;
 }
@@ -200,22 +340,26 @@ __device__ __forceinline__ uint64_t ld_dev(const uint64_t* p) {
 __device__ __forceinline__ void st_dev(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ bool has_tag(uint64_t w, uint32_t tag) { return (uint32_t)(w & kTagBits) == tag; }
-// Re-read a published word until it carries `tag` (bounded by the thread's budget).
-__device__ __forceinline__ uint64_t settle(const uint64_t* p, uint64_t w, uint32_t tag, int& budget) {
+__device__ __forceinline__ bool has_tag(uint64_t w, uint32_t tag) { return (uint32_t)w == tag; }
+// Re-reads a published word until it carries `tag`; a thread spends at most `budget`
+// re-reads over all its waits.  `ok` turns false when a word is still stale once the
+// budget is spent (the caller then falls back and reports it).
+__device__ __forceinline__ uint64_t settle(const uint64_t* p, uint64_t w, uint32_t tag, int& budget, bool& ok) {
   while (!has_tag(w, tag) && budget > 0) {
     --budget;
     __builtin_amdgcn_s_sleep(1);
     w = ld_dev(p);
   }
+  ok = ok && has_tag(w, tag);
   return w;
 }
 // The tag a call uses, from the word that holds it (0 in a fresh workspace reads as 1),
-// and the tag of the next call.
+// and the tag of the next call (after 2^32 - 1 calls it restarts at 1, once the caller
+// has cleared the words the old tags marked).
 __device__ __forceinline__ uint32_t load_tag(const uint32_t* p) {
   const uint32_t t = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return t == 0 ? 1u : t;
 }
-__device__ __forceinline__ uint32_t next_tag(uint32_t t) { return t % 4095u + 1u; }
+__device__ __forceinline__ uint32_t next_tag(uint32_t t) { return t == 0xFFFFFFFFu ? 1u : t + 1u; }
 
 }  // namespace rtp

@@ -14,10 +14,19 @@
 // block masses carry < 1e-6 relative error; exponentials are fp32 hardware exp2 on
 // arguments already reduced in fp64, summed in fp64; wave reductions run on DPP lane
 // moves.  Per block: max_j and sum_j = sum exp(s - max_j); per chunk M_c = max_j max_j,
-// and the chunk publishes e_j = sum_j exp(max_j - M_c) (fp32) and (M_c, Z_c) as tagged
+// and the chunk publishes e_j = sum_j exp(max_j - M_c) and (M_c, Z_c) as tagged fp32
 // words (rtp_common.hpp), then bumps the head's arrival counter; the last workgroup
 // to arrive selects.  So no device-scope fence (an L2 write-back on every workgroup of
-// every XCD) is needed, and a word from the previous call is never taken as current.
+// every XCD) is needed, and a word from an earlier call is never taken as current.  A
+// selecting workgroup whose bounded wait for a word runs out selects every block of its
+// head (a superset of the top-p set) and reports it in the workspace header.
+//
+// Workspace: a header (layout key, sticky status bits, fallback count, a fault-injection
+// word for tests), then one region per (sequence, retrieval head) at a stride that
+// depends only on the blocks per sequence: the head's arrival counter and tag, its chunk
+// words and its block words.  Calls with other batch sizes or head counts reuse it; a
+// call whose blocks per sequence differ from the layout the workspace was first used
+// with is refused on the device (every block selected, status bit set).
 //
 // Selection (last workgroup): M = max_c M_c, Z = sum_c Z_c exp(M_c - M) and every
 // block's mass m_j = e_j exp(M_c - M) / Z in fp32 into LDS, then the greedy threshold
@@ -70,6 +79,7 @@ struct IndexSmem {
   TailSmem<T> sm;
   int flag;
   uint32_t tag;
+  int inject, mismatch;
 };
 template <int T>
 __host__ __device__ constexpr size_t index_smem_bytes(int rows) {
@@ -99,6 +109,32 @@ inline IndexGeom index_geom(int B, int n_ret, int max_ctx, int block, int T, int
   return g;
 }
 
+// Index workspace layout (see the file comment): the header, then per head a 256-byte
+// state record (arrival counter, tag) followed by 2 words per chunk (M_c, Z_c) and one
+// word per block (e_j).  Chunks hold >= 8 blocks, so a head has at most
+// min(2048, ceil(nblk_max / 8)) chunks.
+struct IndexWsHeader {
+  uint32_t layout;     // blocks per sequence of the calls this workspace serves (0: fresh)
+  uint32_t status;     // sticky error bits (RTP_INDEX_WAIT_EXPIRED, RTP_INDEX_LAYOUT_MISMATCH)
+  uint32_t fallbacks;  // selections that fell back to every block
+  uint32_t inject;     // bit 0: every bounded wait gives up at once (failure-path tests)
+};
+struct IndexHeadState {
+  int counter;   // arrival counter, zero between calls
+  uint32_t tag;  // tag of the head's next call (0 in a fresh workspace reads as 1)
+};
+constexpr size_t kIdxWsHeaderBytes = 256;
+constexpr size_t kIdxHeadStateBytes = 256;
+constexpr int kIdxMaxChunks = 2048;  // chunks per head the selection combines
+
+__host__ __device__ inline int index_chunk_cap(int nblk_max) {
+  const int c = (nblk_max + 7) / 8;
+  return c < kIdxMaxChunks ? c : kIdxMaxChunks;
+}
+__host__ __device__ inline size_t index_head_stride(int nblk_max) {
+  return align_up(kIdxHeadStateBytes + (size_t)index_chunk_cap(nblk_max) * 16 + (size_t)nblk_max * 8, 256);
+}
+
 // Global buffers and sizes of the index role.
 struct IndexArgs {
   const uint16_t* q_pre;  // bf16 [B, Hq, 128]
@@ -108,14 +144,23 @@ struct IndexArgs {
   const int* ret_heads;
   const float* top_p;     // [B * n_ret] top-p of each head (top-p rule)
   int topk_blocks;        // > 0: static top-k, keep this many blocks (top_p unused)
-  int Hq, n_ret, max_ctx, nblk_max, chunk_blocks, n_chunk_max;
+  int Hq, n_ret, max_ctx, nblk_max, chunk_blocks, n_chunk_cap;
   int* sel_idx;
   int* sel_cnt;
   uint8_t* sel_mask;  // [B * n_ret, nblk_max] 1 = selected (blocks < nblk), or null
-  int* counters;   // [B * n_ret] arrival counters, zero between calls
-  uint64_t* cmax;  // [B * n_ret, n_chunk_max, 2] tagged (M_c, Z_c)
-  uint64_t* blk_e; // [B * n_ret, nblk_max] tagged e_j
+  IndexWsHeader* hdr;
+  char* regions;       // per-head regions, head_stride bytes apart
+  size_t head_stride;
 };
+__device__ __forceinline__ IndexHeadState* head_state(const IndexArgs& a, size_t head) {
+  return reinterpret_cast<IndexHeadState*>(a.regions + head * a.head_stride);
+}
+__device__ __forceinline__ uint64_t* head_chunk_words(const IndexArgs& a, size_t head) {
+  return reinterpret_cast<uint64_t*>(a.regions + head * a.head_stride + kIdxHeadStateBytes);
+}
+__device__ __forceinline__ uint64_t* head_block_words(const IndexArgs& a, size_t head) {
+  return head_chunk_words(a, head) + 2 * (size_t)a.n_chunk_cap;
+}
 
 // ------------------------------------------------------------------ selection helpers
 // Composite selection key of block j with fp32 mass m >= 0: the mass bits (order-
@@ -394,13 +439,27 @@ __device__ __noinline__ uint64_t select_threshold(const float* __restrict__ sm_m
 }
 
 // ------------------------------------------------------------------ the index role
+// Every block of head (b, r) selected (blocks < nblk): the list 0 .. nblk - 1, its count
+// and the mask.  The fallback of a selection that cannot run.
+template <int T>
+__device__ __forceinline__ void select_all(const IndexArgs& a, size_t head, int nblk) {
+  int* out = a.sel_idx + head * a.nblk_max;
+  uint8_t* mask = a.sel_mask ? a.sel_mask + head * a.nblk_max : nullptr;
+  for (int j = threadIdx.x; j < nblk; j += T) {
+    out[j] = j;
+    if (mask) mask[j] = 1;
+  }
+  if (threadIdx.x == 0) a.sel_cnt[head] = nblk;
+}
+
 // Scores chunk c of head (b, r) and publishes its words; returns true in the workgroup
-// that must select (the last of the head to arrive).  The call's tag is read from
-// *tag_word and left in S->tag.  Workgroups of chunks past the sequence's end return
-// false at once.
+// that must select (the last of the head to arrive).  The call's tag is read from the
+// head's state and left in S->tag.  Workgroups of chunks past the sequence's end return
+// false at once.  When the workspace was laid out for another number of blocks per
+// sequence, nothing of it is touched: chunk 0 selects every block of the head and sets
+// the header's status bit, and every workgroup returns false.
 template <int BK, int T>
-__device__ __forceinline__ bool index_chunk(const IndexArgs& a, int c, int r, int b, const uint32_t* tag_word,
-                                            IndexSmem<T>* S) {
+__device__ __forceinline__ bool index_chunk(const IndexArgs& a, int c, int r, int b, IndexSmem<T>* S) {
   static_assert(T >= 256 && T % kWave == 0, "the q_idx product and the bins take 256 threads");
   constexpr int W = T / kWave;
   constexpr int NL = BK / 32;          // 1 KB loads per lane per block
@@ -440,8 +499,16 @@ __device__ __forceinline__ bool index_chunk(const IndexArgs& a, int c, int r, in
   uint4 cur[U][NL];
   if (jj < j1) load(cur, jj, N - 1);
 
-  // ---- this call's tag; q_idx = W^Q_r q_pre[b, hq] in fp64 (16 outputs x 16 partial dots)
-  if (tid == 0) S->tag = load_tag(tag_word);
+  // ---- this call's tag and the workspace's layout key; q_idx = W^Q_r q_pre[b, hq] in
+  // fp64 (16 outputs x 16 partial dots)
+  if (tid == 0) {
+    S->tag = load_tag(&head_state(a, head)->tag);
+    const uint32_t lay = __hip_atomic_load(&a.hdr->layout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    S->inject = (int)__hip_atomic_load(&a.hdr->inject, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    S->mismatch = lay != 0u && lay != (uint32_t)a.nblk_max;
+    if (lay == 0u && c == 0)  // a fresh workspace takes this call's layout
+      __hip_atomic_store(&a.hdr->layout, (uint32_t)a.nblk_max, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   if (tid < 256) {
     const int hq = a.ret_heads[r];
     const int i = tid >> 4, part = tid & 15;
@@ -460,6 +527,16 @@ __device__ __forceinline__ bool index_chunk(const IndexArgs& a, int c, int r, in
     if (part == 0) S->qidx[i] = x;
   }
   __syncthreads();
+  if (S->mismatch) {
+    if (c == 0) {
+      select_all<T>(a, head, nblk);
+      if (tid == 0) {
+        atomicOr(&a.hdr->status, (uint32_t)RTP_INDEX_LAYOUT_MISMATCH);
+        atomicAdd(&a.hdr->fallbacks, 1u);
+      }
+    }
+    return false;
+  }
   const uint32_t tag = S->tag;
   double qh[8];
 #pragma unroll
@@ -530,7 +607,7 @@ __device__ __forceinline__ bool index_chunk(const IndexArgs& a, int c, int r, in
 
   // ---- publish e_j = sum_j exp(max_j - M_c) (fp32) and the chunk's (M_c, Z_c = sum_j e_j);
   // the last workgroup of (b, r) to arrive selects
-  uint64_t* e_io = a.blk_e + head * a.nblk_max;
+  uint64_t* e_io = head_block_words(a, head);
   if (wave == 0) {
     constexpr int PL = kIdxMaxChunkBlocks / kWave;  // blocks of the chunk per lane
     const int nb = j1 - j0;
@@ -554,10 +631,11 @@ __device__ __forceinline__ bool index_chunk(const IndexArgs& a, int c, int r, in
     }
     const double zc = wave_sum(zl);
     if (lane == 0) {
-      uint64_t* cs = a.cmax + (head * a.n_chunk_max + c) * 2;
-      st_dev(cs, tagged(mc, tag));
-      st_dev(cs + 1, tagged(zc, tag));
-      S->flag = atomicAdd(&a.counters[head], 1) == nch - 1;
+      // M_c is the largest of fp32 block maxima, so fp32 holds it exactly
+      uint64_t* cs = head_chunk_words(a, head) + 2 * c;
+      st_dev(cs, tagged_f32((float)mc, tag));
+      st_dev(cs + 1, tagged_f32((float)zc, tag));
+      S->flag = atomicAdd(&head_state(a, head)->counter, 1) == nch - 1;
     }
   }
   __syncthreads();
@@ -566,7 +644,9 @@ __device__ __forceinline__ bool index_chunk(const IndexArgs& a, int c, int r, in
 
 // The selection of head (b, r), run by the workgroup index_chunk picked: writes the
 // ascending selected block ids and their count (and, if asked, one byte per block:
-// 1 = selected), and resets the head's arrival counter.
+// 1 = selected), and resets the head's arrival counter.  If a word of this call is still
+// stale when the bounded wait runs out (or the header asks for that failure), every
+// block is selected and the header's status bit and fallback count record it.
 template <int T>
 __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int r, int b, IndexSmem<T>* S) {
   constexpr int W = T / kWave;
@@ -578,12 +658,14 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int r, 
   const uint32_t tag = S->tag;
   TailSmem<T>& sm = S->sm;
   float* s_mass = index_masses<T>(S);
-  const uint64_t* e_io = a.blk_e + head * a.nblk_max;
+  const uint64_t* e_io = head_block_words(a, head);
 
   // ---- M = max_c M_c, Z = sum_c Z_c exp(M_c - M); then m_j = e_j exp(M_c - M) / Z for
   // every block, into LDS
-  int budget = kSpinBudget;
-  const uint64_t* cs = a.cmax + head * a.n_chunk_max * 2;
+  const bool inject = (S->inject & 1) != 0;
+  int budget = inject ? 0 : kSpinBudget;
+  bool ok = !inject;
+  const uint64_t* cs = head_chunk_words(a, head);
   if (tid < kBins) {
     sm.bmass[tid] = 0;
     sm.bcnt[tid] = 0;
@@ -619,87 +701,89 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int r, 
     cz[k] = 0.0;
     if (i < nch) {
       const uint64_t x = ld_dev(cs + 2 * i), z = ld_dev(cs + 2 * i + 1);
-      cm[k] = untag(settle(cs + 2 * i, x, tag, budget));
-      cz[k] = untag(settle(cs + 2 * i + 1, z, tag, budget));
+      cm[k] = (double)untag_f32(settle(cs + 2 * i, x, tag, budget, ok));
+      cz[k] = (double)untag_f32(settle(cs + 2 * i + 1, z, tag, budget, ok));
     }
   }
   {
     const double mw = wave_max(fmax(cm[0], cm[1]));
     if (lane == 0) sm.f64[wave] = mw;
   }
-  __syncthreads();
-  double M = sm.f64[0];
+  bool failed = __syncthreads_or(!ok) != 0;  // uniform
+  if (!failed) {
+    double M = sm.f64[0];
 #pragma unroll
-  for (int w2 = 1; w2 < W; ++w2) M = fmax(M, sm.f64[w2]);
-  double f[2], zloc = 0.0;
+    for (int w2 = 1; w2 < W; ++w2) M = fmax(M, sm.f64[w2]);
+    double f[2], zloc = 0.0;
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    f[k] = cm[k] == -INFINITY ? 0.0 : exp(cm[k] - M);
-    zloc += cz[k] * f[k];
-  }
-  {
-    const double zw = wave_sum(zloc);
-    if (lane == 0) sm.f64b[wave] = zw;
-  }
-  __syncthreads();
-  double Z = sm.f64b[0];
-#pragma unroll
-  for (int w2 = 1; w2 < W; ++w2) Z += sm.f64b[w2];
-  const double invZ = 1.0 / Z;
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int i = tid + k * T;
-    if (i < nch) S->f[i] = f[k] * invZ;
-  }
-  __syncthreads();
-  // masses into LDS; the same pass builds the first threshold level over the blocks above
-  // the floor: bin = (bits - lo1) >> shift1, the top bin also takes any larger
-  const int cshift = __ffs(a.chunk_blocks) - 1;
-  for (int i0 = 0; i0 < rows; i0 += LB) {
-    if (i0 > 0) {
-#pragma unroll
-      for (int u = 0; u < LB; ++u) {
-        const int j = (i0 + u) * T + tid;
-        w[u] = (i0 + u < rows && j < nblk) ? ld_dev(e_io + j) : 0ull;
-      }
+    for (int k = 0; k < 2; ++k) {
+      f[k] = cm[k] == -INFINITY ? 0.0 : exp(cm[k] - M);
+      zloc += cz[k] * f[k];
     }
-    bool ok = true;
-#pragma unroll
-    for (int u = 0; u < LB; ++u) {
-      const int j = (i0 + u) * T + tid;
-      if (i0 + u < rows && j < nblk) ok = ok && has_tag(w[u], tag);
+    {
+      const double zw = wave_sum(zloc);
+      if (lane == 0) sm.f64b[wave] = zw;
     }
-    if (!ok) {
+    __syncthreads();
+    double Z = sm.f64b[0];
 #pragma unroll
-      for (int u = 0; u < LB; ++u) {
-        const int j = (i0 + u) * T + tid;
-        if (i0 + u < rows && j < nblk) w[u] = settle(e_io + j, w[u], tag, budget);
-      }
+    for (int w2 = 1; w2 < W; ++w2) Z += sm.f64b[w2];
+    const double invZ = 1.0 / Z;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = tid + k * T;
+      if (i < nch) S->f[i] = f[k] * invZ;
     }
+    __syncthreads();
+    // masses into LDS; the same pass builds the first threshold level over the blocks above
+    // the floor: bin = (bits - lo1) >> shift1, the top bin also takes any larger
+    const int cshift = __ffs(a.chunk_blocks) - 1;
+    for (int i0 = 0; i0 < rows; i0 += LB) {
+      if (i0 > 0) {
 #pragma unroll
-    for (int u = 0; u < LB; ++u) {
-      const int j = (i0 + u) * T + tid;
-      if (i0 + u < rows) {
-        float m = -1.0f;  // no block
-        if (j < nblk) {
-          m = (float)((double)untag_f32(w[u]) * S->f[j >> cshift]);
-          const uint32_t bits = __float_as_uint(m);
-          if (pick && bits >= lbits) {
-            const int bin = level_bin(bits, lo1, shift1);
-            atomicAdd((unsigned long long*)&sm.bmass[bin], count ? 1ull : (unsigned long long)fixed_bits(bits));
-            atomicAdd(&sm.bcnt[bin], 1u);
-          }
+        for (int u = 0; u < LB; ++u) {
+          const int j = (i0 + u) * T + tid;
+          w[u] = (i0 + u < rows && j < nblk) ? ld_dev(e_io + j) : 0ull;
         }
-        s_mass[j] = m;
+      }
+      bool fresh = true;
+#pragma unroll
+      for (int u = 0; u < LB; ++u) {
+        const int j = (i0 + u) * T + tid;
+        if (i0 + u < rows && j < nblk) fresh = fresh && has_tag(w[u], tag);
+      }
+      if (!fresh) {
+#pragma unroll
+        for (int u = 0; u < LB; ++u) {
+          const int j = (i0 + u) * T + tid;
+          if (i0 + u < rows && j < nblk) w[u] = settle(e_io + j, w[u], tag, budget, ok);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < LB; ++u) {
+        const int j = (i0 + u) * T + tid;
+        if (i0 + u < rows) {
+          float m = -1.0f;  // no block
+          if (j < nblk) {
+            m = (float)((double)untag_f32(w[u]) * S->f[j >> cshift]);
+            const uint32_t bits = __float_as_uint(m);
+            if (pick && bits >= lbits) {
+              const int bin = level_bin(bits, lo1, shift1);
+              atomicAdd((unsigned long long*)&sm.bmass[bin], count ? 1ull : (unsigned long long)fixed_bits(bits));
+              atomicAdd(&sm.bcnt[bin], 1u);
+            }
+          }
+          s_mass[j] = m;
+        }
       }
     }
+    failed = __syncthreads_or(!ok) != 0;
   }
-  __syncthreads();
 
   // ---- threshold key: block j is selected iff key_of(m_j, j) >= thr
   uint64_t thr = 0;
   bool all = true, ready = false;
-  if (pick) {
+  if (pick && !failed) {
     const uint64_t P = count ? (uint64_t)kb : (uint64_t)ceil(ldexp((double)p, 62));
     if (wave == 0) {
       scan_level<T>(0, P, lo1, 0xFFFFFFFFu, shift1, sm);
@@ -719,9 +803,10 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int r, 
   uint8_t* mask = a.sel_mask ? a.sel_mask + head * a.nblk_max : nullptr;
   int total = nblk;
   if (all) {
-    for (int j = tid; j < nblk; j += T) {
-      out[j] = j;
-      if (mask) mask[j] = 1;
+    select_all<T>(a, head, nblk);
+    if (failed && tid == 0) {
+      atomicOr(&a.hdr->status, (uint32_t)RTP_INDEX_WAIT_EXPIRED);
+      atomicAdd(&a.hdr->fallbacks, 1u);
     }
   } else {
     auto sel = [&](int i, float m) { return m >= 0.f && key_at<T>(i, m) >= thr; };
@@ -735,9 +820,25 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int r, 
     });
   }
   if (tid == 0) {
-    a.sel_cnt[head] = total;
-    __hip_atomic_store(&a.counters[head], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
+    if (!all) a.sel_cnt[head] = total;
+    __hip_atomic_store(&head_state(a, head)->counter, 0, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
   }
+}
+
+// After the selection: the head's tag advances for the next call.  When it wraps (after
+// 2^32 - 1 calls), the head's words are cleared first, so no word written under an old
+// tag can carry a new one.
+template <int T>
+__device__ __forceinline__ void index_advance_tag(const IndexArgs& a, size_t head, uint32_t tag) {
+  const uint32_t nt = next_tag(tag);
+  if (nt == 1u) {
+    uint64_t* w = head_chunk_words(a, head);
+    const int n = 2 * a.n_chunk_cap + a.nblk_max;
+    for (int i = threadIdx.x; i < n; i += T) st_dev(w + i, 0ull);
+  }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&head_state(a, head)->tag, nt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace rtp

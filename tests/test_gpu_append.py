@@ -118,3 +118,79 @@ def test_append_then_step(name):
     run = Run(inp, tensors=t, tag=f"{name} after append")
     check_selection(run)
     check_outputs(run, [(b, int(h)) for b in range(B) for h in inp.ret_heads])
+
+
+def _boundary_vectors():
+    """w and k bit vectors whose exact dot products sit on or next to a bf16 rounding
+    boundary (ties with tails of either sign far below fp64's reach, cancellation,
+    subnormal and overflowing sums, signed zeros), plus ties with random tails."""
+    from key_cases import CASES, vec
+    ws = [CASES[n][0] for n in sorted(CASES)]
+    ks = [CASES[n][1] for n in sorted(CASES)]
+    g = np.random.default_rng(77)
+    for it in range(19):
+        n = int(g.integers(-20, 20))
+        e = n - 1 - int(g.integers(20, 90))
+        sgn = 1.0 if it % 2 else -1.0
+        w, k = vec((float(int(g.integers(128, 256))) * 2.0 ** n, 1.0), (2.0 ** (n - 1), 1.0),
+                   (sgn * 2.0 ** (e // 2), 2.0 ** (e - e // 2)))
+        ws.append(w)
+        ks.append(k)
+    return np.stack(ws), np.stack(ks)
+
+
+def test_append_keys_exact_sum_rounded_once():
+    """rtp_cache_append's index keys against oracle.index_key (the exact sum rounded once)
+    on every pairing of 32 boundary w rows (two retrieval heads of 16 dims) with 32
+    boundary k vectors (one per sequence): among them the tie-with-tail input that a
+    rounded fp64 sum gets wrong, its negative and its just-below-tie twin."""
+    ws, ks = _boundary_vectors()
+    n_ret, B = 2, ks.shape[0]
+    say(f"[gpu] append keys: {B} k vectors x {ws.shape[0]} w rows")
+    w_k = ws.reshape(n_ret, 16, 128)
+    Hq = Hkv = n_ret  # one KV group per retrieval head; every group sees the same k_pre
+    k_pre = np.repeat(ks[:, None, :], Hkv, axis=1)
+    g = np.random.default_rng(3)
+    max_ctx = 4
+    lens = [1 + (b % max_ctx) for b in range(B)]
+    caches = [_bits(g, (B, Hkv, max_ctx, 128)), _bits(g, (B, Hkv, max_ctx, 128)), _bits(g, (B, n_ret, max_ctx, 16))]
+    k_new, v_new = _bits(g, (B, Hkv, 128)), _bits(g, (B, Hkv, 128))
+    got = _run_append(B, Hq, Hkv, n_ret, max_ctx, lens, k_new, v_new, k_pre, w_k, list(range(n_ret)), caches)
+    ki = got[2]
+    bad = []
+    for b in range(B):
+        for r in range(n_ret):
+            want = O.index_key(w_k[r], ks[b])
+            have = ki[b, r, lens[b] - 1]
+            if not np.array_equal(have, want):
+                bad.append((b, r, [hex(x) for x in have[have != want]], [hex(x) for x in want[have != want]]))
+    assert not bad, bad[:4]
+    # the counterexample pairing itself: w row "tie_plus_tail" with its own k
+    from key_cases import CASES
+    i = sorted(CASES).index("tie_plus_tail")
+    assert ki[i, i // 16, lens[i] - 1, i % 16] == 0x3F81
+
+
+def test_prompt_keys_exact_sum_rounded_once():
+    """rtp_prefill_index_keys on the same boundary pairings: 32 prompt rows (the k
+    vectors) against 32 w rows, bit for bit against oracle.index_key."""
+    ws, ks = _boundary_vectors()
+    n_ret, T = 2, ks.shape[0]
+    say(f"[gpu] prompt keys: {T} rows x {ws.shape[0]} w rows")
+    w_k = ws.reshape(n_ret, 16, 128)
+    Hq, Hkv = 4, 2
+    k_pre = np.repeat(ks[None, None], Hkv, axis=1)          # [1, Hkv, T, 128]
+    ret = [1, 2]                                             # KV groups 0 and 1
+    k_idx = torch.zeros((1, n_ret, T, 16), dtype=torch.int16, device="cuda")
+    sl = torch.tensor([T], dtype=torch.int32, device="cuda")
+    rh = torch.tensor(ret, dtype=torch.int32, device="cuda")
+    abi.rtp_prefill_index_keys(_dev(k_pre), _dev(w_k), sl, rh, 1, Hq, Hkv, n_ret, T, k_idx)
+    torch.cuda.synchronize()
+    ki = k_idx.cpu().numpy().view(np.uint16)
+    bad = []
+    for t in range(T):
+        for r in range(n_ret):
+            want = O.index_key(w_k[r], ks[t])
+            if not np.array_equal(ki[0, r, t], want):
+                bad.append((t, r))
+    assert not bad, bad[:8]
