@@ -27,7 +27,8 @@
  *   - Every tensor argument is a DEVICE pointer owned by the caller, contiguous,
  *     row-major, with the layout given at each argument.  bf16 tensors are passed as
  *     const void* (raw bf16 bits).  The library allocates nothing and keeps no global
- *     mutable state; it is reentrant for disjoint workspaces.
+ *     mutable state (except rtp_decode_step_noalloc's fixed device scratch and its per-
+ *     device bookkeeping); it is reentrant for disjoint workspaces.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Each call
  *     checks its scalar arguments on the host (no device access, no synchronization),
  *     then enqueues its kernels on `stream` and returns.  Buffers must stay alive until
@@ -43,7 +44,8 @@
  *   - Return codes: RTP_OK; RTP_EINVAL for a null pointer, a non-positive size, an
  *     inconsistent shape or a workspace that is too small; RTP_EUNSUPPORTED for a block
  *     size or head grouping outside the fixed set; RTP_ELAUNCH when HIP reports a
- *     launch error.  On any error nothing is enqueued, except for RTP_ELAUNCH.
+ *     launch error; RTP_ESCRATCH when rtp_decode_step_noalloc's sizes need more than its
+ *     fixed scratch.  On any error nothing is enqueued, except for RTP_ELAUNCH.
  *   - n_ret == 0 (resp. n_loc == 0, n_heads == 0) is a no-op returning RTP_OK.
  */
 #ifndef RTP_H_
@@ -62,7 +64,8 @@ typedef enum {
   RTP_OK = 0,
   RTP_EINVAL = 1,
   RTP_EUNSUPPORTED = 2,
-  RTP_ELAUNCH = 3
+  RTP_ELAUNCH = 3,
+  RTP_ESCRATCH = 4
 } rtp_status;
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -321,6 +324,35 @@ rtp_status rtp_decode_step(const void* q_pre, const void* w_q, const void* k_idx
                            void* ws_index, size_t ws_index_bytes, void* ws_local, size_t ws_local_bytes,
                            const int* kv_slot, int n_full, const void* k_ring, const void* v_ring, int n_ring,
                            void* stream, void* side_stream, void* ev_fork, void* ev_join);
+
+/*
+ * rtp_decode_step for callers that cannot allocate or pass workspaces (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same step with
+ * the same kernels and arguments, except that the index workspace, the local heads'
+ * workspace and the split partials (o_part, lse_part) live in a fixed array in the
+ * library's device memory (rtp_decode_step_noalloc_limit() bytes on each GPU it runs on,
+ * held until the process ends): at most 16 MiB of index workspace
+ * (rtp_index_topp_workspace_size), 8 MiB of local workspace
+ * (rtp_local_window_workspace_size) and 8 MiB of partials (B * n_ret * n_split * 516
+ * bytes, rounded up), else RTP_ESCRATCH and nothing is enqueued.  It calls no allocating
+ * routine.  The array's device address is looked up once per device (with that device
+ * current); `stream` must belong to the current device.  The index part is cleared with a
+ * fill kernel on `stream` at the first call on a device and whenever ceil(max_ctx / block)
+ * changes; it keeps its per-head state between calls otherwise.  Every call on a GPU
+ * shares that GPU's array: calls that overlap on one GPU (other streams, other host
+ * threads) race and must be serialized by the caller.  The index workspace's status words
+ * are not reported by this entry point (a head whose wait ran out still selects every
+ * block).  Outputs sel_idx, sel_cnt, sel_mask and out as in rtp_decode_step.
+ */
+size_t rtp_decode_step_noalloc_limit(void);
+rtp_status rtp_decode_step_noalloc(const void* q_pre, const void* w_q, const void* k_idx, const void* q,
+                                   const void* k_cache, const void* v_cache, const int* seq_lens,
+                                   const int* ret_heads, const int* loc_heads, const float* top_p, int k_tokens,
+                                   int B, int Hq, int Hkv, int n_ret, int n_loc, int max_ctx, int block,
+                                   int split_tokens, int window, int sinks,
+                                   int* sel_idx, int* sel_cnt, unsigned char* sel_mask, float* out,
+                                   const int* kv_slot, int n_full, const void* k_ring, const void* v_ring,
+                                   int n_ring, void* stream, void* side_stream, void* ev_fork, void* ev_join);
 
 /*
  * Ring fill after a prefill (KV placement above): for every ring group (kv_slot[g] < 0),

@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librtp.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "rtp.h")
 
-RTP_OK, RTP_EINVAL, RTP_EUNSUPPORTED, RTP_ELAUNCH = 0, 1, 2, 3
+RTP_OK, RTP_EINVAL, RTP_EUNSUPPORTED, RTP_ELAUNCH, RTP_ESCRATCH = 0, 1, 2, 3, 4
 
 _lib = None
 
@@ -42,6 +42,8 @@ _SIGS = {
     "rtp_local_window_attn": ([_vp] * 5 + [_i] * 7 + [_vp, _vp, _sz, _vp, _i, _vp, _vp, _i, _vp], _i),
     "rtp_decode_step": ([_vp] * 10 + [_i] * 11 + [_vp] * 6 + [_vp, _sz, _vp, _sz] + [_vp, _i, _vp, _vp, _i]
                         + [_vp] * 4, _i),
+    "rtp_decode_step_noalloc_limit": ([], _sz),
+    "rtp_decode_step_noalloc": ([_vp] * 10 + [_i] * 11 + [_vp] * 4 + [_vp, _i, _vp, _vp, _i] + [_vp] * 4, _i),
     "rtp_cache_append": ([_vp] * 6 + [_i] * 5 + [_vp] * 3 + [_vp, _i, _vp, _vp, _i, _i, _i, _vp], _i),
     "rtp_prefill_attn": ([_vp] * 5 + [_i] * 7 + [_vp, _vp], _i),
     "rtp_prefill_index_keys": ([_vp] * 4 + [_i] * 5 + [_vp, _vp], _i),
@@ -186,6 +188,24 @@ def rtp_sparse_attn_split(q, k_cache, v_cache, seq_lens, ret_heads, sel_idx, sel
                                      _p(sel_idx), _p(sel_cnt), _p(sel_mask), B, Hq, Hkv, n_ret, max_ctx, block,
                                      split_tokens, _p(o_part), _p(lse_part), _p(kv_slot), n_full, _s(stream))
     _check("rtp_sparse_attn_split", st)
+
+
+def rtp_decode_step_noalloc_limit() -> int:
+    return int(lib().rtp_decode_step_noalloc_limit())
+
+
+def rtp_decode_step_noalloc(q_pre, w_q, k_idx, q, k_cache, v_cache, seq_lens, ret_heads, loc_heads, top_p, k_tokens,
+                            B, Hq, Hkv, n_ret, n_loc, max_ctx, block, split_tokens, window, sinks,
+                            sel_idx, sel_cnt, sel_mask, out, stream=None, kv_slot=None, n_full=0, k_ring=None,
+                            v_ring=None, n_ring=0, side_stream=None, ev_fork=None, ev_join=None) -> None:
+    """rtp_decode_step with its workspaces and partials in the library's fixed device scratch."""
+    side = None if side_stream is None else _s(side_stream)
+    st = lib().rtp_decode_step_noalloc(_p(q_pre), _p(w_q), _p(k_idx), _p(q), _p(k_cache), _p(v_cache),
+                                       _p(seq_lens), _p(ret_heads), _p(loc_heads), _p(top_p), int(k_tokens), B, Hq,
+                                       Hkv, n_ret, n_loc, max_ctx, block, split_tokens, window, sinks, _p(sel_idx),
+                                       _p(sel_cnt), _p(sel_mask), _p(out), _p(kv_slot), n_full, _p(k_ring),
+                                       _p(v_ring), n_ring, _s(stream), side, ev_fork, ev_join)
+    _check("rtp_decode_step_noalloc", st)
 
 
 def rtp_cache_append(k_new, v_new, k_pre, w_k, seq_lens, ret_heads, B, Hq, Hkv, n_ret, max_ctx,

@@ -266,6 +266,7 @@ extern "C" const char* rtp_status_string(int status) {
     case RTP_EINVAL: return "RTP_EINVAL: invalid argument";
     case RTP_EUNSUPPORTED: return "RTP_EUNSUPPORTED: size outside the supported set";
     case RTP_ELAUNCH: return "RTP_ELAUNCH: kernel launch failed";
+    case RTP_ESCRATCH: return "RTP_ESCRATCH: sizes beyond the no-allocation entry point's fixed scratch";
     default: return "RTP_UNKNOWN";
   }
 }

@@ -218,3 +218,21 @@ def test_ring_fill_rejects():
     assert fill(k=None) == abi.RTP_EINVAL
     assert fill(kr=FAKE + 8) == abi.RTP_EINVAL          # misaligned
     assert fill(n_ring=0) == abi.RTP_OK                 # no-op
+
+
+def test_noalloc_step_limit_and_rejects():
+    """The no-allocation step states its scratch (32 MiB) and rejects sizes beyond it, or
+    invalid ones, before any device call."""
+    assert abi.rtp_decode_step_noalloc_limit() == 32 << 20
+    assert "ESCRATCH" in abi.status_string(abi.RTP_ESCRATCH)
+    f = abi.lib().rtp_decode_step_noalloc
+
+    def call(B=1, Hq=8, Hkv=2, n_ret=2, n_loc=6, max_ctx=4096, block=64, split=256, window=64, sinks=4):
+        return f(*([FAKE] * 10), 0, B, Hq, Hkv, n_ret, n_loc, max_ctx, block, split, window, sinks,
+                 FAKE, FAKE, None, FAKE, None, 0, None, None, 0, None, None, None, None)
+    assert call(B=64, Hq=32, Hkv=8, n_ret=32, n_loc=0, max_ctx=1 << 20, block=128, split=128) == abi.RTP_ESCRATCH
+    assert call(B=8, Hq=32, Hkv=8, n_ret=16, n_loc=16, max_ctx=1 << 20, block=128, split=128) == abi.RTP_ESCRATCH
+    assert call(block=32) == abi.RTP_EUNSUPPORTED
+    assert call(split=100) == abi.RTP_EINVAL
+    assert call(n_ret=5, n_loc=5) == abi.RTP_EINVAL
+    assert call(window=0, sinks=0) == abi.RTP_EINVAL
