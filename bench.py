@@ -1,11 +1,13 @@
 """Decode-step benchmark of the sparse attention path on one MI355X.
 
 One step = the whole hot path for one decode token of every sequence and query
-head of a workload: rtp_index_topp -> rtp_sparse_attn_split -> rtp_split_reduce for
-the retrieval heads, rtp_local_window_attn (second stream) for the local heads.
+head of a workload, one rtp_decode_step call, three launches on one stream:
+rtp_index_topp (scores and block selection of the retrieval heads) -> rtp_decode_attn
+(the retrieval heads' block-sparse split attention and the local heads' window attention
+in one grid) -> rtp_decode_merge (both kinds of partials -> outputs).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ctx128k]
-                    [--also ctx1m,ctx128k@topk4096]
+                    [--also ctx1m,ctx128k@topk4096,mixed,ctx32k,tiny] [--minimal]
 
 A workload name with "@topkK" runs the step with the static top-k rule (a budget of K
 tokens, rtp_index_topk) in place of top-p.
@@ -37,17 +39,16 @@ if ROOT not in sys.path:
 
 METRIC = "sparse-decode step latency (µs) + effective HBM GB/s at 128K and 1M ctx"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, vendor figure
-KERNEL_NAMES = {                # call -> the kernel it launches (the local call also merges)
+KERNEL_NAMES = {                # launch of the step -> its kernel
     "index_topp": "index_topp_kernel",
     "index_topk": "index_topp_kernel",
-    "sparse_attn": "sparse_attn_kernel",
-    "split_reduce": "merge_kernel",
-    "local_window": "local_window_kernel",
+    "decode_attn": "step_attn_kernel",
+    "decode_merge": "merge_step_kernel",
 }
 
 
-CALL_NAMES = {"index_topp": "rtp_index_topp", "index_topk": "rtp_index_topk", "sparse_attn": "rtp_sparse_attn_split",
-              "split_reduce": "rtp_split_reduce", "local_window": "rtp_local_window_attn"}
+CALL_NAMES = {"index_topp": "rtp_index_topp", "index_topk": "rtp_index_topk", "decode_attn": "rtp_decode_attn",
+              "decode_merge": "rtp_decode_merge"}
 
 
 def log(*a) -> None:
@@ -70,33 +71,29 @@ def local_token_mask(n: int, window: int, sinks: int) -> np.ndarray:
 
 
 def algorithmic_bytes(cfg, inp, sel_idx: np.ndarray, sel_cnt: np.ndarray) -> Dict[str, float]:
-    """Bytes each call (and the whole step) must move for the given block selection.
+    """Bytes each launch of the step (and the whole step) must move for the given block
+    selection.
 
     index_topp:   W^Q (4 KiB a retrieval head) + 32 B per cached token per retrieval
                   head (16 bf16 index dims) + the q_pre row + the selected-block list.
-    sparse_attn:  512 B (K and V rows, 128 bf16 each) per (KV head, token) in the union
-                  of the group's retrieval heads' selected blocks + the q rows.
-    split_reduce: the fp32 output rows of the retrieval heads.
-    local_window: 512 B per (KV head, token) in sinks + window for groups holding local
-                  heads + q rows + fp32 output rows.
-    step:         the sum, with K/V counted once per (KV head, token) over the union of
-                  both token sets.
+    decode_attn:  512 B (K and V rows, 128 bf16 each) per (KV head, token) in the union,
+                  over the group's heads, of the retrieval heads' selected blocks and (for
+                  groups with local heads) the sinks + window, + every query row (256 B).
+    decode_merge: the fp32 output rows (512 B) of every query head.
+    step:         the sum.  Partials (split and window) are scratch and not counted.
     """
     G = cfg.Hq // cfg.Hkv
     ret = [int(h) for h in inp.ret_heads]
     loc = [int(h) for h in inp.loc_heads]
-    out = dict(index_topp=0.0, sparse_attn=0.0, split_reduce=0.0, local_window=0.0, step=0.0)
+    out = dict(index_topp=0.0, decode_attn=0.0, decode_merge=0.0, step=0.0)
     out["index_topp"] += len(ret) * 16 * 128 * 2
-    kv_step = 0
+    kv_sel = kv_win = 0
     for b in range(cfg.B):
         n = int(inp.seq_lens[b])
         for r in range(len(ret)):
-            cnt = int(sel_cnt[b, r])
-            out["index_topp"] += 32.0 * n + 256 + 4 * cnt + 4
-            out["sparse_attn"] += 256
-            out["split_reduce"] += 512
-        for h in loc:
-            out["local_window"] += 256 + 512
+            out["index_topp"] += 32.0 * n + 256 + 4 * int(sel_cnt[b, r]) + 4
+        out["decode_attn"] += 256.0 * (len(ret) + len(loc))
+        out["decode_merge"] += 512.0 * (len(ret) + len(loc))
         for g in range(cfg.Hkv):
             rs = [r for r, h in enumerate(ret) if h // G == g]
             has_loc = any(h // G == g for h in loc)
@@ -104,18 +101,19 @@ def algorithmic_bytes(cfg, inp, sel_idx: np.ndarray, sel_cnt: np.ndarray) -> Dic
             for r in rs:
                 sel |= block_token_mask(sel_idx[b, r, :int(sel_cnt[b, r])], cfg.block, n)
             win = local_token_mask(n, cfg.window, cfg.sinks) if has_loc else np.zeros(n, dtype=bool)
-            out["sparse_attn"] += 512.0 * int(sel.sum())
-            out["local_window"] += 512.0 * int(win.sum())
-            kv_step += int((sel | win).sum())
-    kv_sep = (out["sparse_attn"] + out["local_window"]) - 256 * cfg.B * len(ret) - 768 * cfg.B * len(loc)
-    out["step"] = (out["index_topp"] + out["sparse_attn"] + out["split_reduce"] + out["local_window"]
-                   - kv_sep + 512.0 * kv_step)
+            out["decode_attn"] += 512.0 * int((sel | win).sum())
+            kv_sel += int(sel.sum())
+            kv_win += int(win.sum())
+    out["step"] = out["index_topp"] + out["decode_attn"] + out["decode_merge"]
     out["kv_tokens_selected"] = float(sum(int(sel_cnt[b, r]) for b in range(cfg.B) for r in range(len(ret))))
+    out["kv_rows_selected_union"] = float(kv_sel)
+    out["kv_rows_window"] = float(kv_win)
     return out
 
 
 # ------------------------------------------------------------------ traffic records
-KERNEL_SOURCE = {"index_topp_kernel": "index_topp.hip", "sparse_attn_kernel": "sparse_attn.hip",
+KERNEL_SOURCE = {"index_topp_kernel": "index_topp.hip", "step_attn_kernel": "sparse_attn.hip",
+                 "merge_step_kernel": "sparse_attn.hip", "sparse_attn_kernel": "sparse_attn.hip",
                  "merge_kernel": "sparse_attn.hip", "local_window_kernel": "sparse_attn.hip",
                  "prefill_kernel": "prefill_attn.hip"}
 
@@ -166,9 +164,10 @@ def read_traffic(workload: str, kernel: str) -> Optional[float]:
 
 
 # ------------------------------------------------------------------ GPU measurement
-def measure(label: str, steps: int, warmup: int, cold_iters: int, calib_copy: bool) -> Dict:
+def measure(label: str, steps: int, warmup: int, cold_iters: int, calib_copy: bool, minimal: bool = False) -> Dict:
     """One workload; label = a workload name, optionally with "@topkK" (static top-k rule,
-    budget K tokens)."""
+    budget K tokens).  minimal: only the warm-up and the timed steps (for profiler runs
+    whose traces should hold the step's kernels alone)."""
     import torch
 
     import workloads as W
@@ -195,28 +194,38 @@ def measure(label: str, steps: int, warmup: int, cold_iters: int, calib_copy: bo
     if k_tokens:
         alg["index_topk"] = alg.pop("index_topp")
 
-    # timed region: `steps` back-to-back decode steps, inputs resident in HBM
+    # timed region: `steps` back-to-back decode steps, inputs resident in HBM, with an
+    # event between consecutive steps on the stream they run on (per-step durations)
     main = torch.cuda.current_stream(dev)
     for _ in range(warmup):
         step(t)
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs_step = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     w0 = time.perf_counter()
-    ev0.record(main)
-    for _ in range(steps):
+    evs_step[0].record(main)
+    for i in range(steps):
         step(t)
-    ev1.record(main)
+        evs_step[i + 1].record(main)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    ms_per_step = ev0.elapsed_time(ev1) / steps
-    log(f"[bench] {label}: {steps} steps, {ms_per_step * 1e3:.1f} us/step (host {wall * 1e6 / steps:.1f} us/step)")
+    ms_per_step = evs_step[0].elapsed_time(evs_step[-1]) / steps
+    per_step_us = [evs_step[i].elapsed_time(evs_step[i + 1]) * 1e3 for i in range(steps)]
+    log(f"[bench] {label}: {steps} steps, {ms_per_step * 1e3:.1f} us/step (median {np.median(per_step_us):.1f}, "
+        f"host {wall * 1e6 / steps:.1f} us/step)")
+    if minimal:
+        res = dict(workload=name, label=label, k_tokens=k_tokens, cfg=cfg, inp=inp, alg=alg, latency_us=ms_per_step * 1e3,
+                   per_step_us=per_step_us, wall_us=wall * 1e6 / steps, kern_us={}, dominant=None, append_us=None,
+                   cold_us=None, dense_us=None, gbs=alg["step"] / (ms_per_step * 1e-3) / 1e9, sel_frac=None)
+        del step, t
+        torch.cuda.empty_cache()
+        return res
 
-    # per-call durations: the four calls one after another on the main stream, with
-    # events around each call on that stream
+    # per-launch durations: the step's three launches one after another on the stream the
+    # step runs on, with events around each launch on that stream
     calls = [("index_topk", step.index_topk) if k_tokens else ("index_topp", step.index_topp),
-             ("sparse_attn", step.sparse_attn),
-             ("split_reduce", step.reduce), ("local_window", step.local)]
-    calls = [(k, f) for k, f in calls if (cfg.n_ret if k != "local_window" else cfg.n_loc)]
+             ("decode_attn", step.attn), ("decode_merge", step.merge)]
+    if not cfg.n_ret:
+        calls = calls[1:]
     per = {k: [] for k, _ in calls}
     iters = max(steps, 20)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(iters)]
@@ -299,7 +308,8 @@ def measure(label: str, steps: int, warmup: int, cold_iters: int, calib_copy: bo
     lat_us = ms_per_step * 1e3
     dom = max(kern_us, key=kern_us.get)
     res = dict(
-        workload=name, label=label, k_tokens=k_tokens, cfg=cfg, inp=inp, alg=alg, latency_us=lat_us, wall_us=wall * 1e6 / steps,
+        workload=name, label=label, k_tokens=k_tokens, cfg=cfg, inp=inp, alg=alg, latency_us=lat_us,
+        per_step_us=per_step_us, wall_us=wall * 1e6 / steps,
         kern_us=kern_us, dominant=dom, append_us=append_us, cold_us=float(np.median(cold)) if cold else None,
         dense_us=dense_us,
         gbs=alg["step"] / (lat_us * 1e-6) / 1e9,
@@ -413,24 +423,149 @@ def roofline_of(r: Dict) -> Dict:
 
 
 # ------------------------------------------------------------------ CPU baseline
+_ORACLE_ARRAYS = ("seq_lens", "ret_heads", "loc_heads", "top_p", "q", "w_q", "k_cache", "v_cache", "k_idx")
+
+
+def _oracle_worker(args):
+    """Pool worker (a fresh interpreter that never touches the GPU): the oracle on a share
+    of the step's (sequence, head) items, reading the inputs from shared memory."""
+    import types
+    from multiprocessing import shared_memory
+
+    from oracle import rtp_oracle as O
+    cfg, specs, items = args
+    shms, arrs = [], {}
+    for name, (shm_name, shape, dtype) in specs.items():
+        shm = shared_memory.SharedMemory(name=shm_name)
+        shms.append(shm)
+        arrs[name] = np.ndarray(shape, dtype=dtype, buffer=shm.buf)
+    inp = types.SimpleNamespace(cfg=cfg, q_pre=arrs["q"], **arrs)
+    t0 = time.perf_counter()
+    O.decode_step(inp, items)
+    dt = time.perf_counter() - t0
+    del inp, arrs
+    for shm in shms:
+        shm.close()
+    return dt
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(r: Dict, reps: int) -> Dict:
-    """The fp64 oracle (unchanged) over the same workload on the host, one BLAS thread."""
+    """The fp64 oracle (unchanged) over the whole step of the same workload on the host:
+    once on one core (one BLAS thread), once on every core this process may use (a pool of
+    fresh worker processes over the step's (sequence, head) items, inputs in shared
+    memory, one BLAS thread each); median of `reps` runs each."""
+    import multiprocessing as mp
+    from multiprocessing import shared_memory
+
     from threadpoolctl import threadpool_limits
 
     from oracle import rtp_oracle as O
 
     inp, cfg = r["inp"], r["cfg"]
-    times = []
+    one = []
     with threadpool_limits(limits=1):
         for _ in range(reps):
             t0 = time.perf_counter()
             O.decode_step(inp)
-            times.append(time.perf_counter() - t0)
-    sec = statistics.median(times)
-    return {"value": round(r["alg"]["step"] / sec / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"whole {cfg.name} step ({cfg.B} seqs x {cfg.Hq} heads), median of {reps} runs, "
-                      f"{sec:.2f} s each; GB/s = the step's algorithmic bytes / oracle time",
-            "seconds_per_step": round(sec, 3)}
+            one.append(time.perf_counter() - t0)
+    sec1 = statistics.median(one)
+
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    items = [(b, h) for b in range(cfg.B) for h in range(cfg.Hq)]
+    shms, specs = [], {}
+    try:
+        for name in _ORACLE_ARRAYS:
+            a = np.ascontiguousarray(getattr(inp, name))
+            shm = shared_memory.SharedMemory(create=True, size=max(1, a.nbytes))
+            np.ndarray(a.shape, dtype=a.dtype, buffer=shm.buf)[...] = a
+            shms.append(shm)
+            specs[name] = (shm.name, a.shape, a.dtype.str)
+        # the heaviest items first, dealt round-robin, so the shares finish together
+        shares = [items[i::cores] for i in range(cores)]
+        env = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+        for k in env:
+            os.environ[k] = "1"
+        try:
+            ctx = mp.get_context("spawn")
+            with ctx.Pool(cores) as pool:
+                pool.map(_oracle_worker, [(cfg, specs, sh[:1]) for sh in shares])  # workers warm
+                multi = []
+                for _ in range(reps):
+                    t0 = time.perf_counter()
+                    pool.map(_oracle_worker, [(cfg, specs, sh) for sh in shares])
+                    multi.append(time.perf_counter() - t0)
+        finally:
+            for k, v in env.items():
+                if v is None:
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
+    finally:
+        for shm in shms:
+            shm.close()
+            shm.unlink()
+    secn = statistics.median(multi)
+    gb = r["alg"]["step"] / 1e9
+    return {"value": round(gb / secn, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"the whole {cfg.name} step ({cfg.B} seqs x {cfg.Hq} heads, every head), median of {reps} runs "
+                      f"on {cores} cores ({secn:.3f} s) and on 1 core ({sec1:.3f} s); GB/s = the step's "
+                      f"algorithmic bytes / oracle time",
+            "seconds_per_step": round(secn, 4), "one_core": {"value": round(gb / sec1, 4), "seconds_per_step":
+                                                              round(sec1, 4), "cores": 1},
+            "cpu_model": cpu_model()}
+
+
+# ------------------------------------------------------------------ streaming ceiling
+def stream_ceiling(gib: float = 4.0, reps: int = 10) -> Dict:
+    """A plain read-only stream (rtp_stream_read) over a fresh `gib` GiB buffer, with
+    non-temporal and with cached 16-byte loads, at a few grid sizes; the best of each."""
+    import torch
+
+    from long_context_sparse_amd import abi
+
+    nbytes = int(gib * (1 << 30))
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(65535, dtype=torch.int32, device="cuda")
+    out = {}
+    for nt in (True, False):
+        best = 0.0
+        for wgs in (1024, 2048, 4096, 8192):
+            abi.rtp_stream_read(buf, sink, wgs, nt)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                abi.rtp_stream_read(buf, sink, wgs, nt)
+            e1.record()
+            torch.cuda.synchronize()
+            gbs = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+            best = max(best, gbs)
+        out["nontemporal_gbs" if nt else "cached_gbs"] = round(best, 1)
+    del buf, sink
+    torch.cuda.empty_cache()
+    out["bytes"] = nbytes
+    log(f"[bench] streaming read ceiling: {out['nontemporal_gbs']} GB/s non-temporal, {out['cached_gbs']} GB/s cached")
+    return out
+
+
+def step_stats(r: Dict) -> Dict:
+    """Median, 10th and 90th percentile of the per-step durations (µs) and their GB/s."""
+    v = np.asarray(r["per_step_us"], dtype=np.float64)
+    p10, p50, p90 = (float(np.percentile(v, q)) for q in (10, 50, 90))
+    gb = r["alg"]["step"] / 1e3
+    return {"median_us": round(p50, 2), "p10_us": round(p10, 2), "p90_us": round(p90, 2),
+            "median_effective_gbs": round(gb / p50, 1), "steps": int(v.size)}
 
 
 def main(argv: Optional[List[str]] = None) -> int:
@@ -439,13 +574,16 @@ def main(argv: Optional[List[str]] = None) -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="ctx128k")
-    ap.add_argument("--also", default="ctx1m,ctx128k@topk4096",
+    ap.add_argument("--also", default="ctx1m,ctx128k@topk4096,mixed,ctx32k,tiny",
                     help="comma-separated extra workloads ('' for none); name@topkK: static top-k rule")
     ap.add_argument("--prefill", default="32768,131072",
                     help="comma-separated prompt lengths for the prefill pass ('' for none)")
     ap.add_argument("--cold-iters", type=int, default=20)
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stream-ceiling", action="store_true")
+    ap.add_argument("--minimal", action="store_true",
+                    help="only the warm-up and timed steps of each workload (for profiler runs)")
     ap.add_argument("--calib-copy", action="store_true", help="also run a 1 GiB device copy (counter scaling)")
     a = ap.parse_args(argv)
     if a.gpus != 1:
@@ -457,10 +595,16 @@ def main(argv: Optional[List[str]] = None) -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
 
-    head = measure(a.workload, a.steps, a.warmup, a.cold_iters, a.calib_copy)
+    head = measure(a.workload, a.steps, a.warmup, a.cold_iters, a.calib_copy, a.minimal)
     extras = {}
     for name in [x for x in a.also.split(",") if x and x != a.workload]:
-        extras[name] = measure(name, a.steps, a.warmup, a.cold_iters, False)
+        extras[name] = measure(name, a.steps, a.warmup, a.cold_iters, False, a.minimal)
+    if a.minimal:
+        print(json.dumps({"minimal": True, **{r["label"]: {"latency_us": round(r["latency_us"], 2), **step_stats(r)}
+                                               for r in [head, *extras.values()]}}), flush=True)
+        return 0
+
+    ceiling = None if a.no_stream_ceiling else stream_ceiling()
 
     prefill = {}
     for n in [int(x) for x in a.prefill.split(",") if x]:
@@ -471,9 +615,16 @@ def main(argv: Optional[List[str]] = None) -> int:
         log("[bench] cpu baseline (oracle)")
         cpu = cpu_baseline(head, a.cpu_reps)
 
+    def roof(r):
+        x = roofline_of(r)
+        if ceiling:
+            x["frac_of_measured_stream_ceiling"] = round(x["achieved"] / ceiling["nontemporal_gbs"], 4)
+        return x
+
     def summary(r):
         return {"latency_us": round(r["latency_us"], 2), "effective_gbs": round(r["gbs"], 1),
                 "frac_of_peak": round(r["gbs"] / PEAK_HBM_GBS, 4), "alg_bytes": int(r["alg"]["step"]),
+                "per_step": step_stats(r),
                 "cold_latency_us": None if r["cold_us"] is None else round(r["cold_us"], 2),
                 "cold_effective_gbs": None if not r["cold_us"] else round(r["alg"]["step"] / r["cold_us"] / 1e3, 1),
                 "call_us": {CALL_NAMES[k]: round(v, 2) for k, v in r["kern_us"].items()},
@@ -481,7 +632,7 @@ def main(argv: Optional[List[str]] = None) -> int:
                 "dense_decode_us": round(r["dense_us"], 1),
                 "speedup_vs_dense_decode": round(r["dense_us"] / r["latency_us"], 2),
                 "mean_selected_block_fraction": round(r["sel_frac"], 4),
-                "roofline": roofline_of(r), "config": config_of(r["cfg"], r["k_tokens"])}
+                "roofline": roof(r), "config": config_of(r["cfg"], r["k_tokens"])}
 
     line = {
         "metric": METRIC, "value": round(head["gbs"], 1), "unit": "GB/s", "n_gpus": 1, "steps": a.steps,
@@ -490,8 +641,10 @@ def main(argv: Optional[List[str]] = None) -> int:
         "config": config_of(head["cfg"], head["k_tokens"]),
         "latency_us": round(head["latency_us"], 2),
         "frac_of_peak": round(head["gbs"] / PEAK_HBM_GBS, 4),
-        "roofline": roofline_of(head),
+        "per_step": step_stats(head),
+        "roofline": roof(head),
         "cpu_baseline": cpu,
+        "stream_ceiling": ceiling,
         "detail": summary(head),
         "also": {k: summary(v) for k, v in extras.items()},
         "prefill": prefill,

@@ -294,16 +294,49 @@ rtp_status rtp_cache_append(const void* k_new, const void* v_new, const void* k_
                             void* stream);
 
 /*
- * One decode step in one host call: the four calls above, enqueued in their order for
- * the same arguments (Strikes-Back architecture paragraph: Kernel 1, Kernel 2 and the
- * reduce; Review, Adaptive sparse attention: local heads).  rtp_local_window_attn goes to
- * side_stream, forked from `stream` by recording ev_fork on it and joined back by
- * recording ev_join on side_stream and making `stream` wait for it, so the local heads
- * overlap the retrieval heads' calls; with side_stream, ev_fork or ev_join NULL (or
- * n_ret == 0 or n_loc == 0) everything runs on `stream`.  The caller owns the streams
- * and the events (hipEvent_t as void*, created without timing); the library creates
- * nothing.  Every argument is checked (as by each call) before anything is enqueued;
- * after that it returns the first failing call's status.
+ * The decode step's attention in one launch: rtp_sparse_attn_split's partials for the
+ * retrieval heads (Strikes-Back method item 2 and architecture paragraph, Kernel 2) and
+ * the local heads' window + sink partials (Review, Adaptive sparse attention: local heads
+ * keep a window and sinks; the same token set T as rtp_local_window_attn) written to
+ * ws_local, computed by the workgroups of one grid: the split attention's first (KV groups
+ * heaviest first), the local heads' after them, so these fill the compute units the split
+ * attention's last workgroups leave idle.  rtp_decode_merge turns both into outputs.
+ *
+ *   every argument as in rtp_sparse_attn_split (retrieval heads; NULL and ignored when
+ *   n_ret == 0) and rtp_local_window_attn (local heads; ignored when n_loc == 0); ws_local
+ *   holds the local partials (>= rtp_local_window_workspace_size bytes, 256-byte aligned)
+ */
+rtp_status rtp_decode_attn(const void* q, const void* k_cache, const void* v_cache, const int* seq_lens,
+                           const int* ret_heads, const int* sel_idx, const int* sel_cnt,
+                           const unsigned char* sel_mask, const int* loc_heads, int B, int Hq, int Hkv,
+                           int n_ret, int n_loc, int max_ctx, int block, int split_tokens, int window,
+                           int sinks, float* o_part, float* lse_part, void* ws_local, size_t ws_local_bytes,
+                           const int* kv_slot, int n_full, const void* k_ring, const void* v_ring, int n_ring,
+                           void* stream);
+
+/*
+ * The decode step's merge in one launch (Strikes-Back architecture paragraph, the
+ * cross-split reduce): out[b, ret_heads[i]] from the retrieval heads' split partials as
+ * rtp_split_reduce computes it, and out[b, loc_heads[i]] from the local heads' window
+ * partials rtp_decode_attn left in ws_local, with the same log-sum-exp rule.
+ *
+ *   o_part, lse_part  as written by rtp_decode_attn (n_split = ceil(max_ctx / split_tokens))
+ *   ws_local          the local workspace of rtp_decode_attn (same sizes)
+ *   out               out fp32 [B, Hq, 128]; rows ret_heads[] and loc_heads[] are written
+ */
+rtp_status rtp_decode_merge(const float* o_part, const float* lse_part, const int* ret_heads,
+                            const int* loc_heads, int B, int Hq, int Hkv, int n_ret, int n_loc, int max_ctx,
+                            int split_tokens, int window, int sinks, const void* ws_local,
+                            size_t ws_local_bytes, float* out, void* stream);
+
+/*
+ * One decode step in one host call, three launches on `stream` (Strikes-Back
+ * architecture paragraph: Kernel 1, Kernel 2 and the reduce; Review, Adaptive sparse
+ * attention: local heads): rtp_index_topp (or rtp_index_topk), rtp_decode_attn and
+ * rtp_decode_merge for the same arguments.  The outputs equal those of the separate
+ * calls rtp_index_topp, rtp_sparse_attn_split, rtp_split_reduce and rtp_local_window_attn.
+ * Every argument is checked before anything is enqueued; after that it returns the first
+ * failing call's status.
  *
  *   k_tokens           0: the top-p rule with top_p (rtp_index_topp); > 0: the static top-k
  *                      rule with this budget (rtp_index_topk; top_p may then be NULL)
@@ -311,7 +344,7 @@ rtp_status rtp_cache_append(const void* k_new, const void* v_new, const void* k_
  *                      ceil(max_ctx / split_tokens))
  *   ws_index           workspace of rtp_index_topp; ws_local of rtp_local_window_attn
  *   kv_slot, n_full, k_ring, v_ring, n_ring   KV placement (above), passed to the split
- *                      attention and the local heads' call
+ *                      attention and the local heads
  *   every other argument as in the four calls
  */
 rtp_status rtp_decode_step(const void* q_pre, const void* w_q, const void* k_idx, const void* q,
@@ -323,7 +356,7 @@ rtp_status rtp_decode_step(const void* q_pre, const void* w_q, const void* k_idx
                            float* o_part, float* lse_part, float* out,
                            void* ws_index, size_t ws_index_bytes, void* ws_local, size_t ws_local_bytes,
                            const int* kv_slot, int n_full, const void* k_ring, const void* v_ring, int n_ring,
-                           void* stream, void* side_stream, void* ev_fork, void* ev_join);
+                           void* stream);
 
 /*
  * rtp_decode_step for callers that cannot allocate or pass workspaces (code under HIP
@@ -352,7 +385,7 @@ rtp_status rtp_decode_step_noalloc(const void* q_pre, const void* w_q, const voi
                                    int split_tokens, int window, int sinks,
                                    int* sel_idx, int* sel_cnt, unsigned char* sel_mask, float* out,
                                    const int* kv_slot, int n_full, const void* k_ring, const void* v_ring,
-                                   int n_ring, void* stream, void* side_stream, void* ev_fork, void* ev_join);
+                                   int n_ring, void* stream);
 
 /*
  * Ring fill after a prefill (KV placement above): for every ring group (kv_slot[g] < 0),
@@ -409,6 +442,18 @@ rtp_status rtp_prefill_attn(const void* q, const void* k, const void* v, const i
 rtp_status rtp_prefill_index_keys(const void* k_pre, const void* w_k, const int* seq_lens,
                                   const int* ret_heads, int B, int Hq, int Hkv, int n_ret, int max_ctx,
                                   void* k_idx, void* stream);
+
+/*
+ * Calibration probe (not part of the decode path): reads `bytes` of device memory at
+ * `src` once with 16-byte loads (non-temporal when `nontemporal` != 0, as the path's
+ * streams use; else ordinary cached loads) over a grid-stride loop of n_workgroups
+ * 256-thread workgroups, and writes one folded word per workgroup to sink[n_workgroups]
+ * (so no load is dropped).  Timing it gives the read-only streaming rate the HBM-bound
+ * kernels are compared with.  bytes a multiple of 16, src 16-byte aligned, 1 <=
+ * n_workgroups <= 65535; else RTP_EINVAL.
+ */
+rtp_status rtp_stream_read(const void* src, size_t bytes, unsigned int* sink, int n_workgroups, int nontemporal,
+                           void* stream);
 
 #ifdef __cplusplus
 }

@@ -41,9 +41,12 @@ _SIGS = {
     "rtp_local_window_workspace_size": ([_i] * 7, _sz),
     "rtp_local_window_attn": ([_vp] * 5 + [_i] * 7 + [_vp, _vp, _sz, _vp, _i, _vp, _vp, _i, _vp], _i),
     "rtp_decode_step": ([_vp] * 10 + [_i] * 11 + [_vp] * 6 + [_vp, _sz, _vp, _sz] + [_vp, _i, _vp, _vp, _i]
-                        + [_vp] * 4, _i),
+                        + [_vp], _i),
+    "rtp_decode_attn": ([_vp] * 9 + [_i] * 10 + [_vp] * 3 + [_sz, _vp, _i, _vp, _vp, _i, _vp], _i),
+    "rtp_decode_merge": ([_vp] * 4 + [_i] * 9 + [_vp, _sz, _vp, _vp], _i),
     "rtp_decode_step_noalloc_limit": ([], _sz),
-    "rtp_decode_step_noalloc": ([_vp] * 10 + [_i] * 11 + [_vp] * 4 + [_vp, _i, _vp, _vp, _i] + [_vp] * 4, _i),
+    "rtp_decode_step_noalloc": ([_vp] * 10 + [_i] * 11 + [_vp] * 4 + [_vp, _i, _vp, _vp, _i] + [_vp], _i),
+    "rtp_stream_read": ([_vp, _sz, _vp, _i, _i, _vp], _i),
     "rtp_cache_append": ([_vp] * 6 + [_i] * 5 + [_vp] * 3 + [_vp, _i, _vp, _vp, _i, _i, _i, _vp], _i),
     "rtp_prefill_attn": ([_vp] * 5 + [_i] * 7 + [_vp, _vp], _i),
     "rtp_prefill_index_keys": ([_vp] * 4 + [_i] * 5 + [_vp, _vp], _i),
@@ -197,15 +200,39 @@ def rtp_decode_step_noalloc_limit() -> int:
 def rtp_decode_step_noalloc(q_pre, w_q, k_idx, q, k_cache, v_cache, seq_lens, ret_heads, loc_heads, top_p, k_tokens,
                             B, Hq, Hkv, n_ret, n_loc, max_ctx, block, split_tokens, window, sinks,
                             sel_idx, sel_cnt, sel_mask, out, stream=None, kv_slot=None, n_full=0, k_ring=None,
-                            v_ring=None, n_ring=0, side_stream=None, ev_fork=None, ev_join=None) -> None:
+                            v_ring=None, n_ring=0) -> None:
     """rtp_decode_step with its workspaces and partials in the library's fixed device scratch."""
-    side = None if side_stream is None else _s(side_stream)
     st = lib().rtp_decode_step_noalloc(_p(q_pre), _p(w_q), _p(k_idx), _p(q), _p(k_cache), _p(v_cache),
                                        _p(seq_lens), _p(ret_heads), _p(loc_heads), _p(top_p), int(k_tokens), B, Hq,
                                        Hkv, n_ret, n_loc, max_ctx, block, split_tokens, window, sinks, _p(sel_idx),
                                        _p(sel_cnt), _p(sel_mask), _p(out), _p(kv_slot), n_full, _p(k_ring),
-                                       _p(v_ring), n_ring, _s(stream), side, ev_fork, ev_join)
+                                       _p(v_ring), n_ring, _s(stream))
     _check("rtp_decode_step_noalloc", st)
+
+
+def rtp_decode_attn(q, k_cache, v_cache, seq_lens, ret_heads, sel_idx, sel_cnt, sel_mask, loc_heads, B, Hq, Hkv,
+                    n_ret, n_loc, max_ctx, block, split_tokens, window, sinks, o_part, lse_part, ws_local,
+                    stream=None, kv_slot=None, n_full=0, k_ring=None, v_ring=None, n_ring=0) -> None:
+    st = lib().rtp_decode_attn(_p(q), _p(k_cache), _p(v_cache), _p(seq_lens), _p(ret_heads), _p(sel_idx),
+                               _p(sel_cnt), _p(sel_mask), _p(loc_heads), B, Hq, Hkv, n_ret, n_loc, max_ctx, block,
+                               split_tokens, window, sinks, _p(o_part), _p(lse_part), _p(ws_local), _nbytes(ws_local),
+                               _p(kv_slot), n_full, _p(k_ring), _p(v_ring), n_ring, _s(stream))
+    _check("rtp_decode_attn", st)
+
+
+def rtp_decode_merge(o_part, lse_part, ret_heads, loc_heads, B, Hq, Hkv, n_ret, n_loc, max_ctx, split_tokens, window,
+                     sinks, ws_local, out, stream=None) -> None:
+    st = lib().rtp_decode_merge(_p(o_part), _p(lse_part), _p(ret_heads), _p(loc_heads), B, Hq, Hkv, n_ret, n_loc,
+                                max_ctx, split_tokens, window, sinks, _p(ws_local), _nbytes(ws_local), _p(out),
+                                _s(stream))
+    _check("rtp_decode_merge", st)
+
+
+def rtp_stream_read(src, sink, n_workgroups: int, nontemporal: bool = True, stream=None) -> None:
+    """Calibration probe: one read-only pass over `src` (see rtp.h)."""
+    st = lib().rtp_stream_read(_p(src), _nbytes(src), _p(sink), int(n_workgroups), int(bool(nontemporal)),
+                               _s(stream))
+    _check("rtp_stream_read", st)
 
 
 def rtp_cache_append(k_new, v_new, k_pre, w_k, seq_lens, ret_heads, B, Hq, Hkv, n_ret, max_ctx,

@@ -1,6 +1,9 @@
-// One decode step as a single host call: the four calls of the path enqueued in order
-// from C, so the host pays one call instead of four plus the event calls (the step's
-// enqueue cost decides the latency when the device work is short, as at 1M tokens).
+// One decode step as a single host call on one stream, three launches: the index call
+// (scoring and selection), the attention launch (block-sparse split attention of the
+// retrieval heads and window attention of the local heads in one grid) and the merge of
+// both kinds of partials.  No second stream and no events: on
+// this part a fork/join of two streams costs tens of microseconds of host time per step,
+// as much as a whole 1M step on the device.
 
 #include <mutex>
 
@@ -65,41 +68,25 @@ extern "C" rtp_status rtp_decode_step(
     int k_tokens, int B, int Hq, int Hkv, int n_ret, int n_loc, int max_ctx, int block, int split_tokens, int window,
     int sinks, int* sel_idx, int* sel_cnt, unsigned char* sel_mask, float* o_part, float* lse_part, float* out,
     void* ws_index, size_t ws_index_bytes, void* ws_local, size_t ws_local_bytes, const int* kv_slot,
-    int n_full, const void* k_ring, const void* v_ring, int n_ring, void* stream, void* side_stream, void* ev_fork,
-    void* ev_join) {
+    int n_full, const void* k_ring, const void* v_ring, int n_ring, void* stream) {
   const rtp_status chk = check_step(q_pre, w_q, k_idx, q, k_cache, v_cache, seq_lens, ret_heads, loc_heads, top_p,
                                     k_tokens, B, Hq, Hkv, n_ret, n_loc, max_ctx, block, split_tokens, window, sinks,
                                     sel_idx, sel_cnt, o_part, lse_part, out, ws_index, ws_index_bytes, ws_local,
                                     ws_local_bytes, kv_slot, n_full, k_ring, v_ring, n_ring);
   if (chk != RTP_OK) return chk;
-  const int n_split = n_ret > 0 ? ceil_div(max_ctx, split_tokens) : 0;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool fork = n_loc > 0 && n_ret > 0 && side_stream && ev_fork && ev_join;
   rtp_status st = RTP_OK;
-  if (n_loc > 0) {
-    hipStream_t ls = s;
-    if (fork) {
-      ls = static_cast<hipStream_t>(side_stream);
-      if (hipEventRecord(static_cast<hipEvent_t>(ev_fork), s) != hipSuccess ||
-          hipStreamWaitEvent(ls, static_cast<hipEvent_t>(ev_fork), 0) != hipSuccess)
-        return RTP_ELAUNCH;
-    }
-    st = rtp_local_window_attn(q, k_cache, v_cache, seq_lens, loc_heads, B, Hq, Hkv, n_loc, max_ctx, window,
-                               sinks, out, ws_local, ws_local_bytes, kv_slot, n_full, k_ring, v_ring, n_ring, ls);
-    if (st != RTP_OK) return st;
-    if (fork && hipEventRecord(static_cast<hipEvent_t>(ev_join), ls) != hipSuccess) return RTP_ELAUNCH;
-  }
-  if (n_ret > 0) {
+  if (n_ret > 0)
     st = k_tokens > 0 ? rtp_index_topk(q_pre, w_q, k_idx, seq_lens, ret_heads, k_tokens, B, Hq, n_ret, max_ctx,
                                        block, sel_idx, sel_cnt, sel_mask, ws_index, ws_index_bytes, stream)
                       : rtp_index_topp(q_pre, w_q, k_idx, seq_lens, ret_heads, top_p, B, Hq, n_ret, max_ctx, block,
                                        sel_idx, sel_cnt, sel_mask, ws_index, ws_index_bytes, stream);
-    if (st == RTP_OK)
-      st = rtp_sparse_attn_split(q, k_cache, v_cache, seq_lens, ret_heads, sel_idx, sel_cnt, sel_mask, B, Hq, Hkv,
-                                 n_ret, max_ctx, block, split_tokens, o_part, lse_part, kv_slot, n_full, stream);
-    if (st == RTP_OK) st = rtp_split_reduce(o_part, lse_part, ret_heads, B, Hq, n_ret, n_split, out, stream);
-  }
-  if (fork && hipStreamWaitEvent(s, static_cast<hipEvent_t>(ev_join), 0) != hipSuccess) return RTP_ELAUNCH;
+  if (st == RTP_OK)
+    st = rtp_decode_attn(q, k_cache, v_cache, seq_lens, ret_heads, sel_idx, sel_cnt, sel_mask, loc_heads, B, Hq, Hkv,
+                         n_ret, n_loc, max_ctx, block, split_tokens, window, sinks, o_part, lse_part, ws_local,
+                         ws_local_bytes, kv_slot, n_full, k_ring, v_ring, n_ring, stream);
+  if (st == RTP_OK)
+    st = rtp_decode_merge(o_part, lse_part, ret_heads, loc_heads, B, Hq, Hkv, n_ret, n_loc, max_ctx, split_tokens,
+                          window, sinks, ws_local, ws_local_bytes, out, stream);
   return st;
 }
 
@@ -142,8 +129,7 @@ extern "C" rtp_status rtp_decode_step_noalloc(
     const void* v_cache, const int* seq_lens, const int* ret_heads, const int* loc_heads, const float* top_p,
     int k_tokens, int B, int Hq, int Hkv, int n_ret, int n_loc, int max_ctx, int block, int split_tokens, int window,
     int sinks, int* sel_idx, int* sel_cnt, unsigned char* sel_mask, float* out, const int* kv_slot, int n_full,
-    const void* k_ring, const void* v_ring, int n_ring, void* stream, void* side_stream, void* ev_fork,
-    void* ev_join) {
+    const void* k_ring, const void* v_ring, int n_ring, void* stream) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_ctx <= 0 || n_ret < 0 || n_loc < 0 || n_ret + n_loc > Hq)
     return RTP_EINVAL;
   // the scratch each part needs, against its share of the array
@@ -204,5 +190,5 @@ extern "C" rtp_status rtp_decode_step_noalloc(
                          Hq, Hkv, n_ret, n_loc, max_ctx, block, split_tokens, window, sinks, sel_idx, sel_cnt,
                          sel_mask, n_ret > 0 ? o_part : nullptr, n_ret > 0 ? lse_part : nullptr, out,
                          n_ret > 0 ? idx_ws : nullptr, ws_index, n_loc > 0 ? loc_ws : nullptr, ws_local, kv_slot,
-                         n_full, k_ring, v_ring, n_ring, stream, side_stream, ev_fork, ev_join);
+                         n_full, k_ring, v_ring, n_ring, stream);
 }

@@ -4,8 +4,8 @@
 // gfx950 launch: grid (chunk, retrieval head, sequence), 1024 threads = 16 wave64, one
 // workgroup per compute unit at a time (its registers and LDS allow one), so the chunks
 // are sized for about one workgroup per compute unit and the scoring runs in a single
-// wave of workgroups; the selecting workgroup of each head then has 16 waves for the
-// threshold search.  Each head's tag word lives in its workspace region and is advanced
+// wave of workgroups.  The selecting workgroup of each head runs its passes over blocks
+// on all 16 waves and its serial steps on one.  Each head's tag word lives in its workspace region and is advanced
 // by the head's selecting workgroup at the end of every call.
 
 #include "rtp_index.hpp"
@@ -15,7 +15,7 @@ namespace {
 
 constexpr int kIdxThreads = 1024;
 
-static_assert(kIdxMaxChunks <= 2 * kIdxThreads, "the selection reads two chunk words per thread");
+static_assert(kIdxMaxChunks % kIdxThreads == 0, "chunk words per thread");
 
 struct K1Layout {
   IndexGeom g;
@@ -48,15 +48,20 @@ K1Layout k1_layout(int B, int n_ret, int max_ctx, int block, int target) {
   return L;
 }
 
+// One index workgroup: chunk c of head (b, r); the last of the head to finish selects.
+template <int BK>
+__device__ __forceinline__ void index_role(const IndexArgs& a, int c, int r, int b, unsigned char* smem) {
+  auto* S = reinterpret_cast<IndexSmem<kIdxThreads>*>(smem);
+  const size_t head = (size_t)b * a.n_ret + r;
+  if (!index_chunk<BK, kIdxThreads>(a, c, r, b, S)) return;
+  index_select<kIdxThreads>(a, BK, b, head, S);
+  index_advance_tag<kIdxThreads>(a, head, S->tag);
+}
+
 template <int BK>
 __global__ __launch_bounds__(kIdxThreads) void index_topp_kernel(IndexArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  auto* S = reinterpret_cast<IndexSmem<kIdxThreads>*>(smem_raw);
-  const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
-  const size_t head = (size_t)b * a.n_ret + r;
-  if (!index_chunk<BK, kIdxThreads>(a, c, r, b, S)) return;
-  index_select<kIdxThreads>(a, BK, r, b, S);
-  index_advance_tag<kIdxThreads>(a, head, S->tag);
+  index_role<BK>(a, blockIdx.x, blockIdx.y, blockIdx.z, smem_raw);
 }
 
 }  // namespace
@@ -72,17 +77,13 @@ extern "C" size_t rtp_index_topp_workspace_size(int B, int n_ret, int max_ctx, i
 
 namespace {
 
-// Checks the arguments and enqueues kernel 1 with either selection rule: top_p per head
-// (topk_blocks == 0) or a fixed number of blocks per head (topk_blocks > 0).
-rtp_status index_launch(const void* q_pre, const void* w_q, const void* k_idx, const int* seq_lens,
-                        const int* ret_heads, const float* top_p, int topk_blocks, int B, int Hq, int n_ret,
-                        int max_ctx, int block, int* sel_idx, int* sel_cnt, unsigned char* sel_mask,
-                        void* workspace, size_t ws_bytes, void* stream) {
-  if (B <= 0 || Hq <= 0 || n_ret < 0 || n_ret > Hq || max_ctx <= 0) return RTP_EINVAL;
-  if (block != 64 && block != 128) return RTP_EUNSUPPORTED;
-  if (ceil_div(max_ctx, block) > kIdxMaxBlocks) return RTP_EUNSUPPORTED;
-  if (B > 65535 || n_ret > 65535) return RTP_EUNSUPPORTED;
-  if (n_ret == 0) return RTP_OK;
+// Checks kernel 1's arguments (n_ret > 0) and fills its arguments, grid and LDS size, with
+// either selection rule: top_p per head (topk_blocks == 0) or a fixed number of blocks per
+// head (topk_blocks > 0).
+rtp_status index_prepare(const void* q_pre, const void* w_q, const void* k_idx, const int* seq_lens,
+                         const int* ret_heads, const float* top_p, int topk_blocks, int B, int Hq, int n_ret,
+                         int max_ctx, int block, int* sel_idx, int* sel_cnt, unsigned char* sel_mask,
+                         void* workspace, size_t ws_bytes, IndexArgs& args, dim3& grid, size_t& dyn) {
   if (!q_pre || !w_q || !k_idx || !seq_lens || !ret_heads || (topk_blocks == 0 && !top_p) || !sel_idx ||
       !sel_cnt || !workspace)
     return RTP_EINVAL;
@@ -91,14 +92,40 @@ rtp_status index_launch(const void* q_pre, const void* w_q, const void* k_idx, c
   if (ws_bytes < k1_layout(B, n_ret, max_ctx, block, 1).total) return RTP_EINVAL;
   const K1Layout L = k1_layout(B, n_ret, max_ctx, block, compute_units());
   char* ws = static_cast<char*>(workspace);
-  IndexArgs args{static_cast<const uint16_t*>(q_pre), static_cast<const uint16_t*>(w_q),
-                 static_cast<const uint16_t*>(k_idx), seq_lens, ret_heads, topk_blocks ? nullptr : top_p,
-                 topk_blocks, Hq, n_ret, max_ctx, L.g.nblk_max, L.g.chunk_blocks, index_chunk_cap(L.g.nblk_max),
-                 sel_idx, sel_cnt, sel_mask, reinterpret_cast<IndexWsHeader*>(ws), ws + kIdxWsHeaderBytes,
-                 L.stride};
-  dim3 grid(L.g.n_chunk, n_ret, B);
+  args = IndexArgs{static_cast<const uint16_t*>(q_pre), static_cast<const uint16_t*>(w_q),
+                   static_cast<const uint16_t*>(k_idx), seq_lens, ret_heads, topk_blocks ? nullptr : top_p,
+                   topk_blocks, Hq, n_ret, max_ctx, L.g.nblk_max, L.g.chunk_blocks, index_chunk_cap(L.g.nblk_max),
+                   sel_idx, sel_cnt, sel_mask, reinterpret_cast<IndexWsHeader*>(ws), ws + kIdxWsHeaderBytes,
+                   L.stride};
+  grid = dim3(L.g.n_chunk, n_ret, B);
+  dyn = index_smem_bytes<kIdxThreads>(L.g.rows);
+  return RTP_OK;
+}
+
+rtp_status index_scalar_check(int B, int Hq, int n_ret, int max_ctx, int block) {
+  if (B <= 0 || Hq <= 0 || n_ret < 0 || n_ret > Hq || max_ctx <= 0) return RTP_EINVAL;
+  if (block != 64 && block != 128) return RTP_EUNSUPPORTED;
+  if (ceil_div(max_ctx, block) > kIdxMaxBlocks) return RTP_EUNSUPPORTED;
+  if (B > 65535 || n_ret > 65535) return RTP_EUNSUPPORTED;
+  return RTP_OK;
+}
+
+// Checks the arguments and enqueues kernel 1 alone.
+rtp_status index_launch(const void* q_pre, const void* w_q, const void* k_idx, const int* seq_lens,
+                        const int* ret_heads, const float* top_p, int topk_blocks, int B, int Hq, int n_ret,
+                        int max_ctx, int block, int* sel_idx, int* sel_cnt, unsigned char* sel_mask,
+                        void* workspace, size_t ws_bytes, void* stream) {
+  const rtp_status sc = index_scalar_check(B, Hq, n_ret, max_ctx, block);
+  if (sc != RTP_OK) return sc;
+  if (n_ret == 0) return RTP_OK;
+  IndexArgs args{};
+  dim3 grid;
+  size_t dyn = 0;
+  const rtp_status st = index_prepare(q_pre, w_q, k_idx, seq_lens, ret_heads, top_p, topk_blocks, B, Hq, n_ret,
+                                      max_ctx, block, sel_idx, sel_cnt, sel_mask, workspace, ws_bytes, args, grid,
+                                      dyn);
+  if (st != RTP_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const size_t dyn = index_smem_bytes<kIdxThreads>(L.g.rows);
   if (block == 64)
     hipLaunchKernelGGL(index_topp_kernel<64>, grid, dim3(kIdxThreads), dyn, s, args);
   else

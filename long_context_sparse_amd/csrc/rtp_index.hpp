@@ -33,15 +33,17 @@
 // exactly: a key = (fp32 mass bits, inverted block id) orders blocks by mass with ties
 // by ascending id; masses are summed as fixed-point integers (2^-62 units) so every
 // cumulative sum is exact and order-independent.  Blocks below (1 - p) / (2 nblk) can
-// never be selected and stay out; the pass that writes the masses also builds the first
-// 256-bin LDS histogram of (count, mass) of the others, an eighth of an octave per bin
-// from that floor; one wave scans it for the bin where the cumulative mass from the top
-// crosses p.  While more than 64 candidates of unequal mass remain, a further level bins
-// the candidates by (bits - lo) >> shift (>= 128x narrower each time); the last <= 64
-// candidates are gathered (the same pass counts the blocks above them) and ranked
-// exactly by one wave, and a run of equal masses is resolved by count in ascending
-// block order.  The selected ids are written in ascending order by a ballot-based
-// ordered compaction and the arrival counter is reset.
+// never be selected and stay out; the pass that writes the masses gathers the others into
+// a candidate list (one LDS atomic per wave and row) and builds the first 256-bin LDS
+// histogram of (count, mass) of them, an eighth of an octave per bin from that floor; one
+// wave scans it for the bin where the cumulative mass from the top crosses p.  While more
+// than 64 candidates of unequal mass remain, a further level bins the candidates of the
+// crossing range by (bits - lo) >> shift (>= 128x narrower each time); the last <= 64 are
+// gathered and ranked exactly, and a run of equal masses is resolved by count in
+// ascending block order (found on an LDS bitmap).  Every pass after the masses runs over
+// the candidate list only (a handful of blocks for a peaked head).  The selected ids are
+// written in ascending order from an LDS bitmap of the selected blocks (a prefix count of
+// its words gives each block its slot) and the arrival counter is reset.
 #pragma once
 
 #include "rtp_common.hpp"
@@ -49,50 +51,58 @@
 namespace rtp {
 
 constexpr int kIdxMaxChunkBlocks = 256;
-constexpr int kIdxMaxBlocks = 16384;            // blocks per sequence the selection holds
-constexpr int kBins = 256;                      // histogram bins per refinement level
-constexpr int kFinal = kWave;                   // candidates ranked directly (one per lane)
-constexpr int kRowTab = kIdxMaxBlocks / kWave;  // (row, wave) entries of the selection
-constexpr int kRowBatch = 4;                    // selection rows read together (see for_rows)
+constexpr int kIdxMaxBlocks = 16384;             // blocks per sequence the selection holds
+constexpr int kIdxMaxChunks = 2048;              // chunks per head the selection combines
+constexpr int kBins = 256;                       // histogram bins per refinement level
+constexpr int kFinal = kWave;                    // candidates ranked directly (one per lane)
+constexpr int kBitWords = kIdxMaxBlocks / 32;    // words of a block bitmap
+constexpr int kMassBatch = 8;                    // block words a thread loads before using them
 
-template <int T>
+constexpr int kBitWordsPerLane = kBitWords / kWave;  // bitmap words a lane of one wave scans
+
 struct TailSmem {
-  uint64_t bmass[kBins];  // per bin: fixed-point mass
-  uint32_t bcnt[kBins];   // per bin: candidate count
-  int rowtab[kRowTab];    // per (row, wave) counts, then exclusive prefixes
-  double f64[T / kWave], f64b[T / kWave];
-  uint64_t above[kFinal];  // final candidates: fixed-point mass of the larger keys
-  int wn[T / kWave];       // final candidates gathered by each wave
+  uint64_t bmass[kBins];        // per bin: fixed-point mass
+  uint32_t bcnt[kBins];         // per bin: candidate count
+  uint32_t sel[kBitWords];      // bitmap of the selected blocks
+  uint32_t tie[kBitWords];      // bitmap of the candidates of one tied mass
+  uint32_t wpre[kBitWords];     // exclusive prefix of the bitmap words' bit counts
+  uint64_t fkey[kFinal], fw[kFinal];  // the last <= kFinal candidates: keys and weights
   uint64_t cab, thr;
   uint32_t lo, hi;
-  int cnt, total, found, ready;
+  int cnt, found, ncand, nfinal, total;
 };
 
-// LDS of the index role; the per-block masses (rows * T floats) follow it.
+// LDS of the index role; the per-block masses (rows * T floats) and the candidate list
+// (rows * T block ids) follow it.
 template <int T>
 struct IndexSmem {
   double qidx[kIndexDim];
   double mx[kIdxMaxChunkBlocks], sum[kIdxMaxChunkBlocks];  // scoring: per-block max, sum
-  // selection: per-chunk factor exp(M_c - M) / Z; after the masses are formed, the
-  // final candidates each wave gathers (2 * kFinal words a wave)
-  double f[2 * T];
-  TailSmem<T> sm;
+  // selection: the chunk words (M_c, Z_c as fp32), then the chunk factors exp(M_c - M) / Z
+  // (fp32); after the masses are formed, the final candidates each wave gathers (2 *
+  // kFinal words a wave)
+  float cm[kIdxMaxChunks], cz[kIdxMaxChunks];
+  TailSmem sm;
   int flag;
   uint32_t tag;
   int inject, mismatch;
 };
 template <int T>
 __host__ __device__ constexpr size_t index_smem_bytes(int rows) {
-  return (sizeof(IndexSmem<T>) + 15) / 16 * 16 + (size_t)rows * T * sizeof(float);
+  return (sizeof(IndexSmem<T>) + 15) / 16 * 16 + (size_t)rows * T * (sizeof(float) + sizeof(uint16_t));
 }
 template <int T>
 __device__ __forceinline__ float* index_masses(IndexSmem<T>* S) {
   return reinterpret_cast<float*>(reinterpret_cast<char*>(S) + (sizeof(IndexSmem<T>) + 15) / 16 * 16);
 }
+template <int T>
+__device__ __forceinline__ uint16_t* index_cands(IndexSmem<T>* S, int rows) {
+  return reinterpret_cast<uint16_t*>(index_masses<T>(S) + (size_t)rows * T);
+}
 
 // Chunking of the index role: at least `target` workgroups over the batch where the
-// blocks allow, 8..256 blocks (a power of two) a chunk, at most 2 * T chunks per head.  rows = blocks per thread in the selection,
-// rounded up to a multiple of kRowBatch.
+// blocks allow, 8..256 blocks (a power of two) a chunk, at most 2 * T chunks per head.
+// rows = blocks per thread in the selection.
 struct IndexGeom {
   int nblk_max, chunk_blocks, n_chunk, rows;
 };
@@ -105,7 +115,7 @@ inline IndexGeom index_geom(int B, int n_ret, int max_ctx, int block, int T, int
   while (ceil_div(g.nblk_max, cb) > 2 * T && cb < kIdxMaxChunkBlocks) cb <<= 1;
   g.chunk_blocks = cb;
   g.n_chunk = ceil_div(g.nblk_max, cb);
-  g.rows = ceil_div(ceil_div(g.nblk_max, T), kRowBatch) * kRowBatch;
+  g.rows = ceil_div(g.nblk_max, T);
   return g;
 }
 
@@ -125,7 +135,6 @@ struct IndexHeadState {
 };
 constexpr size_t kIdxWsHeaderBytes = 256;
 constexpr size_t kIdxHeadStateBytes = 256;
-constexpr int kIdxMaxChunks = 2048;  // chunks per head the selection combines
 
 __host__ __device__ inline int index_chunk_cap(int nblk_max) {
   const int c = (nblk_max + 7) / 8;
@@ -183,84 +192,31 @@ __device__ __forceinline__ int level_bin(uint32_t bits, uint32_t lo, int shift) 
   return (int)min((bits - lo) >> shift, (uint32_t)(kBins - 1));
 }
 
-// Selection rows: block j = row * T + thread, row < rows, masses in LDS (< 0 for no
-// block; rows is a multiple of kRowBatch and the rows past the sequence's blocks hold
-// -1).  Every pass reads a thread's masses kRowBatch rows at a time, unconditionally,
-// so the LDS latencies overlap.
-template <int T, class F>
-__device__ __forceinline__ void for_rows(const float* __restrict__ sm_m, int rows, F f) {
-  const int tid = threadIdx.x;
-  for (int i0 = 0; i0 < rows; i0 += kRowBatch) {
-    float mm[kRowBatch];
-#pragma unroll
-    for (int u = 0; u < kRowBatch; ++u) mm[u] = sm_m[(i0 + u) * T + tid];
-#pragma unroll
-    for (int u = 0; u < kRowBatch; ++u) f(i0 + u, mm[u]);
-  }
-}
-
-// A wave's count of a per-row predicate ballot, kept in lane `row` of one register (rows
-// <= 64) and stored to rowtab once after the pass.
-__device__ __forceinline__ int count_into_lane(int cntv, uint64_t bal, int row) {
-  return (int)(threadIdx.x & 63) == row ? (int)__popcll(bal) : cntv;
-}
-template <int T>
-__device__ __forceinline__ void store_row_counts(int cntv, int rows, TailSmem<T>& sm) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane < rows) sm.rowtab[lane * (T / kWave) + wave] = cntv;
-}
-
-// One wave: turns rowtab[0 .. rows * waves) of per-(row, wave) counts into exclusive
-// prefixes in ascending block order and stores their total in sm.total.
-template <int T>
-__device__ __forceinline__ void rowtab_scan(int rows, TailSmem<T>& sm) {
+// One wave: exclusive prefix of the bit counts of bitmap words [0, nwords) (consecutive
+// words per lane) into sm.wpre, their total into sm.total.
+__device__ __forceinline__ void bitmap_prefix_wave(const uint32_t* __restrict__ bits, int nwords, TailSmem& sm) {
   const int lane = threadIdx.x & 63;
-  constexpr int R = kRowTab / 64;  // table entries a lane
-  const int n = rows * (T / kWave);
-  int v[R], tot = 0;
+  uint32_t c[kBitWordsPerLane], v = 0;
 #pragma unroll
-  for (int k = 0; k < R; ++k) {
-    const int idx = lane * R + k;
-    v[k] = idx < n ? sm.rowtab[idx] : 0;
-    tot += v[k];
+  for (int k = 0; k < kBitWordsPerLane; ++k) {
+    const int i = lane * kBitWordsPerLane + k;
+    c[k] = i < nwords ? (uint32_t)__popc(bits[i]) : 0u;
+    v += c[k];
   }
-  const int incl = (int)wave_incl_scan_u32((uint32_t)tot);
-  int run = incl - tot;
+  const uint32_t incl = wave_incl_scan_u32(v);
+  uint32_t off = incl - v;
 #pragma unroll
-  for (int k = 0; k < R; ++k) {
-    const int idx = lane * R + k;
-    if (idx < n) sm.rowtab[idx] = run;
-    run += v[k];
+  for (int k = 0; k < kBitWordsPerLane; ++k) {
+    const int i = lane * kBitWordsPerLane + k;
+    if (i < nwords) sm.wpre[i] = off;
+    off += c[k];
   }
-  if (lane == 63) sm.total = incl;
+  if (lane == 63) sm.total = (int)incl;
 }
 
-// For a predicate on (row, mass), fills rowtab with the exclusive prefix, in ascending
-// block order, of the satisfying blocks per (row, wave) and returns their total; the
-// ordinal of a satisfying block is then rowtab[row * waves + wave] + (satisfying
-// lanes below it in its wave).
-template <int T, class Pred>
-__device__ __forceinline__ int rows_prefix(const float* __restrict__ sm_m, int rows, Pred pred,
-                                           TailSmem<T>& sm) {
-  const int wave = threadIdx.x >> 6;
-  int cntv = 0;
-  for_rows<T>(sm_m, rows, [&](int i, float m) { cntv = count_into_lane(cntv, __ballot(pred(i, m)), i); });
-  store_row_counts<T>(cntv, rows, sm);
-  __syncthreads();
-  if (wave == 0) rowtab_scan<T>(rows, sm);
-  __syncthreads();
-  return sm.total;
-}
-
-template <int T>
-__device__ __forceinline__ int ordinal(bool flag, int i, const TailSmem<T>& sm) {
-  const int wave = threadIdx.x >> 6;
-  return sm.rowtab[i * (T / kWave) + wave] + __popcll(__ballot(flag) & lanemask_lt());
-}
-
-template <int T>
-__device__ __forceinline__ uint64_t key_at(int i, float m) {
-  return key_of(m, i * T + (int)threadIdx.x);
+// Slot of block j among the set bits of a bitmap whose word prefixes are in sm.wpre.
+__device__ __forceinline__ int bitmap_rank(const uint32_t* __restrict__ bits, int j, const TailSmem& sm) {
+  return (int)sm.wpre[j >> 5] + __popc(bits[j >> 5] & ((1u << (j & 31)) - 1u));
 }
 
 // One wave: scans the bins from the top for the bin where cab + (mass of the bins above
@@ -268,9 +224,8 @@ __device__ __forceinline__ uint64_t key_at(int i, float m) {
 // (sm.cnt) and bit range [sm.lo, sm.hi]; sets sm.found.  Bin b of a level over [lo, hi]
 // holds the bits lo + (b << shift) ..; the top bin also takes everything above.  The bins
 // are cleared for the next level.
-template <int T>
 __device__ __forceinline__ void scan_level(uint64_t cab, uint64_t P, uint32_t lo, uint32_t hi, int shift,
-                                           TailSmem<T>& sm) {
+                                           TailSmem& sm) {
   const int lane = threadIdx.x & 63;
   // lane l holds bins kBins-1-4l .. kBins-4-4l (descending mass)
   uint64_t bm[4];
@@ -302,51 +257,46 @@ __device__ __forceinline__ void scan_level(uint64_t cab, uint64_t P, uint32_t lo
   }
 }
 
-// Exact greedy top-p threshold over the masses in LDS, after a first level whose result
-// (sm.cab, sm.cnt, sm.lo, sm.hi) is in place.  Returns the key of the last admitted
-// block: the selected set is every block whose key is >= it.  When sm.ready is set on
-// return, sm.rowtab already holds the exclusive prefix per (row, wave) of the selected
-// blocks and sm.total their number.  Preconditions: the bins are zero.  wbuf: LDS for
-// the final candidates, 2 * kFinal words per wave.
+// Exact greedy top-p threshold over the candidates cand[0, nc) (their masses in sm_m),
+// after a first level whose result (sm.cab, sm.cnt, sm.lo, sm.hi) is in place.  Returns
+// the key of the last admitted block: the selected set is every candidate whose key is
+// >= it.  Passes over the candidates run on all T threads; scans and the final ranking on
+// wave 0 alone (the other waves wait at the barrier, issuing nothing).  Preconditions:
+// the bins, sm.tie and sm.nfinal are zero.
 //
-// Candidates are the blocks whose mass bits lie in [lo, hi], with fixed mass `cab`
-// strictly above them, and cab < P <= cab + mass(candidates) holds throughout.  A
-// level puts every candidate into one of kBins bins by (bits - lo) >> shift, a
-// monotone map, so bins are contiguous ranges of mass (about log-uniform, since fp32
-// bits grow with log2 of the value); one wave scans the bins from the top, finds the
-// bin where cab + cumulative mass crosses P and takes its bit range as the new candidate
-// range (at least kBins/2 times narrower).  It ends when <= kFinal candidates remain
-// (ranked exactly: every wave compares each candidate with a share of the others), or
-// when the range is a single mass value: the threshold is then the k-th candidate in
-// ascending block order, k = ceil((P - cab) / mass).
+// Candidates of a level are those whose mass bits lie in [lo, hi], with fixed mass `cab`
+// strictly above them, and cab < P <= cab + mass(candidates) holds throughout.  A level
+// puts every candidate into one of kBins bins by (bits - lo) >> shift, a monotone map, so
+// bins are contiguous ranges of mass (about log-uniform, since fp32 bits grow with log2
+// of the value); one wave scans the bins from the top, finds the bin where cab +
+// cumulative mass crosses P and takes its bit range as the new range (at least kBins/2
+// times narrower).  It ends when <= kFinal candidates remain (ranked exactly by one wave,
+// one candidate a lane), or when the range is a single mass value: the threshold is then
+// the k-th candidate in ascending block order, k = ceil((P - cab) / mass).
 template <int T>
-__device__ __noinline__ uint64_t select_threshold(const float* __restrict__ sm_m, int rows, uint64_t P,
-                                                  TailSmem<T>& sm, uint64_t* __restrict__ wbuf, bool count) {
+__device__ __noinline__ uint64_t select_threshold(const float* __restrict__ sm_m, const uint16_t* __restrict__ cand,
+                                                  int nc, int nblk, uint64_t P, TailSmem& sm, bool count) {
   // a block's weight: its fixed-point mass (top-p), or 1 (static top-k: P is then the
   // number of blocks to keep)
   auto wgt = [&](uint32_t bits) { return count ? 1ull : fixed_bits(bits); };
-  constexpr int W = T / kWave;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint64_t cab = uni64(sm.cab);
   int cnt = __builtin_amdgcn_readfirstlane(sm.cnt);
   uint32_t lo = __builtin_amdgcn_readfirstlane(sm.lo);
   uint32_t hi = __builtin_amdgcn_readfirstlane(sm.hi);
-  auto cand = [&](float m) {
-    const uint32_t bits = __float_as_uint(m);
-    return m >= 0.f && bits >= lo && bits <= hi;
-  };
   while (cnt > kFinal && lo < hi) {
     const uint32_t span = hi - lo;
     const int shift = max(0, 32 - (int)__clz(span) - 8);  // (span >> shift) < kBins
-    for_rows<T>(sm_m, rows, [&](int i, float m) {
-      if (cand(m)) {
-        const int bin = level_bin(__float_as_uint(m), lo, shift);
-        atomicAdd((unsigned long long*)&sm.bmass[bin], (unsigned long long)wgt(__float_as_uint(m)));
+    for (int k = tid; k < nc; k += T) {
+      const uint32_t bits = __float_as_uint(sm_m[cand[k]]);
+      if (bits >= lo && bits <= hi) {
+        const int bin = level_bin(bits, lo, shift);
+        atomicAdd((unsigned long long*)&sm.bmass[bin], (unsigned long long)wgt(bits));
         atomicAdd(&sm.bcnt[bin], 1u);
       }
-    });
+    }
     __syncthreads();
-    if (wave == 0) scan_level<T>(cab, P, lo, hi, shift, sm);
+    if (wave == 0) scan_level(cab, P, lo, hi, shift, sm);
     __syncthreads();
     cab = uni64(sm.cab);
     cnt = __builtin_amdgcn_readfirstlane(sm.cnt);
@@ -354,85 +304,63 @@ __device__ __noinline__ uint64_t select_threshold(const float* __restrict__ sm_m
     hi = __builtin_amdgcn_readfirstlane(sm.hi);
   }
   if (cnt > kFinal) {
-    // every candidate has mass bits lo: admit them in ascending block order
-    if (tid == 0) {
-      sm.thr = 0;
-      sm.ready = 0;
+    // every candidate left has mass bits lo: admit them in ascending block order, the
+    // k-th of them found on a bitmap of the tied blocks
+    if (tid == 0) sm.thr = 0;
+    for (int k = tid; k < nc; k += T) {
+      const int j = cand[k];
+      if (__float_as_uint(sm_m[j]) == lo) atomicOr(&sm.tie[j >> 5], 1u << (j & 31));
     }
-    auto tie = [&](int i, float m) { return m >= 0.f && __float_as_uint(m) == lo; };
-    rows_prefix<T>(sm_m, rows, tie, sm);
-    const uint64_t f = wgt(lo);
-    if (f == 0) return 0;  // cannot happen while the invariant holds
-    const uint64_t k = (P - cab + f - 1) / f;  // >= 1, <= cnt
-    for_rows<T>(sm_m, rows, [&](int i, float m) {
-      const bool c = tie(i, m);
-      const int ord = ordinal<T>(c, i, sm);
-      if (c && (uint64_t)ord + 1 == k) sm.thr = key_at<T>(i, m);
-    });
+    __syncthreads();
+    if (wave == 0) {
+      const int nwords = ceil_div(nblk, 32);
+      bitmap_prefix_wave(sm.tie, nwords, sm);
+      const uint64_t f = wgt(lo);
+      const uint32_t kk = (uint32_t)(f ? (P - cab + f - 1) / f : 1);  // >= 1, <= cnt
+      // the word holding the kk-th tied block, then the bit within it
+#pragma unroll
+      for (int q = 0; q < kBitWordsPerLane; ++q) {
+        const int i = lane * kBitWordsPerLane + q;
+        if (i < nwords) {
+          uint32_t word = sm.tie[i];
+          const uint32_t before = sm.wpre[i];
+          if (before < kk && kk <= before + (uint32_t)__popc(word)) {
+            for (uint32_t r = kk - before; r > 1; --r) word &= word - 1u;  // drop the lower bits
+            sm.thr = key_of(__uint_as_float(lo), i * 32 + __ffs(word) - 1);
+          }
+        }
+      }
+    }
     __syncthreads();
     return uni64(sm.thr);
   }
-  // the last <= kFinal candidates: each wave gathers its own in wbuf (slots from a
-  // wave-uniform running count, no atomics); the same pass counts, per (row, wave), the
-  // blocks above the candidates' range (all selected)
-  uint64_t* wk = wbuf + wave * 2 * kFinal;
-  int nw = 0, cntv = 0;
-  for_rows<T>(sm_m, rows, [&](int i, float m) {
-    const uint32_t bits = __float_as_uint(m);
-    const bool c = cand(m);
-    const uint64_t bc = __ballot(c);
-    if (c) {
-      const int slot = nw + (int)__popcll(bc & lanemask_lt());
+  // the last <= kFinal candidates: appended to one short list, then ranked by wave 0
+  for (int k = tid; k < nc; k += T) {
+    const int j = cand[k];
+    const uint32_t bits = __float_as_uint(sm_m[j]);
+    if (bits >= lo && bits <= hi) {
+      const int slot = atomicAdd(&sm.nfinal, 1);
       if (slot < kFinal) {
-        wk[slot] = key_at<T>(i, m);
-        wk[kFinal + slot] = wgt(bits);
+        sm.fkey[slot] = key_of(__uint_as_float(bits), j);
+        sm.fw[slot] = wgt(bits);
       }
     }
-    nw += (int)__popcll(bc);
-    cntv = count_into_lane(cntv, __ballot(m >= 0.f && bits > hi), i);
-  });
-  store_row_counts<T>(cntv, rows, sm);
-  if (lane == 0) sm.wn[wave] = min(nw, kFinal);
-  if (wave == 0) sm.above[lane] = 0;
-  __syncthreads();
-  // every wave holds the candidates one per lane (lane < nf), in wave order
-  int nf = 0, sw = 0, sk = 0;
-  for (int w2 = 0; w2 < W; ++w2) {
-    const int c2 = sm.wn[w2];
-    if (lane >= nf && lane < nf + c2) {
-      sw = w2;
-      sk = lane - nf;
-    }
-    nf += c2;
   }
-  nf = min(nf, kFinal);
-  const uint64_t my = lane < nf ? wbuf[sw * 2 * kFinal + sk] : 0ull;
-  const uint64_t f = lane < nf ? wbuf[sw * 2 * kFinal + kFinal + sk] : 0ull;
-  // rank by key (keys are distinct): wave w sums the masses of the larger keys among
-  // candidates w, w + W, ...
-  uint64_t part = 0;
-  for (int i = wave; i < nf; i += W) {
-    const uint64_t ki = readlane_u64(my, i), fi = readlane_u64(f, i);
-    part += ki > my ? fi : 0ull;
-  }
-  if (lane < nf && part) atomicAdd((unsigned long long*)&sm.above[lane], (unsigned long long)part);
   __syncthreads();
   if (wave == 0) {
+    const int nf = min(sm.nfinal, kFinal);
+    const uint64_t my = lane < nf ? sm.fkey[lane] : 0ull;
+    const uint64_t f = lane < nf ? sm.fw[lane] : 0ull;
+    // rank by key (keys are distinct): the mass of the larger keys
+    uint64_t above = 0;
+    for (int i = 0; i < nf; ++i) {
+      const uint64_t ki = readlane_u64(my, i), fi = readlane_u64(f, i);
+      above += ki > my ? fi : 0ull;
+    }
     // the crossing candidate has cab + (mass of the larger keys) < P <= that + its own
-    const uint64_t above = lane < nf ? sm.above[lane] : 0ull;
     const uint64_t cb = __ballot(lane < nf && cab + above < P && cab + above + f >= P);
     const uint64_t thr = cb ? readlane_u64(my, __ffsll((long long)cb) - 1) : 0ull;
-    // the selected candidates join the per-(row, wave) counts (LDS operations of one
-    // wave complete in order, so the scan below sees them)
-    if (cb && lane < nf && my >= thr) {
-      const int j = (int)(0xFFFFFFFFu - (uint32_t)my);
-      atomicAdd(&sm.rowtab[(j / T) * W + (j % T) / kWave], 1);
-    }
-    if (cb) rowtab_scan<T>(rows, sm);
-    if (lane == 0) {
-      sm.thr = thr;
-      sm.ready = cb != 0;
-    }
+    if (lane == 0) sm.thr = thr;
   }
   __syncthreads();
   return uni64(sm.thr);
@@ -646,31 +574,64 @@ __device__ __forceinline__ bool index_chunk(const IndexArgs& a, int c, int r, in
 // ascending selected block ids and their count (and, if asked, one byte per block:
 // 1 = selected), and resets the head's arrival counter.  If a word of this call is still
 // stale when the bounded wait runs out (or the header asks for that failure), every
-// block is selected and the header's status bit and fallback count record it.
+// block is selected and the header's status bit and fallback count record it.  Passes
+// over blocks or candidates run on all T threads; the chunk statistics, the bin scans,
+// the final ranking and the bitmap prefix on wave 0 alone, while the other waves wait at
+// the next barrier.
 template <int T>
-__device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int r, int b, IndexSmem<T>* S) {
-  constexpr int W = T / kWave;
+__device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int b, size_t head, IndexSmem<T>* S) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const size_t head = (size_t)b * a.n_ret + r;
   const int N = a.seq_lens[b];
   const int nblk = (N + BK - 1) / BK;
   const int nch = (nblk + a.chunk_blocks - 1) / a.chunk_blocks;
+  const int rows = ceil_div(nblk, T);  // block j = row * T + thread
   const uint32_t tag = S->tag;
-  TailSmem<T>& sm = S->sm;
+  TailSmem& sm = S->sm;
   float* s_mass = index_masses<T>(S);
+  uint16_t* cand = index_cands<T>(S, rows);
   const uint64_t* e_io = head_block_words(a, head);
-
-  // ---- M = max_c M_c, Z = sum_c Z_c exp(M_c - M); then m_j = e_j exp(M_c - M) / Z for
-  // every block, into LDS
+  const uint64_t* cs = head_chunk_words(a, head);
   const bool inject = (S->inject & 1) != 0;
   int budget = inject ? 0 : kSpinBudget;
   bool ok = !inject;
-  const uint64_t* cs = head_chunk_words(a, head);
+
+  // ---- the head's words, by every thread (one memory round trip): chunk words (M_c, Z_c)
+  // into LDS, the first rows of block words into registers
+  constexpr int CW = kIdxMaxChunks / T;  // chunk words per thread
+  uint64_t x[CW], z[CW];
+#pragma unroll
+  for (int k = 0; k < CW; ++k) {
+    const int i = tid + k * T;
+    x[k] = i < nch ? ld_dev(cs + 2 * i) : 0ull;
+    z[k] = i < nch ? ld_dev(cs + 2 * i + 1) : 0ull;
+  }
+  uint64_t w[kMassBatch];
+#pragma unroll
+  for (int u = 0; u < kMassBatch; ++u) {
+    const int j = u * T + tid;
+    w[u] = (u < rows && j < nblk) ? ld_dev(e_io + j) : 0ull;
+  }
   if (tid < kBins) {
     sm.bmass[tid] = 0;
     sm.bcnt[tid] = 0;
   }
-  if (tid == 0) sm.found = 0;
+  for (int i = tid; i < kBitWords; i += T) {
+    sm.sel[i] = 0;
+    sm.tie[i] = 0;
+  }
+  if (tid == 0) {
+    sm.found = 0;
+    sm.ncand = 0;
+    sm.nfinal = 0;
+  }
+#pragma unroll
+  for (int k = 0; k < CW; ++k) {
+    const int i = tid + k * T;
+    if (i < nch) {
+      S->cm[i] = untag_f32(settle(cs + 2 * i, x[k], tag, budget, ok));
+      S->cz[i] = untag_f32(settle(cs + 2 * i + 1, z[k], tag, budget, ok));
+    }
+  }
   // static top-k keeps topk_blocks blocks: the same search with every block weighing 1
   // and P = the number of blocks
   const int kb = a.topk_blocks;
@@ -679,101 +640,71 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int r, 
   const bool pick = count ? kb < nblk : (p < 1.0f && nblk > 1);  // else every block is selected
   // Top-p: every block of mass below (1 - p) / (2 nblk) is outside the selection and
   // below its threshold: with total mass ~1 the threshold exceeds (total - p) / nblk.
-  // Such blocks stay out of the histograms (peaked heads have thousands of them).
+  // Such blocks stay out of the candidates (peaked heads have thousands of them).
   const uint32_t lbits = count ? 0u : __float_as_uint(fmaxf(0.f, 0.5f * (1.0f - p - 1e-6f) / (float)nblk));
   // first level: 1/8-octave bins (bits >> 20) from the floor up, which span 32 octaves
   // (everything above goes to the top bin); without a floor, half-octave bins from 0
   const int shift1 = lbits ? 20 : 22;
   const uint32_t lo1 = lbits & ~((1u << shift1) - 1u);
-  const int rows = ceil_div(ceil_div(nblk, T), kRowBatch) * kRowBatch;  // rows past nblk hold -1
-  constexpr int LB = 16;  // global reads in flight per thread
-  uint64_t w[LB];         // the first LB rows' words go out before the reductions below
-#pragma unroll
-  for (int u = 0; u < LB; ++u) {
-    const int j = u * T + tid;
-    w[u] = (u < rows && j < nblk) ? ld_dev(e_io + j) : 0ull;
-  }
-  double cm[2], cz[2];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {  // nch <= 2 * T
-    const int i = tid + k * T;
-    cm[k] = -INFINITY;
-    cz[k] = 0.0;
-    if (i < nch) {
-      const uint64_t x = ld_dev(cs + 2 * i), z = ld_dev(cs + 2 * i + 1);
-      cm[k] = (double)untag_f32(settle(cs + 2 * i, x, tag, budget, ok));
-      cz[k] = (double)untag_f32(settle(cs + 2 * i + 1, z, tag, budget, ok));
-    }
-  }
-  {
-    const double mw = wave_max(fmax(cm[0], cm[1]));
-    if (lane == 0) sm.f64[wave] = mw;
-  }
   bool failed = __syncthreads_or(!ok) != 0;  // uniform
+
+  // ---- wave 0: M = max_c M_c (an fp32 value), Z = sum_c Z_c exp(M_c - M); the chunk
+  // factors exp(M_c - M) / Z (fp32) replace the chunk words
+  if (!failed && wave == 0) {
+    float mloc = -INFINITY;
+    for (int i = lane; i < nch; i += kWave) mloc = fmaxf(mloc, S->cm[i]);
+    const double M = (double)wave_maxf(mloc);
+    double zloc = 0.0;
+    for (int i = lane; i < nch; i += kWave) {
+      const float cmi = S->cm[i];
+      const double e = cmi == -INFINITY ? 0.0 : exp((double)cmi - M);
+      zloc += (double)S->cz[i] * e;
+      S->cz[i] = (float)e;  // kept until Z is known
+    }
+    const double invZ = 1.0 / wave_sum(zloc);
+    for (int i = lane; i < nch; i += kWave) S->cm[i] = (float)((double)S->cz[i] * invZ);
+  }
+  __syncthreads();
+
+  // ---- every thread: m_j = e_j exp(M_c - M) / Z into LDS; the same pass gathers the
+  // candidates (blocks at or above the floor) and builds the first threshold level over
+  // them: bin = (bits - lo1) >> shift1, the top bin also takes any larger
   if (!failed) {
-    double M = sm.f64[0];
-#pragma unroll
-    for (int w2 = 1; w2 < W; ++w2) M = fmax(M, sm.f64[w2]);
-    double f[2], zloc = 0.0;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      f[k] = cm[k] == -INFINITY ? 0.0 : exp(cm[k] - M);
-      zloc += cz[k] * f[k];
-    }
-    {
-      const double zw = wave_sum(zloc);
-      if (lane == 0) sm.f64b[wave] = zw;
-    }
-    __syncthreads();
-    double Z = sm.f64b[0];
-#pragma unroll
-    for (int w2 = 1; w2 < W; ++w2) Z += sm.f64b[w2];
-    const double invZ = 1.0 / Z;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int i = tid + k * T;
-      if (i < nch) S->f[i] = f[k] * invZ;
-    }
-    __syncthreads();
-    // masses into LDS; the same pass builds the first threshold level over the blocks above
-    // the floor: bin = (bits - lo1) >> shift1, the top bin also takes any larger
     const int cshift = __ffs(a.chunk_blocks) - 1;
-    for (int i0 = 0; i0 < rows; i0 += LB) {
+    const float* fch = S->cm;
+    for (int i0 = 0; i0 < rows; i0 += kMassBatch) {
       if (i0 > 0) {
 #pragma unroll
-        for (int u = 0; u < LB; ++u) {
+        for (int u = 0; u < kMassBatch; ++u) {
           const int j = (i0 + u) * T + tid;
           w[u] = (i0 + u < rows && j < nblk) ? ld_dev(e_io + j) : 0ull;
         }
       }
-      bool fresh = true;
 #pragma unroll
-      for (int u = 0; u < LB; ++u) {
+      for (int u = 0; u < kMassBatch; ++u) {
         const int j = (i0 + u) * T + tid;
-        if (i0 + u < rows && j < nblk) fresh = fresh && has_tag(w[u], tag);
-      }
-      if (!fresh) {
-#pragma unroll
-        for (int u = 0; u < LB; ++u) {
-          const int j = (i0 + u) * T + tid;
-          if (i0 + u < rows && j < nblk) w[u] = settle(e_io + j, w[u], tag, budget, ok);
-        }
+        if (i0 + u < rows && j < nblk) w[u] = settle(e_io + j, w[u], tag, budget, ok);
       }
 #pragma unroll
-      for (int u = 0; u < LB; ++u) {
+      for (int u = 0; u < kMassBatch; ++u) {
+        if (i0 + u >= rows) break;  // uniform
         const int j = (i0 + u) * T + tid;
-        if (i0 + u < rows) {
-          float m = -1.0f;  // no block
-          if (j < nblk) {
-            m = (float)((double)untag_f32(w[u]) * S->f[j >> cshift]);
-            const uint32_t bits = __float_as_uint(m);
-            if (pick && bits >= lbits) {
-              const int bin = level_bin(bits, lo1, shift1);
-              atomicAdd((unsigned long long*)&sm.bmass[bin], count ? 1ull : (unsigned long long)fixed_bits(bits));
-              atomicAdd(&sm.bcnt[bin], 1u);
-            }
+        const bool v = j < nblk;
+        const float m = v ? untag_f32(w[u]) * fch[j >> cshift] : -1.0f;  // -1: no block
+        s_mass[j] = m;
+        const uint32_t bits = __float_as_uint(m);
+        const bool c = v && pick && bits >= lbits;
+        const uint64_t bal = __ballot(c);
+        if (bal) {  // uniform
+          if (c) {
+            const int bin = level_bin(bits, lo1, shift1);
+            atomicAdd((unsigned long long*)&sm.bmass[bin], count ? 1ull : (unsigned long long)fixed_bits(bits));
+            atomicAdd(&sm.bcnt[bin], 1u);
           }
-          s_mass[j] = m;
+          int base = 0;
+          if (lane == 0) base = atomicAdd(&sm.ncand, (int)__popcll(bal));
+          base = __builtin_amdgcn_readfirstlane(base);
+          if (c) cand[base + (int)__popcll(bal & lanemask_lt())] = (uint16_t)j;
         }
       }
     }
@@ -782,26 +713,26 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int r, 
 
   // ---- threshold key: block j is selected iff key_of(m_j, j) >= thr
   uint64_t thr = 0;
-  bool all = true, ready = false;
+  bool all = true;
+  int nc = 0;
   if (pick && !failed) {
     const uint64_t P = count ? (uint64_t)kb : (uint64_t)ceil(ldexp((double)p, 62));
     if (wave == 0) {
-      scan_level<T>(0, P, lo1, 0xFFFFFFFFu, shift1, sm);
+      scan_level(0, P, lo1, 0xFFFFFFFFu, shift1, sm);
       // the pruned blocks were not counted: the candidates start at the floor
       if (lane == 0 && sm.found) sm.lo = min(max(sm.lo, lbits), sm.hi);
     }
     __syncthreads();
     if (sm.found) {  // else the total mass is below p: every block
       all = false;
-      thr = select_threshold<T>(s_mass, rows, P, sm, reinterpret_cast<uint64_t*>(S->f), count);
-      ready = sm.ready;
+      nc = sm.ncand;
+      thr = select_threshold<T>(s_mass, cand, nc, nblk, P, sm, count);
     }
   }
 
-  // ---- ordered compaction of the selected ids (ascending)
+  // ---- ordered compaction of the selected ids (ascending), from a bitmap of them
   int* out = a.sel_idx + head * a.nblk_max;
   uint8_t* mask = a.sel_mask ? a.sel_mask + head * a.nblk_max : nullptr;
-  int total = nblk;
   if (all) {
     select_all<T>(a, head, nblk);
     if (failed && tid == 0) {
@@ -809,18 +740,21 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int r, 
       atomicAdd(&a.hdr->fallbacks, 1u);
     }
   } else {
-    auto sel = [&](int i, float m) { return m >= 0.f && key_at<T>(i, m) >= thr; };
-    total = ready ? sm.total : rows_prefix<T>(s_mass, rows, sel, sm);
-    for_rows<T>(s_mass, rows, [&](int i, float m) {
-      const bool sl = sel(i, m);
-      const int ord = ordinal<T>(sl, i, sm);
-      const int j = i * T + tid;
-      if (sl) out[ord] = j;
-      if (mask && j < nblk) mask[j] = sl;
-    });
+    for (int k = tid; k < nc; k += T) {
+      const int j = cand[k];
+      if (key_of(s_mass[j], j) >= thr) atomicOr(&sm.sel[j >> 5], 1u << (j & 31));
+    }
+    __syncthreads();
+    if (wave == 0) bitmap_prefix_wave(sm.sel, ceil_div(nblk, 32), sm);
+    __syncthreads();
+    for (int j = tid; j < nblk; j += T) {
+      const bool sl = (sm.sel[j >> 5] >> (j & 31)) & 1u;
+      if (sl) out[bitmap_rank(sm.sel, j, sm)] = j;
+      if (mask) mask[j] = sl;
+    }
   }
   if (tid == 0) {
-    if (!all) a.sel_cnt[head] = total;
+    if (!all) a.sel_cnt[head] = sm.total;
     __hip_atomic_store(&head_state(a, head)->counter, 0, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
   }

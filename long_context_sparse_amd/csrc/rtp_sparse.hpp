@@ -387,4 +387,57 @@ __device__ __forceinline__ bool local_split(const LocalArgs& a, int c, int g, in
   return true;
 }
 
+// The local heads' partials in a workspace: lse [B, n_loc, n_split], then o [B, n_loc,
+// n_split, 128], for a window split of split_tokens (split 0 holds the sinks).
+struct LocalLayout {
+  int split_tokens, n_split;
+  size_t off_lse, off_o, total;
+};
+inline LocalLayout local_layout_for(int B, int n_loc, int window, int split_tokens) {
+  LocalLayout L{};
+  L.split_tokens = split_tokens;
+  L.n_split = 1 + ceil_div(window, split_tokens);
+  L.off_lse = 0;
+  L.off_o = align_up((size_t)B * n_loc * L.n_split * sizeof(float), 256);
+  L.total = L.off_o + align_up((size_t)B * n_loc * L.n_split * kHeadDim * sizeof(float), 256);
+  return L;
+}
+// Host checks of the local heads' arguments shared by rtp_local_window_attn and the
+// decode step's attention launch (n_loc > 0); fills L with `layout`'s split.
+template <class LayoutFn>
+inline rtp_status local_args_check(const void* q, const void* k_cache, const void* v_cache, const int* seq_lens,
+                                   const int* loc_heads, int B, int Hq, int Hkv, int n_loc, int max_ctx, int window,
+                                   int sinks, const void* workspace, size_t ws_bytes, const int* kv_slot, int n_full,
+                                   const void* k_ring, const void* v_ring, int n_ring, LayoutFn layout,
+                                   LocalLayout& L) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || n_loc < 0 || n_loc > Hq || max_ctx <= 0) return RTP_EINVAL;
+  if (Hq % Hkv || window < 0 || sinks < 0 || window + sinks < 1) return RTP_EINVAL;
+  {
+    const int G = Hq / Hkv;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return RTP_EUNSUPPORTED;
+  }
+  if (!q || !seq_lens || !loc_heads || !workspace) return RTP_EINVAL;
+  if (kv_slot) {
+    // full caches may be absent when every group is in the ring, and the reverse
+    if (n_full < 0 || n_full > Hkv || n_ring < 0 || n_ring > Hkv || n_full + n_ring < 1 || n_full + n_ring > Hkv)
+      return RTP_EINVAL;
+    if (n_full > 0 && (!k_cache || !v_cache)) return RTP_EINVAL;
+    if (n_ring > 0 && (!k_ring || !v_ring)) return RTP_EINVAL;
+    if (((uintptr_t)k_ring | (uintptr_t)v_ring) & 15) return RTP_EINVAL;
+  } else if (!k_cache || !v_cache) {
+    return RTP_EINVAL;
+  }
+  if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache) & 15) return RTP_EINVAL;
+  if ((uintptr_t)workspace & 255) return RTP_EINVAL;
+  L = layout(B, Hkv, n_loc, window < max_ctx ? window : max_ctx);
+  if (ws_bytes < L.total) return RTP_EINVAL;
+  if (L.n_split > 65535 || B > 65535) return RTP_EUNSUPPORTED;
+  return RTP_OK;
+}
+
+// the local heads' window split (256-thread workgroups)
+inline LocalLayout local_layout(int B, int Hkv, int n_loc, int window) {
+  return local_layout_for(B, n_loc, window, local_split_tokens(B, Hkv, window));
+}
+
 }  // namespace rtp

@@ -1,10 +1,15 @@
-"""One decode step of the sparse attention path, as four librtp calls.
+"""One decode step of the sparse attention path, as one librtp call (three launches).
 
 DecodeStep owns the device buffers the calls need (selected-block lists and masks,
-split partials, workspaces, output) and issues them through one rtp_decode_step call:
+split partials, workspaces, output) and issues them through one rtp_decode_step call,
+three launches on the current stream:
 
-  retrieval heads:  rtp_index_topp (or rtp_index_topk) -> rtp_sparse_attn_split -> rtp_split_reduce
-  local heads:      rtp_local_window_attn (on a second stream, overlapping the above)
+  rtp_index_topp (or rtp_index_topk)   retrieval heads: scores and block selection
+  rtp_decode_attn                      retrieval heads' split attention + local heads' window
+  rtp_decode_merge                     both kinds of partials -> the output rows
+
+The four separate calls of the path (rtp_index_topp, rtp_sparse_attn_split,
+rtp_split_reduce, rtp_local_window_attn) stay available one by one.
 
 The inputs may place KV groups in sink + window rings (keys "kv_slot", "k_ring",
 "v_ring"; see the KV placement note in include/rtp.h): the full caches then hold only
@@ -48,8 +53,7 @@ class StepShape:
 
 
 class DecodeStep:
-    def __init__(self, shape: StepShape, device: str = "cuda", overlap: bool = True, use_mask: bool = True,
-                 k_tokens: int = 0):
+    def __init__(self, shape: StepShape, device: str = "cuda", use_mask: bool = True, k_tokens: int = 0):
         """k_tokens = 0: the top-p rule (the inputs' top_p); > 0: the static top-k rule
         with this budget in tokens."""
         self.s = shape
@@ -73,10 +77,6 @@ class DecodeStep:
                if s.n_loc else 0)
         self.ws_index = torch.zeros(max(ws1, 256), dtype=torch.uint8, device=dev)
         self.ws_local = torch.zeros(max(ws2, 256), dtype=torch.uint8, device=dev)
-        self.overlap = overlap and s.n_loc > 0 and s.n_ret > 0
-        self.side = torch.cuda.Stream(device=dev) if self.overlap else None
-        self._fork = abi.event_create() if self.overlap else None
-        self._join = abi.event_create() if self.overlap else None
         self._key = None
         self._vals = None
         self._step_fn = abi.lib().rtp_decode_step
@@ -116,6 +116,22 @@ class DecodeStep:
         abi.rtp_split_reduce(self.o_part, self.lse_part, t["ret_heads"], s.B, s.Hq, s.n_ret, s.n_split,
                              self.out, stream)
 
+    # -- the step's own launches after the index call ---------------------------------
+    def attn(self, t: Dict[str, torch.Tensor], stream=None) -> None:
+        s = self.s
+        abi.rtp_decode_attn(t["q"], t["k_cache"], t["v_cache"], t["seq_lens"],
+                            t["ret_heads"] if s.n_ret else None, self.sel_idx if s.n_ret else None,
+                            self.sel_cnt if s.n_ret else None, self.sel_mask if s.n_ret else None,
+                            t["loc_heads"] if s.n_loc else None, s.B, s.Hq, s.Hkv, s.n_ret, s.n_loc, s.max_ctx,
+                            s.block, s.split_tokens, s.window, s.sinks, self.o_part, self.lse_part, self.ws_local,
+                            stream, **self.placement(t))
+
+    def merge(self, t: Dict[str, torch.Tensor], stream=None) -> None:
+        s = self.s
+        abi.rtp_decode_merge(self.o_part, self.lse_part, t["ret_heads"] if s.n_ret else None,
+                             t["loc_heads"] if s.n_loc else None, s.B, s.Hq, s.Hkv, s.n_ret, s.n_loc, s.max_ctx,
+                             s.split_tokens, s.window, s.sinks, self.ws_local, self.out, stream)
+
     def local(self, t: Dict[str, torch.Tensor], stream=None) -> None:
         s = self.s
         abi.rtp_local_window_attn(t["q"], t["k_cache"], t["v_cache"], t["seq_lens"], t["loc_heads"],
@@ -129,7 +145,6 @@ class DecodeStep:
         s = self.s
         p = abi.device_ptr
         z = lambda name: p(t[name]) if t[name].numel() else None  # noqa: E731
-        side = self.side.cuda_stream if self.overlap else None
         pl = self.placement(t)
         o = lambda x: None if x is None else p(x)  # noqa: E731
         return (z("q_pre") if s.n_ret else None, z("w_q") if s.n_ret else None, z("k_idx") if s.n_ret else None,
@@ -140,15 +155,13 @@ class DecodeStep:
                 p(self.sel_mask) if self.sel_mask is not None else None, p(self.o_part), p(self.lse_part),
                 p(self.out), p(self.ws_index), abi.nbytes(self.ws_index), p(self.ws_local),
                 abi.nbytes(self.ws_local), o(pl["kv_slot"]), pl["n_full"], o(pl["k_ring"]), o(pl["v_ring"]),
-                pl["n_ring"], main, side, self._fork, self._join)
+                pl["n_ring"], main)
 
     def __call__(self, t: Dict[str, torch.Tensor]) -> torch.Tensor:
         """Enqueue one decode step on the current stream; returns the fp32 [B, Hq, 128] output.
 
-        One rtp_decode_step call: the local heads' call goes to a second stream (forked
-        from and joined back into the current one with events) so it overlaps the
-        retrieval heads' three calls.  The arguments are converted once per (set of
-        tensors, stream)."""
+        One rtp_decode_step call (three launches on that stream).  The arguments are
+        converted once per (set of tensors, stream)."""
         main = torch.cuda.current_stream(self.device).cuda_stream
         vals = tuple(t.values())
         key = (main,) + tuple(map(id, vals))

@@ -154,7 +154,7 @@ def test_cache_append_rejects():
 def test_decode_step_rejects():
     L = abi.lib()
     args = [FAKE] * 10 + [0] + [1, 8, 2, 2, 6, 4096, 64, 1024, 1024, 4] + [FAKE] * 6 + \
-        [FAKE, 1 << 30, FAKE, 1 << 30] + [None, 0, None, None, 0] + [None] * 4
+        [FAKE, 1 << 30, FAKE, 1 << 30] + [None, 0, None, None, 0] + [None]
     bad = list(args)
     bad[11] = 0                                        # B = 0
     assert L.rtp_decode_step(*bad) == abi.RTP_EINVAL
@@ -229,10 +229,39 @@ def test_noalloc_step_limit_and_rejects():
 
     def call(B=1, Hq=8, Hkv=2, n_ret=2, n_loc=6, max_ctx=4096, block=64, split=256, window=64, sinks=4):
         return f(*([FAKE] * 10), 0, B, Hq, Hkv, n_ret, n_loc, max_ctx, block, split, window, sinks,
-                 FAKE, FAKE, None, FAKE, None, 0, None, None, 0, None, None, None, None)
+                 FAKE, FAKE, None, FAKE, None, 0, None, None, 0, None)
     assert call(B=64, Hq=32, Hkv=8, n_ret=32, n_loc=0, max_ctx=1 << 20, block=128, split=128) == abi.RTP_ESCRATCH
     assert call(B=8, Hq=32, Hkv=8, n_ret=16, n_loc=16, max_ctx=1 << 20, block=128, split=128) == abi.RTP_ESCRATCH
     assert call(block=32) == abi.RTP_EUNSUPPORTED
     assert call(split=100) == abi.RTP_EINVAL
     assert call(n_ret=5, n_loc=5) == abi.RTP_EINVAL
     assert call(window=0, sinks=0) == abi.RTP_EINVAL
+
+
+def test_decode_attn_and_merge_reject():
+    L = abi.lib()
+
+    def attn(B=1, Hq=8, Hkv=2, n_ret=2, n_loc=6, block=64, split=1024, window=1024, sinks=4, ws_bytes=1 << 30,
+             o=FAKE, loc=FAKE, q=FAKE):
+        return L.rtp_decode_attn(q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, loc, B, Hq, Hkv, n_ret, n_loc, 4096,
+                                 block, split, window, sinks, o, FAKE, FAKE, ws_bytes, None, 0, None, None, 0, None)
+    assert attn(B=0) == abi.RTP_EINVAL
+    assert attn(n_ret=3) == abi.RTP_EINVAL            # more heads than query heads
+    assert attn(Hkv=3) == abi.RTP_EINVAL
+    assert attn(block=32) == abi.RTP_EUNSUPPORTED
+    assert attn(split=100) == abi.RTP_EINVAL
+    assert attn(o=None) == abi.RTP_EINVAL
+    assert attn(loc=None) == abi.RTP_EINVAL
+    assert attn(window=0, sinks=0) == abi.RTP_EINVAL
+    assert attn(ws_bytes=16) == abi.RTP_EINVAL         # local workspace too small
+    assert attn(q=FAKE + 8) == abi.RTP_EINVAL          # misaligned
+    assert attn(n_ret=0, n_loc=0) == abi.RTP_OK        # nothing to do
+
+    def merge(B=1, n_ret=2, n_loc=6, split=1024, ws_bytes=1 << 30, out=FAKE):
+        return L.rtp_decode_merge(FAKE, FAKE, FAKE, FAKE, B, 8, 2, n_ret, n_loc, 4096, split, 1024, 4, FAKE,
+                                  ws_bytes, out, None)
+    assert merge(B=0) == abi.RTP_EINVAL
+    assert merge(out=None) == abi.RTP_EINVAL
+    assert merge(split=0) == abi.RTP_EINVAL
+    assert merge(ws_bytes=16) == abi.RTP_EINVAL
+    assert merge(n_ret=0, n_loc=0) == abi.RTP_OK

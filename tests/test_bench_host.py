@@ -33,20 +33,20 @@ def test_algorithmic_bytes_hand_worked():
     sel_cnt = np.array([[2]])
     a = bench.algorithmic_bytes(cfg, inp, sel_idx, sel_cnt)
     assert a["index_topp"] == 4096 + 32 * 300 + 256 + 4 * 2 + 4
-    assert a["sparse_attn"] == 512 * 108 + 256
-    assert a["split_reduce"] == 512
-    assert a["local_window"] == 512 * 68 + 256 + 512
-    assert a["step"] == a["index_topp"] + a["split_reduce"] + 256 + 256 + 512 + 512 * 128
+    assert a["decode_attn"] == 512 * 128 + 256 * 2          # the union once, both query rows
+    assert a["decode_merge"] == 512 * 2                      # both fp32 output rows
+    assert a["kv_rows_selected_union"] == 108 and a["kv_rows_window"] == 68
+    assert a["step"] == a["index_topp"] + a["decode_attn"] + a["decode_merge"]
 
 
 def test_traffic_record_follows_kernel_sources(monkeypatch):
     # the committed record is read while its sources are unchanged, and dropped after
-    rec = bench.read_traffic("ctx128k", "sparse_attn")
+    rec = bench.read_traffic("ctx128k", "decode_attn")
     if rec is None:
-        pytest.skip("no current traffic record for the split attention at 128K")
+        pytest.skip("no current traffic record for the step's attention launch at 128K")
     assert rec > 0
     monkeypatch.setattr(bench, "kernel_source_hash", lambda kernel: "0" * 16)
-    assert bench.read_traffic("ctx128k", "sparse_attn") is None
+    assert bench.read_traffic("ctx128k", "decode_attn") is None
 
 
 def test_kernel_source_hash_covers_included_headers(tmp_path, monkeypatch):

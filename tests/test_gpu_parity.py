@@ -9,7 +9,7 @@ import torch
 
 import workloads as W
 from gpu_util import Run, check_outputs, check_selection, say
-from long_context_sparse_amd import abi
+from long_context_sparse_amd import DecodeStep, abi
 from oracle import accept as A
 from oracle import rtp_oracle as O
 
@@ -256,15 +256,33 @@ def test_block_masks_match_lists_and_give_the_same_partials():
     assert torch.equal(l2, m.step.lse_part)
 
 
-def test_one_stream_matches_two_streams():
-    """rtp_decode_step without a side stream (everything in order on one stream) gives the
-    same bits as the forked step."""
-    cfg = W.custom_config(name="streams", B=2, Hkv=2, Hq=8, n_ret=3, ctx=(7000, 3001), block=64, window=600,
+@pytest.mark.parametrize("n_ret,n_loc_all", [(3, False), (0, True), (8, False)])
+def test_step_matches_the_four_calls(n_ret, n_loc_all):
+    """rtp_decode_step (index, one attention launch for both head kinds, one merge) against
+    the four separate calls rtp_index_topp, rtp_sparse_attn_split, rtp_split_reduce and
+    rtp_local_window_attn: the same block sets and the same output bits, with both head
+    kinds, with no retrieval heads, and with no local heads; both against the oracle."""
+    cfg = W.custom_config(name=f"calls{n_ret}", B=2, Hkv=2, Hq=8, n_ret=n_ret, ctx=(7000, 3001), block=64, window=600,
                           sinks=4, split_tokens=512, kind="peaked_diffuse")
     inp = W.make_inputs(cfg)
     t = W.to_device(inp)
-    two = Run(inp, tensors=t, tag="two streams")
-    one = Run(inp, tensors=t, tag="one stream", overlap=False)
-    assert not one.step.overlap and two.step.overlap
-    assert np.array_equal(one.out_h, two.out_h)
-    assert np.array_equal(one.sel_cnt, two.sel_cnt)
+    step = Run(inp, tensors=t, tag=f"step n_ret={n_ret}")
+    calls = DecodeStep(step.step.s)
+    out = torch.full_like(calls.out, float("nan"))
+    calls.out = out
+    if cfg.n_ret:
+        calls.index_topp(t)
+        calls.sparse_attn(t)
+        calls.reduce(t)
+    if cfg.n_loc:
+        calls.local(t)
+    torch.cuda.synchronize()
+    sep = out.cpu().numpy().astype(np.float64)
+    ret = [int(h) for h in inp.ret_heads]
+    loc = [int(h) for h in inp.loc_heads]
+    assert np.array_equal(sep[:, ret], step.out_h[:, ret])
+    assert np.array_equal(sep[:, loc], step.out_h[:, loc])
+    if cfg.n_ret:
+        assert torch.equal(calls.sel_cnt.cpu(), torch.from_numpy(step.sel_cnt))
+        check_selection(step)
+    check_outputs(step)

@@ -67,29 +67,31 @@ def test_prefill_small_all_rows(name):
     _check_rows(pin, out, items)
 
 
-def test_prefill_32k_sampled():
-    """A 32K-token prompt at the pages' prefill configuration (32 query heads over 8 KV
-    heads, 4 retrieval heads, sink 4 + window 8192): sampled rows at tile and window
-    edges of retrieval and local heads."""
-    cfg = W.custom_config(name="prefill32k", seed=70, B=1, Hq=32, Hkv=8, n_ret=4, ret_heads=(3, 9, 20, 30),
-                          ctx=(32768,), window=8192, sinks=4)
-    pin = W.make_prefill_inputs(cfg)
-    say("[gpu] prefill 32K: Hq=32 Hkv=8 ret=(3, 9, 20, 30) window=8192 sinks=4")
-    out, _ = _run(pin)
-    rows = [0, 1, 3, 4, 63, 64, 127, 128, 8191, 8192, 8195, 8196, 20000, 32766, 32767]
-    _check_rows(pin, out, [(0, h, rows) for h in (3, 9, 0, 17, 31)])
+BENCH_RET = (3, 9, 15, 20, 30)  # the benchmark's prefill configuration: 32 query / 8 KV heads
 
 
-def test_prefill_128k_sampled():
-    """A 128K-token prompt (8 query heads over 2 KV heads, retrieval heads 1 and 6, sink 4
-    + window 8192): sampled rows across the whole prompt, both head kinds."""
-    cfg = W.custom_config(name="prefill128k", seed=71, B=1, Hq=8, Hkv=2, n_ret=2, ret_heads=(1, 6),
-                          ctx=(131072,), window=8192, sinks=4)
+def _bench_rows(N, seed):
+    """Rows at every kind of edge of the prefill kernel (256-query tiles, 64-key tiles, the
+    sink and window boundaries for sink 4 + window 8192, the prompt's end) plus seeded
+    random rows, 24 per head."""
+    edges = [0, 1, 3, 4, 5, 63, 64, 255, 256, 4095, 8191, 8192, 8195, 8196, 8197, N // 2, N - 257, N - 256,
+             N - 2, N - 1]
+    g = np.random.default_rng(seed)
+    rnd = sorted(int(x) for x in g.choice(N, size=4, replace=False))
+    return sorted(set(edges + rnd))
+
+
+@pytest.mark.parametrize("N", [32768, 131072])
+def test_prefill_bench_configuration_sampled(N):
+    """The benchmark's prefill pass (32 query heads over 8 KV heads, retrieval heads
+    3, 9, 15, 20, 30, sink 4 + window 8192) at 32K and 128K: 24 rows of every one of the 32
+    heads (768 rows), at tile, sink, window and prompt edges and seeded random positions."""
+    cfg = W.custom_config(name=f"prefill{N // 1024}k_bench", seed=70 + N // 32768, B=1, Hq=32, Hkv=8, n_ret=5,
+                          ret_heads=BENCH_RET, ctx=(N,), window=8192, sinks=4)
     pin = W.make_prefill_inputs(cfg)
-    say("[gpu] prefill 128K: Hq=8 Hkv=2 ret=(1, 6) window=8192 sinks=4")
+    say(f"[gpu] prefill {N}: Hq=32 Hkv=8 ret={BENCH_RET} window=8192 sinks=4")
     out, _ = _run(pin)
-    rows = [0, 5, 255, 256, 8195, 8196, 65535, 65536, 100000, 131071]
-    _check_rows(pin, out, [(0, h, rows) for h in (1, 6, 0, 7)])
+    _check_rows(pin, out, [(0, h, _bench_rows(N, 1000 + h)) for h in range(32)])
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,ret,ctx", [(2, 8, 2, (0, 3, 6), (500, 77)), (1, 4, 4, (2,), (1,))])

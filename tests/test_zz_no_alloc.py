@@ -19,11 +19,11 @@ def _cfg(name, B, n_ret, ctx, seed):
                            split_tokens=256, window=256, sinks=4, top_p=tuple([0.9] * n_ret), kind="peaked_diffuse")
 
 
-def _compare(cfg, fork):
+def _compare(cfg):
     inp = W.make_inputs(cfg)
     t = W.to_device(inp)
-    say(f"[gpu] no-alloc step {cfg.name}: B={cfg.B} n_ret={cfg.n_ret} max_ctx={cfg.max_ctx} fork={fork}")
-    ref = DecodeStep(shape_of(cfg), overlap=fork)
+    say(f"[gpu] no-alloc step {cfg.name}: B={cfg.B} n_ret={cfg.n_ret} max_ctx={cfg.max_ctx}")
+    ref = DecodeStep(shape_of(cfg))
     out_ref = ref(t).clone()
     torch.cuda.synchronize()
     s = shape_of(cfg)
@@ -32,12 +32,10 @@ def _compare(cfg, fork):
     sel_cnt = torch.zeros((s.B, s.n_ret), dtype=torch.int32, device="cuda")
     sel_mask = torch.zeros((s.B, s.n_ret, nblk), dtype=torch.uint8, device="cuda")
     out = torch.full((s.B, s.Hq, 128), float("nan"), dtype=torch.float32, device="cuda")
-    side = torch.cuda.Stream() if fork else None
-    evs = (abi.event_create(), abi.event_create()) if fork else (None, None)
     abi.rtp_decode_step_noalloc(t["q_pre"], t["w_q"], t["k_idx"], t["q"], t["k_cache"], t["v_cache"], t["seq_lens"],
                                 t["ret_heads"], t["loc_heads"], t["top_p"], 0, s.B, s.Hq, s.Hkv, s.n_ret, s.n_loc,
                                 s.max_ctx, s.block, s.split_tokens, s.window, s.sinks, sel_idx, sel_cnt, sel_mask,
-                                out, side_stream=side, ev_fork=evs[0], ev_join=evs[1])
+                                out)
     torch.cuda.synchronize()
     assert torch.equal(sel_cnt, ref.sel_cnt)
     for b in range(s.B):
@@ -54,9 +52,9 @@ def test_noalloc_step_matches_the_step_with_workspaces():
     g = np.random.default_rng(12)
     a = _cfg("noalloc_a", 3, 3, (3000, 777, 2048), 61)
     b = _cfg("noalloc_b", 2, 2, (1500, 64), 62)       # smaller: fewer sequences, heads and blocks
-    _compare(a, fork=True)
-    _compare(b, fork=False)
-    _compare(a, fork=True)
+    _compare(a)
+    _compare(b)
+    _compare(a)
     del g
 
 
