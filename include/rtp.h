@@ -330,13 +330,19 @@ rtp_status rtp_decode_merge(const float* o_part, const float* lse_part, const in
                             size_t ws_local_bytes, float* out, void* stream);
 
 /*
- * One decode step in one host call, three launches on `stream` (Strikes-Back
- * architecture paragraph: Kernel 1, Kernel 2 and the reduce; Review, Adaptive sparse
- * attention: local heads): rtp_index_topp (or rtp_index_topk), rtp_decode_attn and
- * rtp_decode_merge for the same arguments.  The outputs equal those of the separate
- * calls rtp_index_topp, rtp_sparse_attn_split, rtp_split_reduce and rtp_local_window_attn.
- * Every argument is checked before anything is enqueued; after that it returns the first
- * failing call's status.
+ * One decode step in one host call, three launches (Strikes-Back architecture paragraph:
+ * Kernel 1, Kernel 2 and the reduce; Review, Adaptive sparse attention: local heads):
+ * rtp_index_topp (or rtp_index_topk), rtp_decode_attn and rtp_decode_merge for the same
+ * arguments, on `stream`.  When side_stream, ev_fork and ev_join are given, there are
+ * retrieval and local heads, and the local heads' K/V bytes (B * Hkv * min(window + sinks,
+ * max_ctx) * 512) are at least 64 MiB and half the index keys' (B * n_ret * max_ctx * 32), the local
+ * heads' part of rtp_decode_attn goes to side_stream instead (forked from `stream` by
+ * recording ev_fork and waiting for it; joined by recording ev_join there and making
+ * `stream` wait for it before the merge), so it overlaps the index kernel; the caller owns
+ * the streams and the events (hipEvent_t as void*, created without timing).  The outputs
+ * equal those of the separate calls rtp_index_topp, rtp_sparse_attn_split,
+ * rtp_split_reduce and rtp_local_window_attn either way.  Every argument is checked before
+ * anything is enqueued; after that it returns the first failing call's status.
  *
  *   k_tokens           0: the top-p rule with top_p (rtp_index_topp); > 0: the static top-k
  *                      rule with this budget (rtp_index_topk; top_p may then be NULL)
@@ -356,7 +362,7 @@ rtp_status rtp_decode_step(const void* q_pre, const void* w_q, const void* k_idx
                            float* o_part, float* lse_part, float* out,
                            void* ws_index, size_t ws_index_bytes, void* ws_local, size_t ws_local_bytes,
                            const int* kv_slot, int n_full, const void* k_ring, const void* v_ring, int n_ring,
-                           void* stream);
+                           void* stream, void* side_stream, void* ev_fork, void* ev_join);
 
 /*
  * rtp_decode_step for callers that cannot allocate or pass workspaces (code under HIP
@@ -373,7 +379,7 @@ rtp_status rtp_decode_step(const void* q_pre, const void* w_q, const void* k_idx
  * fill kernel on `stream` at the first call on a device and whenever ceil(max_ctx / block)
  * changes; it keeps its per-head state between calls otherwise.  Every call on a GPU
  * shares that GPU's array: calls that overlap on one GPU (other streams, other host
- * threads) race and must be serialized by the caller.  The index workspace's status words
+ * threads) race and must be serialized by the caller.  It runs on `stream` alone.  The index workspace's status words
  * are not reported by this entry point (a head whose wait ran out still selects every
  * block).  Outputs sel_idx, sel_cnt, sel_mask and out as in rtp_decode_step.
  */

@@ -41,7 +41,7 @@ _SIGS = {
     "rtp_local_window_workspace_size": ([_i] * 7, _sz),
     "rtp_local_window_attn": ([_vp] * 5 + [_i] * 7 + [_vp, _vp, _sz, _vp, _i, _vp, _vp, _i, _vp], _i),
     "rtp_decode_step": ([_vp] * 10 + [_i] * 11 + [_vp] * 6 + [_vp, _sz, _vp, _sz] + [_vp, _i, _vp, _vp, _i]
-                        + [_vp], _i),
+                        + [_vp] * 4, _i),
     "rtp_decode_attn": ([_vp] * 9 + [_i] * 10 + [_vp] * 3 + [_sz, _vp, _i, _vp, _vp, _i, _vp], _i),
     "rtp_decode_merge": ([_vp] * 4 + [_i] * 9 + [_vp, _sz, _vp, _vp], _i),
     "rtp_decode_step_noalloc_limit": ([], _sz),

@@ -68,13 +68,36 @@ extern "C" rtp_status rtp_decode_step(
     int k_tokens, int B, int Hq, int Hkv, int n_ret, int n_loc, int max_ctx, int block, int split_tokens, int window,
     int sinks, int* sel_idx, int* sel_cnt, unsigned char* sel_mask, float* o_part, float* lse_part, float* out,
     void* ws_index, size_t ws_index_bytes, void* ws_local, size_t ws_local_bytes, const int* kv_slot,
-    int n_full, const void* k_ring, const void* v_ring, int n_ring, void* stream) {
+    int n_full, const void* k_ring, const void* v_ring, int n_ring, void* stream, void* side_stream, void* ev_fork,
+    void* ev_join) {
   const rtp_status chk = check_step(q_pre, w_q, k_idx, q, k_cache, v_cache, seq_lens, ret_heads, loc_heads, top_p,
                                     k_tokens, B, Hq, Hkv, n_ret, n_loc, max_ctx, block, split_tokens, window, sinks,
                                     sel_idx, sel_cnt, o_part, lse_part, out, ws_index, ws_index_bytes, ws_local,
                                     ws_local_bytes, kv_slot, n_full, k_ring, v_ring, n_ring);
   if (chk != RTP_OK) return chk;
+  // The local heads go to side_stream, overlapping the index kernel, when their window
+  // bytes are at least 64 MiB and at least half the index keys' bytes (then they fill the
+  // index kernel's selection tail and share its HBM time, and the step is long enough to
+  // hide the events' host cost); otherwise everything runs on `stream`, the local heads'
+  // workgroups in the attention launch after the split attention's, and no event is
+  // recorded (a fork and join cost tens of microseconds of host time).
+  const double index_bytes = (double)B * n_ret * max_ctx * 32.0;
+  const double local_bytes = (double)B * Hkv * (double)(window + sinks < max_ctx ? window + sinks : max_ctx) * 512.0;
+  const bool fork = n_ret > 0 && n_loc > 0 && side_stream && ev_fork && ev_join && 2.0 * local_bytes >= index_bytes &&
+                    local_bytes >= 67108864.0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
   rtp_status st = RTP_OK;
+  if (fork) {
+    hipStream_t ls = static_cast<hipStream_t>(side_stream);
+    if (hipEventRecord(static_cast<hipEvent_t>(ev_fork), s) != hipSuccess ||
+        hipStreamWaitEvent(ls, static_cast<hipEvent_t>(ev_fork), 0) != hipSuccess)
+      return RTP_ELAUNCH;
+    st = rtp_decode_attn(q, k_cache, v_cache, seq_lens, nullptr, nullptr, nullptr, nullptr, loc_heads, B, Hq, Hkv, 0,
+                         n_loc, max_ctx, block, split_tokens, window, sinks, nullptr, nullptr, ws_local, ws_local_bytes,
+                         kv_slot, n_full, k_ring, v_ring, n_ring, ls);
+    if (st != RTP_OK) return st;
+    if (hipEventRecord(static_cast<hipEvent_t>(ev_join), ls) != hipSuccess) return RTP_ELAUNCH;
+  }
   if (n_ret > 0)
     st = k_tokens > 0 ? rtp_index_topk(q_pre, w_q, k_idx, seq_lens, ret_heads, k_tokens, B, Hq, n_ret, max_ctx,
                                        block, sel_idx, sel_cnt, sel_mask, ws_index, ws_index_bytes, stream)
@@ -82,8 +105,9 @@ extern "C" rtp_status rtp_decode_step(
                                        sel_idx, sel_cnt, sel_mask, ws_index, ws_index_bytes, stream);
   if (st == RTP_OK)
     st = rtp_decode_attn(q, k_cache, v_cache, seq_lens, ret_heads, sel_idx, sel_cnt, sel_mask, loc_heads, B, Hq, Hkv,
-                         n_ret, n_loc, max_ctx, block, split_tokens, window, sinks, o_part, lse_part, ws_local,
-                         ws_local_bytes, kv_slot, n_full, k_ring, v_ring, n_ring, stream);
+                         n_ret, fork ? 0 : n_loc, max_ctx, block, split_tokens, window, sinks, o_part, lse_part,
+                         ws_local, ws_local_bytes, kv_slot, n_full, k_ring, v_ring, n_ring, stream);
+  if (fork && hipStreamWaitEvent(s, static_cast<hipEvent_t>(ev_join), 0) != hipSuccess) return RTP_ELAUNCH;
   if (st == RTP_OK)
     st = rtp_decode_merge(o_part, lse_part, ret_heads, loc_heads, B, Hq, Hkv, n_ret, n_loc, max_ctx, split_tokens,
                           window, sinks, ws_local, ws_local_bytes, out, stream);
@@ -190,5 +214,5 @@ extern "C" rtp_status rtp_decode_step_noalloc(
                          Hq, Hkv, n_ret, n_loc, max_ctx, block, split_tokens, window, sinks, sel_idx, sel_cnt,
                          sel_mask, n_ret > 0 ? o_part : nullptr, n_ret > 0 ? lse_part : nullptr, out,
                          n_ret > 0 ? idx_ws : nullptr, ws_index, n_loc > 0 ? loc_ws : nullptr, ws_local, kv_slot,
-                         n_full, k_ring, v_ring, n_ring, stream);
+                         n_full, k_ring, v_ring, n_ring, stream, nullptr, nullptr, nullptr);
 }

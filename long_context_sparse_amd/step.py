@@ -2,7 +2,8 @@
 
 DecodeStep owns the device buffers the calls need (selected-block lists and masks,
 split partials, workspaces, output) and issues them through one rtp_decode_step call,
-three launches on the current stream:
+three launches on the current stream (the local heads' part on a second stream when
+their bytes are comparable to the index keys'):
 
   rtp_index_topp (or rtp_index_topk)   retrieval heads: scores and block selection
   rtp_decode_attn                      retrieval heads' split attention + local heads' window
@@ -53,9 +54,12 @@ class StepShape:
 
 
 class DecodeStep:
-    def __init__(self, shape: StepShape, device: str = "cuda", use_mask: bool = True, k_tokens: int = 0):
+    def __init__(self, shape: StepShape, device: str = "cuda", use_mask: bool = True, k_tokens: int = 0,
+                 overlap: bool = True):
         """k_tokens = 0: the top-p rule (the inputs' top_p); > 0: the static top-k rule
-        with this budget in tokens."""
+        with this budget in tokens.  overlap: give rtp_decode_step a second stream and two
+        events, which it uses when the local heads' bytes are comparable to the index
+        keys' (False: one stream always)."""
         self.s = shape
         self.k_tokens = int(k_tokens)
         dev = torch.device(device)
@@ -77,6 +81,10 @@ class DecodeStep:
                if s.n_loc else 0)
         self.ws_index = torch.zeros(max(ws1, 256), dtype=torch.uint8, device=dev)
         self.ws_local = torch.zeros(max(ws2, 256), dtype=torch.uint8, device=dev)
+        self.overlap = overlap and s.n_loc > 0 and s.n_ret > 0
+        self.side = torch.cuda.Stream(device=dev) if self.overlap else None
+        self._fork = abi.event_create() if self.overlap else None
+        self._join = abi.event_create() if self.overlap else None
         self._key = None
         self._vals = None
         self._step_fn = abi.lib().rtp_decode_step
@@ -145,6 +153,7 @@ class DecodeStep:
         s = self.s
         p = abi.device_ptr
         z = lambda name: p(t[name]) if t[name].numel() else None  # noqa: E731
+        side = self.side.cuda_stream if self.overlap else None
         pl = self.placement(t)
         o = lambda x: None if x is None else p(x)  # noqa: E731
         return (z("q_pre") if s.n_ret else None, z("w_q") if s.n_ret else None, z("k_idx") if s.n_ret else None,
@@ -155,7 +164,7 @@ class DecodeStep:
                 p(self.sel_mask) if self.sel_mask is not None else None, p(self.o_part), p(self.lse_part),
                 p(self.out), p(self.ws_index), abi.nbytes(self.ws_index), p(self.ws_local),
                 abi.nbytes(self.ws_local), o(pl["kv_slot"]), pl["n_full"], o(pl["k_ring"]), o(pl["v_ring"]),
-                pl["n_ring"], main)
+                pl["n_ring"], main, side, self._fork, self._join)
 
     def __call__(self, t: Dict[str, torch.Tensor]) -> torch.Tensor:
         """Enqueue one decode step on the current stream; returns the fp32 [B, Hq, 128] output.

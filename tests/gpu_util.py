@@ -27,7 +27,7 @@ class Run:
     """One GPU decode step on a workload, with host copies of its outputs."""
 
     def __init__(self, inp: W.DecodeInputs, tensors=None, split_tokens: Optional[int] = None, tag: str = "",
-                 use_mask: bool = True, k_tokens: int = 0):
+                 use_mask: bool = True, k_tokens: int = 0, overlap: bool = True):
         cfg = inp.cfg
         self.inp = inp
         self.k_tokens = k_tokens
@@ -36,7 +36,7 @@ class Run:
             f"split={split_tokens or cfg.split_tokens} window={cfg.window} sinks={cfg.sinks} seed={cfg.seed} "
             f"{'masks' if use_mask else 'lists'}{f' top-k {k_tokens}' if k_tokens else ''}")
         self.t = tensors if tensors is not None else W.to_device(inp)
-        self.step = DecodeStep(shape_of(cfg, split_tokens), use_mask=use_mask, k_tokens=k_tokens)
+        self.step = DecodeStep(shape_of(cfg, split_tokens), use_mask=use_mask, k_tokens=k_tokens, overlap=overlap)
         self.out = self.step(self.t)
         torch.cuda.synchronize()
         self.out_h = self.out.cpu().numpy().astype(np.float64)

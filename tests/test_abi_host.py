@@ -154,7 +154,7 @@ def test_cache_append_rejects():
 def test_decode_step_rejects():
     L = abi.lib()
     args = [FAKE] * 10 + [0] + [1, 8, 2, 2, 6, 4096, 64, 1024, 1024, 4] + [FAKE] * 6 + \
-        [FAKE, 1 << 30, FAKE, 1 << 30] + [None, 0, None, None, 0] + [None]
+        [FAKE, 1 << 30, FAKE, 1 << 30] + [None, 0, None, None, 0] + [None] * 4
     bad = list(args)
     bad[11] = 0                                        # B = 0
     assert L.rtp_decode_step(*bad) == abi.RTP_EINVAL

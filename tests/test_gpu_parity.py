@@ -256,18 +256,21 @@ def test_block_masks_match_lists_and_give_the_same_partials():
     assert torch.equal(l2, m.step.lse_part)
 
 
-@pytest.mark.parametrize("n_ret,n_loc_all", [(3, False), (0, True), (8, False)])
-def test_step_matches_the_four_calls(n_ret, n_loc_all):
+@pytest.mark.parametrize("n_ret,window,overlap", [(3, 8192, True), (3, 8192, False), (3, 600, True),
+                                                  (0, 8192, True), (32, 600, True)])
+def test_step_matches_the_four_calls(n_ret, window, overlap):
     """rtp_decode_step (index, one attention launch for both head kinds, one merge) against
     the four separate calls rtp_index_topp, rtp_sparse_attn_split, rtp_split_reduce and
     rtp_local_window_attn: the same block sets and the same output bits, with both head
-    kinds, with no retrieval heads, and with no local heads; both against the oracle."""
-    cfg = W.custom_config(name=f"calls{n_ret}", B=2, Hkv=2, Hq=8, n_ret=n_ret, ctx=(7000, 3001), block=64, window=600,
-                          sinks=4, split_tokens=512, kind="peaked_diffuse")
+    kinds (the local heads on the second stream: window 8192 over 8 KV heads and 2
+    sequences, 67 MB of K/V; or in the attention launch: window 600, or no second stream
+    given), with no retrieval heads, and with no local heads; both against the oracle."""
+    cfg = W.custom_config(name=f"calls{n_ret}", B=2, Hkv=8, Hq=32, n_ret=n_ret, ctx=(20000, 9001), block=64,
+                          window=window, sinks=4, split_tokens=1024, kind="peaked_diffuse")
     inp = W.make_inputs(cfg)
     t = W.to_device(inp)
-    step = Run(inp, tensors=t, tag=f"step n_ret={n_ret}")
-    calls = DecodeStep(step.step.s)
+    step = Run(inp, tensors=t, tag=f"step n_ret={n_ret} window={window} overlap={overlap}", overlap=overlap)
+    calls = DecodeStep(step.step.s, overlap=False)
     out = torch.full_like(calls.out, float("nan"))
     calls.out = out
     if cfg.n_ret:
