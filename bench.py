@@ -143,10 +143,15 @@ def kernel_source_hash(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
+def traffic_file(label: str, kernel: str) -> str:
+    """File name of the counter summary of `kernel` on workload `label` ("@" -> "_")."""
+    return f"{kernel}_{label.replace('@', '_')}_traffic.md"
+
+
 def read_traffic(workload: str, kernel: str) -> Optional[float]:
     """HBM bytes per launch of `kernel` from the committed counter summary, or None
     when there is none or it was taken on other kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"{KERNEL_NAMES.get(kernel, kernel)}_{workload}_traffic.md")
+    path = os.path.join(ROOT, "profiles", traffic_file(workload, KERNEL_NAMES.get(kernel, kernel)))
     if not os.path.exists(path):
         return None
     vals = {}
@@ -164,10 +169,28 @@ def read_traffic(workload: str, kernel: str) -> Optional[float]:
 
 
 # ------------------------------------------------------------------ GPU measurement
+_SLEEP_CYCLES_PER_US: List[float] = []
+
+
+def gpu_wait(us: float) -> None:
+    """Occupies the current stream for about `us` microseconds (torch's spin kernel,
+    calibrated once), so that launches enqueued behind it start back to back."""
+    import torch
+    if not _SLEEP_CYCLES_PER_US:
+        torch.cuda._sleep(1000)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.cuda._sleep(1_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_US.append(1_000_000 / max(a.elapsed_time(b) * 1e3, 1.0))
+    torch.cuda._sleep(int(us * _SLEEP_CYCLES_PER_US[0]))
+
+
 def measure(label: str, steps: int, warmup: int, cold_iters: int, calib_copy: bool, minimal: bool = False) -> Dict:
     """One workload; label = a workload name, optionally with "@topkK" (static top-k rule,
-    budget K tokens).  minimal: only the warm-up and the timed steps (for profiler runs
-    whose traces should hold the step's kernels alone)."""
+    budget K tokens).  minimal: only the warm-up, the timed steps and the per-launch timing
+    (for profiler runs whose traces should hold the step's kernels alone)."""
     import torch
 
     import workloads as W
@@ -212,33 +235,43 @@ def measure(label: str, steps: int, warmup: int, cold_iters: int, calib_copy: bo
     per_step_us = [evs_step[i].elapsed_time(evs_step[i + 1]) * 1e3 for i in range(steps)]
     log(f"[bench] {label}: {steps} steps, {ms_per_step * 1e3:.1f} us/step (median {np.median(per_step_us):.1f}, "
         f"host {wall * 1e6 / steps:.1f} us/step)")
-    if minimal:
-        res = dict(workload=name, label=label, k_tokens=k_tokens, cfg=cfg, inp=inp, alg=alg, latency_us=ms_per_step * 1e3,
-                   per_step_us=per_step_us, wall_us=wall * 1e6 / steps, kern_us={}, dominant=None, append_us=None,
-                   cold_us=None, dense_us=None, gbs=alg["step"] / (ms_per_step * 1e-3) / 1e9, sel_frac=None)
-        del step, t
-        torch.cuda.empty_cache()
-        return res
-
-    # per-launch durations: the step's three launches one after another on the stream the
-    # step runs on, with events around each launch on that stream
+    # per-launch durations: each of the step's three launches repeated back to back on the
+    # stream the step runs on (every launch rewrites the same outputs from the same
+    # inputs), one event pair around each block of `reps` launches.  The block is queued
+    # behind a GPU-side wait long enough for the host to enqueue all of it, so the GPU runs
+    # the launches back to back whatever the host's per-call cost.
     calls = [("index_topk", step.index_topk) if k_tokens else ("index_topp", step.index_topp),
              ("decode_attn", step.attn), ("decode_merge", step.merge)]
     if not cfg.n_ret:
         calls = calls[1:]
-    per = {k: [] for k, _ in calls}
-    iters = max(steps, 20)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(iters)]
-    for it in range(iters):
-        evs[it][0].record(main)
-        for i, (k, f) in enumerate(calls):
+    reps = 20
+    kern_us = {}
+    for k, f in calls:
+        f(t, main)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gpu_wait(reps * 100.0)
+        e0.record(main)
+        for _ in range(reps):
             f(t, main)
-            evs[it][i + 1].record(main)
-    torch.cuda.synchronize()
-    for it in range(iters):
-        for i, (k, _) in enumerate(calls):
-            per[k].append(evs[it][i].elapsed_time(evs[it][i + 1]) * 1e3)
-    kern_us = {k: float(np.mean(v)) for k, v in per.items()}
+        e1.record(main)
+        torch.cuda.synchronize()
+        kern_us[k] = e0.elapsed_time(e1) * 1e3 / reps
+    if calib_copy:
+        # plain device copy of known size, for scaling HBM counters (1 GiB read + 1 GiB written)
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if minimal:
+        res = dict(workload=name, label=label, k_tokens=k_tokens, cfg=cfg, inp=inp, alg=alg, latency_us=ms_per_step * 1e3,
+                   per_step_us=per_step_us, wall_us=wall * 1e6 / steps, kern_us=kern_us,
+                   dominant=max(kern_us, key=kern_us.get), append_us=None, cold_us=None, dense_us=None,
+                   gbs=alg["step"] / (ms_per_step * 1e-3) / 1e9, sel_frac=None)
+        del step, t
+        torch.cuda.empty_cache()
+        return res
 
     # cold caches: a 1 GiB write evicts L2 and the 256 MB last-level cache before each step
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -295,15 +328,6 @@ def measure(label: str, steps: int, warmup: int, cold_iters: int, calib_copy: bo
     torch.cuda.synchronize()
     dense_us = d0.elapsed_time(d1) * 1e3 / 10
     del ws_d, out_d
-
-    if calib_copy:
-        # plain device copy of known size, for scaling HBM counters (1 GiB read + 1 GiB written)
-        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
 
     lat_us = ms_per_step * 1e3
     dom = max(kern_us, key=kern_us.get)
@@ -583,7 +607,8 @@ def main(argv: Optional[List[str]] = None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stream-ceiling", action="store_true")
     ap.add_argument("--minimal", action="store_true",
-                    help="only the warm-up and timed steps of each workload (for profiler runs)")
+                    help="per workload only the warm-up, the timed steps and the per-launch timing, and the "
+                         "prefill passes asked for (for profiler runs)")
     ap.add_argument("--calib-copy", action="store_true", help="also run a 1 GiB device copy (counter scaling)")
     a = ap.parse_args(argv)
     if a.gpus != 1:
@@ -599,16 +624,18 @@ def main(argv: Optional[List[str]] = None) -> int:
     extras = {}
     for name in [x for x in a.also.split(",") if x and x != a.workload]:
         extras[name] = measure(name, a.steps, a.warmup, a.cold_iters, False, a.minimal)
-    if a.minimal:
-        print(json.dumps({"minimal": True, **{r["label"]: {"latency_us": round(r["latency_us"], 2), **step_stats(r)}
-                                               for r in [head, *extras.values()]}}), flush=True)
-        return 0
-
-    ceiling = None if a.no_stream_ceiling else stream_ceiling()
-
     prefill = {}
     for n in [int(x) for x in a.prefill.split(",") if x]:
         prefill[f"prefill{n // 1024}k"] = measure_prefill(n, 5 if n <= 65536 else 2, dense_too=n <= 65536)
+    if a.minimal:
+        print(json.dumps({"minimal": True, **{r["label"]: {
+            "latency_us": round(r["latency_us"], 2), "per_step": step_stats(r),
+            "call_us": {CALL_NAMES[k]: round(v, 2) for k, v in r["kern_us"].items()},
+            "alg_bytes": {CALL_NAMES[k]: int(r["alg"][k]) for k in r["kern_us"]},
+            "roofline": roofline_of(r)} for r in [head, *extras.values()]}, "prefill": prefill}), flush=True)
+        return 0
+
+    ceiling = None if a.no_stream_ceiling else stream_ceiling()
 
     cpu = None
     if not a.no_cpu_baseline:

@@ -9,14 +9,18 @@
 // queries of one head (32 per wave) and walks 64-key tiles: all tiles up to the
 // diagonal for a retrieval head, the sink tiles and the window's tiles for a local head
 // (the tiles in between are never loaded).  Each tile is copied to LDS once for all
-// eight waves (four copy K, four copy V).  Per tile and wave:
+// eight waves (four copy K, four copy V); the next tile's loads are in flight over this
+// tile's compute.  Per tile and wave:
 //   S^T = K Q^T   16 v_mfma_f32_32x32x16_bf16 (K from LDS as the A operand, the wave's
 //                 queries held in registers as the B operand), so each lane's
 //                 accumulators belong to one query: the online softmax needs only the
 //                 lane's own values and one exchange with lane ^ 32;
 //   O^T += V^T P^T  16 v_mfma_f32_32x32x16_f16: P^T straight from the S^T accumulators
 //                 (rounded to fp16: p in [0, 1], 11 significant bits), V^T from LDS,
-//                 where the tile is stored transposed and converted to fp16 once.
+//                 where the tile is stored transposed and converted to fp16 once; each
+//                 V^T row's 4-key quads sit at XOR-swizzled slots, so that neither the
+//                 transposing stores (16 lanes on rows 8 apart) nor the operand reads (16
+//                 lanes on consecutive rows) meet twice in an LDS bank.
 // Products of bf16 q and k are exact in the fp32 accumulators; V goes to fp16 exactly
 // for |v| in [2^-14, 65504] (smaller values keep an absolute error below 2^-25; larger
 // ones are out of range).  Rows past a prompt's end are never read (loads clamp to its
@@ -37,7 +41,7 @@ constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kPfM = 32 * kPfWaves;        // queries per workgroup
 constexpr int kPfN = 64;                   // keys per tile
 constexpr int kKStride = kHeadDim + 8;     // bf16 per K row in LDS (272 B: b128 reads spread over banks)
-constexpr int kVStride = kPfN + 4;         // fp16 per V^T row in LDS (136 B)
+constexpr int kVStride = kPfN;             // fp16 per V^T row in LDS (128 B; banks spread by the quad swizzle)
 
 struct PrefillArgs {
   const uint16_t* q;  // bf16 [B, Hq, T, 128]
@@ -64,6 +68,10 @@ __device__ __forceinline__ float sum_pair(float v) {
   const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
+
+// Slot of key quad q (keys 4q .. 4q + 3 of the tile) in V^T row r (dim r): q XOR a
+// function of r that differs between any 16 consecutive rows and between rows 8 apart.
+__device__ __forceinline__ int vslot(int r, int q) { return (q ^ (r >> 3) ^ r) & 15; }
 
 // two waves per SIMD: at most 256 VGPRs a wave
 __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
@@ -117,17 +125,24 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
     const uint16_t* qrow = a.q + (((size_t)b * a.Hq + h) * a.T + min(qi, N - 1)) * kHeadDim + 8 * hi;
 #pragma unroll
     for (int c = 0; c < 8; ++c) qreg[c] = ld16(qrow + 16 * c);
+    // the query rows are waited for here, once: otherwise the compiler's wait for them
+    // inside the loop (vector loads retire in order) would also wait for the next tile's
+    // loads issued just before each tile's MFMAs
+#pragma unroll
+    for (int c = 0; c < 8; ++c) asm volatile("" ::"v"(qreg[c].x), "v"(qreg[c].y), "v"(qreg[c].z), "v"(qreg[c].w));
   }
 
-  // tile copies: waves 4-7 move K (1024 chunks of 16 B, 4 a thread), waves 0-3 move V
-  // (4 keys x 8 dims a thread, stored transposed in fp16)
+  // tile copies: waves 4-7 move K (1024 chunks of 16 B, 4 a thread); waves 0-3 move V,
+  // thread (dim chunk dc = ct % 16, key quad kq = ct / 16) taking dims 8 dc .. 8 dc + 7 of
+  // keys 4 kq .. 4 kq + 3 (16 lanes read one 256-byte row), stored transposed in fp16
   constexpr int kCopy = kPfThreads / 2;
   const bool do_k = tid >= kCopy, do_v = tid < kCopy;
   const int ct = tid & (kCopy - 1);
+  const int dc = ct & 15, kq = ct >> 4;
   uint4 kreg[4], vreg[4];
+  auto tile_of = [&](int t) { return t < n0 ? t : r1b + (t - n0); };
   auto gload = [&](int t) {
-    const int kt = t < n0 ? t : r1b + (t - n0);
-    const int key0 = kt * kPfN;
+    const int key0 = tile_of(t) * kPfN;
     if (do_k) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -138,9 +153,9 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
     }
     if (do_v) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {  // keys 4 (ct / 16) + e, dims 8 (ct % 16) + 0..7
-        const int key = min(key0 + 4 * (ct >> 4) + e, N - 1);
-        vreg[e] = ld16(vbase + (size_t)key * kHeadDim + (ct & 15) * 8);
+      for (int e = 0; e < 4; ++e) {
+        const int key = min(key0 + 4 * kq + e, N - 1);
+        vreg[e] = ld16(vbase + (size_t)key * kHeadDim + dc * 8);
       }
     }
   };
@@ -153,7 +168,6 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
       }
     }
     if (do_v) {
-      const int kg = ct >> 4, dc = ct & 15;
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
         f16x4_t hv;
@@ -162,7 +176,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
           const uint32_t w = word(vreg[e], d >> 1);
           hv[e] = (_Float16)((d & 1) ? bf_hi(w) : bf_lo(w));
         }
-        *reinterpret_cast<f16x4_t*>(&sv[(dc * 8 + d) * kVStride + kg * 4]) = hv;
+        const int r = dc * 8 + d;
+        *reinterpret_cast<f16x4_t*>(&sv[r * kVStride + 4 * vslot(r, kq)]) = hv;
       }
     }
   };
@@ -177,90 +192,96 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
 
   if (ntiles > 0) gload(0);
   for (int t = 0; t < ntiles; ++t) {
-    const int kt = t < n0 ? t : r1b + (t - n0);
-    const int key0 = kt * kPfN, key1 = key0 + kPfN - 1;
     __syncthreads();  // the previous tile's LDS reads are done
     lstore();
     __syncthreads();
     if (t + 1 < ntiles) gload(t + 1);  // in flight over this tile's compute
 
+    const int key0 = tile_of(t) * kPfN, key1 = key0 + kPfN - 1;
     // wave-uniform: skip a tile no query of this wave attends to; mask only at edges
     const bool skip = qw0 >= N || key0 > qw1 || (!ret && key0 >= S && key1 <= qw0 - W);
-    if (skip) continue;
-    const bool full = key1 <= qw0 && (ret || key1 < S || key0 > qw1 - W);
+    if (!skip) {
+      const bool full = key1 <= qw0 && (ret || key1 < S || key0 > qw1 - W);
+      const uint16_t* skb = sk;
+      const _Float16* svb = sv;
 
-    f32x16_t s[2];
+      f32x16_t s[2];
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
+      for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
-      const uint16_t* krow = &sk[(32 * sb + (lane & 31)) * kKStride + 8 * hi];
+        for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
+        const uint16_t* krow = &skb[(32 * sb + (lane & 31)) * kKStride + 8 * hi];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const uint4 kv = *reinterpret_cast<const uint4*>(krow + 16 * c);
-        s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv),
-                                                         __builtin_bit_cast(bf16x8_t, qreg[c]), s[sb], 0, 0, 0);
+        for (int c = 0; c < 8; ++c) {
+          const uint4 kv = *reinterpret_cast<const uint4*>(krow + 16 * c);
+          s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv),
+                                                           __builtin_bit_cast(bf16x8_t, qreg[c]), s[sb], 0, 0, 0);
+        }
       }
-    }
-    // lane's scores: key key0 + 32 sb + 8 (r / 4) + 4 hi + r % 4, query qi (raw q.k)
-    // masks as compares of the element's compile-time key offset c (key = kb + c) with
-    // three per-lane bounds: key <= qi, key < S (sink), key > qi - W (window)
-    float mt_ = -INFINITY;
-    if (full) {
+      // lane's scores: key key0 + 32 sb + 8 (r / 4) + 4 hi + r % 4, query qi (raw q.k)
+      // masks as compares of the element's compile-time key offset c (key = kb + c) with
+      // three per-lane bounds: key <= qi, key < S (sink), key > qi - W (window)
+      float mt_ = -INFINITY;
+      if (full) {
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
+        for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mt_ = fmaxf(mt_, s[sb][r]);
-    } else {
-      const int kb = key0 + 4 * hi;
-      const int d_causal = qi - kb, d_win = qi - W - kb, d_sink = S - kb;
+          for (int r = 0; r < 16; ++r) mt_ = fmaxf(mt_, s[sb][r]);
+      } else {
+        const int kb = key0 + 4 * hi;
+        const int d_causal = qi - kb, d_win = qi - W - kb, d_sink = S - kb;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int c = 32 * sb + 8 * (r >> 2) + (r & 3);
+            const bool ok = (c <= d_causal) & (ret | (c < d_sink) | (c > d_win));
+            s[sb][r] = ok ? s[sb][r] : -INFINITY;
+            mt_ = fmaxf(mt_, s[sb][r]);
+          }
+      }
+      mt_ = max_pair(mt_);
+      // rescale only when some query's maximum grew (wave-uniform branch); elsewhere the
+      // factor would be exactly 1
+      if (__ballot(mt_ > m_run) != 0) {
+        const float m_new = fmaxf(m_run, mt_);
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * scale);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
+      }
+      // p = 2^((s - m) scale); nothing attended yet (m = -inf): p = 0 for every key
+      const float msc = m_run == -INFINITY ? 0.f : m_run * scale;
+      float ls = 0.f;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int c = 32 * sb + 8 * (r >> 2) + (r & 3);
-          const bool ok = (c <= d_causal) & (ret | (c < d_sink) | (c > d_win));
-          s[sb][r] = ok ? s[sb][r] : -INFINITY;
-          mt_ = fmaxf(mt_, s[sb][r]);
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[sb][r], scale, -msc));
+          s[sb][r] = p;
+          ls += p;
         }
-    }
-    mt_ = max_pair(mt_);
-    // rescale only when some query's maximum grew (wave-uniform branch); elsewhere the
-    // factor would be exactly 1
-    if (__ballot(mt_ > m_run) != 0) {
-      const float m_new = fmaxf(m_run, mt_);
-      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * scale);
-      m_run = m_new;
-      l_run *= alpha;
+      l_run += ls;
+      // P^T operand of chunk c: keys 16 c + 4 hi + 0..3 and 16 c + 8 + 4 hi + 0..3
+      f16x8_t pb[4];
 #pragma unroll
-      for (int d = 0; d < 4; ++d)
+      for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
-    }
-    // p = 2^((s - m) scale); nothing attended yet (m = -inf): p = 0 for every key
-    const float msc = m_run == -INFINITY ? 0.f : m_run * scale;
-    float ls = 0.f;
+        for (int u = 0; u < 8; ++u) pb[c][u] = (_Float16)s[c >> 1][8 * (c & 1) + u];
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
+      for (int c = 0; c < 4; ++c) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[sb][r], scale, -msc));
-        s[sb][r] = p;
-        ls += p;
-      }
-    l_run += ls;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      f16x8_t pb;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) pb[u] = (_Float16)s[c >> 1][8 * (c & 1) + u];
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const _Float16* vrow = &sv[(32 * d + (lane & 31)) * kVStride + 16 * c + 4 * hi];
-        const f16x4_t lo = *reinterpret_cast<const f16x4_t*>(vrow);
-        const f16x4_t up = *reinterpret_cast<const f16x4_t*>(vrow + 8);
-        const f16x8_t av = {lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
-        acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb, acc[d], 0, 0, 0);
+        for (int d = 0; d < 4; ++d) {
+          const int r = 32 * d + (lane & 31);
+          const _Float16* vrow = &svb[r * kVStride];
+          const f16x4_t lo = *reinterpret_cast<const f16x4_t*>(vrow + 4 * vslot(r, 4 * c + hi));
+          const f16x4_t up = *reinterpret_cast<const f16x4_t*>(vrow + 4 * vslot(r, 4 * c + 2 + hi));
+          const f16x8_t av = {lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+          acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb[c], acc[d], 0, 0, 0);
+        }
       }
     }
   }
