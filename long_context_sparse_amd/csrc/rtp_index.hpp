@@ -711,12 +711,54 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int b, 
     failed = __syncthreads_or(!ok) != 0;
   }
 
-  // ---- threshold key: block j is selected iff key_of(m_j, j) >= thr
+  // ---- threshold key: block j is selected iff key_of(m_j, j) >= thr.  A block below the
+  // floor is never a candidate and its key lies below every candidate's, so the test
+  // holds for every block.
+  int* out = a.sel_idx + head * a.nblk_max;
+  uint8_t* mask = a.sel_mask ? a.sel_mask + head * a.nblk_max : nullptr;
+  const uint64_t P = count ? (uint64_t)kb : (uint64_t)ceil(ldexp((double)p, 62));
+  const int ncand = sm.ncand;  // written before the last barrier: uniform
   uint64_t thr = 0;
   bool all = true;
-  int nc = 0;
-  if (pick && !failed) {
-    const uint64_t P = count ? (uint64_t)kb : (uint64_t)ceil(ldexp((double)p, 62));
+  if (pick && !failed && ncand <= kFinal) {
+    // few candidates (the usual case): wave 0 ranks them exactly, one a lane (the mass of
+    // the larger keys decides, as in the last level of the general search), writes the
+    // selected ids in ascending order and their count, and leaves the threshold for the
+    // mask pass; no crossing (total below p) selects every block
+    if (wave == 0) {
+      const bool v = lane < ncand;
+      const int j = v ? (int)cand[lane] : 0;
+      const uint32_t bits = v ? __float_as_uint(s_mass[j]) : 0u;
+      const uint64_t my = v ? key_of(__uint_as_float(bits), j) : 0ull;
+      const uint64_t f = v ? (count ? 1ull : fixed_bits(bits)) : 0ull;
+      uint64_t above = 0;
+      for (int i = 0; i < ncand; ++i) {
+        const uint64_t ki = readlane_u64(my, i), fi = readlane_u64(f, i);
+        above += ki > my ? fi : 0ull;
+      }
+      const uint64_t cb = __ballot(v && above < P && above + f >= P);
+      if (cb) {
+        const uint64_t t = readlane_u64(my, __ffsll((long long)cb) - 1);
+        const bool sl = v && my >= t;
+        const uint64_t sb = __ballot(sl);
+        int rank = 0;  // selected ids below this one
+        for (uint64_t m = sb; m; m &= m - 1) rank += __builtin_amdgcn_readlane(j, __ffsll((long long)m) - 1) < j;
+        if (sl) out[rank] = j;
+        if (lane == 0) {
+          sm.thr = t;
+          sm.found = 1;
+          sm.total = (int)__popcll(sb);
+        }
+      }
+    }
+    __syncthreads();
+    if (sm.found) {
+      all = false;
+      thr = uni64(sm.thr);
+      if (mask)
+        for (int j = tid; j < nblk; j += T) mask[j] = key_of(s_mass[j], j) >= thr;
+    }
+  } else if (pick && !failed) {
     if (wave == 0) {
       scan_level(0, P, lo1, 0xFFFFFFFFu, shift1, sm);
       // the pruned blocks were not counted: the candidates start at the floor
@@ -725,32 +767,31 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int b, 
     __syncthreads();
     if (sm.found) {  // else the total mass is below p: every block
       all = false;
-      nc = sm.ncand;
-      thr = select_threshold<T>(s_mass, cand, nc, nblk, P, sm, count);
+      thr = select_threshold<T>(s_mass, cand, ncand, nblk, P, sm, count);
+      // ordered compaction of the selected ids (ascending): a bitmap of them in block
+      // order, one ballot per 64 blocks (no atomics), its word prefixes, then the writes
+      for (int i = 0; i < rows; ++i) {
+        const int j = i * T + tid;
+        const uint64_t bal = __ballot(j < nblk && key_of(s_mass[j], j) >= thr);
+        const int w0 = (i * T + wave * kWave) >> 5;
+        if (lane == 0) sm.sel[w0] = (uint32_t)bal;
+        if (lane == 32) sm.sel[w0 + 1] = (uint32_t)(bal >> 32);
+      }
+      __syncthreads();
+      if (wave == 0) bitmap_prefix_wave(sm.sel, ceil_div(nblk, 32), sm);
+      __syncthreads();
+      for (int j = tid; j < nblk; j += T) {
+        const bool sl = (sm.sel[j >> 5] >> (j & 31)) & 1u;
+        if (sl) out[bitmap_rank(sm.sel, j, sm)] = j;
+        if (mask) mask[j] = sl;
+      }
     }
   }
-
-  // ---- ordered compaction of the selected ids (ascending), from a bitmap of them
-  int* out = a.sel_idx + head * a.nblk_max;
-  uint8_t* mask = a.sel_mask ? a.sel_mask + head * a.nblk_max : nullptr;
   if (all) {
     select_all<T>(a, head, nblk);
     if (failed && tid == 0) {
       atomicOr(&a.hdr->status, (uint32_t)RTP_INDEX_WAIT_EXPIRED);
       atomicAdd(&a.hdr->fallbacks, 1u);
-    }
-  } else {
-    for (int k = tid; k < nc; k += T) {
-      const int j = cand[k];
-      if (key_of(s_mass[j], j) >= thr) atomicOr(&sm.sel[j >> 5], 1u << (j & 31));
-    }
-    __syncthreads();
-    if (wave == 0) bitmap_prefix_wave(sm.sel, ceil_div(nblk, 32), sm);
-    __syncthreads();
-    for (int j = tid; j < nblk; j += T) {
-      const bool sl = (sm.sel[j >> 5] >> (j & 31)) & 1u;
-      if (sl) out[bitmap_rank(sm.sel, j, sm)] = j;
-      if (mask) mask[j] = sl;
     }
   }
   if (tid == 0) {
