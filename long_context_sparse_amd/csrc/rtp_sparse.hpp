@@ -44,12 +44,14 @@ struct LocalSmem {
   float acc[kAttnWaves * G * kHeadDim];
 };
 
-// Window split of the local heads: >= ~1024 workgroups over the batch, 64..4096 tokens a
-// split; split 0 holds the sinks, so there are 1 + ceil(window / split) splits.
+// Window split of the local heads: >= ~1024 workgroups over the batch where splits of at
+// least 128 tokens allow (a shorter split leaves each wave one 16-token sub-tile and the
+// merge more partials than it saves), 128..4096 tokens a split; split 0 holds the sinks,
+// so there are 1 + ceil(window / split) splits.
 inline int local_split_tokens(int B, int Hkv, int window) {
   const long long groups = (long long)B * Hkv;
   int st = 4096;
-  while (st > 64 && groups * ceil_div(window > 1 ? window : 1, st) < 1024) st >>= 1;
+  while (st > 128 && groups * ceil_div(window > 1 ? window : 1, st) < 1024) st >>= 1;
   return st;
 }
 
