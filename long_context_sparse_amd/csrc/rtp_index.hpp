@@ -720,6 +720,7 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int b, 
   const int ncand = sm.ncand;  // written before the last barrier: uniform
   uint64_t thr = 0;
   bool all = true;
+  int nsel = 0;  // selected blocks (read by thread 0)
   if (pick && !failed && ncand <= kFinal) {
     // few candidates (the usual case): wave 0 ranks them exactly, one a lane (the mass of
     // the larger keys decides, as in the last level of the general search), writes the
@@ -755,6 +756,7 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int b, 
     if (sm.found) {
       all = false;
       thr = uni64(sm.thr);
+      nsel = sm.total;
       if (mask)
         for (int j = tid; j < nblk; j += T) mask[j] = key_of(s_mass[j], j) >= thr;
     }
@@ -768,22 +770,42 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int b, 
     if (sm.found) {  // else the total mass is below p: every block
       all = false;
       thr = select_threshold<T>(s_mass, cand, ncand, nblk, P, sm, count);
-      // ordered compaction of the selected ids (ascending): a bitmap of them in block
-      // order, one ballot per 64 blocks (no atomics), its word prefixes, then the writes
+      // ordered compaction of the selected ids (ascending): one ballot per unit of 64
+      // blocks (row i, wave w: blocks i T + 64 w ..) into a bitmap, no atomics; then every
+      // wave scans the units' counts itself (lane l holds units 4 l .. 4 l + 3) and writes
+      // its own units' ids at their ranks, so no further barrier is needed
+      constexpr int W = T / kWave;
       for (int i = 0; i < rows; ++i) {
         const int j = i * T + tid;
         const uint64_t bal = __ballot(j < nblk && key_of(s_mass[j], j) >= thr);
-        const int w0 = (i * T + wave * kWave) >> 5;
+        const int w0 = 2 * (i * W + wave);
         if (lane == 0) sm.sel[w0] = (uint32_t)bal;
         if (lane == 32) sm.sel[w0 + 1] = (uint32_t)(bal >> 32);
       }
       __syncthreads();
-      if (wave == 0) bitmap_prefix_wave(sm.sel, ceil_div(nblk, 32), sm);
-      __syncthreads();
-      for (int j = tid; j < nblk; j += T) {
-        const bool sl = (sm.sel[j >> 5] >> (j & 31)) & 1u;
-        if (sl) out[bitmap_rank(sm.sel, j, sm)] = j;
-        if (mask) mask[j] = sl;
+      static_assert(4 * kWave * 2 >= kBitWords, "a wave's lanes cover every unit");
+      const int nunits = rows * W;
+      uint32_t uc[4], v = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int u = 4 * lane + k;
+        uc[k] = u < nunits ? (uint32_t)(__popc(sm.sel[2 * u]) + __popc(sm.sel[2 * u + 1])) : 0u;
+        v += uc[k];
+      }
+      const uint32_t incl = wave_incl_scan_u32(v);
+      const uint32_t excl = incl - v;
+      nsel = (int)__builtin_amdgcn_readlane(incl, 63);
+      for (int i = 0; i < rows; ++i) {
+        const int u = i * W + wave, ul = u >> 2, uk = u & 3;  // held by lane ul, slot uk
+        const uint32_t pre = __builtin_amdgcn_readlane(excl, ul) +
+                             (uk > 0 ? __builtin_amdgcn_readlane(uc[0], ul) : 0u) +
+                             (uk > 1 ? __builtin_amdgcn_readlane(uc[1], ul) : 0u) +
+                             (uk > 2 ? __builtin_amdgcn_readlane(uc[2], ul) : 0u);
+        const uint64_t bal = ((uint64_t)sm.sel[2 * u + 1] << 32) | sm.sel[2 * u];
+        const int j = i * T + tid;
+        const bool sl = (bal >> lane) & 1ull;
+        if (sl) out[pre + (uint32_t)__popcll(bal & lanemask_lt())] = j;
+        if (mask && j < nblk) mask[j] = sl;
       }
     }
   }
@@ -795,7 +817,7 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int b, 
     }
   }
   if (tid == 0) {
-    if (!all) a.sel_cnt[head] = sm.total;
+    if (!all) a.sel_cnt[head] = nsel;
     __hip_atomic_store(&head_state(a, head)->counter, 0, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
   }

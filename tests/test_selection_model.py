@@ -3,10 +3,11 @@ oracle with the acceptance rule on large, tied and near-tied mass vectors.
 
 The model restates the algorithm the index kernel runs in its last workgroup
 (fp32 block masses, composite keys (mass bits, inverted block id), fixed-point
-masses in 2^-62 units, a first 256-bin level of half-octave bins over all blocks, then
-refinement by 256-bin histograms over the mass bits while more than 64 candidates of
-unequal mass remain, exact ranking of the rest, and the equal-mass case resolved by
-count in ascending block order).  It exercises the algorithm's logic at sizes and
+masses in 2^-62 units; at most 64 candidates above the pruning floor are ranked
+exactly at once; otherwise a first 256-bin level of eighth-octave bins from the
+floor (half-octave bins from 0 without one), then refinement by 256-bin histograms
+over the mass bits while more than 64 candidates of unequal mass remain, exact ranking
+of the rest, and the equal-mass case resolved by count in ascending block order).  It exercises the algorithm's logic at sizes and
 distributions the device sees (up to 16384 blocks) without a GPU; the device code
 itself is covered by the GPU parity tests.
 """
@@ -70,6 +71,18 @@ def model_select(m64, p, prune=True):
     # first level: over the blocks above the pruning floor, built in the same pass as the
     # masses
     floor = prune_floor(p, n) if prune else 0
+    cand_all = [j for j in range(n) if bits[j] >= floor]
+    if len(cand_all) <= FINAL:
+        # few candidates: ranked exactly at once (no crossing: every block)
+        run, thr = 0, None
+        for j in sorted(cand_all, key=lambda j: keys[j], reverse=True):
+            if run < P <= run + fm[j]:
+                thr = keys[j]
+                break
+            run += fm[j]
+        if thr is None:
+            return np.arange(n), 0
+        return np.array(sorted(j for j in cand_all if keys[j] >= thr)), 0
     shift1 = 20 if floor else 22     # eighth-octave bins from the floor, else half-octave from 0
     lo1 = floor & ~((1 << shift1) - 1)
     r = _level(bits, fm, lo1, 0xFFFFFFFF, shift1, 0, P, floor)
