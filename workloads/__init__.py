@@ -136,7 +136,7 @@ def _named() -> Dict[str, DecodeConfig]:
         ret_heads=(0, 1, 2, 3))
     c["ctx32k"] = DecodeConfig(
         name="ctx32k", seed=2, B=1, Hkv=8, Hq=32, n_ret=8, ctx=(32768,), block=64,
-        top_p=(0.95,) * 8, window=1024, sinks=4, split_tokens=4096, kind="needles3x",
+        top_p=(0.95,) * 8, window=1024, sinks=4, split_tokens=2048, kind="needles3x",
         needles=(1, 8))
     # window unspecified for 128K and 1M: the pages' main configuration (8192 + 4 sinks)
     c["ctx128k"] = DecodeConfig(
@@ -147,7 +147,7 @@ def _named() -> Dict[str, DecodeConfig]:
         top_p=(0.95,) * 4, window=8192, sinks=4, split_tokens=65536, kind="depth_needles")
     c["mixed"] = DecodeConfig(
         name="mixed", seed=5, B=16, Hkv=8, Hq=32, n_ret=6, ctx=_mixed_ctx(5), block=64,
-        top_p=_mixed_p(5, 6), window=2048, sinks=4, split_tokens=1024, kind="peaked_diffuse")
+        top_p=_mixed_p(5, 6), window=2048, sinks=4, split_tokens=4096, kind="peaked_diffuse")
     return c
 
 
