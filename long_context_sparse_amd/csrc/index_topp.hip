@@ -1,10 +1,10 @@
 // Kernel 1 of the decode path as its own launch: low-rank index scoring and exact
 // block top-p (the device code and its description are in rtp_index.hpp).
 //
-// gfx950 launch: grid (chunk, retrieval head, sequence), 1024 threads = 16 wave64, one
-// workgroup per compute unit at a time (its registers and LDS allow one), so the chunks
-// are sized for about one workgroup per compute unit and the scoring runs in a single
-// wave of workgroups.  The selecting workgroup of each head runs its passes over blocks
+// gfx950 launch: grid (chunk, retrieval head, sequence), 1024 threads = 16 wave64; the
+// chunks are sized for about one workgroup per compute unit, so the scoring runs in a
+// single wave of workgroups; a larger grid (many heads with long sequences) gets a build
+// that fits two workgroups per unit.  The selecting workgroup of each head runs its passes over blocks
 // on all 16 waves and its serial steps on one.  Each head's tag word lives in its workspace region and is advanced
 // by the head's selecting workgroup at the end of every call.
 
@@ -49,19 +49,23 @@ K1Layout k1_layout(int B, int n_ret, int max_ctx, int block, int target) {
 }
 
 // One index workgroup: chunk c of head (b, r); the last of the head to finish selects.
-template <int BK>
+template <int BK, int WPS>
 __device__ __forceinline__ void index_role(const IndexArgs& a, int c, int r, int b, unsigned char* smem) {
   auto* S = reinterpret_cast<IndexSmem<kIdxThreads>*>(smem);
   const size_t head = (size_t)b * a.n_ret + r;
   if (!index_chunk<BK, kIdxThreads>(a, c, r, b, S)) return;
-  index_select<kIdxThreads>(a, BK, b, head, S);
+  index_select<kIdxThreads, WPS>(a, BK, b, head, S);
   index_advance_tag<kIdxThreads>(a, head, S->tag);
 }
 
-template <int BK>
-__global__ __launch_bounds__(kIdxThreads) void index_topp_kernel(IndexArgs a) {
+// WPS = waves a SIMD must hold: 4 (one workgroup per compute unit, the registers the
+// code wants) for grids of at most one workgroup per unit, 8 (two workgroups per unit,
+// at most 64 VGPRs with a few spilled) for larger grids, whose later workgroups then
+// start while a unit's first one is still scoring or selecting.
+template <int BK, int WPS>
+__global__ __launch_bounds__(kIdxThreads, WPS) void index_topp_kernel(IndexArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  index_role<BK>(a, blockIdx.x, blockIdx.y, blockIdx.z, smem_raw);
+  index_role<BK, WPS>(a, blockIdx.x, blockIdx.y, blockIdx.z, smem_raw);
 }
 
 }  // namespace
@@ -126,10 +130,18 @@ rtp_status index_launch(const void* q_pre, const void* w_q, const void* k_idx, c
                                       dyn);
   if (st != RTP_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (block == 64)
-    hipLaunchKernelGGL(index_topp_kernel<64>, grid, dim3(kIdxThreads), dyn, s, args);
-  else
-    hipLaunchKernelGGL(index_topp_kernel<128>, grid, dim3(kIdxThreads), dyn, s, args);
+  const bool one_wave = (long long)grid.x * grid.y * grid.z <= compute_units();
+  if (block == 64) {
+    if (one_wave)
+      hipLaunchKernelGGL((index_topp_kernel<64, 4>), grid, dim3(kIdxThreads), dyn, s, args);
+    else
+      hipLaunchKernelGGL((index_topp_kernel<64, 8>), grid, dim3(kIdxThreads), dyn, s, args);
+  } else {
+    if (one_wave)
+      hipLaunchKernelGGL((index_topp_kernel<128, 4>), grid, dim3(kIdxThreads), dyn, s, args);
+    else
+      hipLaunchKernelGGL((index_topp_kernel<128, 8>), grid, dim3(kIdxThreads), dyn, s, args);
+  }
   return hipGetLastError() == hipSuccess ? RTP_OK : RTP_ELAUNCH;
 }
 

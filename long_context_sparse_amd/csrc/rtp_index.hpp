@@ -272,8 +272,9 @@ __device__ __forceinline__ void scan_level(uint64_t cab, uint64_t P, uint32_t lo
 // cumulative mass crosses P and takes its bit range as the new range (at least kBins/2
 // times narrower).  It ends when <= kFinal candidates remain (ranked exactly by one wave,
 // one candidate a lane), or when the range is a single mass value: the threshold is then
-// the k-th candidate in ascending block order, k = ceil((P - cab) / mass).
-template <int T>
+// the k-th candidate in ascending block order, k = ceil((P - cab) / mass).  V tells
+// kernel builds with different register budgets apart, so each gets its own copy.
+template <int T, int V>
 __device__ __noinline__ uint64_t select_threshold(const float* __restrict__ sm_m, const uint16_t* __restrict__ cand,
                                                   int nc, int nblk, uint64_t P, TailSmem& sm, bool count) {
   // a block's weight: its fixed-point mass (top-p), or 1 (static top-k: P is then the
@@ -577,8 +578,8 @@ __device__ __forceinline__ bool index_chunk(const IndexArgs& a, int c, int r, in
 // block is selected and the header's status bit and fallback count record it.  Passes
 // over blocks or candidates run on all T threads; the chunk statistics, the bin scans,
 // the final ranking and the bitmap prefix on wave 0 alone, while the other waves wait at
-// the next barrier.
-template <int T>
+// the next barrier.  V: the kernel build (select_threshold).
+template <int T, int V>
 __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int b, size_t head, IndexSmem<T>* S) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int N = a.seq_lens[b];
@@ -769,7 +770,7 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int b, 
     __syncthreads();
     if (sm.found) {  // else the total mass is below p: every block
       all = false;
-      thr = select_threshold<T>(s_mass, cand, ncand, nblk, P, sm, count);
+      thr = select_threshold<T, V>(s_mass, cand, ncand, nblk, P, sm, count);
       // ordered compaction of the selected ids (ascending): one ballot per unit of 64
       // blocks (row i, wave w: blocks i T + 64 w ..) into a bitmap, no atomics; then every
       // wave scans the units' counts itself (lane l holds units 4 l .. 4 l + 3) and writes
