@@ -1,9 +1,10 @@
-// One decode step as a single host call on one stream, three launches: the index call
-// (scoring and selection), the attention launch (block-sparse split attention of the
-// retrieval heads and window attention of the local heads in one grid) and the merge of
-// both kinds of partials.  No second stream and no events: on
-// this part a fork/join of two streams costs tens of microseconds of host time per step,
-// as much as a whole 1M step on the device.
+// One decode step as a single host call, three launches on the caller's stream: the
+// index call (scoring and selection), the attention launch (block-sparse split attention
+// of the retrieval heads and window attention of the local heads in one grid) and the
+// merge of both kinds of partials.  Only when the local heads' window bytes are large does
+// their attention move to a caller-owned second stream, overlapping the index kernel; a
+// fork/join of two streams costs tens of microseconds of host time and a few microseconds
+// of device time per step, as much as a whole 1M step.
 
 #include <mutex>
 
