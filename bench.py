@@ -237,9 +237,10 @@ def measure(label: str, steps: int, warmup: int, cold_iters: int, calib_copy: bo
         f"host {wall * 1e6 / steps:.1f} us/step)")
     # per-launch durations: each of the step's three launches repeated back to back on the
     # stream the step runs on (every launch rewrites the same outputs from the same
-    # inputs), one event pair around each block of `reps` launches.  The block is queued
-    # behind a GPU-side wait long enough for the host to enqueue all of it, so the GPU runs
-    # the launches back to back whatever the host's per-call cost.
+    # inputs), one event pair around each block of `reps` launches, the median of three
+    # blocks.  A block is queued behind a GPU-side wait long enough for the host to
+    # enqueue all of it, so the GPU runs the launches back to back whatever the host's
+    # per-call cost.
     calls = [("index_topk", step.index_topk) if k_tokens else ("index_topp", step.index_topp),
              ("decode_attn", step.attn), ("decode_merge", step.merge)]
     if not cfg.n_ret:
@@ -248,14 +249,17 @@ def measure(label: str, steps: int, warmup: int, cold_iters: int, calib_copy: bo
     kern_us = {}
     for k, f in calls:
         f(t, main)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        gpu_wait(reps * 100.0)
-        e0.record(main)
-        for _ in range(reps):
-            f(t, main)
-        e1.record(main)
-        torch.cuda.synchronize()
-        kern_us[k] = e0.elapsed_time(e1) * 1e3 / reps
+        blocks = []
+        for _ in range(3):  # the median of three blocks (a host stall longer than the wait shows in one)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            gpu_wait(reps * 100.0)
+            e0.record(main)
+            for _ in range(reps):
+                f(t, main)
+            e1.record(main)
+            torch.cuda.synchronize()
+            blocks.append(e0.elapsed_time(e1) * 1e3 / reps)
+        kern_us[k] = float(np.median(blocks))
     if calib_copy:
         # plain device copy of known size, for scaling HBM counters (1 GiB read + 1 GiB written)
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
