@@ -18,9 +18,15 @@
 //   O^T += V^T P^T  16 v_mfma_f32_32x32x16_f16: P^T straight from the S^T accumulators
 //                 (rounded to fp16: p in [0, 1], 11 significant bits), V^T from LDS,
 //                 where the tile is stored transposed and converted to fp16 once; each
-//                 V^T row's 4-key quads sit at XOR-swizzled slots, so that neither the
-//                 transposing stores (16 lanes on rows 8 apart) nor the operand reads (16
-//                 lanes on consecutive rows) meet twice in an LDS bank.
+//                 V^T row's 4-key quads sit at XOR-swizzled slots, so that within 16
+//                 lanes neither the transposing stores (rows 8 apart) nor the operand
+//                 reads (consecutive rows) meet twice in a bank pair.  The LDS has 64
+//                 banks and serves 32 lanes of a b64 access at a time, so both still
+//                 pair up two-way; a layout free of that as well (quad slots
+//                 q ^ (r >> 1) ^ (r >> 3), stores alternating row parity by lane) took
+//                 the conflict counter to zero but cost more VALU than it saved.
+// The MFMAs of each block are scheduled with their LDS operand reads kReadAhead reads
+// ahead (sched_group_barrier), the two score accumulators alternating.
 // Products of bf16 q and k are exact in the fp32 accumulators; V goes to fp16 exactly
 // for |v| in [2^-14, 65504] (smaller values keep an absolute error below 2^-25; larger
 // ones are out of range).  Rows past a prompt's end are never read (loads clamp to its
@@ -42,6 +48,7 @@ constexpr int kPfM = 32 * kPfWaves;        // queries per workgroup
 constexpr int kPfN = 64;                   // keys per tile
 constexpr int kKStride = kHeadDim + 8;     // bf16 per K row in LDS (272 B: b128 reads spread over banks)
 constexpr int kVStride = kPfN;             // fp16 per V^T row in LDS (128 B; banks spread by the quad swizzle)
+constexpr int kReadAhead = 6;             // LDS operand reads in flight ahead of the MFMAs
 
 struct PrefillArgs {
   const uint16_t* q;  // bf16 [B, Hq, T, 128]
@@ -207,17 +214,28 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
 
       f32x16_t s[2];
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
+      for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
-        const uint16_t* krow = &skb[(32 * sb + (lane & 31)) * kKStride + 8 * hi];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
+      for (int c = 0; c < 8; ++c) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          const uint16_t* krow = &skb[(32 * sb + (lane & 31)) * kKStride + 8 * hi];
           const uint4 kv = *reinterpret_cast<const uint4*>(krow + 16 * c);
           s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv),
                                                            __builtin_bit_cast(bf16x8_t, qreg[c]), s[sb], 0, 0, 0);
         }
       }
+      // schedule: the K operand reads run kReadAhead reads ahead of the MFMAs (masks:
+      // 0x100 LDS reads, 0x008 MFMA), so an MFMA rarely waits on the LDS
+      __builtin_amdgcn_sched_group_barrier(0x100, kReadAhead, 0);
+#pragma unroll
+      for (int i = 0; i < 16 - kReadAhead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kReadAhead, 0);
       // lane's scores: key key0 + 32 sb + 8 (r / 4) + 4 hi + r % 4, query qi (raw q.k)
       // masks as compares of the element's compile-time key offset c (key = kb + c) with
       // three per-lane bounds: key <= qi, key < S (sink), key > qi - W (window)
@@ -283,6 +301,14 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(PrefillArgs a) {
           acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb[c], acc[d], 0, 0, 0);
         }
       }
+      // the same for the V operand reads, two per MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kReadAhead, 1);
+#pragma unroll
+      for (int i = 0; i < 16 - kReadAhead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kReadAhead, 1);
     }
   }
 
