@@ -218,23 +218,28 @@ def measure(label: str, steps: int, warmup: int, cold_iters: int, calib_copy: bo
         alg["index_topk"] = alg.pop("index_topp")
 
     # timed region: `steps` back-to-back decode steps, inputs resident in HBM, with an
-    # event between consecutive steps on the stream they run on (per-step durations)
+    # event between consecutive steps on the stream they run on (per-step durations).
+    # The steps are queued behind a spin of ~60 us a step, so the GPU runs them back to
+    # back: the events time the GPU's work, and a host stall while queueing (or a host
+    # slower than the step) does not show up as GPU idle time; the host's own queueing
+    # rate is reported beside it.
     main = torch.cuda.current_stream(dev)
     for _ in range(warmup):
         step(t)
     torch.cuda.synchronize()
     evs_step = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    gpu_wait(60.0 * steps)
     w0 = time.perf_counter()
     evs_step[0].record(main)
     for i in range(steps):
         step(t)
         evs_step[i + 1].record(main)
-    torch.cuda.synchronize()
     wall = time.perf_counter() - w0
+    torch.cuda.synchronize()
     ms_per_step = evs_step[0].elapsed_time(evs_step[-1]) / steps
     per_step_us = [evs_step[i].elapsed_time(evs_step[i + 1]) * 1e3 for i in range(steps)]
-    log(f"[bench] {label}: {steps} steps, {ms_per_step * 1e3:.1f} us/step (median {np.median(per_step_us):.1f}, "
-        f"host {wall * 1e6 / steps:.1f} us/step)")
+    log(f"[bench] {label}: {steps} steps, {ms_per_step * 1e3:.1f} us/step (median {np.median(per_step_us):.1f}; "
+        f"host queueing {wall * 1e6 / steps:.1f} us/step)")
     # per-launch durations: each of the step's three launches repeated back to back on the
     # stream the step runs on (every launch rewrites the same outputs from the same
     # inputs), one event pair around each block of `reps` launches, the median of three
@@ -656,6 +661,7 @@ def main(argv: Optional[List[str]] = None) -> int:
         return {"latency_us": round(r["latency_us"], 2), "effective_gbs": round(r["gbs"], 1),
                 "frac_of_peak": round(r["gbs"] / PEAK_HBM_GBS, 4), "alg_bytes": int(r["alg"]["step"]),
                 "per_step": step_stats(r),
+                "host_queueing_us_per_step": round(r["wall_us"], 2),
                 "cold_latency_us": None if r["cold_us"] is None else round(r["cold_us"], 2),
                 "cold_effective_gbs": None if not r["cold_us"] else round(r["alg"]["step"] / r["cold_us"] / 1e3, 1),
                 "call_us": {CALL_NAMES[k]: round(v, 2) for k, v in r["kern_us"].items()},
