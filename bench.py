@@ -592,6 +592,43 @@ def stream_ceiling(gib: float = 4.0, reps: int = 10) -> Dict:
     return out
 
 
+def mfma_ceiling(iters: int = 4096, reps: int = 5) -> Dict:
+    """Back-to-back bf16 32x32x16 MFMAs on every SIMD (rtp_mfma_rate) at a few grid sizes,
+    the best TFLOP/s: with seeded N(0, 1) operands (like the prefill's q and K), the
+    ceiling the MFMA-bound prefill is compared with, and with all-one operands, which the
+    part runs at a higher clock."""
+    import torch
+
+    from long_context_sparse_amd import abi
+
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1234)
+    operands = {"normal": torch.randn((2, 64, 8), generator=g, device="cuda").to(torch.bfloat16),
+                "ones": torch.ones((2, 64, 8), device="cuda", dtype=torch.bfloat16)}
+    res = {}
+    for kind, ops in operands.items():
+        best = 0.0
+        for wgs in (1024, 2048, 4096):
+            out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+            abi.rtp_mfma_rate(ops, out, wgs, iters)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                abi.rtp_mfma_rate(ops, out, wgs, iters)
+            e1.record()
+            torch.cuda.synchronize()
+            flops = wgs * 16.0 * iters * 32768.0 * reps
+            best = max(best, flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+            del out
+        res["bf16_tflops" if kind == "normal" else "bf16_tflops_all_one_operands"] = round(best, 1)
+    res["frac_of_rated_peak"] = round(res["bf16_tflops"] / PEAK_MFMA_TFLOPS, 4)
+    log(f"[bench] MFMA ceiling: {res['bf16_tflops']} TFLOP/s bf16 with N(0,1) operands "
+        f"({res['frac_of_rated_peak']} of the rated {PEAK_MFMA_TFLOPS:.0f}); "
+        f"{res['bf16_tflops_all_one_operands']} with all-one operands")
+    return res
+
+
 def step_stats(r: Dict) -> Dict:
     """Median, 10th and 90th percentile of the per-step durations (µs) and their GB/s."""
     v = np.asarray(r["per_step_us"], dtype=np.float64)
@@ -614,7 +651,7 @@ def main(argv: Optional[List[str]] = None) -> int:
     ap.add_argument("--cold-iters", type=int, default=20)
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-stream-ceiling", action="store_true")
+    ap.add_argument("--no-stream-ceiling", action="store_true", help="skip the measured HBM and MFMA ceilings")
     ap.add_argument("--minimal", action="store_true",
                     help="per workload only the warm-up, the timed steps and the per-launch timing, and the "
                          "prefill passes asked for (for profiler runs)")
@@ -645,6 +682,10 @@ def main(argv: Optional[List[str]] = None) -> int:
         return 0
 
     ceiling = None if a.no_stream_ceiling else stream_ceiling()
+    mceil = None if a.no_stream_ceiling or not prefill else mfma_ceiling()
+    if mceil:
+        for v in prefill.values():
+            v["roofline"]["frac_of_measured_mfma_ceiling"] = round(v["roofline"]["achieved"] / mceil["bf16_tflops"], 4)
 
     cpu = None
     if not a.no_cpu_baseline:
@@ -682,6 +723,7 @@ def main(argv: Optional[List[str]] = None) -> int:
         "roofline": roof(head),
         "cpu_baseline": cpu,
         "stream_ceiling": ceiling,
+        "mfma_ceiling": mceil,
         "detail": summary(head),
         "also": {k: summary(v) for k, v in extras.items()},
         "prefill": prefill,

@@ -461,6 +461,19 @@ rtp_status rtp_prefill_index_keys(const void* k_pre, const void* w_k, const int*
 rtp_status rtp_stream_read(const void* src, size_t bytes, unsigned int* sink, int n_workgroups, int nontemporal,
                            void* stream);
 
+/*
+ * Calibration probe (not part of the path): n_workgroups 256-thread workgroups, each wave
+ * issuing iters x 4 back-to-back v_mfma_f32_32x32x16_bf16 (32768 flops each) on four
+ * independent accumulators, so timing it gives the bf16 MFMA rate the prefill kernel is
+ * compared with (flops = n_workgroups * 16 * iters * 32768).  ops: device bf16 [2][64][8],
+ * 16-byte aligned: lane l's eight A values, then its eight B values, the same in every
+ * wave (the rate depends on the operands' bit patterns, so pass data like the workload's).
+ * out[n_workgroups * 256] (device fp32): each thread's sum of its 64 accumulator elements
+ * (4 x iters x the lane's 16 elements of A B in the MFMA's output layout).
+ * 1 <= n_workgroups <= 65535, 1 <= iters <= 16384; else RTP_EINVAL.
+ */
+rtp_status rtp_mfma_rate(const void* ops, float* out, int n_workgroups, int iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -47,6 +47,7 @@ _SIGS = {
     "rtp_decode_step_noalloc_limit": ([], _sz),
     "rtp_decode_step_noalloc": ([_vp] * 10 + [_i] * 11 + [_vp] * 4 + [_vp, _i, _vp, _vp, _i] + [_vp], _i),
     "rtp_stream_read": ([_vp, _sz, _vp, _i, _i, _vp], _i),
+    "rtp_mfma_rate": ([_vp, _vp, _i, _i, _vp], _i),
     "rtp_cache_append": ([_vp] * 6 + [_i] * 5 + [_vp] * 3 + [_vp, _i, _vp, _vp, _i, _i, _i, _vp], _i),
     "rtp_prefill_attn": ([_vp] * 5 + [_i] * 7 + [_vp, _vp], _i),
     "rtp_prefill_index_keys": ([_vp] * 4 + [_i] * 5 + [_vp, _vp], _i),
@@ -233,6 +234,15 @@ def rtp_stream_read(src, sink, n_workgroups: int, nontemporal: bool = True, stre
     st = lib().rtp_stream_read(_p(src), _nbytes(src), _p(sink), int(n_workgroups), int(bool(nontemporal)),
                                _s(stream))
     _check("rtp_stream_read", st)
+
+
+def rtp_mfma_rate(ops, out, n_workgroups: int, iters: int, stream=None) -> None:
+    """Calibration probe: back-to-back bf16 MFMAs (see rtp.h); `ops` bf16 [2, 64, 8], `out`
+    holds n_workgroups * 256 fp32."""
+    if ops.numel() * ops.element_size() < 2048 or out.numel() < int(n_workgroups) * 256:
+        raise ValueError("rtp_mfma_rate: ops needs 2 x 64 x 8 bf16 and out n_workgroups * 256 values")
+    st = lib().rtp_mfma_rate(_p(ops), _p(out), int(n_workgroups), int(iters), _s(stream))
+    _check("rtp_mfma_rate", st)
 
 
 def rtp_cache_append(k_new, v_new, k_pre, w_k, seq_lens, ret_heads, B, Hq, Hkv, n_ret, max_ctx,

@@ -265,3 +265,17 @@ def test_decode_attn_and_merge_reject():
     assert merge(split=0) == abi.RTP_EINVAL
     assert merge(ws_bytes=16) == abi.RTP_EINVAL
     assert merge(n_ret=0, n_loc=0) == abi.RTP_OK
+
+
+def test_probes_reject():
+    L = abi.lib()
+    F = ctypes.c_void_p(FAKE)
+    assert L.rtp_mfma_rate(None, F, 1, 1, None) == 1
+    assert L.rtp_mfma_rate(F, None, 1, 1, None) == 1
+    assert L.rtp_mfma_rate(ctypes.c_void_p(FAKE + 8), F, 1, 1, None) == 1
+    assert L.rtp_mfma_rate(F, F, 0, 1, None) == 1
+    assert L.rtp_mfma_rate(F, F, 65536, 1, None) == 1
+    assert L.rtp_mfma_rate(F, F, 1, 0, None) == 1
+    assert L.rtp_mfma_rate(F, F, 1, 16385, None) == 1
+    assert L.rtp_stream_read(F, ctypes.c_size_t(24), F, 1, 1, None) == 1
+    assert L.rtp_stream_read(F, ctypes.c_size_t(16), F, 0, 1, None) == 1
