@@ -58,6 +58,34 @@ __device__ __forceinline__ void index_role(const IndexArgs& a, int c, int r, int
   index_advance_tag<kIdxThreads>(a, head, S->tag);
 }
 
+// Grid z is a rank, not a sequence: the workgroups of rank z serve the sequence with the
+// z-th most tokens (ties by index), so a ragged batch's longest sequences, whose chunks and
+// selections take longest, are dispatched first and the grid ends on the short ones.
+// Every workgroup ranks the lengths itself (one round of loads; batches over
+// kIdxOrderMax keep the index order).
+constexpr int kIdxOrderMax = 256;
+
+__device__ __forceinline__ int index_seq_of_rank(const int* __restrict__ seq_lens, int rank) {
+  const int B = gridDim.z;
+  if (B == 1 || B > kIdxOrderMax) return rank;
+  __shared__ int s_len[kIdxOrderMax];
+  __shared__ int s_seq;
+  const int t = threadIdx.x;
+  if (t < B) s_len[t] = seq_lens[t];
+  __syncthreads();
+  if (t < B) {
+    const int lt = s_len[t];
+    int rk = 0;
+    for (int j = 0; j < B; ++j) {
+      const int lj = s_len[j];
+      rk += (lj > lt) | ((lj == lt) & (j < t));
+    }
+    if (rk == rank) s_seq = t;
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(s_seq);
+}
+
 // WPS = waves a SIMD must hold: 4 (one workgroup per compute unit, the registers the
 // code wants) for grids of at most one workgroup per unit, 8 (two workgroups per unit,
 // at most 64 VGPRs with a few spilled) for larger grids, whose later workgroups then
@@ -65,7 +93,12 @@ __device__ __forceinline__ void index_role(const IndexArgs& a, int c, int r, int
 template <int BK, int WPS>
 __global__ __launch_bounds__(kIdxThreads, WPS) void index_topp_kernel(IndexArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  index_role<BK, WPS>(a, blockIdx.x, blockIdx.y, blockIdx.z, smem_raw);
+  // Workgroups go to the XCDs round-robin by linear id, so with chunk = x a chunk index
+  // would land on the same XCD for every head, and a ragged batch (whose short sequences
+  // have only their first chunks) would load the XCDs of the low chunk indices most; the
+  // chunk index is rotated by the head and sequence instead.
+  const int c = (int)((blockIdx.x + blockIdx.y + (size_t)blockIdx.z * gridDim.y) % gridDim.x);
+  index_role<BK, WPS>(a, c, blockIdx.y, index_seq_of_rank(a.seq_lens, blockIdx.z), smem_raw);
 }
 
 }  // namespace
