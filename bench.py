@@ -672,7 +672,7 @@ def main(argv: Optional[List[str]] = None) -> int:
         extras[name] = measure(name, a.steps, a.warmup, a.cold_iters, False, a.minimal)
     prefill = {}
     for n in [int(x) for x in a.prefill.split(",") if x]:
-        prefill[f"prefill{n // 1024}k"] = measure_prefill(n, 5 if n <= 65536 else 2, dense_too=n <= 65536)
+        prefill[f"prefill{n // 1024}k"] = measure_prefill(n, 5 if n <= 65536 else 2, dense_too=n <= 131072)
     if a.minimal:
         print(json.dumps({"minimal": True, **{r["label"]: {
             "latency_us": round(r["latency_us"], 2), "per_step": step_stats(r),
