@@ -171,3 +171,21 @@ def test_tag_wrap_clears_the_words():
         assert host[base:base + 4].view(np.int32)[0] == 0, h  # arrival counter reset
     check_selection(IndexRun(inp, ws, "call with tag 1"))
     assert _header(ws)[HDR_STATUS] == 0
+
+
+@pytest.mark.parametrize("lens,seed", [
+    ((2900, 100, 2900, 1, 1777, 64, 2900, 1, 2900), 46),  # equal lengths: ranked by index
+    (tuple(np.random.default_rng(47).integers(1, 300, size=260)), 47),  # over 256: index order
+])
+def test_ragged_batch_order_serves_every_sequence(lens, seed):
+    """The index grid takes sequences longest first (each workgroup ranks the lengths,
+    ties by index; batches over 256 sequences keep the index order): every (sequence,
+    head) is served exactly once and matches the oracle, with repeated and tiny lengths."""
+    B = len(lens)
+    cfg = _cfg(f"order_b{B}", B, 2, lens, seed)
+    ws = torch.zeros(abi.rtp_index_topp_workspace_size(B, 2, cfg.max_ctx, 64), dtype=torch.uint8, device="cuda")
+    inp = W.make_inputs(cfg)
+    for tag in ("first call", "second call"):
+        run = IndexRun(inp, ws, f"B={B} {tag}")
+        check_selection(run)
+    assert _header(ws)[HDR_STATUS] == 0 and _header(ws)[HDR_FALLBACKS] == 0
