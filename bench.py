@@ -217,29 +217,38 @@ def measure(label: str, steps: int, warmup: int, cold_iters: int, calib_copy: bo
     if k_tokens:
         alg["index_topk"] = alg.pop("index_topp")
 
-    # timed region: `steps` back-to-back decode steps, inputs resident in HBM, with an
-    # event between consecutive steps on the stream they run on (per-step durations).
-    # The steps are queued behind a spin of ~60 us a step, so the GPU runs them back to
-    # back: the events time the GPU's work, and a host stall while queueing (or a host
-    # slower than the step) does not show up as GPU idle time; the host's own queueing
-    # rate is reported beside it.
+    # timed region: `steps` back-to-back decode steps, inputs resident in HBM, between two
+    # events on the stream they run on.  The steps are queued behind a spin of ~60 us a
+    # step, so the GPU runs them back to back: the events time the GPU's work, and a host
+    # stall while queueing (or a host slower than the step) does not show up as GPU idle
+    # time; the host's own queueing rate is reported beside it.  The per-step spread comes
+    # from a second block of `steps` steps with an event after every step: each such event
+    # is a marker packet of its own on the stream (2.5-5 us a step measured), so that block
+    # times the steps plus their markers and gives the distribution, not the mean.
     main = torch.cuda.current_stream(dev)
     for _ in range(warmup):
         step(t)
     torch.cuda.synchronize()
-    evs_step = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     gpu_wait(60.0 * steps)
     w0 = time.perf_counter()
+    ev0.record(main)
+    for i in range(steps):
+        step(t)
+    ev1.record(main)
+    wall = time.perf_counter() - w0
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / steps
+    evs_step = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    gpu_wait(60.0 * steps)
     evs_step[0].record(main)
     for i in range(steps):
         step(t)
         evs_step[i + 1].record(main)
-    wall = time.perf_counter() - w0
     torch.cuda.synchronize()
-    ms_per_step = evs_step[0].elapsed_time(evs_step[-1]) / steps
     per_step_us = [evs_step[i].elapsed_time(evs_step[i + 1]) * 1e3 for i in range(steps)]
-    log(f"[bench] {label}: {steps} steps, {ms_per_step * 1e3:.1f} us/step (median {np.median(per_step_us):.1f}; "
-        f"host queueing {wall * 1e6 / steps:.1f} us/step)")
+    log(f"[bench] {label}: {steps} steps, {ms_per_step * 1e3:.1f} us/step (per-step events: median "
+        f"{np.median(per_step_us):.1f}; host queueing {wall * 1e6 / steps:.1f} us/step)")
     # per-launch durations: each of the step's three launches repeated back to back on the
     # stream the step runs on (every launch rewrites the same outputs from the same
     # inputs), one event pair around each block of `reps` launches, the median of three
@@ -630,12 +639,14 @@ def mfma_ceiling(iters: int = 4096, reps: int = 5) -> Dict:
 
 
 def step_stats(r: Dict) -> Dict:
-    """Median, 10th and 90th percentile of the per-step durations (µs) and their GB/s."""
+    """Median, 10th and 90th percentile of the per-step durations (µs) and their GB/s,
+    from the block timed with an event after every step (each step's time includes its
+    event's marker packet; the mean latency comes from the block without them)."""
     v = np.asarray(r["per_step_us"], dtype=np.float64)
     p10, p50, p90 = (float(np.percentile(v, q)) for q in (10, 50, 90))
     gb = r["alg"]["step"] / 1e3
     return {"median_us": round(p50, 2), "p10_us": round(p10, 2), "p90_us": round(p90, 2),
-            "median_effective_gbs": round(gb / p50, 1), "steps": int(v.size)}
+            "median_effective_gbs": round(gb / p50, 1), "steps": int(v.size), "includes_step_events": True}
 
 
 def main(argv: Optional[List[str]] = None) -> int:
