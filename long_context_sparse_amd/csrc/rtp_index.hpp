@@ -24,7 +24,7 @@
 // Workspace: a header (layout key, sticky status bits, fallback count, a fault-injection
 // word for tests), then one region per (sequence, retrieval head) at a stride that
 // depends only on the blocks per sequence: the head's arrival counter and tag, its chunk
-// words and its block words.  Calls with other batch sizes or head counts reuse it; a
+// words, its block words and its chunks' heavy-block lists.  Calls with other batch sizes or head counts reuse it; a
 // call whose blocks per sequence differ from the layout the workspace was first used
 // with is refused on the device (every block selected, status bit set).
 //
@@ -57,6 +57,9 @@ constexpr int kBins = 256;                       // histogram bins per refinemen
 constexpr int kFinal = kWave;                    // candidates ranked directly (one per lane)
 constexpr int kBitWords = kIdxMaxBlocks / 32;    // words of a block bitmap
 constexpr int kMassBatch = 8;                    // block words a thread loads before using them
+constexpr int kListSlots = 8;                    // heavy blocks a chunk lists (e_j >= Z_c / 8)
+constexpr int kListWords = 1 + 2 * kListSlots;   // a chunk's list: its count, then (e_j, j) pairs
+constexpr int kListMaxChunks = 128;              // chunks per head that publish lists
 
 constexpr int kBitWordsPerLane = kBitWords / kWave;  // bitmap words a lane of one wave scans
 
@@ -70,6 +73,13 @@ struct TailSmem {
   uint64_t cab, thr;
   uint32_t lo, hi;
   int cnt, found, ncand, nfinal, total;
+  // the chunks' heavy-block lists: counts, fp32 Z_c, the bound on every unlisted block's
+  // mass (fp32 bits), the listed blocks, those gathered above the bound, a list
+  // overflowed or a wait ran out, the lists decided
+  int lcnt[kListMaxChunks];
+  float lz[kListMaxChunks];
+  uint32_t ubound;
+  int nlist, ngath, lbad, lok;
 };
 
 // LDS of the index role; the per-block masses (rows * T floats) and the candidate list
@@ -120,9 +130,10 @@ inline IndexGeom index_geom(int B, int n_ret, int max_ctx, int block, int T, int
 }
 
 // Index workspace layout (see the file comment): the header, then per head a 256-byte
-// state record (arrival counter, tag) followed by 2 words per chunk (M_c, Z_c) and one
-// word per block (e_j).  Chunks hold >= 8 blocks, so a head has at most
-// min(2048, ceil(nblk_max / 8)) chunks.
+// state record (arrival counter, tag) followed by 2 words per chunk (M_c, Z_c), one
+// word per block (e_j) and, for the first 128 chunks, a list of kListWords words (the
+// count of blocks with e_j >= Z_c / 8, then up to 8 (e_j, j) pairs).  Chunks hold >= 8
+// blocks, so a head has at most min(2048, ceil(nblk_max / 8)) chunks.
 struct IndexWsHeader {
   uint32_t layout;     // blocks per sequence of the calls this workspace serves (0: fresh)
   uint32_t status;     // sticky error bits (RTP_INDEX_WAIT_EXPIRED, RTP_INDEX_LAYOUT_MISMATCH)
@@ -140,8 +151,14 @@ __host__ __device__ inline int index_chunk_cap(int nblk_max) {
   const int c = (nblk_max + 7) / 8;
   return c < kIdxMaxChunks ? c : kIdxMaxChunks;
 }
+__host__ __device__ inline int index_list_cap(int nblk_max) {
+  const int c = index_chunk_cap(nblk_max);
+  return c < kListMaxChunks ? c : kListMaxChunks;
+}
 __host__ __device__ inline size_t index_head_stride(int nblk_max) {
-  return align_up(kIdxHeadStateBytes + (size_t)index_chunk_cap(nblk_max) * 16 + (size_t)nblk_max * 8, 256);
+  return align_up(kIdxHeadStateBytes + (size_t)index_chunk_cap(nblk_max) * 16 + (size_t)nblk_max * 8 +
+                      (size_t)index_list_cap(nblk_max) * kListWords * 8,
+                  256);
 }
 
 // Global buffers and sizes of the index role.
@@ -169,6 +186,15 @@ __device__ __forceinline__ uint64_t* head_chunk_words(const IndexArgs& a, size_t
 }
 __device__ __forceinline__ uint64_t* head_block_words(const IndexArgs& a, size_t head) {
   return head_chunk_words(a, head) + 2 * (size_t)a.n_chunk_cap;
+}
+__device__ __forceinline__ uint64_t* head_list_words(const IndexArgs& a, size_t head) {
+  return head_block_words(a, head) + (size_t)a.nblk_max;
+}
+// Whether a head's chunks publish heavy-block lists and its selection tries them first:
+// top-p, at most kListMaxChunks chunks, and more than two rows of blocks a thread (below
+// that the full mass pass is short and the lists do not repay their words).
+__device__ __forceinline__ bool index_lists(const IndexArgs& a, int nblk, int nch, int T) {
+  return a.topk_blocks == 0 && nch <= kListMaxChunks && nblk > 2 * T;
 }
 
 // ------------------------------------------------------------------ selection helpers
@@ -549,16 +575,39 @@ __device__ __forceinline__ bool index_chunk(const IndexArgs& a, int c, int r, in
     }
     const double mc = wave_max(xm);
     double zl = 0.0;
+    float ev[PL];  // -1: no block
 #pragma unroll
     for (int q = 0; q < PL; ++q) {
       const int k = lane + kWave * q;
+      ev[q] = -1.0f;
       if (k < nb) {
         const float e = (float)(S->sum[k] * (double)fast_exp2((float)((x[q] - mc) * kLog2e)));
         st_dev(e_io + j0 + k, tagged_f32(e, tag));
         zl += (double)e;
+        ev[q] = e;
       }
     }
     const double zc = wave_sum(zl);
+    // the chunk's heavy blocks (e_j >= Z_c / 8 in fp32, so at most 8 unless Z_c is
+    // degenerate), ascending, and their count; the selection may decide from these lists
+    // alone (index_select)
+    if (index_lists(a, nblk, nch, T)) {
+      uint64_t* lw = head_list_words(a, head) + (size_t)c * kListWords;
+      const float lim = (float)zc * 0.125f;
+      int n = 0;
+#pragma unroll
+      for (int q = 0; q < PL; ++q) {
+        const bool hv = ev[q] >= lim;
+        const uint64_t bal = __ballot(hv);
+        const int pos = n + (int)__popcll(bal & lanemask_lt());
+        if (hv && pos < kListSlots) {
+          st_dev(lw + 1 + 2 * pos, tagged_f32(ev[q], tag));
+          st_dev(lw + 2 + 2 * pos, tagged_f32(__uint_as_float((uint32_t)(j0 + lane + kWave * q)), tag));
+        }
+        n += (int)__popcll(bal);
+      }
+      if (lane == 0) st_dev(lw, tagged_f32(__uint_as_float((uint32_t)n), tag));
+    }
     if (lane == 0) {
       // M_c is the largest of fp32 block maxima, so fp32 holds it exactly
       uint64_t* cs = head_chunk_words(a, head) + 2 * c;
@@ -612,6 +661,20 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int b, 
     const int j = u * T + tid;
     w[u] = (u < rows && j < nblk) ? ld_dev(e_io + j) : 0ull;
   }
+  // with lists (index_lists): the chunks' heavy-block lists too (thread tid: chunk tid's
+  // count; chunk tid / 8's entry tid % 8)
+  static_assert(T >= kListMaxChunks * kListSlots, "one list entry a thread");
+  const bool lists = index_lists(a, nblk, nch, T);  // uniform
+  const uint64_t* lw = head_list_words(a, head);
+  const int lc = tid / kListSlots, ls = tid % kListSlots;
+  uint64_t lcw = 0, lvw = 0, liw = 0;
+  if (lists) {
+    if (tid < nch) lcw = ld_dev(lw + (size_t)tid * kListWords);
+    if (lc < nch) {
+      lvw = ld_dev(lw + (size_t)lc * kListWords + 1 + 2 * ls);
+      liw = ld_dev(lw + (size_t)lc * kListWords + 2 + 2 * ls);
+    }
+  }
   if (tid < kBins) {
     sm.bmass[tid] = 0;
     sm.bcnt[tid] = 0;
@@ -624,6 +687,11 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int b, 
     sm.found = 0;
     sm.ncand = 0;
     sm.nfinal = 0;
+    sm.ubound = 0u;
+    sm.nlist = 0;
+    sm.ngath = 0;
+    sm.lbad = 0;
+    sm.lok = 0;
   }
 #pragma unroll
   for (int k = 0; k < CW; ++k) {
@@ -632,6 +700,10 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int b, 
       S->cm[i] = untag_f32(settle(cs + 2 * i, x[k], tag, budget, ok));
       S->cz[i] = untag_f32(settle(cs + 2 * i + 1, z[k], tag, budget, ok));
     }
+  }
+  if (lists && tid < nch) {
+    sm.lcnt[tid] = (int)__float_as_uint(untag_f32(settle(lw + (size_t)tid * kListWords, lcw, tag, budget, ok)));
+    sm.lz[tid] = S->cz[tid];
   }
   // static top-k keeps topk_blocks blocks: the same search with every block weighing 1
   // and P = the number of blocks
@@ -649,8 +721,19 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int b, 
   const uint32_t lo1 = lbits & ~((1u << shift1) - 1u);
   bool failed = __syncthreads_or(!ok) != 0;  // uniform
 
+  // the listed entries this call wrote (slots below their chunk's count), by the threads
+  // that hold them; a wait that runs out only rules the lists out here (the full pass
+  // below reports it)
+  const bool lv = lists && !failed && lc < nch && ls < min(sm.lcnt[lc], kListSlots);
+  if (lv) {
+    lvw = settle(lw + (size_t)lc * kListWords + 1 + 2 * ls, lvw, tag, budget, ok);
+    liw = settle(lw + (size_t)lc * kListWords + 2 + 2 * ls, liw, tag, budget, ok);
+    if (!ok) sm.lbad = 1;
+  }
+
   // ---- wave 0: M = max_c M_c (an fp32 value), Z = sum_c Z_c exp(M_c - M); the chunk
-  // factors exp(M_c - M) / Z (fp32) replace the chunk words
+  // factors f_c = exp(M_c - M) / Z (fp32) replace the chunk words.  With lists: the
+  // number of listed blocks and U, the largest fl(fl(Z_c / 8) f_c) (see below)
   if (!failed && wave == 0) {
     float mloc = -INFINITY;
     for (int i = lane; i < nch; i += kWave) mloc = fmaxf(mloc, S->cm[i]);
@@ -663,14 +746,96 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int b, 
       S->cz[i] = (float)e;  // kept until Z is known
     }
     const double invZ = 1.0 / wave_sum(zloc);
-    for (int i = lane; i < nch; i += kWave) S->cm[i] = (float)((double)S->cz[i] * invZ);
+    float bl = 0.0f, nl = 0.0f;
+    for (int i = lane; i < nch; i += kWave) {
+      const float f = (float)((double)S->cz[i] * invZ);
+      S->cm[i] = f;
+      if (lists) {
+        const int n = sm.lcnt[i];
+        if (n > kListSlots) sm.lbad = 1;
+        nl += (float)n;
+        bl = fmaxf(bl, (sm.lz[i] * 0.125f) * f);
+      }
+    }
+    if (lists) {
+      bl = wave_maxf(bl);
+      nl = wave_sumf(nl);  // at most 256 a chunk over <= 128 chunks: exact in fp32
+      if (lane == 0) {
+        sm.ubound = __float_as_uint(bl);
+        sm.nlist = (int)nl;
+      }
+    }
   }
   __syncthreads();
+
+
+  // ---- the lists alone decide when they can.  A block chunk c did not list has e_j <
+  // Z_c / 8, so its mass m_j = e_j f_c is at most fl(fl(Z_c / 8) f_c) (rounding is
+  // monotone).  With U the largest such bound over the chunks, every block of mass above
+  // U is listed; if those blocks reach P in the greedy order (descending key, fixed-point
+  // sums as below), every other block ranks after the crossing one, so their prefix is
+  // the head's exact selection: their holders gather them, wave 0 ranks them.  Otherwise (nothing
+  // listed, a list overflowed, a wait ran out, more than kFinal blocks above U, or their
+  // mass short of P) the full pass below decides.
+  bool decided = false;
+  if (lists && pick && !failed && sm.nlist > 0) {  // uniform
+    const uint64_t P = (uint64_t)ceil(ldexp((double)p, 62));  // top-p (lists are never used by top-k)
+    const float m = lv ? untag_f32(lvw) * S->cm[lc] : 0.0f;
+    const bool g = lv && __float_as_uint(m) > sm.ubound;
+    const uint64_t bal = __ballot(g);
+    if (bal) {  // uniform
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&sm.ngath, (int)__popcll(bal));
+      base = __builtin_amdgcn_readfirstlane(base);
+      const int slot = base + (int)__popcll(bal & lanemask_lt());
+      if (g && slot < kFinal) {
+        sm.fkey[slot] = key_of(m, (int)__float_as_uint(untag_f32(liw)));
+        sm.fw[slot] = fixed_bits(__float_as_uint(m));
+      }
+    }
+    __syncthreads();
+    if (wave == 0 && !sm.lbad && sm.ngath <= kFinal) {
+      const int kept = sm.ngath;
+      const bool v = lane < kept;
+      const uint64_t my = v ? sm.fkey[lane] : 0ull;
+      const uint64_t f = v ? sm.fw[lane] : 0ull;
+      uint64_t above = 0;
+      for (int i = 0; i < kept; ++i) {
+        const uint64_t ki = readlane_u64(my, i), fi = readlane_u64(f, i);
+        above += ki > my ? fi : 0ull;
+      }
+      const uint64_t cb = __ballot(v && above < P && above + f >= P);
+      if (cb) {  // every kept block lies above U, the crossing one too
+        const uint64_t t = readlane_u64(my, __ffsll((long long)cb) - 1);
+        const bool sl = v && my >= t;
+        const uint64_t sb = __ballot(sl);
+        const int j = (int)(0xFFFFFFFFu - (uint32_t)my);
+        int rank = 0;  // selected ids below this one
+        for (uint64_t q = sb; q; q &= q - 1) rank += __builtin_amdgcn_readlane(j, __ffsll((long long)q) - 1) < j;
+        if (sl) {
+          a.sel_idx[head * a.nblk_max + rank] = j;
+          atomicOr(&sm.sel[j >> 5], 1u << (j & 31));
+        }
+        if (lane == 0) {
+          sm.total = (int)__popcll(sb);
+          sm.lok = 1;
+        }
+      }
+    }
+    __syncthreads();
+    if (sm.lok) {
+      decided = true;
+      if (a.sel_mask) {
+        uint8_t* m8 = a.sel_mask + head * a.nblk_max;
+        for (int j = tid; j < nblk; j += T) m8[j] = (sm.sel[j >> 5] >> (j & 31)) & 1u;
+      }
+    }
+  }
 
   // ---- every thread: m_j = e_j exp(M_c - M) / Z into LDS; the same pass gathers the
   // candidates (blocks at or above the floor) and builds the first threshold level over
   // them: bin = (bits - lo1) >> shift1, the top bin also takes any larger
-  if (!failed) {
+  if (!failed && !decided) {
     const int cshift = __ffs(a.chunk_blocks) - 1;
     const float* fch = S->cm;
     for (int i0 = 0; i0 < rows; i0 += kMassBatch) {
@@ -720,9 +885,10 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int b, 
   const uint64_t P = count ? (uint64_t)kb : (uint64_t)ceil(ldexp((double)p, 62));
   const int ncand = sm.ncand;  // written before the last barrier: uniform
   uint64_t thr = 0;
-  bool all = true;
-  int nsel = 0;  // selected blocks (read by thread 0)
-  if (pick && !failed && ncand <= kFinal) {
+  bool all = !decided;
+  int nsel = decided ? sm.total : 0;  // selected blocks (read by thread 0)
+  if (decided) {
+  } else if (pick && !failed && ncand <= kFinal) {
     // few candidates (the usual case): wave 0 ranks them exactly, one a lane (the mass of
     // the larger keys decides, as in the last level of the general search), writes the
     // selected ids in ascending order and their count, and leaves the threshold for the
@@ -832,7 +998,7 @@ __device__ __forceinline__ void index_advance_tag(const IndexArgs& a, size_t hea
   const uint32_t nt = next_tag(tag);
   if (nt == 1u) {
     uint64_t* w = head_chunk_words(a, head);
-    const int n = 2 * a.n_chunk_cap + a.nblk_max;
+    const int n = 2 * a.n_chunk_cap + a.nblk_max + index_list_cap(a.nblk_max) * kListWords;
     for (int i = threadIdx.x; i < n; i += T) st_dev(w + i, 0ull);
   }
   if (threadIdx.x == 0)
