@@ -768,18 +768,17 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int b, 
   }
   __syncthreads();
 
-
   // ---- the lists alone decide when they can.  A block chunk c did not list has e_j <
   // Z_c / 8, so its mass m_j = e_j f_c is at most fl(fl(Z_c / 8) f_c) (rounding is
   // monotone).  With U the largest such bound over the chunks, every block of mass above
   // U is listed; if those blocks reach P in the greedy order (descending key, fixed-point
   // sums as below), every other block ranks after the crossing one, so their prefix is
-  // the head's exact selection: their holders gather them, wave 0 ranks them.  Otherwise (nothing
-  // listed, a list overflowed, a wait ran out, more than kFinal blocks above U, or their
-  // mass short of P) the full pass below decides.
+  // the head's exact selection: their holders gather them, wave 0 ranks them.
+  // Otherwise (nothing listed, a list overflowed, a wait ran out, more than kFinal
+  // blocks above U, or their mass short of P) the full pass below decides.
   bool decided = false;
   if (lists && pick && !failed && sm.nlist > 0) {  // uniform
-    const uint64_t P = (uint64_t)ceil(ldexp((double)p, 62));  // top-p (lists are never used by top-k)
+    const uint64_t P = (uint64_t)ceil(ldexp((double)p, 62));  // top-p: top-k never uses lists
     const float m = lv ? untag_f32(lvw) * S->cm[lc] : 0.0f;
     const bool g = lv && __float_as_uint(m) > sm.ubound;
     const uint64_t bal = __ballot(g);
