@@ -123,9 +123,17 @@ def _hip_lib() -> ctypes.CDLL:
     return _hip
 
 
-def event_create() -> int:
+# Flags of the events that order the step's two streams on one device: no timing
+# (hipEventDisableTiming) and no system-scope fence at the record
+# (hipEventDisableSystemFence), which only the host or other devices would need; the
+# producer's writes stay visible to the other stream's kernels on the same device.
+EVENT_DEVICE_ORDER = 0x2 | 0x20000000
+
+
+def event_create(flags: int = 0x2) -> int:
+    """A HIP event (default: hipEventDisableTiming)."""
     ev = ctypes.c_void_p()
-    st = _hip_lib().hipEventCreateWithFlags(ctypes.byref(ev), 0x2)  # hipEventDisableTiming
+    st = _hip_lib().hipEventCreateWithFlags(ctypes.byref(ev), flags)
     if st != 0:
         raise RuntimeError(f"hipEventCreateWithFlags failed ({st})")
     return ev.value

@@ -83,8 +83,8 @@ class DecodeStep:
         self.ws_local = torch.zeros(max(ws2, 256), dtype=torch.uint8, device=dev)
         self.overlap = overlap and s.n_loc > 0 and s.n_ret > 0
         self.side = torch.cuda.Stream(device=dev) if self.overlap else None
-        self._fork = abi.event_create() if self.overlap else None
-        self._join = abi.event_create() if self.overlap else None
+        self._fork = abi.event_create(abi.EVENT_DEVICE_ORDER) if self.overlap else None
+        self._join = abi.event_create(abi.EVENT_DEVICE_ORDER) if self.overlap else None
         self._key = None
         self._vals = None
         self._step_fn = abi.lib().rtp_decode_step

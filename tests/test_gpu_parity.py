@@ -289,3 +289,31 @@ def test_step_matches_the_four_calls(n_ret, window, overlap):
         assert torch.equal(calls.sel_cnt.cpu(), torch.from_numpy(step.sel_cnt))
         check_selection(step)
     check_outputs(step)
+
+
+def test_two_stream_step_tracks_changing_queries():
+    """The step with the local heads on the second stream (ordered by the fork and join
+    events) against the one-stream step, over 8 back-to-back steps whose queries change
+    on the device before each one: outputs bit-identical and the same block sets at every
+    step.  A join that let the merge read the previous step's local partials, or a fork
+    that let the local heads read the previous queries, would show as a difference,
+    since consecutive steps no longer share their inputs."""
+    cfg = W.custom_config(name="fork_loop", B=2, Hkv=8, Hq=32, n_ret=3, ctx=(20000, 9001), block=64,
+                          window=8192, sinks=4, split_tokens=1024, kind="peaked_diffuse")
+    inp = W.make_inputs(cfg)
+    t = W.to_device(inp)
+    two = Run(inp, tensors=t, tag="fork_loop two streams", overlap=True)
+    assert two.step.overlap and two.step.side is not None
+    one = DecodeStep(two.step.s, overlap=False)
+    gen = torch.Generator(device=t["q"].device).manual_seed(11)
+    for i in range(8):
+        # new queries for every head (the index and the attention read the same rows)
+        qn = torch.randn(t["q"].shape, device=t["q"].device, generator=gen).to(torch.bfloat16)
+        t["q"].copy_(qn)
+        a = two.step(t).clone()
+        b = one(t).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), f"step {i}: outputs differ between the two-stream and one-stream steps"
+        assert torch.equal(two.step.sel_cnt, one.sel_cnt), f"step {i}: block counts differ"
+        assert torch.equal(two.step.sel_idx, one.sel_idx), f"step {i}: block lists differ"
+    say("      8 steps with changing queries: two-stream and one-stream steps bit-identical")
