@@ -655,16 +655,17 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int b, 
     x[k] = i < nch ? ld_dev(cs + 2 * i) : 0ull;
     z[k] = i < nch ? ld_dev(cs + 2 * i + 1) : 0ull;
   }
+  // with lists (index_lists): the chunks' heavy-block lists instead of the first block
+  // words, which only the full pass needs (thread tid: chunk tid's count; chunk tid / 8's
+  // entry tid % 8)
+  static_assert(T >= kListMaxChunks * kListSlots, "one list entry a thread");
+  const bool lists = index_lists(a, nblk, nch, T);  // uniform
   uint64_t w[kMassBatch];
 #pragma unroll
   for (int u = 0; u < kMassBatch; ++u) {
     const int j = u * T + tid;
-    w[u] = (u < rows && j < nblk) ? ld_dev(e_io + j) : 0ull;
+    w[u] = (!lists && u < rows && j < nblk) ? ld_dev(e_io + j) : 0ull;
   }
-  // with lists (index_lists): the chunks' heavy-block lists too (thread tid: chunk tid's
-  // count; chunk tid / 8's entry tid % 8)
-  static_assert(T >= kListMaxChunks * kListSlots, "one list entry a thread");
-  const bool lists = index_lists(a, nblk, nch, T);  // uniform
   const uint64_t* lw = head_list_words(a, head);
   const int lc = tid / kListSlots, ls = tid % kListSlots;
   uint64_t lcw = 0, lvw = 0, liw = 0;
@@ -838,7 +839,7 @@ __device__ __forceinline__ void index_select(const IndexArgs& a, int BK, int b, 
     const int cshift = __ffs(a.chunk_blocks) - 1;
     const float* fch = S->cm;
     for (int i0 = 0; i0 < rows; i0 += kMassBatch) {
-      if (i0 > 0) {
+      if (i0 > 0 || lists) {
 #pragma unroll
         for (int u = 0; u < kMassBatch; ++u) {
           const int j = (i0 + u) * T + tid;
